@@ -1,0 +1,299 @@
+"""Plain, slow, float64 CPU oracle of the TurboQuant quantize / inner-product path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It shares no code,
+table or constant with the HIP library (``kv_cache_embedding_amd``) and imports nothing
+from it; the two meet only in the seeded input arrays of ``workloads``.
+
+Sources (web pages; cited by short name and the passage on the page):
+  [review]    TurboQuant paper review, quant_prune_distill channel (tgviewer.app, post 674)
+  [news]      "Google ускоряет LLM в 8 раз" (comuna.ru, post 6696)
+  [explainer] "TurboQuant: Redefining AI efficiency with extreme compression"
+              (RecSysChannel, tgstat.ru, post 256)
+  [tldr]      TurboQuant two-step TLDR, seeallochnaya channel (postsniper.ru, post 3476)
+
+The pages give the method in prose only.  Readings taken where they are silent:
+  * the codebook is Lloyd-Max for N(0, 1/d) (coordinates of a rotated unit vector are
+    "almost normal"), with L = 2**(b-1) levels for a total budget of b bits;
+  * a coordinate lying exactly on a threshold goes to the upper cell;
+  * the QJL matrix S is Gaussian N(0, 1) with m = d rows, separate from the rotation;
+  * the QJL scale is sqrt(pi/2)/m times the residual norm gamma (the value that makes the
+    estimate exactly unbiased: E|<s, r/|r|>| sign terms average sqrt(2/pi)|r|);
+  * sign(0) is +1 (z = [y >= 0]);
+  * vectors are normalised and their norm nu is stored next to gamma (no other constant);
+  * integer decisions (bucket index, sign bit) are taken in float32, the precision of the
+    GPU kernels: the pages fix none.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "gauss_cell_prob", "gauss_cell_mean", "lloyd_max_gaussian", "gaussian_distortion",
+    "codebook", "normalize_rotate", "bucketize", "residual", "qjl_signs", "quantize",
+    "pack_codes", "unpack_codes", "estimate_ip", "dequantize", "topk", "qjl_alpha",
+]
+
+_SQRT2 = math.sqrt(2.0)
+_INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+
+
+# ------------------------------------------------------------------------ codebook
+# [review, MSE paragraph]: after the random rotation an optimal scalar grid is fitted with
+# the Max-Lloyd algorithm for the target bit width.  [tldr, step 1]: the grid is a 1-D
+# k-means solved in advance for the known bell-shaped coordinate law, denser in the centre.
+# [explainer, step 1]: the optimal thresholds are computed once, ahead of time.
+
+def _phi(t: float) -> float:
+    if math.isinf(t):
+        return 0.0
+    return _INV_SQRT_2PI * math.exp(-0.5 * t * t)
+
+
+def gauss_cell_prob(a: float, b: float) -> float:
+    """P(a < X < b) for X ~ N(0, 1), written to keep tail cells accurate."""
+    if a >= 0.0:
+        return 0.5 * (math.erfc(a / _SQRT2) - math.erfc(b / _SQRT2))
+    if b <= 0.0:
+        return 0.5 * (math.erfc(-b / _SQRT2) - math.erfc(-a / _SQRT2))
+    return 0.5 * (math.erf(b / _SQRT2) - math.erf(a / _SQRT2))
+
+
+def gauss_cell_mean(a: float, b: float) -> float:
+    """E[X | a < X < b] for X ~ N(0, 1): (phi(a) - phi(b)) / P(a < X < b)."""
+    return (_phi(a) - _phi(b)) / gauss_cell_prob(a, b)
+
+
+def lloyd_max_gaussian(bits: int, tol: float = 1e-14, max_iter: int = 200000):
+    """Lloyd-Max quantizer for N(0, 1) with 2**bits levels.
+
+    Alternates the two optimality conditions until the centroids move by less than
+    ``tol``: every threshold is the midpoint of its two neighbouring centroids, and every
+    centroid is the mean of the density over its cell.  Starts from a symmetric grid, and
+    symmetrises the result exactly, so the middle threshold is exactly 0.0.
+
+    Returns (centroids[L] ascending, thresholds[L-1] ascending), in units of sigma = 1.
+    """
+    L = 1 << bits
+    c = [(-(L - 1) + 2.0 * i) / L * 2.0 for i in range(L)]
+    for _ in range(max_iter):
+        t = [0.5 * (c[i] + c[i + 1]) for i in range(L - 1)]
+        edges = [-math.inf] + t + [math.inf]
+        new_c = [gauss_cell_mean(edges[i], edges[i + 1]) for i in range(L)]
+        delta = max(abs(new_c[i] - c[i]) for i in range(L))
+        c = new_c
+        if delta < tol:
+            break
+    else:
+        raise RuntimeError("Lloyd-Max did not converge")
+    c = np.array(c, dtype=np.float64)
+    c = 0.5 * (c - c[::-1])                     # exact odd symmetry
+    t = 0.5 * (c[:-1] + c[1:])
+    return c, t
+
+
+def gaussian_distortion(centroids: np.ndarray, thresholds: np.ndarray) -> float:
+    """E[(X - Q(X))^2] for X ~ N(0, 1) under the given quantizer (sigma = 1 units)."""
+    edges = [-math.inf] + list(thresholds) + [math.inf]
+    total = 0.0
+    for i, c in enumerate(centroids):
+        a, b = edges[i], edges[i + 1]
+        p = gauss_cell_prob(a, b)
+        m1 = _phi(a) - _phi(b)                  # integral of x phi(x) over the cell
+        # integral of x^2 phi(x) = P + a phi(a) - b phi(b)   (with x phi(x) -> 0 at +-inf)
+        ea = 0.0 if math.isinf(a) else a * _phi(a)
+        eb = 0.0 if math.isinf(b) else b * _phi(b)
+        m2 = p + ea - eb
+        total += m2 - 2.0 * c * m1 + c * c * p
+    return total
+
+
+def codebook(bits_mse: int, d: int):
+    """Centroids and thresholds for a rotated coordinate of a unit vector in R^d.
+
+    [explainer, per-component reduction]: a coordinate of a random point of the unit
+    sphere is almost normal with variance 1/d, so the sigma = 1 grid is scaled by 1/sqrt(d).
+    """
+    c, t = lloyd_max_gaussian(bits_mse)
+    s = 1.0 / math.sqrt(d)
+    return c * s, t * s
+
+
+# ------------------------------------------------------------------------ quantizer
+
+def normalize_rotate(x: np.ndarray, Pi: np.ndarray):
+    """nu = |x|, x_n = x / nu and u = Pi x_n, row by row (float64).
+
+    [explainer, caveats]: the vectors must be normalised and multiplied by a random
+    matrix.  [review, MSE paragraph]: the matrix is random orthogonal (not Hadamard).
+    A zero vector gets nu = 0 and x_n = u = 0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    Pi = np.asarray(Pi, dtype=np.float64)
+    nu = np.sqrt(np.sum(x * x, axis=1))
+    safe = np.where(nu > 0.0, nu, 1.0)
+    xn = np.where((nu > 0.0)[:, None], x / safe[:, None], 0.0)
+    u = xn @ Pi.T
+    return nu, xn, u
+
+
+def bucketize(u: np.ndarray, thresholds: np.ndarray, decide_dtype=np.float32) -> np.ndarray:
+    """idx_t = number of thresholds tau_i with u_t >= tau_i.
+
+    [tldr, step 1] / [explainer, step 1]: each coordinate is rounded on its own against the
+    precomputed grid.  A value equal to a threshold goes to the upper cell.  The comparison
+    is made in ``decide_dtype`` (float32 by default, the kernels' precision).
+    """
+    uu = np.asarray(u).astype(decide_dtype)
+    tt = np.asarray(thresholds).astype(decide_dtype)
+    return np.sum(uu[..., None] >= tt, axis=-1).astype(np.int64)
+
+
+def residual(xn: np.ndarray, Pi: np.ndarray, chat: np.ndarray):
+    """r = x_n - Pi^T chat (original space) and gamma = |r|.
+
+    [tldr, step 2]: the residual is the difference between the original vector and its
+    compressed version.
+    """
+    Pi = np.asarray(Pi, dtype=np.float64)
+    r = xn - chat @ Pi
+    return r, np.sqrt(np.sum(r * r, axis=1))
+
+
+def qjl_signs(S: np.ndarray, r: np.ndarray, decide_dtype=np.float32):
+    """y = S r and z_i = [y_i >= 0] (1 bit per projected dimension).
+
+    [tldr, step 2]: the residual is multiplied by another random matrix and only the sign
+    of each result is kept.  [review, inner-product paragraph]: this is the 1-bit QJL stage.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    y = r @ S.T
+    z = (y.astype(decide_dtype) >= 0).astype(np.int64)
+    return y, z
+
+
+def quantize(x, Pi, S, centroids, thresholds):
+    """TurboQuant-prod encoding of each row of x: (b-1)-bit MSE code + 1-bit QJL of the residual.
+
+    [review, inner-product paragraph]: quantize with the MSE-optimal quantizer at one bit
+    less, then the 1-bit residual with QJL.  Returns a dict with idx [n][d], z [n][m],
+    nu [n], gamma [n] and, for diagnostics, u, y.
+    """
+    nu, xn, u = normalize_rotate(x, Pi)
+    idx = bucketize(u, thresholds)
+    chat = np.asarray(centroids, dtype=np.float64)[idx]
+    r, gamma = residual(xn, Pi, chat)
+    y, z = qjl_signs(S, r)
+    return {"idx": idx, "z": z, "nu": nu, "gamma": gamma, "u": u, "y": y}
+
+
+# ------------------------------------------------------------------- canonical layout
+# The pages fix no bit layout.  Layout used by this project: per vector, for each group w
+# of 32 consecutive coordinates, b consecutive little-endian uint32 words; word p < b-1
+# holds bit p of idx, word b-1 holds the QJL signs z; coordinate 32w + j is bit j.
+
+def pack_codes(idx: np.ndarray, z: np.ndarray, b: int) -> np.ndarray:
+    """Pack idx [n][d] (values < 2**(b-1)) and z [n][d] into uint32 codes [n][d/32][b]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    z = np.asarray(z, dtype=np.int64)
+    n, d = idx.shape
+    assert d % 32 == 0 and z.shape == (n, d)
+    planes = [(idx >> p) & 1 for p in range(b - 1)] + [z & 1]
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    out = np.empty((n, d // 32, b), dtype=np.uint32)
+    for p, bits in enumerate(planes):
+        grouped = bits.reshape(n, d // 32, 32).astype(np.uint64)
+        out[:, :, p] = np.sum(grouped * weights, axis=-1).astype(np.uint32)
+    return out
+
+
+def unpack_codes(codes: np.ndarray, b: int):
+    """Inverse of pack_codes: uint32 [n][d/32][b] -> (idx [n][d], z [n][d])."""
+    codes = np.asarray(codes, dtype=np.uint32)
+    n, groups, bb = codes.shape
+    assert bb == b
+    shifts = np.arange(32, dtype=np.uint32)
+    bits = (codes[:, :, :, None] >> shifts) & 1          # [n][groups][b][32]
+    bits = bits.transpose(0, 2, 1, 3).reshape(n, b, groups * 32).astype(np.int64)
+    idx = np.zeros((n, groups * 32), dtype=np.int64)
+    for p in range(b - 1):
+        idx |= bits[:, p] << p
+    return idx, bits[:, b - 1]
+
+
+# ------------------------------------------------------------------------ estimator
+
+def qjl_alpha(m: int) -> float:
+    """Scale of the QJL term: sqrt(pi/2) / m.
+
+    For s ~ N(0, I) and a unit vector rho, E[sign<s, rho> <s, q>] = sqrt(2/pi) <q, rho>, so
+    summing m rows and multiplying by gamma sqrt(pi/2)/m gives <q, r> in expectation.
+    """
+    return math.sqrt(math.pi / 2.0) / m
+
+
+def estimate_ip(q, Pi, S, idx, z, nu, gamma, centroids, mode: str = "prod") -> np.ndarray:
+    """Estimated inner products <q_a, x_k> for every query row a and key row k -> [nq][n].
+
+    [review, problem statement]: one vector of the pair (the key) is quantized, the other
+    (the query) is kept exact, and the inner-product estimate must be unbiased.
+    prod: nu * (<Pi q, chat> + sqrt(pi/2)/m * gamma * <S q, 2z - 1>)   (MSE + QJL)
+    mse : nu * <Pi q, chat>   (the MSE part alone; biased, [news, bias paragraph])
+    """
+    q = np.asarray(q, dtype=np.float64)
+    Pi = np.asarray(Pi, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    nu = np.asarray(nu, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    chat = np.asarray(centroids, dtype=np.float64)[np.asarray(idx)]
+    qh = q @ Pi.T
+    mse = qh @ chat.T
+    if mode == "mse":
+        return mse * nu[None, :]
+    if mode != "prod":
+        raise ValueError(mode)
+    sh = q @ S.T
+    sgn = 2.0 * np.asarray(z, dtype=np.float64) - 1.0
+    qjl = sh @ sgn.T
+    return nu[None, :] * (mse + qjl_alpha(S.shape[0]) * gamma[None, :] * qjl)
+
+
+def dequantize(Pi, S, idx, z, nu, gamma, centroids, mode: str = "prod") -> np.ndarray:
+    """Reconstruction x~ [n][d].
+
+    [review, QJL paragraph]: dequantization is the inverse rotation and a renormalisation.
+    prod: x~ = nu (Pi^T chat + sqrt(pi/2)/m * gamma * S^T (2z - 1));  mse: x~ = nu Pi^T chat.
+    """
+    Pi = np.asarray(Pi, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    nu = np.asarray(nu, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    chat = np.asarray(centroids, dtype=np.float64)[np.asarray(idx)]
+    xt = chat @ Pi
+    if mode == "prod":
+        sgn = 2.0 * np.asarray(z, dtype=np.float64) - 1.0
+        xt = xt + qjl_alpha(S.shape[0]) * gamma[:, None] * (sgn @ S)
+    elif mode != "mse":
+        raise ValueError(mode)
+    return nu[:, None] * xt
+
+
+def topk(scores: np.ndarray, k: int, index_offset: int = 0):
+    """The k largest scores of each row; equal scores are ordered by smaller index.
+
+    [news, vector-search paragraph]: search is a flat scan of estimated inner products.
+    Returns (indices [nq][k] int64, values [nq][k] float64).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    nq, n = scores.shape
+    k = min(k, n)
+    ids = np.empty((nq, k), dtype=np.int64)
+    vals = np.empty((nq, k), dtype=np.float64)
+    cols = np.arange(n)
+    for a in range(nq):
+        order = np.lexsort((cols, -scores[a]))[:k]
+        ids[a] = order + index_offset
+        vals[a] = scores[a, order]
+    return ids, vals
