@@ -1,0 +1,172 @@
+/*
+ * tq.h — C ABI of the MI355X (gfx950) TurboQuant quantize / inner-product library.
+ *
+ * TurboQuant encodes a vector x of dimension d with a budget of b bits per coordinate:
+ *   1. normalise and rotate by a random orthogonal matrix Pi:   u = Pi x / |x|
+ *      ([review, MSE paragraph]; [explainer, caveats]; [tldr, step 1])
+ *   2. quantize every coordinate of u on its own with a (b-1)-bit Lloyd-Max grid
+ *      precomputed for the near-normal law N(0, 1/d)
+ *      ([review, MSE paragraph]; [explainer, step 1]; [tldr, step 1])
+ *   3. take the residual (original minus reconstruction), multiply it by a second random
+ *      matrix S and keep one sign bit per row: the 1-bit QJL sketch
+ *      ([review, inner-product and QJL paragraphs]; [tldr, step 2])
+ *   4. estimate <q, x> for an unquantized query q without bias
+ *      ([review, problem statement]; [explainer, step 2]; [news, bias paragraph]).
+ * Page keys:
+ *   [review]    TurboQuant paper review, quant_prune_distill channel (tgviewer.app, post 674)
+ *   [news]      "Google ускоряет LLM в 8 раз" (comuna.ru, post 6696)
+ *   [explainer] "TurboQuant: Redefining AI efficiency with extreme compression"
+ *               (RecSysChannel, tgstat.ru, post 256)
+ *   [tldr]      TurboQuant two-step TLDR, seeallochnaya channel (postsniper.ru, post 3476)
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers (memory owned by the caller) unless marked HOST.
+ *     The library keeps no persistent allocation of its own.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream). Calls
+ *     enqueue work and return; none synchronizes the stream unless its comment says so.
+ *   - Return value: a tq_status. On any non-zero status except TQ_EHIP nothing was
+ *     enqueued. tq_last_error() gives a message for the calling thread. No C++ exception
+ *     crosses the ABI.
+ *   - Supported shapes: d % 64 == 0, 64 <= d <= 4096; b in {2, 3, 4} total bits
+ *     (b-1 bits of Lloyd-Max index + 1 QJL bit); m = d QJL rows. Individual calls may
+ *     narrow this (TQ_EUNSUPPORTED).
+ *   - n == 0 (or groups/T/nq == 0) is a no-op returning TQ_OK.
+ *   - NaN / Inf inputs give unspecified codes and estimates but never a fault.
+ *   - A zero vector gets nu = 0, its rotated coordinates are taken as 0, and every
+ *     estimate against it is 0.
+ *
+ * Canonical code layout (the pages fix none): codes[n][d/32][b] uint32. For vector v and
+ * coordinate group w (coordinates 32w .. 32w+31), word p < b-1 holds bit p of the
+ * Lloyd-Max index of each coordinate, word b-1 holds the QJL sign bits (1 = projection
+ * >= 0); coordinate 32w + j is bit j. nu[n] = |x|, gamma[n] = |residual of x/|x||, fp32.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* bad argument: shape, null pointer, codebook, enum value */
+  TQ_EUNSUPPORTED = 2,  /* valid by the method but not implemented for this shape */
+  TQ_EHIP = 3,          /* a HIP launch or copy failed; the stream may hold earlier work */
+  TQ_EWORKSPACE = 4     /* workspace smaller than the matching *_ws_bytes() helper */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+typedef enum {
+  TQ_EST_PROD = 0,  /* MSE part + QJL correction: unbiased ([review, inner-product paragraph]) */
+  TQ_EST_MSE = 1    /* MSE part alone: biased ([news, bias paragraph]) */
+} tq_mode;
+
+/*
+ * tq_codebook_build — HOST only, float64. Lloyd-Max quantizer with L = 2^bits_mse levels for
+ * a coordinate distributed N(0, 1/d) ([review, MSE paragraph]: Max-Lloyd grid for the target
+ * bit width; [tldr, step 1]: 1-D k-means solved in advance, denser at the centre).
+ * Alternates "threshold = midpoint of neighbouring centroids" and "centroid = mean of its
+ * cell" to a fixed point (|change| < 1e-14 in sigma units), symmetrised exactly.
+ *   bits_mse   1..8
+ *   d          dimension (sets sigma = 1/sqrt(d)); > 0
+ *   centroids  HOST out [L], ascending
+ *   thresholds HOST out [L-1], ascending, thresholds[i] = (c[i] + c[i+1]) / 2, middle one 0
+ * Errors: TQ_EINVAL for bits_mse or d out of range or NULL outputs.
+ */
+int tq_codebook_build(int bits_mse, int d, double* centroids, double* thresholds);
+
+/* Size in bytes of the device parameter block that tq_prepare fills for (d, b). 0 if invalid. */
+size_t tq_params_bytes(int d, int b);
+
+/*
+ * tq_prepare — fills the device parameter block used by every other call.
+ *   Pi          HOST in [d][d] float32, orthogonal ([review, MSE paragraph]: random orthogonal,
+ *               not Hadamard); u = Pi x uses Pi's rows.
+ *   S           HOST in [d][d] float32, the QJL matrix (m = d rows, [tldr, step 2]).
+ *   centroids   HOST in [2^(b-1)] float64 ascending, odd-symmetric (c[i] = -c[L-1-i]),
+ *               in the units of u (as returned by tq_codebook_build(b-1, d)).
+ *   thresholds  HOST in [2^(b-1)-1] float64 ascending, interleaving the centroids.
+ *   params      DEVICE out, tq_params_bytes(d, b) bytes, 256-byte aligned.
+ * Works on the host in float64 (S' = S Pi^T, operand splits and layouts), then copies to
+ * `params` on `stream` and WAITS for that copy (this call synchronizes `stream`).
+ * Errors: TQ_EINVAL (shape, NULL, unsorted or asymmetric codebook, misaligned params),
+ * TQ_EHIP (copy failed).
+ */
+int tq_prepare(int d, int b, const float* Pi, const float* S, const double* centroids,
+               const double* thresholds, void* params, void* stream);
+
+/*
+ * tq_quantize — encodes n vectors ([review, inner-product paragraph]; [tldr, steps 1-2]).
+ *   params   from tq_prepare(d, b, ...)
+ *   x        [n][d] float32 (x_dtype TQ_F32) or bfloat16 (TQ_BF16), row-major, 16-byte aligned
+ *   codes    out [n][d/32][b] uint32 (canonical layout above)
+ *   nu       out [n] float32, |x|
+ *   gamma    out [n] float32, norm of the residual of x/|x| after the Lloyd-Max stage
+ * Integer decisions (index, sign) are taken in float32 against float32 thresholds.
+ * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EUNSUPPORTED (d other than 128 for
+ * now), TQ_EHIP.
+ */
+int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
+                uint32_t* codes, float* nu, float* gamma, void* stream);
+
+/*
+ * tq_dequantize — reconstruction ([review, QJL paragraph]: inverse rotation and
+ * renormalisation).
+ *   TQ_EST_PROD: xhat = nu (Pi^T chat + sqrt(pi/2)/m * gamma * S^T (2z - 1))
+ *   TQ_EST_MSE : xhat = nu Pi^T chat
+ *   codes/nu/gamma as written by tq_quantize; xhat out [n][d] float32.
+ * Errors: TQ_EINVAL, TQ_EHIP.
+ */
+int tq_dequantize(const void* params, int d, int b, const uint32_t* codes, const float* nu,
+                  const float* gamma, int64_t n, int mode, float* xhat, void* stream);
+
+/* Workspace bytes needed by tq_score_ip for these sizes. */
+size_t tq_score_ws_bytes(int d, int b, int64_t groups, int64_t G, int64_t T);
+
+/*
+ * tq_score_ip — attention logits over a quantized key cache: for every group g (a KV head
+ * of one sequence), each of its G query heads and each of its T keys
+ *   logits[g][h][t] = nu_k (<Pi q, chat_k> + sqrt(pi/2)/m * gamma_k * <S q, 2 z_k - 1>)
+ * (TQ_EST_MSE drops the second term). The raw inner product, no softmax scale
+ * ([review, problem statement]: one side quantized, unbiased; [news, 8x logit paragraph]).
+ *   q        [groups][G][d] float32 or bfloat16 (q_dtype), unquantized
+ *   codes    [groups][T][d/32][b] uint32; nu, gamma [groups][T] float32
+ *   logits   out [groups][G][T] float32
+ *   ws       workspace of at least tq_score_ws_bytes(d, b, groups, G, T) bytes, 256-aligned;
+ *            its contents are scratch (overwritten by this call)
+ * Errors: TQ_EINVAL, TQ_EUNSUPPORTED (d != 128 or G not a multiple of 4 for now),
+ *         TQ_EWORKSPACE, TQ_EHIP.
+ */
+int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
+                const uint32_t* codes, const float* nu, const float* gamma, int64_t groups,
+                int64_t G, int64_t T, int mode, float* logits, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Workspace bytes needed by tq_topk for these sizes. */
+size_t tq_topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k);
+
+/*
+ * tq_topk — flat-scan vector search ([news, vector-search paragraph]: no index to build):
+ * for each of nq queries, the k keys with the largest estimated inner product (same
+ * estimator as tq_score_ip, mode TQ_EST_PROD or TQ_EST_MSE), sorted by decreasing score,
+ * equal scores by increasing key index.
+ *   q       [nq][d] float32 or bfloat16; codes [n][d/32][b]; nu, gamma [n]
+ *   idx     out [nq][k] int32 key indices;  score out [nq][k] float32
+ *   1 <= k <= 1024, k <= n; n < 2^31.
+ * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EWORKSPACE, TQ_EHIP.
+ */
+int tq_topk(const void* params, int d, int b, const void* q, int q_dtype, int64_t nq,
+            const uint32_t* codes, const float* nu, const float* gamma, int64_t n, int k,
+            int mode, int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/* Message describing the last non-OK status returned on the calling thread ("" if none). */
+const char* tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H_ */

@@ -1,0 +1,224 @@
+"""ctypes marshalling for libtq.so: tensors -> (pointer, size) and torch's current stream."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_EWORKSPACE = 0, 1, 2, 3, 4
+TQ_F32, TQ_BF16 = 0, 1
+TQ_EST_PROD, TQ_EST_MSE = 0, 1
+
+_STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_EUNSUPPORTED", 3: "TQ_EHIP", 4: "TQ_EWORKSPACE"}
+_LIB = None
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+
+
+def load_library():
+    """Load libtq.so (after torch, so both use torch's HIP runtime). Raises if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    import torch  # noqa: F401  (loads torch's libamdhip64 first)
+
+    lib = ctypes.CDLL(path)
+    P, I, I64, SZ, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+    sig = {
+        "tq_codebook_build": (I, [I, I, ctypes.POINTER(D), ctypes.POINTER(D)]),
+        "tq_params_bytes": (SZ, [I, I]),
+        "tq_prepare": (I, [I, I, P, P, P, P, P, P]),
+        "tq_quantize": (I, [P, I, I, P, I, I64, P, P, P, P]),
+        "tq_dequantize": (I, [P, I, I, P, P, P, I64, I, P, P]),
+        "tq_score_ws_bytes": (SZ, [I, I, I64, I64, I64]),
+        "tq_score_ip": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P, SZ, P]),
+        "tq_topk_ws_bytes": (SZ, [I, I, I64, I64, I]),
+        "tq_topk": (I, [P, I, I, P, I, I64, P, P, P, I64, I, I, P, P, P, SZ, P]),
+        "tq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def tq_last_error() -> str:
+    return load_library().tq_last_error().decode()
+
+
+def _check(status: int):
+    if status != TQ_OK:
+        raise TQError(status, tq_last_error())
+
+
+# ------------------------------------------------------------------------- helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _dev(t, name: str):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dtype_code(t, name: str) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t, name: str, numel: int, dtype):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------- C calls
+
+def tq_codebook_build(bits_mse: int, d: int):
+    """Host float64 Lloyd-Max codebook for N(0, 1/d): (centroids[L], thresholds[L-1])."""
+    L = 1 << bits_mse if 0 < bits_mse <= 8 else 2
+    c = np.zeros(L, dtype=np.float64)
+    t = np.zeros(max(L - 1, 1), dtype=np.float64)
+    _check(load_library().tq_codebook_build(
+        int(bits_mse), int(d), c.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+        t.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return c, t[:L - 1]
+
+
+def tq_params_bytes(d: int, b: int) -> int:
+    return int(load_library().tq_params_bytes(int(d), int(b)))
+
+
+def tq_prepare(d: int, b: int, Pi: np.ndarray, S: np.ndarray, centroids: np.ndarray,
+               thresholds: np.ndarray, params, stream=None):
+    """Fill the device parameter block `params` (uint8 tensor of tq_params_bytes(d, b))."""
+    torch = _torch()
+    Pi = np.ascontiguousarray(Pi, dtype=np.float32)
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    c = np.ascontiguousarray(centroids, dtype=np.float64)
+    t = np.ascontiguousarray(thresholds, dtype=np.float64)
+    if Pi.shape != (d, d) or S.shape != (d, d):
+        raise ValueError("Pi and S must be d x d")
+    if c.size != 1 << (b - 1) or t.size != (1 << (b - 1)) - 1:
+        raise ValueError("codebook size does not match b")
+    _dev(params, "params")
+    _need(params, "params", tq_params_bytes(d, b), torch.uint8)
+    _check(load_library().tq_prepare(int(d), int(b), Pi.ctypes.data, S.ctypes.data, c.ctypes.data,
+                                     t.ctypes.data, _ptr(params), _stream(stream, params.device)))
+
+
+def tq_quantize(params, d: int, b: int, x, codes, nu, gamma, stream=None):
+    """Encode x [n][d] (float32 or bfloat16) into codes [n][d/32][b] uint32, nu[n], gamma[n]."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError(f"x must be [n][{d}]")
+    n = x.shape[0]
+    for tname, t in (("codes", codes), ("nu", nu), ("gamma", gamma), ("params", params)):
+        _dev(t, tname)
+    _need(codes, "codes", n * (d // 32) * b, torch.int32)
+    _need(nu, "nu", n, torch.float32)
+    _need(gamma, "gamma", n, torch.float32)
+    _check(load_library().tq_quantize(_ptr(params), d, b, _ptr(x), _dtype_code(x, "x"), n,
+                                      _ptr(codes), _ptr(nu), _ptr(gamma),
+                                      _stream(stream, x.device)))
+
+
+def tq_dequantize(params, d: int, b: int, codes, nu, gamma, mode: int, xhat, stream=None):
+    """Reconstruct xhat [n][d] float32 from codes/nu/gamma (n = nu.numel())."""
+    torch = _torch()
+    for tname, t in (("codes", codes), ("nu", nu), ("gamma", gamma), ("xhat", xhat), ("params", params)):
+        _dev(t, tname)
+    n = nu.numel()
+    _need(codes, "codes", n * (d // 32) * b, torch.int32)
+    _need(gamma, "gamma", n, torch.float32)
+    _need(xhat, "xhat", n * d, torch.float32)
+    _check(load_library().tq_dequantize(_ptr(params), d, b, _ptr(codes), _ptr(nu), _ptr(gamma), n,
+                                        int(mode), _ptr(xhat), _stream(stream, nu.device)))
+
+
+def tq_score_ws_bytes(d: int, b: int, groups: int, G: int, T: int) -> int:
+    return int(load_library().tq_score_ws_bytes(d, b, groups, G, T))
+
+
+def tq_score_ip(params, d: int, b: int, q, codes, nu, gamma, groups: int, G: int, T: int,
+                mode: int, logits, ws, stream=None):
+    """logits[groups][G][T] = estimated <q, k> for q [groups][G][d], keys codes [groups][T]."""
+    torch = _torch()
+    for tname, t in (("q", q), ("codes", codes), ("nu", nu), ("gamma", gamma), ("logits", logits),
+                     ("ws", ws), ("params", params)):
+        _dev(t, tname)
+    if q.numel() < groups * G * d:
+        raise ValueError("q holds fewer than groups*G*d elements")
+    _need(codes, "codes", groups * T * (d // 32) * b, torch.int32)
+    _need(nu, "nu", groups * T, torch.float32)
+    _need(gamma, "gamma", groups * T, torch.float32)
+    _need(logits, "logits", groups * G * T, torch.float32)
+    _check(load_library().tq_score_ip(_ptr(params), d, b, _ptr(q), _dtype_code(q, "q"), _ptr(codes),
+                                      _ptr(nu), _ptr(gamma), groups, G, T, int(mode), _ptr(logits),
+                                      _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream, q.device)))
+
+
+def tq_topk_ws_bytes(d: int, b: int, nq: int, n: int, k: int) -> int:
+    return int(load_library().tq_topk_ws_bytes(d, b, nq, n, k))
+
+
+def tq_topk(params, d: int, b: int, q, codes, nu, gamma, n: int, k: int, mode: int, idx, score,
+            ws, stream=None):
+    """Top-k keys by estimated inner product for each query row of q [nq][d]."""
+    torch = _torch()
+    for tname, t in (("q", q), ("codes", codes), ("nu", nu), ("gamma", gamma), ("idx", idx),
+                     ("score", score), ("ws", ws), ("params", params)):
+        _dev(t, tname)
+    if q.dim() != 2 or q.shape[1] != d:
+        raise ValueError(f"q must be [nq][{d}]")
+    nq = q.shape[0]
+    _need(codes, "codes", n * (d // 32) * b, torch.int32)
+    _need(nu, "nu", n, torch.float32)
+    _need(gamma, "gamma", n, torch.float32)
+    _need(idx, "idx", nq * k, torch.int32)
+    _need(score, "score", nq * k, torch.float32)
+    _check(load_library().tq_topk(_ptr(params), d, b, _ptr(q), _dtype_code(q, "q"), nq, _ptr(codes),
+                                  _ptr(nu), _ptr(gamma), n, int(k), int(mode), _ptr(idx), _ptr(score),
+                                  _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream, q.device)))

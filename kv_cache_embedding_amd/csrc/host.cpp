@@ -1,0 +1,372 @@
+// Host side of the C ABI: argument validation, the float64 Lloyd-Max codebook, the
+// parameter block (operand splits and MFMA fragment layouts), and kernel dispatch.
+#include "tq.h"
+#include "tq_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() { return TQ_OK; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_shape(int d, int b) {
+  return d >= 64 && d <= 4096 && d % 64 == 0 && b >= 2 && b <= 4;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ------------------------------------------------------------------ Lloyd-Max (float64)
+// [review, MSE paragraph]: optimal grid by the Max-Lloyd algorithm; [tldr, step 1]: 1-D
+// k-means for the known bell-shaped law, solved once.  The quantizer of a symmetric law
+// is odd-symmetric, so only the positive half is iterated here: positive centroids
+// c_1 < ... < c_H (H = L/2) over cells [t_0 = 0, t_1), ..., [t_{H-1}, +inf), where
+// t_i = (c_i + c_{i+1}) / 2 and c_i = (phi(t_{i-1}) - phi(t_i)) / (Q(t_{i-1}) - Q(t_i)),
+// Q the upper tail of N(0, 1).  L = 2 has the closed form c_1 = phi(0)/Q(0) = sqrt(2/pi).
+
+double std_pdf(double t) { return std::isinf(t) ? 0.0 : std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI); }
+double std_upper_tail(double t) { return std::isinf(t) ? 0.0 : 0.5 * std::erfc(t / std::sqrt(2.0)); }
+
+bool lloyd_max_positive_half(int H, std::vector<double>& c) {
+  c.assign(H, 0.0);
+  for (int i = 0; i < H; ++i) c[i] = (i + 0.5) * 3.0 / H;   // any increasing start
+  std::vector<double> t(H + 1);
+  for (int it = 0; it < 1000000; ++it) {
+    t[0] = 0.0;
+    for (int i = 1; i < H; ++i) t[i] = 0.5 * (c[i - 1] + c[i]);
+    t[H] = INFINITY;
+    double delta = 0.0;
+    for (int i = 0; i < H; ++i) {
+      double num = std_pdf(t[i]) - std_pdf(t[i + 1]);
+      double den = std_upper_tail(t[i]) - std_upper_tail(t[i + 1]);
+      double nc = num / den;
+      delta = std::fmax(delta, std::fabs(nc - c[i]));
+      c[i] = nc;
+    }
+    if (delta < 1e-14) return true;
+  }
+  return false;
+}
+
+// ------------------------------------------------------------------ bf16 helpers (host)
+uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+float bf16_to_f32(uint16_t h) {
+  uint32_t u = uint32_t(h) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+void split_bf16(double v, uint16_t& hi, uint16_t& lo) {
+  hi = bf16_rne(float(v));
+  lo = bf16_rne(float(v - double(bf16_to_f32(hi))));
+}
+
+double dot(const double* a, const double* b, int n) {
+  double s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+  int i = 0;
+  for (; i + 4 <= n; i += 4) {
+    s0 += a[i] * b[i];
+    s1 += a[i + 1] * b[i + 1];
+    s2 += a[i + 2] * b[i + 2];
+    s3 += a[i + 3] * b[i + 3];
+  }
+  for (; i < n; ++i) s0 += a[i] * b[i];
+  return (s0 + s1) + (s2 + s3);
+}
+
+// Output-row permutation of a 32-row MFMA tile: row rho holds canonical coordinate
+// 16*((rho>>2)&1) + 4*(rho>>3) + (rho&3) of the tile, so that in the 32x32 accumulator
+// layout (row = 8*(r/4) + 4*(lane/32) + r%4) lane half h, register r holds coordinate
+// 16h + r.
+int row_coord(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
+
+// Fragments for the fused d = 128 quantize kernel (see quantize.hip for the data flow).
+//   Pi fragment [s][mt][pass][lane][e]: Pi[32mt + row_coord(lane%32)][64*(lane/32) + 8s + e]
+//   S' fragment [mt][s][pass][lane][e]: S'[32mt + row_coord(lane%32)]
+//                                          [32*(s>>1) + 16*(lane/32) + 8*(s&1) + e]
+// pass 0 = bf16 high part, pass 1 = bf16 low part (value - high, rounded).
+void build_quantize_fragments(const std::vector<double>& Pi, const std::vector<double>& Sp,
+                              uint16_t* out) {
+  const int D = 128;
+  uint16_t* pif = out;
+  uint16_t* spf = out + 64 * 1024 / 2;
+  for (int s = 0; s < 8; ++s)
+    for (int mt = 0; mt < 4; ++mt)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          int row = 32 * mt + row_coord(lane % 32);
+          int col = 64 * (lane / 32) + 8 * s + e;
+          uint16_t hi, lo;
+          split_bf16(Pi[size_t(row) * D + col], hi, lo);
+          size_t base = (size_t(s * 4 + mt) * 2) * 64 * 8;
+          pif[base + size_t(lane) * 8 + e] = hi;
+          pif[base + 64 * 8 + size_t(lane) * 8 + e] = lo;
+        }
+  for (int mt = 0; mt < 4; ++mt)
+    for (int s = 0; s < 8; ++s)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          int row = 32 * mt + row_coord(lane % 32);
+          int col = 32 * (s >> 1) + 16 * (lane / 32) + 8 * (s & 1) + e;
+          uint16_t hi, lo;
+          split_bf16(Sp[size_t(row) * D + col], hi, lo);
+          size_t base = (size_t(mt * 8 + s) * 2) * 64 * 8;
+          spf[base + size_t(lane) * 8 + e] = hi;
+          spf[base + 64 * 8 + size_t(lane) * 8 + e] = lo;
+        }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+int tq_codebook_build(int bits_mse, int d, double* centroids, double* thresholds) {
+  if (bits_mse < 1 || bits_mse > 8) return fail(TQ_EINVAL, "bits_mse=%d outside 1..8", bits_mse);
+  if (d <= 0) return fail(TQ_EINVAL, "d=%d must be positive", d);
+  if (!centroids || !thresholds) return fail(TQ_EINVAL, "NULL output pointer");
+  const int L = 1 << bits_mse, H = L / 2;
+  std::vector<double> c;
+  if (!lloyd_max_positive_half(H, c)) return fail(TQ_EINVAL, "Lloyd-Max did not converge");
+  const double sigma = 1.0 / std::sqrt(double(d));
+  for (int i = 0; i < H; ++i) {
+    centroids[H + i] = c[i] * sigma;
+    centroids[H - 1 - i] = -c[i] * sigma;
+  }
+  for (int i = 0; i < L - 1; ++i) thresholds[i] = 0.5 * (centroids[i] + centroids[i + 1]);
+  thresholds[H - 1] = 0.0;
+  return ok();
+}
+
+size_t tq_params_bytes(int d, int b) {
+  if (!valid_shape(d, b)) return 0;
+  return tq::Layout(d, b).total;
+}
+
+int tq_prepare(int d, int b, const float* Pi, const float* S, const double* centroids,
+               const double* thresholds, void* params, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (!Pi || !S || !centroids || !thresholds || !params) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256)) return fail(TQ_EINVAL, "params must be 256-byte aligned");
+  const int L = 1 << (b - 1);
+  double cmax = 0.0;
+  for (int i = 0; i < L; ++i) {
+    if (!std::isfinite(centroids[i])) return fail(TQ_EINVAL, "non-finite centroid");
+    cmax = std::fmax(cmax, std::fabs(centroids[i]));
+  }
+  for (int i = 0; i < L; ++i)
+    if (std::fabs(centroids[i] + centroids[L - 1 - i]) > 1e-12 * cmax)
+      return fail(TQ_EINVAL, "codebook is not odd-symmetric (centroid %d)", i);
+  for (int i = 0; i + 1 < L; ++i) {
+    if (!(centroids[i] < thresholds[i] && thresholds[i] < centroids[i + 1]))
+      return fail(TQ_EINVAL, "thresholds must interleave ascending centroids (index %d)", i);
+    if (std::fabs(thresholds[i] + thresholds[L - 2 - i]) > 1e-12 * cmax)
+      return fail(TQ_EINVAL, "thresholds are not odd-symmetric (index %d)", i);
+  }
+  const tq::Layout lay(d, b);
+  std::vector<unsigned char> blob(lay.total, 0);
+
+  // header
+  tq::Header h;
+  std::memset(&h, 0, sizeof(h));
+  h.magic = tq::kMagic;
+  h.d = d;
+  h.b = b;
+  h.L = L;
+  for (int i = 0; i < L - 1; ++i) h.thr[i] = float(thresholds[i]);
+  h.thr[L / 2 - 1] = 0.0f;
+  for (int i = 0; i < L; ++i) h.cen[i] = float(centroids[i]);
+  for (int k = 0; k + L / 2 < L - 1; ++k) h.tpos[k] = float(thresholds[L / 2 + k]);
+  for (int k = 0; k < L / 2; ++k) h.mpos[k] = float(centroids[L / 2 + k]);
+  // Walsh coefficients over the index bits: e_P = (1/L) sum_idx c_idx prod_{p in P} sigma_p.
+  const int B = b - 1;
+  auto walsh = [&](unsigned mask) {
+    double s = 0.0;
+    for (int idx = 0; idx < L; ++idx) {
+      double prod = 1.0;
+      for (int p = 0; p < B; ++p)
+        if (mask & (1u << p)) prod *= ((idx >> p) & 1) ? 1.0 : -1.0;
+      s += centroids[idx] * prod;
+    }
+    return s / L;
+  };
+  for (unsigned mask = 0; mask < (1u << B); ++mask) {
+    int deg = __builtin_popcount(mask);
+    if (deg % 2 == 0 && std::fabs(walsh(mask)) > 1e-12 * cmax)
+      return fail(TQ_EINVAL, "codebook has an even Walsh term (not odd-symmetric)");
+  }
+  unsigned order[4] = {1u, 2u, 4u, 7u};
+  h.ne = (B == 3) ? 4 : B;
+  h.esum = 0.0f;
+  h.emax = 0.0f;
+  for (int i = 0; i < h.ne; ++i) {
+    double e = walsh(order[i]);
+    h.e[i] = float(e);
+    h.esum += float(e);
+    h.emax = std::fmax(h.emax, std::fabs(float(e)));
+  }
+  h.alpha = float(std::sqrt(M_PI / 2.0) / d);
+  std::memcpy(blob.data() + lay.off_hdr, &h, sizeof(h));
+
+  // Pi and S in float32 (row-major), and float64 copies for host products
+  std::memcpy(blob.data() + lay.off_pi, Pi, size_t(d) * d * 4);
+  std::memcpy(blob.data() + lay.off_s, S, size_t(d) * d * 4);
+  std::vector<double> P64(size_t(d) * d), S64(size_t(d) * d);
+  for (size_t i = 0; i < P64.size(); ++i) {
+    P64[i] = Pi[i];
+    S64[i] = S[i];
+    if (!std::isfinite(P64[i]) || !std::isfinite(S64[i]))
+      return fail(TQ_EINVAL, "non-finite entry in Pi or S");
+  }
+  // Pi must be orthogonal: the kernels form the residual in the rotated space.
+  double worst = 0.0;
+  for (int i = 0; i < d; ++i)
+    for (int j = i; j < d; ++j) {
+      double g = dot(&P64[size_t(i) * d], &P64[size_t(j) * d], d) - (i == j ? 1.0 : 0.0);
+      worst = std::fmax(worst, std::fabs(g));
+    }
+  if (worst > 1e-4) return fail(TQ_EINVAL, "Pi is not orthogonal (max |Pi Pi^T - I| = %g)", worst);
+
+  if (lay.qfrag_bytes) {
+    // S' = S Pi^T, so that S r = S' (Pi r) for the residual r (rotated-space residual)
+    std::vector<double> Sp(size_t(d) * d);
+    for (int i = 0; i < d; ++i)
+      for (int k = 0; k < d; ++k) Sp[size_t(i) * d + k] = dot(&S64[size_t(i) * d], &P64[size_t(k) * d], d);
+    build_quantize_fragments(P64, Sp, reinterpret_cast<uint16_t*>(blob.data() + lay.off_qfrag));
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(params, blob.data(), lay.total, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "tq_prepare: copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "tq_prepare: synchronize");
+  return ok();
+}
+
+int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
+                uint32_t* codes, float* nu, float* gamma, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad x_dtype %d", x_dtype);
+  if (n < 0) return fail(TQ_EINVAL, "n=%lld < 0", (long long)n);
+  if (n == 0) return ok();
+  if (!params || !x || !codes || !nu || !gamma) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(nu, 4) ||
+      !aligned(gamma, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x and codes 16 B)");
+  if (d != 128) return fail(TQ_EUNSUPPORTED, "tq_quantize: only d=128 is implemented");
+  hipError_t e = tq::launch_quantize_d128(params, b, x, x_dtype, n, codes, nu, gamma,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize launch");
+  return ok();
+}
+
+int tq_dequantize(const void* params, int d, int b, const uint32_t* codes, const float* nu,
+                  const float* gamma, int64_t n, int mode, float* xhat, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (n < 0) return fail(TQ_EINVAL, "n=%lld < 0", (long long)n);
+  if (n == 0) return ok();
+  if (!params || !codes || !nu || !gamma || !xhat) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(codes, 4) || !aligned(xhat, 4))
+    return fail(TQ_EINVAL, "misaligned pointer");
+  hipError_t e = tq::launch_dequantize(params, d, b, codes, nu, gamma, n, mode, xhat,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_dequantize launch");
+  return ok();
+}
+
+size_t tq_score_ws_bytes(int d, int b, int64_t groups, int64_t G, int64_t T) {
+  (void)d;
+  (void)T;
+  if (b < 2 || b > 4 || groups < 0 || G < 0) return 0;
+  // one operand block per quad of query heads
+  return tq::align256(size_t(groups) * size_t((G + 3) / 4) * tq::score_ws_per_group(b));
+}
+
+int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
+                const uint32_t* codes, const float* nu, const float* gamma, int64_t groups,
+                int64_t G, int64_t T, int mode, float* logits, void* ws, size_t ws_bytes,
+                void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad q_dtype %d", q_dtype);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (groups < 0 || G < 0 || T < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0 || G == 0 || T == 0) return ok();
+  if (T >= (int64_t(1) << 31)) return fail(TQ_EINVAL, "T must be < 2^31");
+  if (!params || !q || !codes || !nu || !gamma || !logits || !ws)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(codes, 16) || !aligned(q, 4) ||
+      !aligned(logits, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; codes 16 B)");
+  if (d != 128 || G % 4 != 0)
+    return fail(TQ_EUNSUPPORTED,
+                "tq_score_ip: implemented for d=128 and G a multiple of 4 (got d=%d G=%lld)", d,
+                (long long)G);
+  if (ws_bytes < tq_score_ws_bytes(d, b, groups, G, T))
+    return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
+                tq_score_ws_bytes(d, b, groups, G, T));
+  hipError_t e = tq::launch_score_d128(params, b, q, q_dtype, codes, nu, gamma, groups, G, T,
+                                       mode, logits, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_score_ip launch");
+  return ok();
+}
+
+size_t tq_topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k) {
+  if (!valid_shape(d, b) || nq < 0 || n < 0 || k < 1 || k > 1024) return 0;
+  return tq::align256(tq::topk_ws_bytes(d, b, nq, n, k));
+}
+
+int tq_topk(const void* params, int d, int b, const void* q, int q_dtype, int64_t nq,
+            const uint32_t* codes, const float* nu, const float* gamma, int64_t n, int k,
+            int mode, int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad q_dtype %d", q_dtype);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (nq < 0 || n < 0) return fail(TQ_EINVAL, "negative size");
+  if (k < 1 || k > 1024) return fail(TQ_EINVAL, "k=%d outside 1..1024", k);
+  if (nq == 0) return ok();
+  if (n < k) return fail(TQ_EINVAL, "k=%d > n=%lld", k, (long long)n);
+  if (n >= (int64_t(1) << 31)) return fail(TQ_EINVAL, "n must be < 2^31");
+  if (!params || !q || !codes || !nu || !gamma || !idx || !score || !ws)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(codes, 16) || !aligned(q, 4))
+    return fail(TQ_EINVAL, "misaligned pointer");
+  size_t need = tq_topk_ws_bytes(d, b, nq, n, k);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipError_t e = tq::launch_topk(params, d, b, q, q_dtype, nq, codes, nu, gamma, n, k, mode, idx,
+                                 score, ws, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(TQ_EUNSUPPORTED, "tq_topk: not implemented for d=%d b=%d", d, b);
+  if (e != hipSuccess) return hip_fail(e, "tq_topk launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,283 @@
+// Fused TurboQuant encoder for d = 128 on gfx950.
+//
+// Per vector x ([review, inner-product paragraph]; [tldr, steps 1-2]):
+//   nu = |x|;  u = Pi x / nu                       rotation   (MFMA, bf16 hi/lo split)
+//   idx_t = #{i : u_t >= tau_i};  chat = c[idx]     Lloyd-Max  (VALU, per coordinate)
+//   r' = u - chat;  gamma = |r'|                   residual in the rotated space
+//   z_i = [ (S' r')_i >= 0 ],  S' = S Pi^T          QJL signs  (MFMA, bf16 hi/lo split)
+// S' r' equals S (x/nu - Pi^T chat), the sketch of the original-space residual, because
+// Pi is orthogonal; this saves the Pi^T chat product.
+//
+// Data flow of one wave (32 vectors, one 32-column MFMA tile):
+//   GEMM1  U^T[128 x 32] = Pi~ X^T with v_mfma_f32_32x32x16_bf16; Pi~ is Pi with its rows
+//          permuted so that lane half h, accumulator register r of row tile mt holds
+//          canonical coordinate 32 mt + 16 h + r of the lane's vector (lane % 32).
+//          Passes: Pi_hi x + Pi_lo x (bf16 input is exact in bf16), plus Pi_hi x_lo for
+//          float32 input (x = x_hi + x_lo).  Fragments of Pi~ are read from LDS.
+//   bucketize in registers against thresholds scaled by nu (no division by nu); the
+//          index bits are shifted into 16-bit half words, the residual is split into
+//          bf16 hi/lo pairs that are directly the B operand of GEMM2.
+//   GEMM2  Y^T = S'~ R'^T, passes S'_hi r_hi + S'_lo r_hi + S'_hi r_lo; the sign of each
+//          output is shifted into half words the same way.
+//   Lanes h = 0 / 1 of a vector swap half words and store whole words (canonical layout).
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int D = 128;
+constexpr int WAVES = 8;                    // waves per workgroup (2 per SIMD)
+constexpr int VPW = 32;                     // vectors per wave tile
+constexpr int FRAG_U4 = 64 * 1024 / 16;     // uint4 per fragment set (Pi~ or S'~)
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+template <int BITS, bool F32IN>
+__global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
+    const unsigned char* __restrict__ params, size_t frag_off, const void* __restrict__ xin,
+    long n, uint32_t* __restrict__ codes, float* __restrict__ nu_out,
+    float* __restrict__ gamma_out) {
+  __shared__ uint4 frag[2 * FRAG_U4];  // [0, FRAG_U4): Pi~ fragments; then S'~ fragments
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(params + frag_off);
+    for (int i = threadIdx.x; i < 2 * FRAG_U4; i += WAVES * 64) frag[i] = src[i];
+  }
+  __syncthreads();
+
+  const Header* hdr = reinterpret_cast<const Header*>(params);
+  constexpr int L = 1 << (BITS - 1);
+  float tp[L / 2 > 1 ? L / 2 - 1 : 1];   // positive thresholds
+  float mp[L / 2];                        // positive centroids
+#pragma unroll
+  for (int k = 0; k < L / 2 - 1; ++k) tp[k] = hdr->tpos[k];
+#pragma unroll
+  for (int k = 0; k < L / 2; ++k) mp[k] = hdr->mpos[k];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kh = lane >> 5;               // lane half: K group of the operands
+  const long ntiles = (n + VPW - 1) / VPW;
+
+  for (long tile = long(blockIdx.x) * WAVES + wave; tile < ntiles; tile += long(gridDim.x) * WAVES) {
+    const long vec = tile * VPW + (lane & 31);
+    const bool valid = vec < n;
+    const long vrow = valid ? vec : n - 1;   // ragged tail: read a valid row, store nothing
+
+    // ---- load this lane's half of the vector (coordinates 64 kh .. 64 kh + 63)
+    bf16x8 xh[8];
+    bf16x8 xl[F32IN ? 8 : 1];
+    float ss = 0.f;
+    if constexpr (!F32IN) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) +
+                                                      vrow * D + 64 * kh);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        uint4 w = p[s];
+        xh[s] = as_bf16x8(w);
+        uint32_t ws4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float a = __uint_as_float(ws4[k] << 16);
+          float b = __uint_as_float(ws4[k] & 0xffff0000u);
+          ss = fmaf(a, a, ss);
+          ss = fmaf(b, b, ss);
+        }
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xin) +
+                                                        vrow * D + 64 * kh);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        float4 a = p[2 * s], b = p[2 * s + 1];
+        float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ss = fmaf(f[e], f[e], ss);
+          __bf16 hi = (__bf16)f[e];
+          xh[s][e] = hi;
+          xl[s][e] = (__bf16)(f[e] - (float)hi);
+        }
+      }
+    }
+    ss += __shfl_xor(ss, 32);
+    const float nu = sqrtf(ss);
+    const float sc = nu > 0.f ? nu : 1.f;   // zero vector: u is taken as 0, grid unscaled
+
+    // ---- per 32-row tile: GEMM1 U^T = Pi~ X^T, then bucketize + residual in registers
+    //      (comparisons against nu-scaled thresholds, so u is never divided by nu)
+    float T[L / 2 > 1 ? L / 2 - 1 : 1], M[L / 2];
+#pragma unroll
+    for (int k = 0; k < L / 2 - 1; ++k) T[k] = tp[k] * sc;
+#pragma unroll
+    for (int k = 0; k < L / 2; ++k) M[k] = mp[k] * sc;
+
+    uint32_t hb[BITS][4];     // [plane][row tile]: this lane's 16-bit half words
+    bf16x8 rh[8], rl[8];      // GEMM2 B operands, K step 2 mt + half
+    float g2 = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 U = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 ahi = as_bf16x8(frag[((s * 4 + mt) * 2 + 0) * 64 + lane]);
+        const bf16x8 alo = as_bf16x8(frag[((s * 4 + mt) * 2 + 1) * 64 + lane]);
+        U = mfma(ahi, xh[s], U);
+        U = mfma(alo, xh[s], U);
+        if constexpr (F32IN) U = mfma(ahi, xl[s], U);
+      }
+      uint32_t w0 = 0, w1 = 0, w2 = 0;
+      float rr[16];
+#pragma unroll
+      for (int r = 15; r >= 0; --r) {
+        const float u = U[r];
+        float c;
+        if constexpr (BITS == 2) {
+          const bool b0 = u >= 0.f;
+          c = b0 ? M[0] : -M[0];
+          w0 = w0 + w0 + uint32_t(b0);
+        } else if constexpr (BITS == 3) {
+          // idx = 2 b1 + b0 over thresholds (-T0, 0, T0)
+          const bool b1 = u >= 0.f;
+          const bool b0 = u >= (b1 ? T[0] : -T[0]);
+          const float mag = (b0 == b1) ? M[1] : M[0];
+          c = b1 ? mag : -mag;
+          w0 = w0 + w0 + uint32_t(b0);
+          w1 = w1 + w1 + uint32_t(b1);
+        } else {
+          // idx = 4 b2 + 2 b1 + b0 over thresholds (-T2, -T1, -T0, 0, T0, T1, T2)
+          const bool b2 = u >= 0.f;
+          const bool b1 = u >= (b2 ? T[1] : -T[1]);
+          const float t2m = (b1 == b2) ? T[2] : T[0];
+          const bool b0 = u >= (b2 ? t2m : -t2m);
+          const bool m1 = (b1 == b2), m0 = (b0 == b2);
+          const float mag = m1 ? (m0 ? M[3] : M[2]) : (m0 ? M[1] : M[0]);
+          c = b2 ? mag : -mag;
+          w0 = w0 + w0 + uint32_t(b0);
+          w1 = w1 + w1 + uint32_t(b1);
+          w2 = w2 + w2 + uint32_t(b2);
+        }
+        const float rv = u - c;
+        rr[r] = rv;
+        g2 = fmaf(rv, rv, g2);
+      }
+      hb[0][mt] = w0;
+      if constexpr (BITS >= 3) hb[1][mt] = w1;
+      if constexpr (BITS >= 4) hb[2][mt] = w2;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = rr[8 * hf + e];
+          const __bf16 hi = (__bf16)v;
+          rh[2 * mt + hf][e] = hi;
+          rl[2 * mt + hf][e] = (__bf16)(v - (float)hi);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    g2 += __shfl_xor(g2, 32);
+    const float gamma = sqrtf(g2) / sc;
+
+    // ---- GEMM2: Y^T = S'~ R'^T, one 32-row tile of projections at a time
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 Y = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 ahi = as_bf16x8(frag[FRAG_U4 + ((mt * 8 + s) * 2 + 0) * 64 + lane]);
+        const bf16x8 alo = as_bf16x8(frag[FRAG_U4 + ((mt * 8 + s) * 2 + 1) * 64 + lane]);
+        Y = mfma(ahi, rh[s], Y);
+        Y = mfma(alo, rh[s], Y);
+        Y = mfma(ahi, rl[s], Y);
+      }
+      uint32_t w = 0;
+#pragma unroll
+      for (int r = 15; r >= 0; --r) w = w + w + uint32_t(Y[r] >= 0.f);
+      hb[BITS - 1][mt] = w;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- assemble whole words: half h = 0 finishes row tiles 0,1; h = 1 tiles 2,3
+    uint32_t out[2 * BITS];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) {
+        const uint32_t send = kh == 0 ? hb[p][2 + k] : hb[p][k];
+        const uint32_t recv = __shfl_xor(send, 32);
+        out[k * BITS + p] = kh == 0 ? (hb[p][k] | (recv << 16)) : (recv | (hb[p][2 + k] << 16));
+      }
+    }
+    if (valid) {
+      uint32_t* dst = codes + (vec * 4 + 2 * kh) * BITS;
+      if constexpr (BITS == 4) {
+        reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+        reinterpret_cast<uint4*>(dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      } else if constexpr (BITS == 3) {
+        reinterpret_cast<uint2*>(dst)[0] = make_uint2(out[0], out[1]);
+        reinterpret_cast<uint2*>(dst)[1] = make_uint2(out[2], out[3]);
+        reinterpret_cast<uint2*>(dst)[2] = make_uint2(out[4], out[5]);
+      } else {
+        reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      }
+      if (kh == 0) {
+        nu_out[vec] = nu;
+        gamma_out[vec] = gamma;
+      }
+    }
+  }
+}
+
+int cu_count() {
+  static int cached = 0;
+  if (!cached) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    cached = c;
+  }
+  return cached;
+}
+
+template <int BITS, bool F32IN>
+hipError_t launch(const void* params, const void* x, int64_t n, uint32_t* codes, float* nu,
+                  float* gamma, hipStream_t s) {
+  const long ntiles = (n + VPW - 1) / VPW;
+  const long need = (ntiles + WAVES - 1) / WAVES;
+  const int grid = int(need < cu_count() ? need : cu_count());
+  hipLaunchKernelGGL((quantize_d128_kernel<BITS, F32IN>), dim3(grid), dim3(WAVES * 64), 0, s,
+                     static_cast<const unsigned char*>(params), Layout(D, BITS).off_qfrag, x,
+                     long(n), codes, nu, gamma);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_dtype, int64_t n,
+                                uint32_t* codes, float* nu, float* gamma, hipStream_t s) {
+  const bool f32 = x_dtype == 0;
+  switch (b) {
+    case 2: return f32 ? launch<2, true>(params, x, n, codes, nu, gamma, s)
+                       : launch<2, false>(params, x, n, codes, nu, gamma, s);
+    case 3: return f32 ? launch<3, true>(params, x, n, codes, nu, gamma, s)
+                       : launch<3, false>(params, x, n, codes, nu, gamma, s);
+    case 4: return f32 ? launch<4, true>(params, x, n, codes, nu, gamma, s)
+                       : launch<4, false>(params, x, n, codes, nu, gamma, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tq

@@ -1,0 +1,80 @@
+// Internal definitions shared by the host ABI code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr uint32_t kMagic = 0x51545152u;   // "RQTQ"
+constexpr int kMaxLevels = 16;             // up to 4 Lloyd-Max bits in the parameter block
+
+// Header at offset 0 of the device parameter block (256 bytes, read by the kernels).
+struct Header {
+  uint32_t magic;
+  int32_t d, b, L;            // dimension, total bits, Lloyd-Max levels = 2^(b-1)
+  float thr[kMaxLevels];      // thresholds[L-1] in units of the rotated unit vector
+  float cen[kMaxLevels];      // centroids[L]
+  float tpos[kMaxLevels / 2]; // positive thresholds thr[L/2 .. L-2] (thr[L/2-1] == 0)
+  float mpos[kMaxLevels / 2]; // positive centroids cen[L/2 .. L-1]
+  // Walsh expansion of the codebook on the index bits (odd terms only):
+  //   cen[idx] = sum_P e[P] * prod_{p in P} (2 bit_p(idx) - 1)
+  // ordered as the scoring kernel walks its bit planes: {b0}, {b1}, {b2}, {b0 b1 b2}.
+  float e[4];
+  int32_t ne;                 // number of Walsh terms used (1, 2 or 4)
+  float esum;                 // sum of e[]
+  float emax;                 // max |e|
+  float alpha;                // sqrt(pi/2) / m
+  float pad[4];
+};
+static_assert(sizeof(Header) <= 256, "header must fit in 256 bytes");
+
+// Byte layout of the device parameter block for (d, b).
+struct Layout {
+  int d = 0, b = 0;
+  size_t off_hdr = 0;
+  size_t off_pi = 0;      // Pi  [d][d] fp32 row-major
+  size_t off_s = 0;       // S   [d][d] fp32 row-major
+  size_t off_qfrag = 0;   // d == 128: quantize MFMA fragments (2 x 64 KiB), else 0 bytes
+  size_t qfrag_bytes = 0;
+  size_t total = 0;
+  Layout(int d_, int b_);
+};
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline Layout::Layout(int d_, int b_) : d(d_), b(b_) {
+  off_hdr = 0;
+  off_pi = 256;
+  off_s = align256(off_pi + size_t(d) * d * 4);
+  off_qfrag = align256(off_s + size_t(d) * d * 4);
+  qfrag_bytes = (d == 128) ? size_t(2) * 64 * 1024 : 0;
+  total = align256(off_qfrag + qfrag_bytes);
+}
+
+// Plane words per key that the scoring kernel feeds to the MFMA: the b-1 index planes,
+// the derived xor plane for 3 index bits, and the QJL sign plane.
+constexpr int score_words(int b) { return b == 4 ? 5 : b; }
+
+// Score workspace: per group, the MFMA query operands and 4 floats per query.
+constexpr size_t score_ws_per_group(int b) {
+  return size_t(2 * score_words(b)) * 64 * 16 + 4 * 4 * 4;
+}
+
+// ---- kernel launchers (defined in the .hip files), return hipError_t
+hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_dtype, int64_t n,
+                                uint32_t* codes, float* nu, float* gamma, hipStream_t s);
+hipError_t launch_score_d128(const void* params, int b, const void* q, int q_dtype,
+                             const uint32_t* codes, const float* nu, const float* gamma,
+                             int64_t groups, int64_t G, int64_t T, int mode, float* logits,
+                             void* ws, hipStream_t s);
+hipError_t launch_dequantize(const void* params, int d, int b, const uint32_t* codes,
+                             const float* nu, const float* gamma, int64_t n, int mode,
+                             float* xhat, hipStream_t s);
+hipError_t launch_topk(const void* params, int d, int b, const void* q, int q_dtype, int64_t nq,
+                       const uint32_t* codes, const float* nu, const float* gamma, int64_t n,
+                       int k, int mode, int32_t* idx, float* score, void* ws, hipStream_t s);
+size_t topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k);
+
+}  // namespace tq

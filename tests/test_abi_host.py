@@ -1,0 +1,122 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every declared call,
+builds the same codebook as the oracle, and rejects bad arguments before enqueuing work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_embedding_amd as tq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tq.lib_path()):
+        pytest.fail("libtq.so is not built: run __graft_entry__.build()")
+    return tq.load_library()
+
+
+def test_library_exports_every_declared_call(lib):
+    names = declared_functions()
+    assert set(names) >= {"tq_codebook_build", "tq_quantize", "tq_dequantize", "tq_score_ip",
+                          "tq_topk", "tq_prepare", "tq_params_bytes", "tq_last_error"}
+    raw = ctypes.CDLL(tq.lib_path())
+    for name in names:
+        assert hasattr(raw, name), name
+        assert hasattr(tq, name), f"python binding lacks {name}"
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("d", [64, 128, 1536])
+def test_codebook_matches_oracle(lib, bits, d):
+    c, t = tq.tq_codebook_build(bits, d)
+    co, to = oracle.codebook(bits, d)
+    assert np.allclose(c, co, rtol=0, atol=1e-9 / np.sqrt(d))
+    assert np.allclose(t, to, rtol=0, atol=1e-9 / np.sqrt(d))
+    assert t[len(t) // 2] == 0.0
+
+
+def test_codebook_rejects_bad_arguments(lib):
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_codebook_build(0, 128)
+    assert e.value.status == tq.TQ_EINVAL
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_codebook_build(3, 0)
+    assert e.value.status == tq.TQ_EINVAL
+
+
+def test_params_bytes_and_workspace_helpers(lib):
+    assert tq.tq_params_bytes(128, 4) > 2 * 128 * 128 * 4
+    assert tq.tq_params_bytes(100, 4) == 0
+    assert tq.tq_params_bytes(128, 5) == 0
+    assert tq.tq_score_ws_bytes(128, 4, 8, 4, 32768) % 256 == 0
+    assert tq.tq_score_ws_bytes(128, 4, 8, 8, 32768) == 2 * tq.tq_score_ws_bytes(128, 4, 8, 4, 32768)
+
+
+def _raw(lib):
+    return lib
+
+
+def test_invalid_arguments_return_status_without_launch(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: every call below fails validation first
+    # bad d / b
+    assert lib.tq_quantize(fake, 100, 4, fake, 0, 10, fake, fake, fake, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize(fake, 128, 5, fake, 0, 10, fake, fake, fake, None) == tq.TQ_EINVAL
+    assert "shape" in tq.tq_last_error()
+    # bad dtype, negative n, NULL pointers
+    assert lib.tq_quantize(fake, 128, 4, fake, 7, 10, fake, fake, fake, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize(fake, 128, 4, fake, 0, -1, fake, fake, fake, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize(fake, 128, 4, None, 0, 10, fake, fake, fake, None) == tq.TQ_EINVAL
+    # misaligned x
+    assert lib.tq_quantize(fake, 128, 4, P(0x1002), 0, 10, fake, fake, fake, None) == tq.TQ_EINVAL
+    # n == 0 is a no-op even with NULL pointers
+    assert lib.tq_quantize(None, 128, 4, None, 0, 0, None, None, None, None) == tq.TQ_OK
+    # unsupported dimension for the fused encoder
+    assert lib.tq_quantize(fake, 256, 4, fake, 0, 10, fake, fake, fake, None) == tq.TQ_EUNSUPPORTED
+    # scoring: bad mode, workspace too small, unsupported G
+    args = (fake, 128, 4, fake, 1, fake, fake, fake, 8, 4, 1024)
+    assert lib.tq_score_ip(*args, 9, fake, fake, 1 << 30, None) == tq.TQ_EINVAL
+    assert lib.tq_score_ip(*args, 0, fake, fake, 16, None) == tq.TQ_EWORKSPACE
+    args3 = (fake, 128, 4, fake, 1, fake, fake, fake, 8, 3, 1024)
+    assert lib.tq_score_ip(*args3, 0, fake, fake, 1 << 30, None) == tq.TQ_EUNSUPPORTED
+    assert lib.tq_score_ip(fake, 128, 4, fake, 1, fake, fake, fake, 0, 4, 1024, 0, None, None, 0,
+                           None) == tq.TQ_OK
+    # top-k: k out of range, k > n
+    assert lib.tq_topk(fake, 128, 4, fake, 0, 10, fake, fake, fake, 100, 0, 0, fake, fake, fake,
+                       1 << 30, None) == tq.TQ_EINVAL
+    assert lib.tq_topk(fake, 128, 4, fake, 0, 10, fake, fake, fake, 5, 10, 0, fake, fake, fake,
+                       1 << 30, None) == tq.TQ_EINVAL
+    # dequantize: bad mode
+    assert lib.tq_dequantize(fake, 128, 4, fake, fake, fake, 10, 3, fake, None) == tq.TQ_EINVAL
+
+
+def test_prepare_rejects_bad_codebook_and_rotation(lib):
+    d, b = 128, 3
+    c, t = tq.tq_codebook_build(b - 1, d)
+    Pi = np.eye(d, dtype=np.float32)
+    S = np.ones((d, d), dtype=np.float32)
+    fake = ctypes.c_void_p(0x100000)
+    def call(Pi_, c_, t_):
+        Pi_ = np.ascontiguousarray(Pi_, np.float32)
+        c_ = np.ascontiguousarray(c_, np.float64)
+        t_ = np.ascontiguousarray(t_, np.float64)
+        return lib.tq_prepare(d, b, Pi_.ctypes.data, S.ctypes.data, c_.ctypes.data, t_.ctypes.data,
+                              fake, None)
+    assert call(Pi, c[::-1], t) == tq.TQ_EINVAL              # not ascending
+    c2 = c.copy(); c2[-1] *= 1.1
+    assert call(Pi, c2, t) == tq.TQ_EINVAL                   # not symmetric
+    assert call(Pi * 1.01, c, t) == tq.TQ_EINVAL             # not orthogonal
+    assert "orthogonal" in tq.tq_last_error()
+    assert lib.tq_prepare(d, b, Pi.ctypes.data, S.ctypes.data, c.ctypes.data, t.ctypes.data,
+                          ctypes.c_void_p(0x100010), None) == tq.TQ_EINVAL   # misaligned params

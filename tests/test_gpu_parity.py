@@ -1,0 +1,163 @@
+"""GPU parity: HIP path vs the CPU oracle on identical seeded inputs (MI355X only)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_embedding_amd as tq
+import oracle
+from workloads import gen
+import tq_testutil as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(tag, rep):
+    print(f"[{tag}] {U.describe(rep)}", flush=True)
+
+
+# ------------------------------------------------------------------------- quantize
+
+@pytest.mark.parametrize("n", [4096, 4096 - 37, 1, 33])
+def test_quantize_toy_f32(n):
+    # Toy workload: unit vectors in R^128 (float32), b = 4.
+    st = U.make_setup(128, 4, cfg=0)
+    x = gen.unit_sphere(n, 128, cfg=0, role=gen.ROLE_DATA)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    rep = U.compare_codes(st, U.host64(x, False), U.codes_np(codes, n, 128, 4),
+                          nu.cpu().numpy(), gamma.cpu().numpy())
+    _report(f"toy n={n}", rep)
+    U.assert_codes_ok(rep)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_quantize_kv_bf16_outliers(b):
+    # KV keys: N(0,1) bf16 with 4 outlier channels per head (x20); 3 heads x 1000 tokens.
+    st = U.make_setup(128, b, cfg=1)
+    chans = gen.outlier_channels(1, 3, 128)
+    keys = np.concatenate([gen.kv_keys_chunk(1, 0, h, 1000, 128, chans[h]) for h in range(3)])
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(keys, True))
+    rep = U.compare_codes(st, U.host64(keys, True), U.codes_np(codes, keys.shape[0], 128, b),
+                          nu.cpu().numpy(), gamma.cpu().numpy())
+    _report(f"kv b={b}", rep)
+    U.assert_codes_ok(rep)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_quantize_f32_nonunit(b):
+    st = U.make_setup(128, b, cfg=5)
+    x = gen.unit_sphere(2000, 128, cfg=5, role=gen.ROLE_DATA) * np.float32(7.5)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    rep = U.compare_codes(st, U.host64(x, False), U.codes_np(codes, 2000, 128, b),
+                          nu.cpu().numpy(), gamma.cpu().numpy())
+    _report(f"f32 nonunit b={b}", rep)
+    U.assert_codes_ok(rep)
+
+
+def test_quantize_zero_vectors_and_empty():
+    st = U.make_setup(128, 4, cfg=6)
+    x = gen.unit_sphere(40, 128, cfg=6, role=gen.ROLE_DATA)
+    x[[0, 7, 39]] = 0.0
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    rep = U.compare_codes(st, U.host64(x, False), U.codes_np(codes, 40, 128, 4),
+                          nu.cpu().numpy(), gamma.cpu().numpy())
+    U.assert_codes_ok(rep)
+    assert nu.cpu().numpy()[[0, 7, 39]].tolist() == [0.0, 0.0, 0.0]
+    # zero vector: all indices L/2 (u = 0 sits on the middle threshold, upper cell)
+    assert np.all(rep["idx"][[0, 7, 39]] == 4)
+    # n = 0: no-op
+    e = torch.empty((0, 128), dtype=torch.float32, device=U.DEV)
+    z = torch.empty(0, dtype=torch.int32, device=U.DEV)
+    f = torch.empty(0, dtype=torch.float32, device=U.DEV)
+    tq.tq_quantize(st.params, 128, 4, e, z, f, f)
+
+
+def test_quantize_nonfinite_inputs_do_not_fault():
+    st = U.make_setup(128, 3, cfg=7)
+    x = gen.unit_sphere(64, 128, cfg=7, role=gen.ROLE_DATA)
+    x[3, 5] = np.nan
+    x[9, 0] = np.inf
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    good = np.array([i not in (3, 9) for i in range(64)])
+    rep = U.compare_codes(st, U.host64(x[good], False),
+                          U.codes_np(codes, 64, 128, 3)[good], nu.cpu().numpy()[good],
+                          gamma.cpu().numpy()[good])
+    U.assert_codes_ok(rep)
+
+
+# --------------------------------------------------------------------------- scoring
+
+def _kv_case(b, cfg, groups, T, G=4):
+    st = U.make_setup(128, b, cfg=cfg)
+    chans = gen.outlier_channels(cfg, groups, 128)
+    keys = np.concatenate([gen.kv_keys_chunk(cfg, 0, h, T, 128, chans[h]) for h in range(groups)])
+    q = gen.kv_queries(cfg, 1, groups * G, 128)[0]
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(keys, True))
+    cn = U.codes_np(codes, groups * T, 128, b)
+    idx, z = oracle.unpack_codes(cn, b)
+    q64 = U.host64(q, True).reshape(groups, G, 128)
+    return st, keys, q, codes, nu, gamma, idx, z, q64
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("mode", [tq.TQ_EST_PROD, tq.TQ_EST_MSE])
+def test_score_kv_parity(b, mode):
+    groups, T = 3, 1000
+    st, keys, q, codes, nu, gamma, idx, z, q64 = _kv_case(b, 11, groups, T)
+    lg = U.gpu_score(st, U.to_device(q, True), codes, nu, gamma, groups, 4, T, mode)
+    err = U.logit_errors(st, q64, idx, z, nu.cpu().numpy(), gamma.cpu().numpy(), lg,
+                         "prod" if mode == tq.TQ_EST_PROD else "mse")
+    print(f"[score b={b} mode={mode}] max |dl|/(|q|nu) = {err:.2e}", flush=True)
+    assert err <= U.LOGIT_TOL
+
+
+@pytest.mark.parametrize("T", [1, 15, 17, 257])
+def test_score_ragged_lengths(T):
+    groups = 2
+    st, keys, q, codes, nu, gamma, idx, z, q64 = _kv_case(4, 12, groups, T)
+    lg = U.gpu_score(st, U.to_device(q, True), codes, nu, gamma, groups, 4, T, tq.TQ_EST_PROD)
+    err = U.logit_errors(st, q64, idx, z, nu.cpu().numpy(), gamma.cpu().numpy(), lg)
+    assert err <= U.LOGIT_TOL
+
+
+def test_score_wide_group_f32_queries():
+    # Toy workload: 64 unit queries against 4096 unit keys in one group (G = 64), float32.
+    st = U.make_setup(128, 4, cfg=0)
+    x = gen.unit_sphere(4096, 128, cfg=0, role=gen.ROLE_DATA)
+    q = gen.unit_sphere(64, 128, cfg=0, role=gen.ROLE_QUERY)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    idx, z = oracle.unpack_codes(U.codes_np(codes, 4096, 128, 4), 4)
+    lg = U.gpu_score(st, U.to_device(q, False), codes, nu, gamma, 1, 64, 4096, tq.TQ_EST_PROD)
+    err = U.logit_errors(st, q.astype(np.float64)[None], idx, z, nu.cpu().numpy(),
+                         gamma.cpu().numpy(), lg)
+    print(f"[score toy G=64] max err {err:.2e}", flush=True)
+    assert err <= U.LOGIT_TOL
+
+
+def test_score_zero_keys_give_zero_logits():
+    st = U.make_setup(128, 3, cfg=13)
+    x = gen.unit_sphere(64, 128, cfg=13, role=gen.ROLE_DATA)
+    x[[2, 50]] = 0.0
+    q = gen.unit_sphere(4, 128, cfg=13, role=gen.ROLE_QUERY)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    lg = U.gpu_score(st, U.to_device(q, False), codes, nu, gamma, 1, 4, 64, tq.TQ_EST_PROD)
+    assert np.all(lg[0][:, [2, 50]] == 0.0)
+
+
+# ------------------------------------------------------------------------ dequantize
+
+@pytest.mark.parametrize("b", [2, 4])
+@pytest.mark.parametrize("mode", [tq.TQ_EST_PROD, tq.TQ_EST_MSE])
+def test_dequantize_parity(b, mode):
+    st = U.make_setup(128, b, cfg=14)
+    x = gen.unit_sphere(300, 128, cfg=14, role=gen.ROLE_DATA) * np.float32(3.0)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    xhat = torch.full((300 * 128,), float("nan"), dtype=torch.float32, device=U.DEV)
+    tq.tq_dequantize(st.params, 128, b, codes, nu, gamma, mode, xhat)
+    torch.cuda.synchronize()
+    idx, z = oracle.unpack_codes(U.codes_np(codes, 300, 128, b), b)
+    ref = oracle.dequantize(st.Pi, st.S, idx, z, nu.cpu().numpy(), gamma.cpu().numpy(), st.c_or,
+                            "prod" if mode == tq.TQ_EST_PROD else "mse")
+    err = np.max(np.abs(xhat.cpu().numpy().reshape(300, 128) - ref)) / 3.0
+    assert err <= 1e-5, err
