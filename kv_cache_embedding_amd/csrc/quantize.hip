@@ -27,20 +27,24 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
 constexpr int WAVES = 8;                    // waves per workgroup (2 per SIMD)
 constexpr int VPW = 32;                     // vectors per wave tile
 constexpr int FRAG_U4 = 64 * 1024 / 16;     // uint4 per fragment set (Pi~ or S'~)
+#ifndef TQ_Q_PHASE_SLEEP
+#define TQ_Q_PHASE_SLEEP 0     // s_sleep units (64 cycles) for the second wave of each SIMD
+#endif
+#ifndef TQ_Q_MFMA_PRIO
+#define TQ_Q_MFMA_PRIO 0       // raise wave priority while issuing MFMA blocks
+#endif
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
-  return __uint_as_float(h16 << 16);
 }
 
 template <int BITS, bool F32IN>
@@ -49,11 +53,37 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     long n, uint32_t* __restrict__ codes, float* __restrict__ nu_out,
     float* __restrict__ gamma_out) {
   __shared__ uint4 frag[2 * FRAG_U4];  // [0, FRAG_U4): Pi~ fragments; then S'~ fragments
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kh = lane >> 5;               // lane half: K group of the operands
+  const long ntiles = (n + VPW - 1) / VPW;
+  const long stride = long(gridDim.x) * WAVES;
+  long tile = long(blockIdx.x) * WAVES + wave;
+
+  // Raw input of this lane's half vector (coordinates 64 kh .. 64 kh + 63), loaded one
+  // tile ahead of its use.
+  constexpr int NRAW = F32IN ? 16 : 8;
+  uint4 raw[NRAW];
+  auto load_tile = [&](long tl) {
+    const long vec = tl * VPW + (lane & 31);
+    const long vrow = vec < n ? vec : n - 1;   // ragged tail: read a valid row, store nothing
+    const uint4* p = F32IN ? reinterpret_cast<const uint4*>(static_cast<const float*>(xin) + vrow * D + 64 * kh)
+                           : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) + vrow * D + 64 * kh);
+#pragma unroll
+    for (int i = 0; i < NRAW; ++i) raw[i] = p[i];
+  };
+  if (tile < ntiles) load_tile(tile);     // in flight while the fragments fill LDS
   {
     const uint4* src = reinterpret_cast<const uint4*>(params + frag_off);
     for (int i = threadIdx.x; i < 2 * FRAG_U4; i += WAVES * 64) frag[i] = src[i];
   }
   __syncthreads();
+#if TQ_Q_PHASE_SLEEP
+  // start the two waves sharing a SIMD out of phase, so that one is in its MFMA blocks
+  // while the other is in its VALU blocks
+  if (wave >= 4) __builtin_amdgcn_s_sleep(TQ_Q_PHASE_SLEEP);
+#endif
 
   const Header* hdr = reinterpret_cast<const Header*>(params);
   constexpr int L = 1 << (BITS - 1);
@@ -64,47 +94,35 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
 #pragma unroll
   for (int k = 0; k < L / 2; ++k) mp[k] = hdr->mpos[k];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int kh = lane >> 5;               // lane half: K group of the operands
-  const long ntiles = (n + VPW - 1) / VPW;
-
-  for (long tile = long(blockIdx.x) * WAVES + wave; tile < ntiles; tile += long(gridDim.x) * WAVES) {
+  for (; tile < ntiles; tile += stride) {
     const long vec = tile * VPW + (lane & 31);
     const bool valid = vec < n;
-    const long vrow = valid ? vec : n - 1;   // ragged tail: read a valid row, store nothing
 
-    // ---- load this lane's half of the vector (coordinates 64 kh .. 64 kh + 63)
+    // ---- operands of GEMM1 and the squared norm
     bf16x8 xh[8];
     bf16x8 xl[F32IN ? 8 : 1];
     float ss = 0.f;
     if constexpr (!F32IN) {
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) +
-                                                      vrow * D + 64 * kh);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        uint4 w = p[s];
-        xh[s] = as_bf16x8(w);
-        uint32_t ws4[4] = {w.x, w.y, w.z, w.w};
+        xh[s] = as_bf16x8(raw[s]);
+        const uint32_t ws4[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          float a = __uint_as_float(ws4[k] << 16);
-          float b = __uint_as_float(ws4[k] & 0xffff0000u);
-          ss = fmaf(a, a, ss);
-          ss = fmaf(b, b, ss);
+          const bf16x2 p2 = __builtin_bit_cast(bf16x2, ws4[k]);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, ss, false);
         }
       }
     } else {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xin) +
-                                                        vrow * D + 64 * kh);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        float4 a = p[2 * s], b = p[2 * s + 1];
-        float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const float4 a = __builtin_bit_cast(float4, raw[2 * s]);
+        const float4 b = __builtin_bit_cast(float4, raw[2 * s + 1]);
+        const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           ss = fmaf(f[e], f[e], ss);
-          __bf16 hi = (__bf16)f[e];
+          const __bf16 hi = (__bf16)f[e];
           xh[s][e] = hi;
           xl[s][e] = (__bf16)(f[e] - (float)hi);
         }
@@ -114,8 +132,43 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     const float nu = sqrtf(ss);
     const float sc = nu > 0.f ? nu : 1.f;   // zero vector: u is taken as 0, grid unscaled
 
-    // ---- per 32-row tile: GEMM1 U^T = Pi~ X^T, then bucketize + residual in registers
-    //      (comparisons against nu-scaled thresholds, so u is never divided by nu)
+    // ---- GEMM1: U^T = Pi~ X^T, one 32-row tile at a time
+#if TQ_Q_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
+    f32x16 U[4];
+#pragma unroll
+    for (int mp = 0; mp < 4; mp += 2) {
+      // two independent accumulation chains (row tiles mp, mp + 1) interleaved
+      U[mp] = f32x16{};
+      U[mp + 1] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int mt = mp + t;
+          const bf16x8 ahi = as_bf16x8(frag[((s * 4 + mt) * 2 + 0) * 64 + lane]);
+          U[mt] = mfma(ahi, xh[s], U[mt]);
+          if constexpr (F32IN) U[mt] = mfma(ahi, xl[s], U[mt]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int mt = mp + t;
+          const bf16x8 alo = as_bf16x8(frag[((s * 4 + mt) * 2 + 1) * 64 + lane]);
+          U[mt] = mfma(alo, xh[s], U[mt]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // bound the fragment reads in flight
+    }
+#if TQ_Q_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
+    // the input registers are free: fetch the next tile while this one is finished
+    if (tile + stride < ntiles) load_tile(tile + stride);
+
+    // ---- bucketize + residual against nu-scaled thresholds (u is never divided by nu).
+    // Bits of the sign plane are the float sign bits of u, shifted in with v_alignbit and
+    // inverted at the end (u is never -0: the MFMA sum starts from +0).
     float T[L / 2 > 1 ? L / 2 - 1 : 1], M[L / 2];
 #pragma unroll
     for (int k = 0; k < L / 2 - 1; ++k) T[k] = tp[k] * sc;
@@ -127,61 +180,61 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     float g2 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      f32x16 U = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 ahi = as_bf16x8(frag[((s * 4 + mt) * 2 + 0) * 64 + lane]);
-        const bf16x8 alo = as_bf16x8(frag[((s * 4 + mt) * 2 + 1) * 64 + lane]);
-        U = mfma(ahi, xh[s], U);
-        U = mfma(alo, xh[s], U);
-        if constexpr (F32IN) U = mfma(ahi, xl[s], U);
-      }
-      uint32_t w0 = 0, w1 = 0, w2 = 0;
+      uint32_t w0 = 0, w1 = 0, ws = 0;
       float rr[16];
 #pragma unroll
       for (int r = 15; r >= 0; --r) {
-        const float u = U[r];
+        const float u = U[mt][r];
+        ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(u), 31);
         float c;
         if constexpr (BITS == 2) {
-          const bool b0 = u >= 0.f;
-          c = b0 ? M[0] : -M[0];
-          w0 = w0 + w0 + uint32_t(b0);
+          c = copysignf(M[0], u);
         } else if constexpr (BITS == 3) {
-          // idx = 2 b1 + b0 over thresholds (-T0, 0, T0)
+          // idx = 2 b1 + b0 over thresholds (-T0, 0, T0); b1 = sign plane
           const bool b1 = u >= 0.f;
-          const bool b0 = u >= (b1 ? T[0] : -T[0]);
-          const float mag = (b0 == b1) ? M[1] : M[0];
-          c = b1 ? mag : -mag;
-          w0 = w0 + w0 + uint32_t(b0);
-          w1 = w1 + w1 + uint32_t(b1);
+          const bool b0 = u >= copysignf(T[0], u);
+          c = copysignf((b0 == b1) ? M[1] : M[0], u);
+          w0 = (w0 << 1) | uint32_t(b0);
         } else {
-          // idx = 4 b2 + 2 b1 + b0 over thresholds (-T2, -T1, -T0, 0, T0, T1, T2)
+          // idx = 4 b2 + 2 b1 + b0 over thresholds (-T2, -T1, -T0, 0, T0, T1, T2); b2 = sign
           const bool b2 = u >= 0.f;
-          const bool b1 = u >= (b2 ? T[1] : -T[1]);
-          const float t2m = (b1 == b2) ? T[2] : T[0];
-          const bool b0 = u >= (b2 ? t2m : -t2m);
-          const bool m1 = (b1 == b2), m0 = (b0 == b2);
-          const float mag = m1 ? (m0 ? M[3] : M[2]) : (m0 ? M[1] : M[0]);
-          c = b2 ? mag : -mag;
-          w0 = w0 + w0 + uint32_t(b0);
-          w1 = w1 + w1 + uint32_t(b1);
-          w2 = w2 + w2 + uint32_t(b2);
+          const bool b1 = u >= copysignf(T[1], u);
+          const bool e1 = (b1 == b2);
+          const bool b0 = u >= copysignf(e1 ? T[2] : T[0], u);
+          const bool e0 = (b0 == b2);
+          c = copysignf(e1 ? (e0 ? M[3] : M[2]) : (e0 ? M[1] : M[0]), u);
+          w0 = (w0 << 1) | uint32_t(b0);
+          w1 = (w1 << 1) | uint32_t(b1);
         }
         const float rv = u - c;
         rr[r] = rv;
         g2 = fmaf(rv, rv, g2);
       }
-      hb[0][mt] = w0;
-      if constexpr (BITS >= 3) hb[1][mt] = w1;
-      if constexpr (BITS >= 4) hb[2][mt] = w2;
+      const uint32_t wsign = ~ws & 0xffffu;     // 1 = u >= 0
+      if constexpr (BITS == 2) {
+        hb[0][mt] = wsign;
+      } else if constexpr (BITS == 3) {
+        hb[0][mt] = w0;
+        hb[1][mt] = wsign;
+      } else {
+        hb[0][mt] = w0;
+        hb[1][mt] = w1;
+        hb[2][mt] = wsign;
+      }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = rr[8 * hf + e];
-          const __bf16 hi = (__bf16)v;
-          rh[2 * mt + hf][e] = hi;
-          rl[2 * mt + hf][e] = (__bf16)(v - (float)hi);
+        for (int e = 0; e < 8; e += 2) {
+          // hi = RNE(v); lo = RNE(v - hi): converted two at a time
+          const f32x2 v2 = {rr[8 * hf + e], rr[8 * hf + e + 1]};
+          const bf16x2 h2 = __builtin_convertvector(v2, bf16x2);
+          const uint32_t hb2 = __builtin_bit_cast(uint32_t, h2);
+          const f32x2 hf2 = {__uint_as_float(hb2 << 16), __uint_as_float(hb2 & 0xffff0000u)};
+          const bf16x2 l2 = __builtin_convertvector(v2 - hf2, bf16x2);
+          rh[2 * mt + hf][e] = h2[0];
+          rh[2 * mt + hf][e + 1] = h2[1];
+          rl[2 * mt + hf][e] = l2[0];
+          rl[2 * mt + hf][e + 1] = l2[1];
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -189,25 +242,42 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     g2 += __shfl_xor(g2, 32);
     const float gamma = sqrtf(g2) / sc;
 
-    // ---- GEMM2: Y^T = S'~ R'^T, one 32-row tile of projections at a time
+    // ---- GEMM2: Y^T = S'~ R'^T, one 32-row tile of projections at a time; the sign
+    //      bits of y are shifted in the same way (y is never -0 either)
+#if TQ_Q_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x16 Y = f32x16{};
+    for (int mp = 0; mp < 4; mp += 2) {
+      f32x16 Y[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 ahi = as_bf16x8(frag[FRAG_U4 + ((mt * 8 + s) * 2 + 0) * 64 + lane]);
-        const bf16x8 alo = as_bf16x8(frag[FRAG_U4 + ((mt * 8 + s) * 2 + 1) * 64 + lane]);
-        Y = mfma(ahi, rh[s], Y);
-        Y = mfma(alo, rh[s], Y);
-        Y = mfma(ahi, rl[s], Y);
-      }
-      uint32_t w = 0;
+        bf16x8 ahi[2];
 #pragma unroll
-      for (int r = 15; r >= 0; --r) w = w + w + uint32_t(Y[r] >= 0.f);
-      hb[BITS - 1][mt] = w;
+        for (int t = 0; t < 2; ++t) {
+          ahi[t] = as_bf16x8(frag[FRAG_U4 + (((mp + t) * 8 + s) * 2 + 0) * 64 + lane]);
+          Y[t] = mfma(ahi[t], rh[s], Y[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 alo = as_bf16x8(frag[FRAG_U4 + (((mp + t) * 8 + s) * 2 + 1) * 64 + lane]);
+          Y[t] = mfma(alo, rh[s], Y[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) Y[t] = mfma(ahi[t], rl[s], Y[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) w = __builtin_amdgcn_alignbit(w, __float_as_uint(Y[t][r]), 31);
+        hb[BITS - 1][mp + t] = ~w & 0xffffu;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-
+#if TQ_Q_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
     // ---- assemble whole words: half h = 0 finishes row tiles 0,1; h = 1 tiles 2,3
     uint32_t out[2 * BITS];
 #pragma unroll

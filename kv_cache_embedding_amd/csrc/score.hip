@@ -45,8 +45,10 @@ int cu_count_s() {
 }
 
 // ------------------------------------------------------------------------ query prep
-// One workgroup per group: qh = Pi q, sh = S q (float32), per-query scales, then the MFMA
-// A operands in register order: ws[g][m][lane][16 bytes], m = 2 word + j.
+// One workgroup per (virtual group, query head h): qh = Pi q, sh = S q (float32, one row
+// per thread), the head's scales, then its rows 4h .. 4h+3 of the MFMA A operands in
+// register order ws[g][m][lane][16 bytes] (m = 2 word + j; lane l holds row l % 16), and
+// its four epilogue constants.
 template <int BITS>
 __global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* __restrict__ params,
                                                            size_t off_pi, size_t off_s,
@@ -54,57 +56,70 @@ __global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* _
                                                            unsigned char* __restrict__ ws) {
   constexpr int NW = score_words(BITS);
   const Header* hdr = reinterpret_cast<const Header*>(params);
-  const long g = blockIdx.x;
-  __shared__ float qv[G][D];
-  __shared__ float qh[G][D];
-  __shared__ float sh[G][D];
-  __shared__ float stats[G][4];   // max|qh|, sum qh, max|sh|, sum sh
+  const long g = blockIdx.x / G;
+  const int h = blockIdx.x % G;
+  __shared__ float qv[D];
+  __shared__ float qh[D];
+  __shared__ float sh[D];
+  __shared__ float stats[4];   // max|qh|, sum qh, max|sh|, sum sh
 
-  for (int i = threadIdx.x; i < G * D; i += 256) {
-    const long off = g * G * D + i;
-    float v;
-    if (q_f32) {
-      v = static_cast<const float*>(q)[off];
-    } else {
-      v = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[off]) << 16);
+  if (threadIdx.x < D) {
+    const long off = (g * G + h) * D + threadIdx.x;
+    qv[threadIdx.x] = q_f32 ? static_cast<const float*>(q)[off]
+                            : __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[off]) << 16);
+  }
+  __syncthreads();
+  {
+    // thread i: row i % D of Pi (i < D) or of S (i >= D)
+    const int row = threadIdx.x % D, type = threadIdx.x / D;
+    const float4* src = reinterpret_cast<const float4*>(params + (type ? off_s : off_pi)) +
+                        size_t(row) * (D / 4);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j4 = 0; j4 < D / 4; j4 += 2) {
+      const float4 m0 = src[j4], m1 = src[j4 + 1];
+      a0 = fmaf(m0.x, qv[4 * j4 + 0], a0);
+      a1 = fmaf(m0.y, qv[4 * j4 + 1], a1);
+      a0 = fmaf(m0.z, qv[4 * j4 + 2], a0);
+      a1 = fmaf(m0.w, qv[4 * j4 + 3], a1);
+      a0 = fmaf(m1.x, qv[4 * j4 + 4], a0);
+      a1 = fmaf(m1.y, qv[4 * j4 + 5], a1);
+      a0 = fmaf(m1.z, qv[4 * j4 + 6], a0);
+      a1 = fmaf(m1.w, qv[4 * j4 + 7], a1);
     }
-    qv[i / D][i % D] = v;
+    (type ? sh : qh)[row] = a0 + a1;
   }
   __syncthreads();
-  const float* Pi = reinterpret_cast<const float*>(params + off_pi);
-  const float* S = reinterpret_cast<const float*>(params + off_s);
-  for (int o = threadIdx.x; o < 2 * G * D; o += 256) {
-    const int type = o / (G * D), h = (o / D) % G, t = o % D;
-    const float* row = (type ? S : Pi) + size_t(t) * D;
-    float acc = 0.f;
-    for (int j = 0; j < D; ++j) acc = fmaf(row[j], qv[h][j], acc);
-    (type ? sh : qh)[h][t] = acc;
-  }
-  __syncthreads();
-  if (threadIdx.x < 4 * G) {
-    const int h = threadIdx.x / 4, stat = threadIdx.x % 4;
-    const float* v = (stat < 2) ? qh[h] : sh[h];
+  if (threadIdx.x < 64) {
+    // 4 statistics, 16 threads each
+    const int stat = threadIdx.x / 16, sub = threadIdx.x % 16;
+    const float* v = (stat < 2) ? qh : sh;
     float r = 0.f;
-    if (stat % 2 == 0) {
-      for (int t = 0; t < D; ++t) r = fmaxf(r, fabsf(v[t]));
-    } else {
-      for (int t = 0; t < D; ++t) r += v[t];
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+      const float x = v[sub + 16 * k];
+      r = (stat % 2 == 0) ? fmaxf(r, fabsf(x)) : r + x;
     }
-    stats[h][stat] = r;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      const float o = __shfl_xor(r, off, 16);
+      r = (stat % 2 == 0) ? fmaxf(r, o) : r + o;
+    }
+    if (sub == 0) stats[stat] = r;
   }
   __syncthreads();
 
   const int ne = hdr->ne;
+  const float ma = hdr->emax * stats[0];
+  const float sa = ma > 0.f ? kDigitRange / ma : 1.f;
+  const float sb = stats[2] > 0.f ? kDigitRange / stats[2] : 1.f;
   unsigned char* base = ws + size_t(g) * score_ws_per_group(BITS);
-  // A operands
-  for (int item = threadIdx.x; item < 2 * NW * 64; item += 256) {
-    const int m = item / 64, lane = item % 64;
+  // this head's A operand chunks: 2 NW MFMAs x 4 K groups x 4 rows
+  for (int item = threadIdx.x; item < 2 * NW * 16; item += 256) {
+    const int m = item / 16, part = (item / 4) % 4, grp = item % 4;
+    const int lane = 16 * grp + 4 * h + part;
     const int word = m / 2, j = m % 2;
-    const int row = lane % 16, h = row / 4, part = row % 4, grp = lane / 16;
     const bool mse_word = word < ne;
-    const float ma = hdr->emax * stats[h][0];
-    const float sa = ma > 0.f ? kDigitRange / ma : 1.f;
-    const float sb = stats[h][2] > 0.f ? kDigitRange / stats[h][2] : 1.f;
     uint32_t packed[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -113,10 +128,10 @@ __global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* _
       for (int bi = 0; bi < 4; ++bi) {
         const int coord = 32 * grp + 8 * bi + 2 * k + j;
         float xval = 0.f;
-        if (mse_word && part < 2) xval = hdr->e[word] * qh[h][coord] * sa;
-        if (!mse_word && part >= 2) xval = sh[h][coord] * sb;
+        if (mse_word && part < 2) xval = hdr->e[word] * qh[coord] * sa;
+        if (!mse_word && part >= 2) xval = sh[coord] * sb;
         // value as an integer; odd bit positions carry weight 2, so keep them even
-        int v = (j == 0) ? int(rintf(xval)) : 2 * int(rintf(0.5f * xval));
+        const int v = (j == 0) ? int(rintf(xval)) : 2 * int(rintf(0.5f * xval));
         const int vj = v >> j;
         const int hi = (vj + 64) >> 7;
         const int lo = vj - 128 * hi;
@@ -127,17 +142,13 @@ __global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* _
     }
     reinterpret_cast<uint4*>(base)[m * 64 + lane] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   }
-  // per-query constants: l = nu (A wA - cA + gamma (B wB - cB))
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    const float ma = hdr->emax * stats[h][0];
-    const float sa = ma > 0.f ? kDigitRange / ma : 1.f;
-    const float sb = stats[h][2] > 0.f ? kDigitRange / stats[h][2] : 1.f;
+  // epilogue constants: l = nu (A wA - cA + gamma (B wB - cB))
+  if (threadIdx.x == 0) {
     float4 c;
     c.x = 2.f / sa;
-    c.y = hdr->esum * stats[h][1];
+    c.y = hdr->esum * stats[1];
     c.z = 2.f * hdr->alpha / sb;
-    c.w = hdr->alpha * stats[h][3];
+    c.w = hdr->alpha * stats[3];
     reinterpret_cast<float4*>(base + size_t(2 * NW) * 64 * 16)[h] = c;
   }
 }
@@ -246,7 +257,7 @@ hipError_t launch_b(const void* params, const void* q, int q_dtype, const uint32
   const Layout lay(D, BITS);
   const long qpg = long(Gq / G);
   const int64_t groups = kv_groups * qpg;       // virtual groups of 4 query heads
-  hipLaunchKernelGGL((score_qprep_kernel<BITS>), dim3(unsigned(groups)), dim3(256), 0, s,
+  hipLaunchKernelGGL((score_qprep_kernel<BITS>), dim3(unsigned(groups * G)), dim3(256), 0, s,
                      static_cast<const unsigned char*>(params), lay.off_pi, lay.off_s, q,
                      q_dtype == 0 ? 1 : 0, static_cast<unsigned char*>(ws));
   hipError_t e = hipGetLastError();
