@@ -1,0 +1,79 @@
+"""GPU top-k search vs the oracle's scores of every key (oracle fed the GPU's codes)."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_embedding_amd as tq
+import oracle
+from workloads import gen
+import tq_testutil as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_scores(st, q64, idx, z, nu, gamma, mode="prod"):
+    ref = oracle.estimate_ip(q64, st.Pi, st.S, idx, z, nu, gamma, st.c_or, mode)
+    scale = np.linalg.norm(q64, axis=1)[:, None] * np.maximum(nu[None, :], 1e-30)
+    return ref, scale
+
+
+@pytest.mark.parametrize("n,nq,k", [(4096, 64, 10), (5000, 130, 7), (2049, 3, 1), (3000, 17, 32)])
+def test_topk_d128_gpu_codes(n, nq, k):
+    # toy workload shape (unit vectors, b = 4) plus ragged tiles, query tiles and k values
+    st = U.make_setup(128, 4, cfg=0)
+    x = gen.unit_sphere(n, 128, cfg=0, role=gen.ROLE_DATA)
+    q = gen.unit_sphere(nq, 128, cfg=0, role=gen.ROLE_QUERY)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    idx_g, sc_g = U.gpu_topk(st, U.to_device(q, False), codes, nu, gamma, n, k, tq.TQ_EST_PROD)
+    idx, z = oracle.unpack_codes(U.codes_np(codes, n, 128, 4), 4)
+    ref, scale = _oracle_scores(st, q.astype(np.float64), idx, z, nu.cpu().numpy(), gamma.cpu().numpy())
+    worst, swapped = U.check_topk(idx_g, sc_g, ref, scale)
+    print(f"[topk d=128 n={n} nq={nq} k={k}] max score err {worst:.2e}, near-tie swaps {swapped}", flush=True)
+    assert worst <= U.LOGIT_TOL
+
+
+def test_topk_mse_mode_and_several_chunks():
+    # n above one key chunk (65536) exercises the chunk loop and the cross-chunk merge
+    st = U.make_setup(128, 2, cfg=31)
+    n, nq, k = 70000, 9, 10
+    x = gen.unit_sphere(n, 128, cfg=31, role=gen.ROLE_DATA)
+    q = gen.unit_sphere(nq, 128, cfg=31, role=gen.ROLE_QUERY)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    idx, z = oracle.unpack_codes(U.codes_np(codes, n, 128, 2), 2)
+    for mode, name in ((tq.TQ_EST_PROD, "prod"), (tq.TQ_EST_MSE, "mse")):
+        idx_g, sc_g = U.gpu_topk(st, U.to_device(q, False), codes, nu, gamma, n, k, mode)
+        ref, scale = _oracle_scores(st, q.astype(np.float64), idx, z, nu.cpu().numpy(),
+                                    gamma.cpu().numpy(), name)
+        worst, swapped = U.check_topk(idx_g, sc_g, ref, scale)
+        print(f"[topk chunks mode={name}] max err {worst:.2e} swaps {swapped}", flush=True)
+        assert worst <= U.LOGIT_TOL
+
+
+@pytest.mark.parametrize("b", [2, 4])
+def test_topk_d1536_oracle_codes(b):
+    # embedding-search shape (d = 1536, low-rank + noise, unit norm) on codes packed by the
+    # oracle: top-k alone, independent of the encoder
+    d, n, nq, k = 1536, 3000, 20, 10
+    st = U.make_setup(d, b, cfg=3)
+    x = gen.lowrank_vectors(n, d, 64, 3.0, cfg=3)
+    q = gen.lowrank_queries(nq, d, 64, 3.0, cfg=3)
+    r = oracle.quantize(x.astype(np.float64), st.Pi, st.S, st.c_or, st.t_or)
+    cn = oracle.pack_codes(r["idx"], r["z"], b)
+    codes = torch.from_numpy(cn.view(np.int32).reshape(-1).copy()).to(U.DEV)
+    nu = torch.from_numpy(r["nu"].astype(np.float32)).to(U.DEV)
+    gamma = torch.from_numpy(r["gamma"].astype(np.float32)).to(U.DEV)
+    idx_g, sc_g = U.gpu_topk(st, U.to_device(q, False), codes, nu, gamma, n, k, tq.TQ_EST_PROD)
+    ref, scale = _oracle_scores(st, q.astype(np.float64), r["idx"], r["z"], nu.cpu().numpy().astype(np.float64),
+                                gamma.cpu().numpy().astype(np.float64))
+    worst, swapped = U.check_topk(idx_g, sc_g, ref, scale)
+    print(f"[topk d=1536 b={b}] max err {worst:.2e} swaps {swapped}", flush=True)
+    assert worst <= U.LOGIT_TOL
+
+
+def test_topk_rejects_large_k():
+    st = U.make_setup(128, 4, cfg=0)
+    x = gen.unit_sphere(100, 128, cfg=0, role=gen.ROLE_DATA)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    with pytest.raises(tq.TQError) as e:
+        U.gpu_topk(st, U.to_device(x[:2], False), codes, nu, gamma, 100, 33, tq.TQ_EST_PROD)
+    assert e.value.status == tq.TQ_EUNSUPPORTED

@@ -159,3 +159,47 @@ def describe(rep: dict) -> str:
             f"z unexcused={rep['unexcused_z']} excused={rep['excused_z']} "
             f"rate={rep['excused_rate']:.2e} nu_err={rep['nu_rel_err']:.1e} "
             f"gamma_err={rep['gamma_abs_err']:.1e}")
+
+
+def gpu_topk(st: Setup, qd: torch.Tensor, codes, nu, gamma, n: int, k: int, mode: int):
+    nq = qd.shape[0]
+    idx = torch.full((nq * k,), -7, dtype=torch.int32, device=DEV)
+    score = torch.full((nq * k,), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.tq_topk_ws_bytes(st.d, st.b, nq, n, k), dtype=torch.uint8, device=DEV)
+    tq.tq_topk(st.params, st.d, st.b, qd, codes, nu, gamma, n, k, mode, idx, score, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy().reshape(nq, k), score.cpu().numpy().reshape(nq, k)
+
+
+def check_topk(idx_g: np.ndarray, score_g: np.ndarray, ref: np.ndarray, scale: np.ndarray):
+    """Compare GPU top-k with the oracle's scores of every key (oracle fed the GPU codes).
+
+    ref [nq][n] float64 oracle scores; scale [nq][n] = |q| nu for the score tolerance.
+    Rules: every returned score within LOGIT_TOL * scale of the oracle's score of that key;
+    scores non-increasing; the returned set equals the oracle's top-k except swaps between
+    keys whose oracle scores differ by at most 4x the largest score error seen for that
+    query (near ties).  Returns (max relative score error, number of queries with swaps).
+    """
+    nq, k = idx_g.shape
+    worst = 0.0
+    swapped = 0
+    for a in range(nq):
+        ids = idx_g[a]
+        assert np.all((ids >= 0) & (ids < ref.shape[1])), ids
+        assert len(set(ids.tolist())) == k
+        err = np.abs(score_g[a].astype(np.float64) - ref[a, ids])
+        rel = err / np.maximum(scale[a, ids], 1e-30)
+        worst = max(worst, float(rel.max()))
+        assert np.all(np.diff(score_g[a]) <= 0), score_g[a]
+        o_ids, o_vals = oracle.topk(ref[a:a + 1], k)
+        o_set, g_set = set(o_ids[0].tolist()), set(ids.tolist())
+        if o_set != g_set:
+            swapped += 1
+            tol = 4.0 * float(err.max()) + 1e-12
+            kth = o_vals[0, -1]
+            for j in g_set - o_set:
+                assert ref[a, j] >= kth - tol, (a, j, ref[a, j], kth, tol)
+            g_min = min(ref[a, j] for j in g_set)
+            for j in o_set - g_set:
+                assert ref[a, j] <= g_min + tol, (a, j, ref[a, j], g_min, tol)
+    return worst, swapped
