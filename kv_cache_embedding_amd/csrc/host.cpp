@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <thread>
 #include <vector>
 
 namespace {
@@ -99,6 +100,23 @@ double dot(const double* a, const double* b, int n) {
   }
   for (; i < n; ++i) s0 += a[i] * b[i];
   return (s0 + s1) + (s2 + s3);
+}
+
+// Run f(i) for i in [0, n) on the host cores (used for the d^3 host products at large d).
+template <class F>
+void parallel_for(int n, F f) {
+  const unsigned hw = std::thread::hardware_concurrency();
+  const int nt = int(hw == 0 ? 1 : (hw > 16 ? 16 : hw));
+  if (n < 64 || nt == 1) {
+    for (int i = 0; i < n; ++i) f(i);
+    return;
+  }
+  std::vector<std::thread> th;
+  for (int t = 0; t < nt; ++t)
+    th.emplace_back([&, t] {
+      for (int i = t; i < n; i += nt) f(i);
+    });
+  for (auto& x : th) x.join();
 }
 
 // Output-row permutation of a 32-row MFMA tile: row rho holds canonical coordinate
@@ -247,20 +265,36 @@ int tq_prepare(int d, int b, const float* Pi, const float* S, const double* cent
       return fail(TQ_EINVAL, "non-finite entry in Pi or S");
   }
   // Pi must be orthogonal: the kernels form the residual in the rotated space.
-  double worst = 0.0;
-  for (int i = 0; i < d; ++i)
+  std::vector<double> row_worst(d, 0.0);
+  parallel_for(d, [&](int i) {
+    double w = 0.0;
     for (int j = i; j < d; ++j) {
       double g = dot(&P64[size_t(i) * d], &P64[size_t(j) * d], d) - (i == j ? 1.0 : 0.0);
-      worst = std::fmax(worst, std::fabs(g));
+      w = std::fmax(w, std::fabs(g));
     }
+    row_worst[i] = w;
+  });
+  double worst = 0.0;
+  for (double w : row_worst) worst = std::fmax(worst, w);
   if (worst > 1e-4) return fail(TQ_EINVAL, "Pi is not orthogonal (max |Pi Pi^T - I| = %g)", worst);
 
-  if (lay.qfrag_bytes) {
+  if (lay.qfrag_bytes || lay.gmat_bytes) {
     // S' = S Pi^T, so that S r = S' (Pi r) for the residual r (rotated-space residual)
     std::vector<double> Sp(size_t(d) * d);
-    for (int i = 0; i < d; ++i)
+    parallel_for(d, [&](int i) {
       for (int k = 0; k < d; ++k) Sp[size_t(i) * d + k] = dot(&S64[size_t(i) * d], &P64[size_t(k) * d], d);
-    build_quantize_fragments(P64, Sp, reinterpret_cast<uint16_t*>(blob.data() + lay.off_qfrag));
+    });
+    if (lay.qfrag_bytes)
+      build_quantize_fragments(P64, Sp, reinterpret_cast<uint16_t*>(blob.data() + lay.off_qfrag));
+    if (lay.gmat_bytes) {
+      // row-major bf16 hi/lo of Pi and S' for the tiled encoder
+      uint16_t* g = reinterpret_cast<uint16_t*>(blob.data() + lay.off_gmat);
+      const size_t dd = size_t(d) * d;
+      for (size_t i = 0; i < dd; ++i) {
+        split_bf16(P64[i], g[i], g[dd + i]);
+        split_bf16(Sp[i], g[2 * dd + i], g[3 * dd + i]);
+      }
+    }
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -281,9 +315,12 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
   if (!aligned(params, 256) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(nu, 4) ||
       !aligned(gamma, 4))
     return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x and codes 16 B)");
-  if (d != 128) return fail(TQ_EUNSUPPORTED, "tq_quantize: only d=128 is implemented");
-  hipError_t e = tq::launch_quantize_d128(params, b, x, x_dtype, n, codes, nu, gamma,
-                                          static_cast<hipStream_t>(stream));
+  if (d % 128 != 0)
+    return fail(TQ_EUNSUPPORTED, "tq_quantize: d must be a multiple of 128 (got %d)", d);
+  hipError_t e = d == 128 ? tq::launch_quantize_d128(params, b, x, x_dtype, n, codes, nu, gamma,
+                                                     static_cast<hipStream_t>(stream))
+                          : tq::launch_quantize_gemm(params, d, b, x, x_dtype, n, codes, nu, gamma,
+                                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tq_quantize launch");
   return ok();
 }

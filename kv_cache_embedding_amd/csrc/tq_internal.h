@@ -38,6 +38,8 @@ struct Layout {
   size_t off_s = 0;       // S   [d][d] fp32 row-major
   size_t off_qfrag = 0;   // d == 128: quantize MFMA fragments (2 x 64 KiB), else 0 bytes
   size_t qfrag_bytes = 0;
+  size_t off_gmat = 0;    // other d (multiple of 128): bf16 Pi_hi, Pi_lo, S'_hi, S'_lo [d][d]
+  size_t gmat_bytes = 0;
   size_t total = 0;
   Layout(int d_, int b_);
 };
@@ -50,7 +52,9 @@ inline Layout::Layout(int d_, int b_) : d(d_), b(b_) {
   off_s = align256(off_pi + size_t(d) * d * 4);
   off_qfrag = align256(off_s + size_t(d) * d * 4);
   qfrag_bytes = (d == 128) ? size_t(2) * 64 * 1024 : 0;
-  total = align256(off_qfrag + qfrag_bytes);
+  off_gmat = align256(off_qfrag + qfrag_bytes);
+  gmat_bytes = (d != 128 && d % 128 == 0) ? size_t(4) * d * d * 2 : 0;
+  total = align256(off_gmat + gmat_bytes);
 }
 
 // Plane words per key that the scoring kernel feeds to the MFMA: the b-1 index planes,
@@ -65,6 +69,9 @@ constexpr size_t score_ws_per_group(int b) {
 // ---- kernel launchers (defined in the .hip files), return hipError_t
 hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_dtype, int64_t n,
                                 uint32_t* codes, float* nu, float* gamma, hipStream_t s);
+hipError_t launch_quantize_gemm(const void* params, int d, int b, const void* x, int x_dtype,
+                                int64_t n, uint32_t* codes, float* nu, float* gamma,
+                                hipStream_t s);
 hipError_t launch_score_d128(const void* params, int b, const void* q, int q_dtype,
                              const uint32_t* codes, const float* nu, const float* gamma,
                              int64_t groups, int64_t G, int64_t T, int mode, float* logits,

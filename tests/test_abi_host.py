@@ -82,8 +82,8 @@ def test_invalid_arguments_return_status_without_launch(lib):
     assert lib.tq_quantize(fake, 128, 4, P(0x1002), 0, 10, fake, fake, fake, None) == tq.TQ_EINVAL
     # n == 0 is a no-op even with NULL pointers
     assert lib.tq_quantize(None, 128, 4, None, 0, 0, None, None, None, None) == tq.TQ_OK
-    # unsupported dimension for the fused encoder
-    assert lib.tq_quantize(fake, 256, 4, fake, 0, 10, fake, fake, fake, None) == tq.TQ_EUNSUPPORTED
+    # a valid dimension that no encoder implements (not a multiple of 128)
+    assert lib.tq_quantize(fake, 192, 4, fake, 0, 10, fake, fake, fake, None) == tq.TQ_EUNSUPPORTED
     # scoring: bad mode, workspace too small, unsupported G
     args = (fake, 128, 4, fake, 1, fake, fake, fake, 8, 4, 1024)
     assert lib.tq_score_ip(*args, 9, fake, fake, 1 << 30, None) == tq.TQ_EINVAL

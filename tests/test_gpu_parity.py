@@ -161,3 +161,31 @@ def test_dequantize_parity(b, mode):
                             "prod" if mode == tq.TQ_EST_PROD else "mse")
     err = np.max(np.abs(xhat.cpu().numpy().reshape(300, 128) - ref)) / 3.0
     assert err <= 1e-5, err
+
+
+# ------------------------------------------------------- tiled encoder (d != 128)
+
+@pytest.mark.parametrize("b,n", [(2, 3000), (4, 16384 + 300)])
+def test_quantize_d1536_lowrank_f32(b, n):
+    # embedding-search law (low rank + noise, unit norm, fp32), d = 1536; n crosses the
+    # 16384-vector chunk of the tiled encoder in the second case
+    st = U.make_setup(1536, b, cfg=3)
+    x = gen.lowrank_vectors(n, 1536, 64, 3.0, cfg=3)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    rep = U.compare_codes(st, U.host64(x, False), U.codes_np(codes, n, 1536, b),
+                          nu.cpu().numpy(), gamma.cpu().numpy())
+    _report(f"d1536 b={b} n={n}", rep)
+    U.assert_codes_ok(rep)
+
+
+def test_quantize_d256_bf16_and_zero_vectors():
+    st = U.make_setup(256, 3, cfg=8)
+    chans = gen.outlier_channels(8, 1, 256)
+    keys = gen.kv_keys_chunk(8, 0, 0, 1000, 256, chans[0])
+    keys[[0, 999]] = 0
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(keys, True))
+    rep = U.compare_codes(st, U.host64(keys, True), U.codes_np(codes, 1000, 256, 3),
+                          nu.cpu().numpy(), gamma.cpu().numpy())
+    _report("d256 bf16 b=3", rep)
+    U.assert_codes_ok(rep)
+    assert nu.cpu().numpy()[[0, 999]].tolist() == [0.0, 0.0]

@@ -77,3 +77,20 @@ def test_topk_rejects_large_k():
     with pytest.raises(tq.TQError) as e:
         U.gpu_topk(st, U.to_device(x[:2], False), codes, nu, gamma, 100, 33, tq.TQ_EST_PROD)
     assert e.value.status == tq.TQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("b", [2, 4])
+def test_topk_d1536_gpu_codes(b):
+    # end to end at d = 1536: tiled encoder, then search
+    d, n, nq, k = 1536, 5000, 40, 10
+    st = U.make_setup(d, b, cfg=3)
+    x = gen.lowrank_vectors(n, d, 64, 3.0, cfg=3)
+    q = gen.lowrank_queries(nq, d, 64, 3.0, cfg=3)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    idx_g, sc_g = U.gpu_topk(st, U.to_device(q, False), codes, nu, gamma, n, k, tq.TQ_EST_PROD)
+    idx, z = oracle.unpack_codes(U.codes_np(codes, n, d, b), b)
+    ref, scale = _oracle_scores(st, q.astype(np.float64), idx, z, nu.cpu().numpy().astype(np.float64),
+                                gamma.cpu().numpy().astype(np.float64))
+    worst, swapped = U.check_topk(idx_g, sc_g, ref, scale)
+    print(f"[topk d=1536 gpu codes b={b}] max err {worst:.2e} swaps {swapped}", flush=True)
+    assert worst <= U.LOGIT_TOL
