@@ -17,7 +17,8 @@ def _oracle_scores(st, q64, idx, z, nu, gamma, mode="prod"):
     return ref, scale
 
 
-@pytest.mark.parametrize("n,nq,k", [(4096, 64, 10), (5000, 130, 7), (2049, 3, 1), (3000, 17, 32)])
+@pytest.mark.parametrize("n,nq,k", [(4096, 64, 10), (5000, 130, 7), (2049, 3, 1), (3000, 17, 32),
+                                    (9000, 300, 10)])
 def test_topk_d128_gpu_codes(n, nq, k):
     # toy workload shape (unit vectors, b = 4) plus ragged tiles, query tiles and k values
     st = U.make_setup(128, 4, cfg=0)
@@ -32,10 +33,11 @@ def test_topk_d128_gpu_codes(n, nq, k):
     assert worst <= U.LOGIT_TOL
 
 
-def test_topk_mse_mode_and_several_chunks():
-    # n above one key chunk (65536) exercises the chunk loop and the cross-chunk merge
+def test_topk_mse_mode_and_long_key_ranges():
+    # 200000 keys with one query tile: each workgroup scans several 256-key blocks, so the
+    # running lists and thresholds carry across blocks before the cross-range merge
     st = U.make_setup(128, 2, cfg=31)
-    n, nq, k = 70000, 9, 10
+    n, nq, k = 200000, 9, 10
     x = gen.unit_sphere(n, 128, cfg=31, role=gen.ROLE_DATA)
     q = gen.unit_sphere(nq, 128, cfg=31, role=gen.ROLE_QUERY)
     codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
@@ -47,6 +49,27 @@ def test_topk_mse_mode_and_several_chunks():
         worst, swapped = U.check_topk(idx_g, sc_g, ref, scale)
         print(f"[topk chunks mode={name}] max err {worst:.2e} swaps {swapped}", flush=True)
         assert worst <= U.LOGIT_TOL
+
+
+def test_topk_b3_bf16_queries_and_zero_query():
+    # KV-key law (bf16, outlier channels), b = 3, bf16 queries; query 5 is all zero, so every
+    # score is 0 and the result is the k smallest indices
+    st = U.make_setup(128, 3, cfg=32)
+    chans = gen.outlier_channels(32, 1, 128)
+    keys = gen.kv_keys_chunk(32, 0, 0, 6000, 128, chans[0])
+    q = gen.kv_queries(32, 1, 12, 128)[0]
+    q[5] = 0
+    n, nq, k = keys.shape[0], q.shape[0], 10
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(keys, True))
+    idx_g, sc_g = U.gpu_topk(st, U.to_device(q, True), codes, nu, gamma, n, k, tq.TQ_EST_PROD)
+    idx, z = oracle.unpack_codes(U.codes_np(codes, n, 128, 3), 3)
+    q64 = U.host64(q, True)
+    ref, scale = _oracle_scores(st, q64, idx, z, nu.cpu().numpy(), gamma.cpu().numpy())
+    keep = [a for a in range(nq) if a != 5]
+    worst, swapped = U.check_topk(idx_g[keep], sc_g[keep], ref[keep], scale[keep])
+    print(f"[topk b=3 bf16] max err {worst:.2e} swaps {swapped}", flush=True)
+    assert worst <= U.LOGIT_TOL
+    assert idx_g[5].tolist() == list(range(k)) and np.all(sc_g[5] == 0.0)
 
 
 @pytest.mark.parametrize("b", [2, 4])
