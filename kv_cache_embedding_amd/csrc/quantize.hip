@@ -180,45 +180,48 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     float g2 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+      // Index bits from |u| against the positive thresholds (a binary search over the
+      // magnitude index k of the level), the level's sign from u: for u >= 0 the index is
+      // L/2 + k, for u < 0 it is L/2 - 1 - k, i.e. the bits of k complemented.  So the index
+      // planes are the k planes xor the sign plane, applied once per 16-coordinate word.
       uint32_t w0 = 0, w1 = 0, ws = 0;
       float rr[16];
 #pragma unroll
       for (int r = 15; r >= 0; --r) {
         const float u = U[mt][r];
-        ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(u), 31);
-        float c;
+        const float a = fabsf(u);
+        ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(u), 31);   // 1 = u < 0
+        float cm;
         if constexpr (BITS == 2) {
-          c = copysignf(M[0], u);
+          cm = M[0];
         } else if constexpr (BITS == 3) {
-          // idx = 2 b1 + b0 over thresholds (-T0, 0, T0); b1 = sign plane
-          const bool b1 = u >= 0.f;
-          const bool b0 = u >= copysignf(T[0], u);
-          c = copysignf((b0 == b1) ? M[1] : M[0], u);
-          w0 = (w0 << 1) | uint32_t(b0);
+          const bool k0 = a >= T[0];
+          cm = k0 ? M[1] : M[0];
+          w0 = (w0 << 1) | uint32_t(k0);
         } else {
-          // idx = 4 b2 + 2 b1 + b0 over thresholds (-T2, -T1, -T0, 0, T0, T1, T2); b2 = sign
-          const bool b2 = u >= 0.f;
-          const bool b1 = u >= copysignf(T[1], u);
-          const bool e1 = (b1 == b2);
-          const bool b0 = u >= copysignf(e1 ? T[2] : T[0], u);
-          const bool e0 = (b0 == b2);
-          c = copysignf(e1 ? (e0 ? M[3] : M[2]) : (e0 ? M[1] : M[0]), u);
-          w0 = (w0 << 1) | uint32_t(b0);
-          w1 = (w1 << 1) | uint32_t(b1);
+          const bool k1 = a >= T[1];
+          const bool k0 = a >= (k1 ? T[2] : T[0]);
+          const float mlo = k0 ? M[1] : M[0];
+          const float mhi = k0 ? M[3] : M[2];
+          cm = k1 ? mhi : mlo;
+          w0 = (w0 << 1) | uint32_t(k0);
+          w1 = (w1 << 1) | uint32_t(k1);
         }
+        const float c = __uint_as_float((__float_as_uint(cm) & 0x7fffffffu) | (__float_as_uint(u) & 0x80000000u));
         const float rv = u - c;
         rr[r] = rv;
         g2 = fmaf(rv, rv, g2);
       }
-      const uint32_t wsign = ~ws & 0xffffu;     // 1 = u >= 0
+      const uint32_t sgn = ws & 0xffffu;          // 1 = u < 0
+      const uint32_t wsign = ~ws & 0xffffu;       // sign plane: 1 = u >= 0
       if constexpr (BITS == 2) {
         hb[0][mt] = wsign;
       } else if constexpr (BITS == 3) {
-        hb[0][mt] = w0;
+        hb[0][mt] = w0 ^ sgn;
         hb[1][mt] = wsign;
       } else {
-        hb[0][mt] = w0;
-        hb[1][mt] = w1;
+        hb[0][mt] = w0 ^ sgn;
+        hb[1][mt] = w1 ^ sgn;
         hb[2][mt] = wsign;
       }
 #pragma unroll
@@ -325,6 +328,7 @@ int cu_count() {
 template <int BITS, bool F32IN>
 hipError_t launch(const void* params, const void* x, int64_t n, uint32_t* codes, float* nu,
                   float* gamma, hipStream_t s) {
+
   const long ntiles = (n + VPW - 1) / VPW;
   const long need = (ntiles + WAVES - 1) / WAVES;
   const int grid = int(need < cu_count() ? need : cu_count());
