@@ -34,12 +34,6 @@ constexpr int D = 128;
 constexpr int WAVES = 8;                    // waves per workgroup (2 per SIMD)
 constexpr int VPW = 32;                     // vectors per wave tile
 constexpr int FRAG_U4 = 64 * 1024 / 16;     // uint4 per fragment set (Pi~ or S'~)
-#ifndef TQ_Q_PHASE_SLEEP
-#define TQ_Q_PHASE_SLEEP 0     // s_sleep units (64 cycles) for the second wave of each SIMD
-#endif
-#ifndef TQ_Q_MFMA_PRIO
-#define TQ_Q_MFMA_PRIO 0       // raise wave priority while issuing MFMA blocks
-#endif
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -53,13 +47,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     long n, uint32_t* __restrict__ codes, float* __restrict__ nu_out,
     float* __restrict__ gamma_out) {
   __shared__ uint4 frag[2 * FRAG_U4];  // [0, FRAG_U4): Pi~ fragments; then S'~ fragments
+  __shared__ int next_tile;            // work queue of this workgroup's tile range
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kh = lane >> 5;               // lane half: K group of the operands
   const long ntiles = (n + VPW - 1) / VPW;
-  const long stride = long(gridDim.x) * WAVES;
-  long tile = long(blockIdx.x) * WAVES + wave;
+  // Each workgroup owns a contiguous range of tiles; its waves take tiles from it through
+  // an LDS counter.  The two waves that share a SIMD do not progress at the same rate (the
+  // older one wins issue arbitration), so a static split would leave the SIMD running one
+  // wave for the last part of the kernel.
+  const long per_wg = (ntiles + gridDim.x - 1) / gridDim.x;
+  const long t_begin = long(blockIdx.x) * per_wg;
+  const long t_end = t_begin + per_wg < ntiles ? t_begin + per_wg : ntiles;
+  long tile = t_begin + wave;            // the first tile of each wave is fixed
+  if (threadIdx.x == 0) next_tile = 0;
+  auto grab = [&]() -> long {            // next tile of this wave (t_end when none is left)
+    int k = 0;
+    if (lane == 0) k = atomicAdd(&next_tile, 1);
+    const long t = t_begin + WAVES + __builtin_amdgcn_readfirstlane(k);
+    return t < t_end ? t : t_end;
+  };
 
   // Raw input of this lane's half vector (coordinates 64 kh .. 64 kh + 63), loaded one
   // tile ahead of its use.
@@ -73,17 +81,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
 #pragma unroll
     for (int i = 0; i < NRAW; ++i) raw[i] = p[i];
   };
-  if (tile < ntiles) load_tile(tile);     // in flight while the fragments fill LDS
+  if (tile < t_end) load_tile(tile);      // in flight while the fragments fill LDS
   {
     const uint4* src = reinterpret_cast<const uint4*>(params + frag_off);
     for (int i = threadIdx.x; i < 2 * FRAG_U4; i += WAVES * 64) frag[i] = src[i];
   }
   __syncthreads();
-#if TQ_Q_PHASE_SLEEP
-  // start the two waves sharing a SIMD out of phase, so that one is in its MFMA blocks
-  // while the other is in its VALU blocks
-  if (wave >= 4) __builtin_amdgcn_s_sleep(TQ_Q_PHASE_SLEEP);
-#endif
 
   const Header* hdr = reinterpret_cast<const Header*>(params);
   constexpr int L = 1 << (BITS - 1);
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
 #pragma unroll
   for (int k = 0; k < L / 2; ++k) mp[k] = hdr->mpos[k];
 
-  for (; tile < ntiles; tile += stride) {
+  while (tile < t_end) {
     const long vec = tile * VPW + (lane & 31);
     const bool valid = vec < n;
 
@@ -133,9 +136,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     const float sc = nu > 0.f ? nu : 1.f;   // zero vector: u is taken as 0, grid unscaled
 
     // ---- GEMM1: U^T = Pi~ X^T, one 32-row tile at a time
-#if TQ_Q_MFMA_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
     f32x16 U[4];
 #pragma unroll
     for (int mp = 0; mp < 4; mp += 2) {
@@ -160,11 +160,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);   // bound the fragment reads in flight
     }
-#if TQ_Q_MFMA_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
     // the input registers are free: fetch the next tile while this one is finished
-    if (tile + stride < ntiles) load_tile(tile + stride);
+    const long next = grab();
+    if (next < t_end) load_tile(next);
 
     // ---- bucketize + residual against nu-scaled thresholds (u is never divided by nu).
     // Bits of the sign plane are the float sign bits of u, shifted in with v_alignbit and
@@ -247,9 +245,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
 
     // ---- GEMM2: Y^T = S'~ R'^T, one 32-row tile of projections at a time; the sign
     //      bits of y are shifted in the same way (y is never -0 either)
-#if TQ_Q_MFMA_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
     for (int mp = 0; mp < 4; mp += 2) {
       f32x16 Y[2] = {f32x16{}, f32x16{}};
@@ -278,9 +273,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-#if TQ_Q_MFMA_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
     // ---- assemble whole words: half h = 0 finishes row tiles 0,1; h = 1 tiles 2,3
     uint32_t out[2 * BITS];
 #pragma unroll
@@ -309,6 +301,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
         gamma_out[vec] = gamma;
       }
     }
+    tile = next;
   }
 }
 

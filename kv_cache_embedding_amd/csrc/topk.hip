@@ -192,8 +192,6 @@ __device__ __forceinline__ uint32_t f16_bits(float v) {
 }
 
 // ------------------------------------------------------------- scan + running top-k
-// vmcnt-only s_waitcnt immediate (expcnt and lgkmcnt left unconstrained)
-constexpr int vmcnt_only(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
 
 template <int B, bool PROD, int KM>
 __global__ __launch_bounds__(256, 1) void topk_scan_kernel(

@@ -84,4 +84,9 @@ hipError_t launch_topk(const void* params, int d, int b, const void* q, int q_dt
                        int k, int mode, int32_t* idx, float* score, void* ws, hipStream_t s);
 size_t topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k);
 
+// vmcnt-only s_waitcnt immediate for gfx9 (expcnt and lgkmcnt left unconstrained).  Direct
+// global -> LDS loads count in vmcnt, and the compiler does not order later LDS reads after
+// them: kernels that use them wait explicitly.
+constexpr int vmcnt_only(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
+
 }  // namespace tq
