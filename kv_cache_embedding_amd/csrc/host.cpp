@@ -257,6 +257,16 @@ int tq_prepare(int d, int b, const float* Pi, const float* S, const double* cent
   // Pi and S in float32 (row-major), and float64 copies for host products
   std::memcpy(blob.data() + lay.off_pi, Pi, size_t(d) * d * 4);
   std::memcpy(blob.data() + lay.off_s, S, size_t(d) * d * 4);
+  if (lay.tr_bytes) {
+    // transposed copies: the scoring query prep reads column k of both with one
+    // contiguous load per wave
+    float* tr = reinterpret_cast<float*>(blob.data() + lay.off_tr);
+    for (int i = 0; i < d; ++i)
+      for (int k = 0; k < d; ++k) {
+        tr[size_t(k) * d + i] = Pi[size_t(i) * d + k];
+        tr[size_t(d) * d + size_t(k) * d + i] = S[size_t(i) * d + k];
+      }
+  }
   std::vector<double> P64(size_t(d) * d), S64(size_t(d) * d);
   for (size_t i = 0; i < P64.size(); ++i) {
     P64[i] = Pi[i];

@@ -29,7 +29,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int G = 4;
-constexpr int UNR = 4;        // tiles loaded ahead per wave iteration
+// Bytes in flight: each wave keeps UNR key tiles of loads outstanding, and the key ranges
+// are sized for WAVES_PER_CU waves per compute unit (both chosen by measurement on the
+// long-context workload: 4 / 16 -> 8 / 32 took the scan from 280 to 258 us).
+constexpr int UNR = 8;               // tiles loaded ahead per wave iteration
+constexpr int WAVES_PER_CU = 32;     // key ranges (waves) per compute unit
 constexpr float kDigitRange = 16000.f;
 
 int cu_count_s() {
@@ -45,81 +49,97 @@ int cu_count_s() {
 }
 
 // ------------------------------------------------------------------------ query prep
-// One workgroup per (virtual group, query head h): qh = Pi q, sh = S q (float32, one row
-// per thread), the head's scales, then its rows 4h .. 4h+3 of the MFMA A operands in
-// register order ws[g][m][lane][16 bytes] (m = 2 word + j; lane l holds row l % 16), and
-// its four epilogue constants.
+// Two workgroups per virtual group (G query heads): type 0 forms qh = Pi q and the MSE rows
+// of the MFMA A operands, type 1 forms sh = S q and the QJL rows; the two halves share
+// nothing.  Thread i accumulates row i % D over half of the columns (i / D), reading
+// column k of the transposed matrix with one contiguous load per wave; all its loads are
+// issued before the first product.  Outputs: rows 4 h + part of the A operands in register
+// order ws[g][m][lane][16 bytes] (m = 2 word + j; lane l holds row l % 16) and the
+// epilogue constants per head.
 template <int BITS>
 __global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* __restrict__ params,
-                                                           size_t off_pi, size_t off_s,
+                                                           size_t off_tr,
                                                            const void* __restrict__ q, int q_f32,
                                                            unsigned char* __restrict__ ws) {
   constexpr int NW = score_words(BITS);
+  constexpr int KH = D / 2;
   const Header* hdr = reinterpret_cast<const Header*>(params);
-  const long g = blockIdx.x / G;
-  const int h = blockIdx.x % G;
-  __shared__ float qv[D];
-  __shared__ float qh[D];
-  __shared__ float sh[D];
-  __shared__ float stats[4];   // max|qh|, sum qh, max|sh|, sum sh
+  const long g = blockIdx.x >> 1;
+  const int type = blockIdx.x & 1;         // 0: Pi (MSE rows), 1: S (QJL rows)
+  const int tid = threadIdx.x;
+  // header fields, read once (a per-lane index into the header would be a memory load in
+  // the packing loop)
+  const float e0 = hdr->e[0], e1 = hdr->e[1], e2 = hdr->e[2], e3 = hdr->e[3];
+  const float emax = hdr->emax, esum = hdr->esum, alpha = hdr->alpha;
+  const int ne = hdr->ne;
+  __shared__ float4 qv[D];                 // q of the G heads, column-major: qv[k] = heads 0..3
+  __shared__ float part_sum[2][G][D];
+  __shared__ float stats[G][2];            // per head: max |v|, sum v
 
-  if (threadIdx.x < D) {
-    const long off = (g * G + h) * D + threadIdx.x;
-    qv[threadIdx.x] = q_f32 ? static_cast<const float*>(q)[off]
-                            : __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[off]) << 16);
+  for (int i = tid; i < G * D; i += 256) {
+    const long off = g * G * D + i;
+    reinterpret_cast<float*>(qv)[(i % D) * G + i / D] =
+        q_f32 ? static_cast<const float*>(q)[off]
+              : __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[off]) << 16);
   }
-  __syncthreads();
   {
-    // thread i: row i % D of Pi (i < D) or of S (i >= D)
-    const int row = threadIdx.x % D, type = threadIdx.x / D;
-    const float4* src = reinterpret_cast<const float4*>(params + (type ? off_s : off_pi)) +
-                        size_t(row) * (D / 4);
-    float a0 = 0.f, a1 = 0.f;
+    const int row = tid % D, half = tid / D;
+    const float* col = reinterpret_cast<const float*>(params + off_tr) + size_t(type) * D * D +
+                       size_t(half) * KH * D + row;
+    float m[KH];
 #pragma unroll
-    for (int j4 = 0; j4 < D / 4; j4 += 2) {
-      const float4 m0 = src[j4], m1 = src[j4 + 1];
-      a0 = fmaf(m0.x, qv[4 * j4 + 0], a0);
-      a1 = fmaf(m0.y, qv[4 * j4 + 1], a1);
-      a0 = fmaf(m0.z, qv[4 * j4 + 2], a0);
-      a1 = fmaf(m0.w, qv[4 * j4 + 3], a1);
-      a0 = fmaf(m1.x, qv[4 * j4 + 4], a0);
-      a1 = fmaf(m1.y, qv[4 * j4 + 5], a1);
-      a0 = fmaf(m1.z, qv[4 * j4 + 6], a0);
-      a1 = fmaf(m1.w, qv[4 * j4 + 7], a1);
+    for (int k = 0; k < KH; ++k) m[k] = col[size_t(k) * D];
+    __syncthreads();                       // q is in LDS
+    float acc[G] = {};
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      const float4 qk = qv[half * KH + k];
+      acc[0] = fmaf(m[k], qk.x, acc[0]);
+      acc[1] = fmaf(m[k], qk.y, acc[1]);
+      acc[2] = fmaf(m[k], qk.z, acc[2]);
+      acc[3] = fmaf(m[k], qk.w, acc[3]);
     }
-    (type ? sh : qh)[row] = a0 + a1;
+#pragma unroll
+    for (int h = 0; h < G; ++h) part_sum[half][h][row] = acc[h];
   }
   __syncthreads();
-  if (threadIdx.x < 64) {
-    // 4 statistics, 16 threads each
-    const int stat = threadIdx.x / 16, sub = threadIdx.x % 16;
-    const float* v = (stat < 2) ? qh : sh;
+  for (int i = tid; i < G * D; i += 256) part_sum[0][i / D][i % D] += part_sum[1][i / D][i % D];
+  __syncthreads();
+  float (*v)[D] = part_sum[0];             // v[h][row]: qh (type 0) or sh (type 1)
+  if (tid < G * 2 * 16) {
+    // G heads x 2 statistics, 16 threads each
+    const int h = tid / 32, stat = (tid / 16) % 2, sub = tid % 16;
     float r = 0.f;
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) {
-      const float x = v[sub + 16 * k];
-      r = (stat % 2 == 0) ? fmaxf(r, fabsf(x)) : r + x;
+      const float x = v[h][sub + 16 * k];
+      r = (stat == 0) ? fmaxf(r, fabsf(x)) : r + x;
     }
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) {
       const float o = __shfl_xor(r, off, 16);
-      r = (stat % 2 == 0) ? fmaxf(r, o) : r + o;
+      r = (stat == 0) ? fmaxf(r, o) : r + o;
     }
-    if (sub == 0) stats[stat] = r;
+    if (sub == 0) stats[h][stat] = r;
   }
   __syncthreads();
 
-  const int ne = hdr->ne;
-  const float ma = hdr->emax * stats[0];
-  const float sa = ma > 0.f ? kDigitRange / ma : 1.f;
-  const float sb = stats[2] > 0.f ? kDigitRange / stats[2] : 1.f;
   unsigned char* base = ws + size_t(g) * score_ws_per_group(BITS);
-  // this head's A operand chunks: 2 NW MFMAs x 4 K groups x 4 rows
-  for (int item = threadIdx.x; item < 2 * NW * 16; item += 256) {
-    const int m = item / 16, part = (item / 4) % 4, grp = item % 4;
+  // A operand chunks of this half: per head 2 NW MFMAs x 4 K groups x 2 rows
+  for (int item = tid; item < G * 2 * NW * 8; item += 256) {
+    const int h = item / (2 * NW * 8), r = item % (2 * NW * 8);
+    const int m = r / 8, part = 2 * type + (r / 4) % 2, grp = r % 4;
     const int lane = 16 * grp + 4 * h + part;
     const int word = m / 2, j = m % 2;
     const bool mse_word = word < ne;
+    const float ew = word == 0 ? e0 : word == 1 ? e1 : word == 2 ? e2 : e3;
+    const float mx = type == 0 ? emax * stats[h][0] : stats[h][0];
+    const float scale = mx > 0.f ? kDigitRange / mx : 1.f;
+    // MSE rows carry e_word Pi q on the codebook words, QJL rows S q on the sign word; the
+    // odd bit positions (j = 1) have weight 2, so their value is halved
+    const float coef = (type == 0) ? (mse_word ? ew : 0.f) : (mse_word ? 0.f : 1.f);
+    const float f = coef * scale * (j ? 0.5f : 1.f);
+    const bool hi_part = (part % 2) == 0;
     uint32_t packed[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -127,29 +147,30 @@ __global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* _
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         const int coord = 32 * grp + 8 * bi + 2 * k + j;
-        float xval = 0.f;
-        if (mse_word && part < 2) xval = hdr->e[word] * qh[coord] * sa;
-        if (!mse_word && part >= 2) xval = sh[coord] * sb;
-        // value as an integer; odd bit positions carry weight 2, so keep them even
-        const int v = (j == 0) ? int(rintf(xval)) : 2 * int(rintf(0.5f * xval));
-        const int vj = v >> j;
+        const int vj = int(rintf(f * v[h][coord]));   // value as an integer: 128 hi + lo
         const int hi = (vj + 64) >> 7;
         const int lo = vj - 128 * hi;
-        const int digit = (part % 2 == 0) ? hi : lo;
-        dw |= uint32_t(uint8_t(int8_t(digit))) << (8 * bi);
+        dw |= uint32_t(uint8_t(int8_t(hi_part ? hi : lo))) << (8 * bi);
       }
       packed[k] = dw;
     }
     reinterpret_cast<uint4*>(base)[m * 64 + lane] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   }
-  // epilogue constants: l = nu (A wA - cA + gamma (B wB - cB))
-  if (threadIdx.x == 0) {
-    float4 c;
-    c.x = 2.f / sa;
-    c.y = hdr->esum * stats[1];
-    c.z = 2.f * hdr->alpha / sb;
-    c.w = hdr->alpha * stats[3];
-    reinterpret_cast<float4*>(base + size_t(2 * NW) * 64 * 16)[h] = c;
+  // epilogue constants: l = nu (A wA - cA + gamma (B wB - cB)); type 0 writes (x, y),
+  // type 1 writes (z, w)
+  if (tid < G) {
+    const int h = tid;
+    float* c = reinterpret_cast<float*>(base + size_t(2 * NW) * 64 * 16) + 4 * h;
+    if (type == 0) {
+      const float ma = emax * stats[h][0];
+      const float sa = ma > 0.f ? kDigitRange / ma : 1.f;
+      c[0] = 2.f / sa;
+      c[1] = esum * stats[h][1];
+    } else {
+      const float sb = stats[h][0] > 0.f ? kDigitRange / stats[h][0] : 1.f;
+      c[2] = 2.f * alpha / sb;
+      c[3] = alpha * stats[h][1];
+    }
   }
 }
 
@@ -257,14 +278,14 @@ hipError_t launch_b(const void* params, const void* q, int q_dtype, const uint32
   const Layout lay(D, BITS);
   const long qpg = long(Gq / G);
   const int64_t groups = kv_groups * qpg;       // virtual groups of 4 query heads
-  hipLaunchKernelGGL((score_qprep_kernel<BITS>), dim3(unsigned(groups * G)), dim3(256), 0, s,
-                     static_cast<const unsigned char*>(params), lay.off_pi, lay.off_s, q,
+  hipLaunchKernelGGL((score_qprep_kernel<BITS>), dim3(unsigned(2 * groups)), dim3(256), 0, s,
+                     static_cast<const unsigned char*>(params), lay.off_tr, q,
                      q_dtype == 0 ? 1 : 0, static_cast<unsigned char*>(ws));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long tiles_per_group = (T + 15) / 16;
   const long total_tiles = long(groups) * tiles_per_group;
-  long tpr = (total_tiles + long(cu_count_s()) * 16 - 1) / (long(cu_count_s()) * 16);
+  long tpr = (total_tiles + long(cu_count_s()) * WAVES_PER_CU - 1) / (long(cu_count_s()) * WAVES_PER_CU);
   if (tpr < 8) tpr = 8;
   tpr = (tpr + UNR - 1) / UNR * UNR;
   const long rpg = (tiles_per_group + tpr - 1) / tpr;

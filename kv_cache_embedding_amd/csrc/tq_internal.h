@@ -40,6 +40,8 @@ struct Layout {
   size_t qfrag_bytes = 0;
   size_t off_gmat = 0;    // other d (multiple of 128): bf16 Pi_hi, Pi_lo, S'_hi, S'_lo [d][d]
   size_t gmat_bytes = 0;
+  size_t off_tr = 0;      // d == 128: Pi^T and S^T fp32 [2][d][d] (column k of Pi at k * d)
+  size_t tr_bytes = 0;
   size_t total = 0;
   Layout(int d_, int b_);
 };
@@ -54,7 +56,9 @@ inline Layout::Layout(int d_, int b_) : d(d_), b(b_) {
   qfrag_bytes = (d == 128) ? size_t(2) * 64 * 1024 : 0;
   off_gmat = align256(off_qfrag + qfrag_bytes);
   gmat_bytes = (d != 128 && d % 128 == 0) ? size_t(4) * d * d * 2 : 0;
-  total = align256(off_gmat + gmat_bytes);
+  off_tr = align256(off_gmat + gmat_bytes);
+  tr_bytes = (d == 128) ? size_t(2) * d * d * 4 : 0;
+  total = align256(off_tr + tr_bytes);
 }
 
 // Plane words per key that the scoring kernel feeds to the MFMA: the b-1 index planes,
