@@ -11,10 +11,10 @@
 // Kernels:
 //   topk_qprep_kernel   Pi q and S q on v_mfma_f32_32x32x2f32 (float32 operands, exact
 //                       products), scaled and written in fp16 MFMA fragment order;
-//   topk_scan_kernel    one workgroup per (128-query tile, key range): 4 waves, one per SIMD,
-//                       each scores 128 queries x 128 keys per 512-key block on
-//                       v_mfma_f32_32x32x16_f16 (4 x 4 tiles, every query fragment feeds
-//                       four MFMAs) with its key operand built in registers (byte-permute
+//   topk_scan_kernel    one workgroup per (32 RT-query tile, key range): 4 waves, one per
+//                       SIMD, each scores 32 RT queries x 32 KT keys per 128 KT-key block on
+//                       v_mfma_f32_32x32x16_f16 (RT x KT tiles, every query fragment feeds
+//                       KT MFMAs) with its key operand built in registers (byte-permute
 //                       lookup of the codebook magnitude + sign-bit insert), then filters
 //                       the block's scores against each query's running k-th best and
 //                       merges the survivors into per-query lists in LDS;
@@ -39,7 +39,8 @@ typedef __attribute__((address_space(3))) void* lptr;         // LDS
 // Tile shape: every wave holds RT x KT = 16 accumulator tiles of 32 x 32 (all 256 AGPRs).
 // Each query fragment read from LDS feeds KT MFMAs and each decoded key operand feeds RT,
 // so RT trades the query-operand traffic (DMA + LDS reads per MFMA, ~1/KT) against the key
-// decode (VALU per MFMA, ~1/RT); on gfx950 only ~2-3 VALU ops hide behind one 32x32x16 MFMA.
+// decode (VALU per MFMA, ~1/RT); on gfx950 about four independent VALU ops issue in the
+// shadow of one 32x32x16 MFMA, further VALU work adds to the time.
 #ifndef TQ_TOPK_RT
 #define TQ_TOPK_RT 8
 #endif
