@@ -1,244 +1,374 @@
-// TurboQuant encoder for any d that is a multiple of 128 (e.g. 1536-dimensional embeddings),
-// as two tiled MFMA GEMMs per chunk of vectors ([review, inner-product paragraph];
-// [tldr, steps 1-2]):
+// TurboQuant encoder for any d that is a multiple of 128 (e.g. 1536-dimensional embeddings)
+// ([review, inner-product paragraph]; [tldr, steps 1-2]), per chunk of vectors:
+//   split:    nu = |x| per vector; float32 x is split into bf16 rows x_hi + x_lo (RNE);
 //   phase 1:  U = X Pi^T (rows = vectors, columns = rotated coordinates); its epilogue
-//             divides by nu, bucketizes, packs the index planes and writes the residual
-//             r' = u - chat as bf16 hi/lo rows to a scratch buffer;
-//   phase 2:  Y = R' S'^T with S' = S Pi^T; its epilogue packs the QJL sign plane.
-// Both use v_mfma_f32_32x32x16_bf16 with hi/lo operand splits (Pi_hi x + Pi_lo x, plus
-// Pi_hi x_lo for float32 inputs; S'_hi r_hi + S'_lo r_hi + S'_hi r_lo), float32
-// accumulation.  In the 32x32 accumulator layout (row = 8(r/4) + 4(lane/32) + r%4,
-// column = lane % 32) a wave ballot over one accumulator register is exactly two packed
-// words of the canonical layout (32 consecutive coordinates of two vectors).
-// nu (phase 1) and gamma (phase 2) are row sums of squares taken while the operand rows
-// stream through the workgroup.
+//             divides by nu, bucketizes, packs the index planes, writes the residual
+//             r' = u - chat as bf16 hi/lo rows to a scratch buffer and its partial sum of
+//             squares per (vector, column tile);
+//   phase 2:  Y = R' S'^T with S' = S Pi^T; its epilogue packs the QJL sign plane and sums
+//             the partials into gamma = |r'|.
+// Both GEMMs run on v_mfma_f32_32x32x16_bf16 with hi/lo operand splits (Pi_hi x_hi +
+// Pi_lo x_hi + Pi_hi x_lo, the last pass only for float32 inputs; S'_hi r_hi + S'_lo r_hi +
+// S'_hi r_lo), float32 accumulation.  In the 32x32 accumulator layout (row = 8(r/4) +
+// 4(lane/32) + r%4, column = lane % 32) a wave ballot over one accumulator register is
+// exactly two packed words of the canonical layout (32 consecutive coordinates of two
+// vectors).
+//
+// Tiling.  A workgroup computes a 256 x 256 output tile with 8 waves (two per SIMD) of
+// 128 x 64: 4 x 2 accumulator tiles of 32 x 32, so every A fragment read from LDS feeds two
+// MFMAs per pass and every B fragment four.  K advances 32 per stage; the operands of a
+// stage come into LDS by direct global -> LDS loads, each 64-lane instruction filling one
+// 1 KiB MFMA fragment in register order (lane l: row l % 32, K offset 8 (l / 32)),
+// double-buffered with one barrier per stage.  Workgroups of one row block run on one XCD
+// (dispatch is round-robin over the 8 XCDs), so its d / 256 column tiles share that XCD's
+// L2 for the rows of X.
 #include "tq_internal.h"
+
+#include <type_traits>
 
 namespace tq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(1))) const void* gptr;   // global
+typedef __attribute__((address_space(3))) void* lptr;         // LDS
 
-constexpr int TM = 128;          // vectors per tile
-constexpr int TN = 128;          // output coordinates per tile
-constexpr int BK = 32;
-constexpr int LDK = BK + 8;      // padded LDS row (bf16 elements)
-constexpr long CHUNK = 16384;    // vectors per pass (scratch: CHUNK x d x 4 bytes)
+constexpr int WT = 256;          // workgroup tile: vectors x coordinates
+constexpr int BK = 32;           // K per stage (two MFMA K steps, 64 bytes of a bf16 row)
+constexpr int WAVES = 8;
+constexpr long CHUNK = 32768;    // vectors per pass
+constexpr int NXCD = 8;
+
+// LDS blocks (1 KiB) of one stage: 16 rows x 32 K of one operand part.  B blocks
+// [part][16-column block 0..15] (32), then A blocks [part][16-row block] (32, or 16 when A
+// has no low part).  Row q of a block holds its 64 bytes as four 16-byte pieces, piece p
+// at slot p ^ ((q / 4) % 4): a direct load fills the block from whole 64-byte row segments
+// (lane L: row L / 4, slot L % 4), and an MFMA fragment read (lane l: row l % 32, piece
+// 2 ks + l / 32) hits 16 distinct bank groups per 16 lanes.
+template <bool ALO>
+struct StageShape {
+  static constexpr int NB = 32;
+  static constexpr int NA = ALO ? 32 : 16;
+  static constexpr int NF = NB + NA;
+  static constexpr int U4 = NF * 64;     // uint4 per stage
+};
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
-  return uint32_t(__builtin_bit_cast(uint16_t, ha)) | (uint32_t(__builtin_bit_cast(uint16_t, hb)) << 16);
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)v));
 }
 
-// PHASE 1: A = x (float32 or bf16), B = Pi (hi/lo). PHASE 2: A = r' (hi/lo), B = S' (hi/lo).
-template <int PHASE, int BITS, bool F32IN>
-__global__ __launch_bounds__(256) void qgemm_kernel(const unsigned char* __restrict__ params,
-                                                     const void* __restrict__ a_src, long rows,
-                                                     const uint16_t* __restrict__ bhi,
-                                                     const uint16_t* __restrict__ blo, int d,
-                                                     long v0, uint32_t* __restrict__ codes,
-                                                     float* __restrict__ nu_out,
-                                                     float* __restrict__ gamma_out,
-                                                     uint16_t* __restrict__ rhi,
-                                                     uint16_t* __restrict__ rlo) {
-  constexpr bool ALO = (PHASE == 2) || F32IN;   // A has a low part
-  __shared__ __bf16 Ah[TM * LDK];
-  __shared__ __bf16 Al[ALO ? TM * LDK : 1];
-  __shared__ __bf16 Bh[TN * LDK];
-  __shared__ __bf16 Bl[TN * LDK];
-  __shared__ float rowscale[TM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  const long r0 = long(blockIdx.x) * TM;       // first row (vector) of the tile in the chunk
-  const int c0 = blockIdx.y * TN;              // first output coordinate of the tile
-  const int srow = tid >> 1, scol = (tid & 1) * 16;
-  const bool row_ok = r0 + srow < rows;
-  float rs = 0.f;                              // sum of squares of this thread's row slice
-
-  f32x16 acc[2][2];
+// ------------------------------------------------------------------------------ split
+// One wave per vector: nu = |x| (float32 sum of squares), and for float32 inputs the bf16
+// rows x_hi = RNE(x), x_lo = RNE(x - x_hi).  Lane l covers coordinates 8 (l + 64 i) .. +7.
+template <bool F32IN>
+__global__ __launch_bounds__(256) void qsplit_kernel(const void* __restrict__ x, long rows, int d,
+                                                      uint16_t* __restrict__ xh,
+                                                      uint16_t* __restrict__ xl, long v0,
+                                                      float* __restrict__ nu_out) {
+  const int lane = threadIdx.x & 63;
+  const long row = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float ss = 0.f;
+  for (int c = 8 * lane; c < d; c += 512) {
+    const size_t off = size_t(row) * d + c;
+    if constexpr (F32IN) {
+      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off + 4);
+      const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int e = 0; e < 8; e += 2) {
+        ss = fmaf(f[e], f[e], ss);
+        ss = fmaf(f[e + 1], f[e + 1], ss);
+        const uint32_t h0 = bf16_bits(f[e]), h1 = bf16_bits(f[e + 1]);
+        h[e / 2] = h0 | (h1 << 16);
+        l[e / 2] = bf16_bits(f[e] - __uint_as_float(h0 << 16)) |
+                   (bf16_bits(f[e + 1] - __uint_as_float(h1 << 16)) << 16);
+      }
+      *reinterpret_cast<uint4*>(xh + off) = make_uint4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<uint4*>(xl + off) = make_uint4(l[0], l[1], l[2], l[3]);
+    } else {
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+      const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xffff0000u);
+        ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) nu_out[v0 + row] = sqrtf(ss);
+}
+
+// ------------------------------------------------------------------------------- GEMMs
+// Direct global -> LDS loads of one stage.  Block f = 8 m + wave of the stage is loaded by
+// this wave: m < 4 are B blocks (part f / 16, column block f % 16), the rest A blocks.  Each
+// source is a uniform base (matrix, part) plus the stage's K offset plus a per-lane byte
+// offset (row or column times the row pitch, plus the K offset of the lane's piece) that
+// does not change from stage to stage.
+template <bool ALO>
+struct DmaPlan {
+  static constexpr int NA = ALO ? 4 : 2;     // A blocks per wave
+  const char* bsrc[4];
+  const char* asrc[NA];
+  uint32_t bo[4];
+  uint32_t ao[NA];
+};
+
+template <bool ALO>
+__device__ __forceinline__ void stage_dma(const DmaPlan<ALO>& p, int k0, uint4* dst, int wave) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    __builtin_amdgcn_global_load_lds((gptr)(p.bsrc[m] + size_t(k0) * 2 + p.bo[m]),
+                                     (lptr)(dst + (WAVES * m + wave) * 64), 16, 0, 0);
+#pragma unroll
+  for (int m = 0; m < DmaPlan<ALO>::NA; ++m)
+    __builtin_amdgcn_global_load_lds((gptr)(p.asrc[m] + size_t(k0) * 2 + p.ao[m]),
+                                     (lptr)(dst + (32 + WAVES * m + wave) * 64), 16, 0, 0);
+}
+
+// One stage of MFMAs for the wave tile (rows 128 wm .., columns 64 wn ..); off[ks] is the
+// lane's byte offset of K step ks within a pair of blocks (see the block layout above).
+template <bool ALO>
+__device__ __forceinline__ void stage_mfma(f32x16 (&acc)[4][2], const uint4* buf,
+                                           const uint32_t (&off)[2], int wm, int wn) {
+  const char* b = reinterpret_cast<const char*>(buf);
+  auto frag = [&](int block, int ks) {
+    return *reinterpret_cast<const bf16x8*>(b + block * 1024 + off[ks]);
+  };
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 bh[2], bl[2], ah[4], al[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int cb = 2 * (2 * wn + j);         // first 16-column block of the column tile
+      bh[j] = frag(cb, ks);
+      bl[j] = frag(16 + cb, ks);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rb = 2 * (4 * wm + i);         // first 16-row block of the row tile
+      ah[i] = frag(32 + rb, ks);
+      if constexpr (ALO) al[i] = frag(48 + rb, ks);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = mfma(bh[j], ah[i], acc[i][j]);
+        acc[i][j] = mfma(bl[j], ah[i], acc[i][j]);
+        if constexpr (ALO) acc[i][j] = mfma(bh[j], al[i], acc[i][j]);
+      }
+  }
+}
+
+// PHASE 1: A = x (hi[/lo]) bf16 rows, B = Pi (hi/lo). PHASE 2: A = r' (hi/lo), B = S' (hi/lo).
+template <int PHASE, int BITS, bool ALO>
+__global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
+    const unsigned char* __restrict__ params, const uint16_t* __restrict__ ahi,
+    const uint16_t* __restrict__ alo, long rows, const uint16_t* __restrict__ bhi,
+    const uint16_t* __restrict__ blo, int d, long v0, int nrb, uint32_t* __restrict__ codes,
+    const float* __restrict__ nu, float* __restrict__ gamma_out, uint16_t* __restrict__ rhi,
+    uint16_t* __restrict__ rlo, float* __restrict__ gpart) {
+  __shared__ uint4 buf0[StageShape<ALO>::U4];
+  __shared__ uint4 buf1[StageShape<ALO>::U4];
+  __shared__ float rowscale[WT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches stay scalar
+  const int wm = wave >> 2, wn = wave & 3;     // wave tile: rows 128 wm .., columns 64 wn ..
+  const int nct = (d + WT - 1) / WT;
+  // block -> (row block, column tile): the column tiles of a row block share an XCD
+  const int xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD;
+  const int rb = (slot / nct) * NXCD + xcd, ct = slot % nct;
+  if (rb >= nrb) return;
+  const long r0 = long(rb) * WT;               // first row (vector) of the tile in the chunk
+  const int c0 = ct * WT;                      // first output coordinate of the tile
+
+  // DMA plan of this wave (ragged rows and columns past d are clamped: they read valid
+  // data whose results are discarded); lane L loads piece (L % 4) ^ ((L / 16) % 4) of row
+  // L / 4 of its blocks
+  const int q = lane >> 2, piece = (lane & 3) ^ ((lane >> 4) & 3);
+  DmaPlan<ALO> plan;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int f = WAVES * m + wave;
+    plan.bsrc[m] = reinterpret_cast<const char*>((f >> 4) ? blo : bhi);
+    int col = c0 + 16 * (f & 15) + q;
+    col = col < d ? col : d - 1;
+    plan.bo[m] = uint32_t((size_t(col) * d + 8 * piece) * 2);
+  }
+#pragma unroll
+  for (int m = 0; m < DmaPlan<ALO>::NA; ++m) {
+    const int fa = WAVES * m + wave;
+    plan.asrc[m] = reinterpret_cast<const char*>(ALO && (fa >> 4) ? alo : ahi);
+    long row = r0 + 16 * (fa & 15) + q;
+    row = row < rows ? row : rows - 1;
+    plan.ao[m] = uint32_t((size_t(row) * d + 8 * piece) * 2);
+  }
+  // fragment read offsets: lane l reads row l % 32 of a 32-row pair of blocks, piece
+  // 2 ks + l / 32
+  uint32_t off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int rr = lane & 31, qq = rr & 15, pp = 2 * ks + (lane >> 5);
+    off[ks] = uint32_t((rr >> 4) * 1024 + qq * 64 + 16 * (pp ^ ((qq >> 2) & 3)));
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  for (int kk = 0; kk < d; kk += BK) {
-    uint4 ah[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, al[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-    if (row_ok) {
-      const size_t off = size_t(r0 + srow) * d + kk + scol;
-      if constexpr (PHASE == 1 && F32IN) {
-        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a_src) + off);
-        float f[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = src[q];
-          f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
-        }
-        uint32_t hw[8], lw[8];
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          rs = fmaf(f[e], f[e], rs);
-          rs = fmaf(f[e + 1], f[e + 1], rs);
-          hw[e / 2] = pack_bf16x2(f[e], f[e + 1]);
-          const float h0 = __uint_as_float(hw[e / 2] << 16), h1 = __uint_as_float(hw[e / 2] & 0xffff0000u);
-          lw[e / 2] = pack_bf16x2(f[e] - h0, f[e + 1] - h1);
-        }
-        ah[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        ah[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-        al[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        al[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-      } else if constexpr (PHASE == 1) {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a_src) + off);
-        ah[0] = src[0];
-        ah[1] = src[1];
-        const uint32_t w8[8] = {ah[0].x, ah[0].y, ah[0].z, ah[0].w, ah[1].x, ah[1].y, ah[1].z, ah[1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lo = __uint_as_float(w8[e] << 16), hi = __uint_as_float(w8[e] & 0xffff0000u);
-          rs = fmaf(lo, lo, fmaf(hi, hi, rs));
-        }
-      } else {
-        const uint4* sh = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a_src) + off);
-        const uint4* sl = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a_src) + size_t(CHUNK) * d + off);
-        ah[0] = sh[0]; ah[1] = sh[1]; al[0] = sl[0]; al[1] = sl[1];
-        const uint32_t h8[8] = {ah[0].x, ah[0].y, ah[0].z, ah[0].w, ah[1].x, ah[1].y, ah[1].z, ah[1].w};
-        const uint32_t l8[8] = {al[0].x, al[0].y, al[0].z, al[0].w, al[1].x, al[1].y, al[1].z, al[1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v0e = __uint_as_float(h8[e] << 16) + __uint_as_float(l8[e] << 16);
-          const float v1e = __uint_as_float(h8[e] & 0xffff0000u) + __uint_as_float(l8[e] & 0xffff0000u);
-          rs = fmaf(v0e, v0e, fmaf(v1e, v1e, rs));
-        }
-      }
-    }
-    const size_t boff = size_t(c0 + srow) * d + kk + scol;
-    const uint4* bsh = reinterpret_cast<const uint4*>(bhi + boff);
-    const uint4* bsl = reinterpret_cast<const uint4*>(blo + boff);
-    const uint4 bh0 = bsh[0], bh1 = bsh[1], bl0 = bsl[0], bl1 = bsl[1];
-    __syncthreads();   // previous step's fragments are consumed
-    *reinterpret_cast<uint4*>(&Ah[srow * LDK + scol]) = ah[0];
-    *reinterpret_cast<uint4*>(&Ah[srow * LDK + scol + 8]) = ah[1];
-    if constexpr (ALO) {
-      *reinterpret_cast<uint4*>(&Al[srow * LDK + scol]) = al[0];
-      *reinterpret_cast<uint4*>(&Al[srow * LDK + scol + 8]) = al[1];
-    }
-    *reinterpret_cast<uint4*>(&Bh[srow * LDK + scol]) = bh0;
-    *reinterpret_cast<uint4*>(&Bh[srow * LDK + scol + 8]) = bh1;
-    *reinterpret_cast<uint4*>(&Bl[srow * LDK + scol]) = bl0;
-    *reinterpret_cast<uint4*>(&Bl[srow * LDK + scol + 8]) = bl1;
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      bf16x8 a_h[2], a_l[2], b_h[2], b_l[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ra = (wm + 32 * i + (lane & 31)) * LDK + ks + 8 * (lane >> 5);
-        const int rb = (wn + 32 * i + (lane & 31)) * LDK + ks + 8 * (lane >> 5);
-        a_h[i] = *reinterpret_cast<const bf16x8*>(&Ah[ra]);
-        if constexpr (ALO) a_l[i] = *reinterpret_cast<const bf16x8*>(&Al[ra]);
-        b_h[i] = *reinterpret_cast<const bf16x8*>(&Bh[rb]);
-        b_l[i] = *reinterpret_cast<const bf16x8*>(&Bl[rb]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = mfma(a_h[i], b_h[j], acc[i][j]);
-          acc[i][j] = mfma(a_h[i], b_l[j], acc[i][j]);
-          if constexpr (ALO) acc[i][j] = mfma(a_l[i], b_h[j], acc[i][j]);
-        }
+  // K loop: stage s is read from buffer s % 2 while stage s + 1 lands in the other one.
+  // The compiler does not order direct LDS loads against later LDS reads, hence the
+  // explicit vmcnt wait before each barrier.
+  const int ns = d / BK;
+  stage_dma(plan, 0, buf0, wave);
+  for (int s = 0; s < ns; s += 2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // this wave's part of stage s landed
+    __syncthreads();                             // ... every wave's; stage s - 1 is consumed
+    if (s + 1 < ns) stage_dma(plan, (s + 1) * BK, buf1, wave);
+    stage_mfma<ALO>(acc, buf0, off, wm, wn);
+    if (s + 1 < ns) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      __syncthreads();
+      if (s + 2 < ns) stage_dma(plan, (s + 2) * BK, buf0, wave);
+      stage_mfma<ALO>(acc, buf1, off, wm, wn);
     }
   }
 
-  // per-row norms: the two threads of a row hold halves of its sum
-  rs += __shfl_xor(rs, 1);
-  if ((tid & 1) == 0) {
-    const float nrm = sqrtf(rs);
-    if constexpr (PHASE == 1) {
-      rowscale[srow] = nrm > 0.f ? 1.f / nrm : 0.f;   // zero vector: u is taken as 0
-      if (blockIdx.y == 0 && row_ok) nu_out[v0 + r0 + srow] = nrm;
-    } else {
-      if (blockIdx.y == 0 && row_ok) gamma_out[v0 + r0 + srow] = nrm;
-    }
-  }
-  __syncthreads();
-
-  const Header* hdr = reinterpret_cast<const Header*>(params);
-  constexpr int L = 1 << (BITS - 1);
-  float T[L / 2 > 1 ? L / 2 - 1 : 1], M[L / 2];
+  const int groups = d / 32;
   if constexpr (PHASE == 1) {
+    if (tid < WT) {
+      const long row = r0 + tid < rows ? r0 + tid : rows - 1;
+      const float nrm = nu[v0 + row];
+      rowscale[tid] = nrm > 0.f ? 1.f / nrm : 0.f;   // zero vector: u is taken as 0
+    }
+    __syncthreads();   // also: every wave is done with buf0 before it holds the partials
+    const Header* hdr = reinterpret_cast<const Header*>(params);
+    constexpr int L = 1 << (BITS - 1);
+    float T[L / 2 > 1 ? L / 2 - 1 : 1], M[L / 2];
 #pragma unroll
     for (int k = 0; k < L / 2 - 1; ++k) T[k] = hdr->tpos[k];
 #pragma unroll
     for (int k = 0; k < L / 2; ++k) M[k] = hdr->mpos[k];
-  }
-  const int groups = d / 32;
+    float* gsum = reinterpret_cast<float*>(buf0);   // [4 wn][256 rows] partial |r'|^2
+    const int h = lane >> 5;
+    // one row tile at a time (a compile-time index keeps the accumulators in registers)
+    auto row_tile = [&](auto it) {
+      constexpr int i = decltype(it)::value;
+      const int vr = 128 * wm + 32 * i + (lane & 31);   // tile row (vector) of this lane
+      const bool okr = r0 + vr < rows;
+      const float rs = rowscale[vr];
+      float g2 = 0.f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+      for (int j = 0; j < 2; ++j) {
+        const int cb = c0 + 64 * wn + 32 * j;    // first coordinate of this 32-column tile
+        const bool okc = cb < d;                 // uniform: padding columns past d
+        const int w = cb / 32;                   // coordinate group of this tile
+        // index bits of the lane's 16 coordinates at their positions 8 g + e (+ 4 h below)
+        uint32_t word[BITS - 1];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = c0 + wn + 32 * j + (lane & 31);
-      const int w = (c0 + wn + 32 * j) / 32;     // coordinate group of this 32-column tile
+        for (int p = 0; p < BITS - 1; ++p) word[p] = 0u;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm + 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-        const int rowA = wm + 32 * i + 8 * (r / 4) + (r % 4);     // vector of bits 0..31
-        const bool okr = r0 + row < rows;
-        if constexpr (PHASE == 1) {
-          const float u = acc[i][j][r] * rowscale[row];
-          bool bit[3] = {false, false, false};
-          float c;
-          if constexpr (BITS == 2) {
-            bit[0] = u >= 0.f;
-            c = bit[0] ? M[0] : -M[0];
-          } else if constexpr (BITS == 3) {
-            bit[1] = u >= 0.f;
-            bit[0] = u >= (bit[1] ? T[0] : -T[0]);
-            const float mag = (bit[0] == bit[1]) ? M[1] : M[0];
-            c = bit[1] ? mag : -mag;
-          } else {
-            bit[2] = u >= 0.f;
-            bit[1] = u >= (bit[2] ? T[1] : -T[1]);
-            const bool e1 = (bit[1] == bit[2]);
-            const float t2 = e1 ? T[2] : T[0];
-            bit[0] = u >= (bit[2] ? t2 : -t2);
-            const bool e0 = (bit[0] == bit[2]);
-            const float mag = e1 ? (e0 ? M[3] : M[2]) : (e0 ? M[1] : M[0]);
-            c = bit[2] ? mag : -mag;
-          }
-          const float rv = u - c;
-          const __bf16 hi = (__bf16)rv;
-          const __bf16 lo = (__bf16)(rv - (float)hi);
-          if (okr) {
-            const size_t ro = size_t(r0 + row) * d + col;
-            rhi[ro] = __builtin_bit_cast(uint16_t, hi);
-            rlo[ro] = __builtin_bit_cast(uint16_t, lo);
-          }
+        for (int g = 0; g < 4; ++g) {
+          uint32_t hp[2] = {0u, 0u}, lp[2] = {0u, 0u};   // bf16 pairs of coordinates 4 h + e
 #pragma unroll
-          for (int p = 0; p < BITS - 1; ++p) {
-            const uint64_t m = __builtin_amdgcn_ballot_w64(bit[p]);
-            if (lane == 0) {
-              if (r0 + rowA < rows)
-                codes[(size_t(v0 + r0 + rowA) * groups + w) * BITS + p] = uint32_t(m);
-              if (r0 + rowA + 4 < rows)
-                codes[(size_t(v0 + r0 + rowA + 4) * groups + w) * BITS + p] = uint32_t(m >> 32);
+          for (int e = 0; e < 4; ++e) {
+            const float u = acc[i][j][4 * g + e] * rs;
+            bool bit[3] = {false, false, false};
+            float c;
+            if constexpr (BITS == 2) {
+              bit[0] = u >= 0.f;
+              c = bit[0] ? M[0] : -M[0];
+            } else if constexpr (BITS == 3) {
+              bit[1] = u >= 0.f;
+              bit[0] = u >= (bit[1] ? T[0] : -T[0]);
+              const float mag = (bit[0] == bit[1]) ? M[1] : M[0];
+              c = bit[1] ? mag : -mag;
+            } else {
+              bit[2] = u >= 0.f;
+              bit[1] = u >= (bit[2] ? T[1] : -T[1]);
+              const bool e1 = (bit[1] == bit[2]);
+              const float t2 = e1 ? T[2] : T[0];
+              bit[0] = u >= (bit[2] ? t2 : -t2);
+              const bool e0 = (bit[0] == bit[2]);
+              const float mag = e1 ? (e0 ? M[3] : M[2]) : (e0 ? M[1] : M[0]);
+              c = bit[2] ? mag : -mag;
             }
+            const float rv = u - c;
+            const uint32_t hb = bf16_bits(rv);
+            const uint32_t lb = bf16_bits(rv - __uint_as_float(hb << 16));
+            const float rq = __uint_as_float(hb << 16) + __uint_as_float(lb << 16);
+            if (okc) g2 = fmaf(rq, rq, g2);      // the residual phase 2 will see
+            hp[e / 2] |= hb << (16 * (e % 2));
+            lp[e / 2] |= lb << (16 * (e % 2));
+#pragma unroll
+            for (int p = 0; p < BITS - 1; ++p) word[p] |= uint32_t(bit[p]) << (8 * g + e);
           }
-        } else {
-          const uint64_t m = __builtin_amdgcn_ballot_w64(acc[i][j][r] >= 0.f);
-          if (lane == 0) {
-            if (r0 + rowA < rows)
-              codes[(size_t(v0 + r0 + rowA) * groups + w) * BITS + BITS - 1] = uint32_t(m);
-            if (r0 + rowA + 4 < rows)
-              codes[(size_t(v0 + r0 + rowA + 4) * groups + w) * BITS + BITS - 1] = uint32_t(m >> 32);
+          // 4 consecutive coordinates: lanes l and l + 32 write 16 contiguous bytes of a row
+          if (okc && okr) {
+            const size_t ro = size_t(r0 + vr) * d + cb + 8 * g + 4 * h;
+            *reinterpret_cast<uint2*>(rhi + ro) = make_uint2(hp[0], hp[1]);
+            *reinterpret_cast<uint2*>(rlo + ro) = make_uint2(lp[0], lp[1]);
           }
         }
+        // lanes l and l + 32 hold the two nibble halves of each byte of the vector's words
+#pragma unroll
+        for (int p = 0; p < BITS - 1; ++p) {
+          word[p] <<= 4 * h;
+          word[p] |= __shfl_xor(word[p], 32);
+        }
+        if (okc && lane < 32 && okr) {
+#pragma unroll
+          for (int p = 0; p < BITS - 1; ++p) codes[(size_t(v0 + r0 + vr) * groups + w) * BITS + p] = word[p];
+        }
       }
+      // row sum over this wave's 64 columns: lanes l and l + 32 share the row
+      g2 += __shfl_xor(g2, 32);
+      if (lane < 32) gsum[wn * WT + vr] = g2;
+    };
+    row_tile(std::integral_constant<int, 0>{});
+    row_tile(std::integral_constant<int, 1>{});
+    row_tile(std::integral_constant<int, 2>{});
+    row_tile(std::integral_constant<int, 3>{});
+    __syncthreads();
+    if (tid < WT && r0 + tid < rows)
+      gpart[size_t(r0 + tid) * nct + ct] =
+          gsum[tid] + gsum[WT + tid] + gsum[2 * WT + tid] + gsum[3 * WT + tid];
+  } else {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int vr = 128 * wm + 32 * i + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int cb = c0 + 64 * wn + 32 * j;
+        const bool okc = cb < d;
+        const int w = cb / 32;
+        uint32_t word = 0u;                      // sign bits of the lane's 16 coordinates
+#pragma unroll
+        for (int r = 0; r < 16; ++r) word |= uint32_t(acc[i][j][r] >= 0.f) << (8 * (r / 4) + r % 4);
+        word <<= 4 * h;
+        word |= __shfl_xor(word, 32);
+        if (okc && lane < 32 && r0 + vr < rows)
+          codes[(size_t(v0 + r0 + vr) * groups + w) * BITS + BITS - 1] = word;
+      }
+    }
+    // gamma = |r'| from the per-column-tile partial sums of phase 1, in column order
+    if (ct == 0 && tid < WT && r0 + tid < rows) {
+      float g = 0.f;
+      for (int t = 0; t < nct; ++t) g += gpart[size_t(r0 + tid) * nct + t];
+      gamma_out[v0 + r0 + tid] = sqrtf(g);
     }
   }
 }
@@ -252,19 +382,32 @@ hipError_t run(const unsigned char* params, const Layout& lay, const void* x, in
   const uint16_t* sph = pil + size_t(d) * d;
   const uint16_t* spl = sph + size_t(d) * d;
   const long ch = n < CHUNK ? long(n) : CHUNK;
+  const int nct = (d + WT - 1) / WT;
+  // scratch: r' hi, r' lo and (float32 input) x hi, x lo, each CHUNK x d bf16; then the
+  // partial sums of |r'|^2, CHUNK x (d / 256) float32
+  const size_t plane = size_t(CHUNK) * d;
+  const size_t bytes = plane * 2 * (F32IN ? 4 : 2) + size_t(CHUNK) * nct * 4;
   uint16_t* scratch = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), size_t(CHUNK) * d * 4, s);
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), bytes, s);
   if (e != hipSuccess) return e;
+  uint16_t* rhi = scratch;
+  uint16_t* rlo = rhi + plane;
+  uint16_t* xh = F32IN ? rlo + plane : nullptr;
+  uint16_t* xl = F32IN ? xh + plane : nullptr;
+  float* gpart = reinterpret_cast<float*>(scratch + plane * (F32IN ? 4 : 2));
   for (long c0 = 0; c0 < n; c0 += ch) {
     const long rows = (n - c0) < ch ? (n - c0) : ch;
-    const dim3 grid(unsigned((rows + TM - 1) / TM), unsigned(d / TN));
+    const int nrb = int((rows + WT - 1) / WT);
+    const dim3 grid(unsigned((nrb + NXCD - 1) / NXCD * NXCD * nct));
     const void* xs = F32IN ? static_cast<const void*>(static_cast<const float*>(x) + size_t(c0) * d)
                            : static_cast<const void*>(static_cast<const uint16_t*>(x) + size_t(c0) * d);
-    hipLaunchKernelGGL((qgemm_kernel<1, BITS, F32IN>), grid, dim3(256), 0, s, params, xs, rows, pih,
-                       pil, d, c0, codes, nu, gamma, scratch, scratch + size_t(CHUNK) * d);
-    hipLaunchKernelGGL((qgemm_kernel<2, BITS, F32IN>), grid, dim3(256), 0, s, params,
-                       static_cast<const void*>(scratch), rows, sph, spl, d, c0, codes, nu, gamma,
-                       nullptr, nullptr);
+    hipLaunchKernelGGL((qsplit_kernel<F32IN>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, xs,
+                       rows, d, xh, xl, c0, nu);
+    const uint16_t* a1 = F32IN ? xh : static_cast<const uint16_t*>(xs);
+    hipLaunchKernelGGL((qgemm_kernel<1, BITS, F32IN>), grid, dim3(WAVES * 64), 0, s, params, a1, xl,
+                       rows, pih, pil, d, c0, nrb, codes, nu, gamma, rhi, rlo, gpart);
+    hipLaunchKernelGGL((qgemm_kernel<2, BITS, true>), grid, dim3(WAVES * 64), 0, s, params, rhi, rlo,
+                       rows, sph, spl, d, c0, nrb, codes, nu, gamma, nullptr, nullptr, gpart);
     e = hipGetLastError();
     if (e != hipSuccess) break;
   }
