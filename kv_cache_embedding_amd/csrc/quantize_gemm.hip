@@ -108,64 +108,126 @@ __global__ __launch_bounds__(256) void qsplit_kernel(const void* __restrict__ x,
 }
 
 // ------------------------------------------------------------------------------- GEMMs
-// Direct global -> LDS loads of one stage.  Block f = 8 m + wave of the stage is loaded by
-// this wave: m < 4 are B blocks (part f / 16, column block f % 16), the rest A blocks.  Each
-// source is a uniform base (matrix, part) plus the stage's K offset plus a per-lane byte
-// offset (row or column times the row pitch, plus the K offset of the lane's piece) that
-// does not change from stage to stage.
+// Direct buffer -> LDS loads of one stage.  Block f = 8 m + wave of the stage is loaded by
+// this wave: m < 4 are B blocks (part f / 16 = m / 2, column block f % 16), the rest A
+// blocks.  Each source is a buffer resource (matrix part) plus the stage's K offset (the
+// scalar offset) plus a per-lane byte offset (row or column times the row pitch, plus the
+// K offset of the lane's piece) that does not change from stage to stage.  Buffer loads
+// rather than global ones: the compiler takes a global load that writes LDS as a pending
+// access to both memories, which turns every later partial wait for LDS reads into a full
+// one.
+constexpr int RSRC_WORD3 = 0x00020000;         // raw (untyped) buffer resource, gfx9 family
+
 template <bool ALO>
 struct DmaPlan {
   static constexpr int NA = ALO ? 4 : 2;     // A blocks per wave
-  const char* bsrc[4];
-  const char* asrc[NA];
+  void* b[2];                                // B parts [hi, lo], bbytes each
+  void* a[ALO ? 2 : 1];                      // A parts, abytes each
+  int bbytes, abytes;
   uint32_t bo[4];
   uint32_t ao[NA];
 };
 
-template <bool ALO>
-__device__ __forceinline__ void stage_dma(const DmaPlan<ALO>& p, int k0, uint4* dst, int wave) {
+// Loads blocks m0 and m0 + 1 of one part: block f = 8 m + wave lands at LDS block base + f.
+__device__ __forceinline__ void dma_pair(__amdgpu_buffer_rsrc_t r, const uint32_t* vo, int m0,
+                                         int k0, uint4* base, int wave) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    __builtin_amdgcn_global_load_lds((gptr)(p.bsrc[m] + size_t(k0) * 2 + p.bo[m]),
-                                     (lptr)(dst + (WAVES * m + wave) * 64), 16, 0, 0);
-#pragma unroll
-  for (int m = 0; m < DmaPlan<ALO>::NA; ++m)
-    __builtin_amdgcn_global_load_lds((gptr)(p.asrc[m] + size_t(k0) * 2 + p.ao[m]),
-                                     (lptr)(dst + (32 + WAVES * m + wave) * 64), 16, 0, 0);
+  for (int m = m0; m < m0 + 2; ++m)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr)(base + (WAVES * m + wave) * 64), 16, vo[m],
+                                             k0 * 2, 0, 0);
 }
 
-// One stage of MFMAs for the wave tile (rows 128 wm .., columns 64 wn ..); off[ks] is the
-// lane's byte offset of K step ks within a pair of blocks (see the block layout above).
 template <bool ALO>
-__device__ __forceinline__ void stage_mfma(f32x16 (&acc)[4][2], const uint4* buf,
-                                           const uint32_t (&off)[2], int wm, int wn) {
-  const char* b = reinterpret_cast<const char*>(buf);
-  auto frag = [&](int block, int ks) {
-    return *reinterpret_cast<const bf16x8*>(b + block * 1024 + off[ks]);
-  };
+__device__ __forceinline__ void stage_dma(const DmaPlan<ALO>& p, int k0, uint4* dst, int wave) {
+  dma_pair(__builtin_amdgcn_make_buffer_rsrc(p.b[0], 0, p.bbytes, RSRC_WORD3), p.bo, 0, k0, dst, wave);
+  dma_pair(__builtin_amdgcn_make_buffer_rsrc(p.b[1], 0, p.bbytes, RSRC_WORD3), p.bo, 2, k0, dst, wave);
+  dma_pair(__builtin_amdgcn_make_buffer_rsrc(p.a[0], 0, p.abytes, RSRC_WORD3), p.ao, 0, k0, dst + 32 * 64,
+           wave);
+  if constexpr (ALO)
+    dma_pair(__builtin_amdgcn_make_buffer_rsrc(p.a[1], 0, p.abytes, RSRC_WORD3), p.ao, 2, k0,
+             dst + 32 * 64, wave);
+}
+
+// The operand fragments of one MFMA K step (16 of a stage's 32) for the wave tile (rows
+// 128 wm .., columns 64 wn ..): B hi/lo of its two 32-column tiles, A hi[/lo] of its four
+// 32-row tiles.
+template <bool ALO>
+struct Frags {
+  bf16x8 bh[2], bl[2], ah[4], al[ALO ? 4 : 1];
+};
+
+// b is the stage buffer plus the lane's byte offset of the K step within a pair of blocks
+// (see the block layout above).
+template <bool ALO>
+__device__ __forceinline__ void read_b(Frags<ALO>& f, const char* b, int wn) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 bh[2], bl[2], ah[4], al[4];
+  for (int j = 0; j < 2; ++j) {
+    const int cb = 2 * (2 * wn + j);           // first 16-column block of the column tile
+    f.bh[j] = *reinterpret_cast<const bf16x8*>(b + cb * 1024);
+    f.bl[j] = *reinterpret_cast<const bf16x8*>(b + (16 + cb) * 1024);
+  }
+}
+
+template <bool ALO>
+__device__ __forceinline__ void read_a(Frags<ALO>& f, const char* b, int wm, int i) {
+  const int rb = 2 * (4 * wm + i);             // first 16-row block of the row tile
+  f.ah[i] = *reinterpret_cast<const bf16x8*>(b + (32 + rb) * 1024);
+  if constexpr (ALO) f.al[i] = *reinterpret_cast<const bf16x8*>(b + (48 + rb) * 1024);
+}
+
+// B is the MFMA's first operand, so acc[i][j] holds the transposed 32 x 32 tile: lane l
+// has row (vector) 32 i + l % 32 and columns (coordinates) 32 j + 8 (r / 4) + 4 (l / 32) +
+// r % 4 in its register r.
+template <bool ALO>
+__device__ __forceinline__ void mfma_row(f32x16 (&acc)[4][2], const Frags<ALO>& f, int i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int cb = 2 * (2 * wn + j);         // first 16-column block of the column tile
-      bh[j] = frag(cb, ks);
-      bl[j] = frag(16 + cb, ks);
-    }
+  for (int j = 0; j < 2; ++j) {
+    acc[i][j] = mfma(f.bh[j], f.ah[i], acc[i][j]);
+    acc[i][j] = mfma(f.bl[j], f.ah[i], acc[i][j]);
+    if constexpr (ALO) acc[i][j] = mfma(f.bh[j], f.al[i], acc[i][j]);
+  }
+}
+
+// The MFMAs of one K step (fragments f) while the next K step's fragments g come in from
+// LDS: g's B fragments first, then its A fragments of each row tile once f's of that row
+// tile are consumed, so the two sets share registers (the scheduling barriers keep that
+// order).
+template <bool ALO>
+__device__ __forceinline__ void mfma_and_read(f32x16 (&acc)[4][2], const Frags<ALO>& f,
+                                              Frags<ALO>& g, const char* b, int wm, int wn) {
+  read_b(g, b, wn);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rb = 2 * (4 * wm + i);         // first 16-row block of the row tile
-      ah[i] = frag(32 + rb, ks);
-      if constexpr (ALO) al[i] = frag(48 + rb, ks);
-    }
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_row(acc, f, i);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(g, b, wm, i);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stage s, held in cur, with its first K step's fragments already in f0: the first K
+// step's MFMAs run while the second one's fragments come in; then (NEXT: stage s + 1
+// exists), once every wave's loads of stage s + 1 (into nxt) have landed and every wave
+// has read cur, the loads of stage s + 2 into cur start (DMA: it exists) and the second K
+// step's MFMAs run while stage s + 1's first fragments come in.  The MFMAs after the
+// barrier find their operands in registers.  The stage kinds are template arguments so
+// that the loop body has no branches and every LDS access keeps its own buffer.
+template <bool ALO, bool NEXT, bool DMA>
+__device__ __forceinline__ void kstage(f32x16 (&acc)[4][2], Frags<ALO>& f0, Frags<ALO>& f1,
+                                       uint4* cur, const uint4* nxt, const DmaPlan<ALO>& plan,
+                                       const uint32_t (&off)[2], int wm, int wn, int wave, int s) {
+  mfma_and_read(acc, f0, f1, reinterpret_cast<const char*>(cur) + off[1], wm, wn);
+  // this wave's direct LDS loads of stage s + 1 and its reads of cur are complete before
+  // the barrier (the compiler orders neither against the barrier by itself)
+  __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (NEXT) {
+    __syncthreads();
+    if constexpr (DMA) stage_dma(plan, (s + 2) * BK, cur, wave);
+    mfma_and_read(acc, f1, f0, reinterpret_cast<const char*>(nxt) + off[0], wm, wn);
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mfma(bh[j], ah[i], acc[i][j]);
-        acc[i][j] = mfma(bl[j], ah[i], acc[i][j]);
-        if constexpr (ALO) acc[i][j] = mfma(bh[j], al[i], acc[i][j]);
-      }
+    for (int i = 0; i < 4; ++i) mfma_row(acc, f1, i);
   }
 }
 
@@ -197,10 +259,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
   // L / 4 of its blocks
   const int q = lane >> 2, piece = (lane & 3) ^ ((lane >> 4) & 3);
   DmaPlan<ALO> plan;
+  plan.b[0] = const_cast<uint16_t*>(bhi);
+  plan.b[1] = const_cast<uint16_t*>(blo);
+  plan.a[0] = const_cast<uint16_t*>(ahi);
+  if constexpr (ALO) plan.a[1] = const_cast<uint16_t*>(alo);
+  plan.bbytes = int(size_t(d) * d * 2);
+  plan.abytes = int(size_t(rows) * d * 2);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int f = WAVES * m + wave;
-    plan.bsrc[m] = reinterpret_cast<const char*>((f >> 4) ? blo : bhi);
     int col = c0 + 16 * (f & 15) + q;
     col = col < d ? col : d - 1;
     plan.bo[m] = uint32_t((size_t(col) * d + 8 * piece) * 2);
@@ -208,7 +275,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
 #pragma unroll
   for (int m = 0; m < DmaPlan<ALO>::NA; ++m) {
     const int fa = WAVES * m + wave;
-    plan.asrc[m] = reinterpret_cast<const char*>(ALO && (fa >> 4) ? alo : ahi);
     long row = r0 + 16 * (fa & 15) + q;
     row = row < rows ? row : rows - 1;
     plan.ao[m] = uint32_t((size_t(row) * d + 8 * piece) * 2);
@@ -229,22 +295,26 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   // K loop: stage s is read from buffer s % 2 while stage s + 1 lands in the other one.
-  // The compiler does not order direct LDS loads against later LDS reads, hence the
-  // explicit vmcnt wait before each barrier.
+  // d is a multiple of 128, so the number of stages is a multiple of 4.
   const int ns = d / BK;
   stage_dma(plan, 0, buf0, wave);
-  for (int s = 0; s < ns; s += 2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // this wave's part of stage s landed
-    __syncthreads();                             // ... every wave's; stage s - 1 is consumed
-    if (s + 1 < ns) stage_dma(plan, (s + 1) * BK, buf1, wave);
-    stage_mfma<ALO>(acc, buf0, off, wm, wn);
-    if (s + 1 < ns) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-      __syncthreads();
-      if (s + 2 < ns) stage_dma(plan, (s + 2) * BK, buf0, wave);
-      stage_mfma<ALO>(acc, buf1, off, wm, wn);
-    }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  __syncthreads();
+  stage_dma(plan, BK, buf1, wave);
+  // The epilogue's arguments are loaded now: a scalar load still in flight during the loop
+  // would turn every partial wait for LDS reads into a full one.
+  asm volatile("" ::"s"(params), "s"(codes), "s"(nu), "s"(gamma_out), "s"(rhi), "s"(rlo),
+               "s"(gpart), "s"(rows), "s"(v0));
+  Frags<ALO> f0, f1;
+  read_b(f0, reinterpret_cast<const char*>(buf0) + off[0], wn);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) read_a(f0, reinterpret_cast<const char*>(buf0) + off[0], wm, i);
+  for (int s = 0; s < ns - 2; s += 2) {
+    kstage<ALO, true, true>(acc, f0, f1, buf0, buf1, plan, off, wm, wn, wave, s);
+    kstage<ALO, true, true>(acc, f0, f1, buf1, buf0, plan, off, wm, wn, wave, s + 1);
   }
+  kstage<ALO, true, false>(acc, f0, f1, buf0, buf1, plan, off, wm, wn, wave, ns - 2);
+  kstage<ALO, false, false>(acc, f0, f1, buf1, buf0, plan, off, wm, wn, wave, ns - 1);
 
   const int groups = d / 32;
   if constexpr (PHASE == 1) {
