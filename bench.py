@@ -191,6 +191,15 @@ def bench_search(args):
     def topk():
         tq.tq_topk(params, d, b, q, codes, nu, gamma, n, k, tq.TQ_EST_PROD, idx, score, ws)
 
+    if args.calibrate_copy_mb:   # a device copy of known size, for scaling HBM byte counters
+        a = torch.empty(args.calibrate_copy_mb * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        bb = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        bb.copy_(a)
+        torch.cuda.synchronize()
+        del a, bb
+
     for _ in range(max(args.warmup, 1)):
         quantize()
         topk()
@@ -241,15 +250,18 @@ def bench_search(args):
             "kernel": "tq_topk (query prep + fused score/select scan + merge)",
             "bound": "mfma", "achieved": t_tflops, "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": t_tflops / FP16_MFMA_PEAK_TFLOPS,
-            "traffic": None,
-            "note": "algorithmic 3 d flop per (query, key) pair; timed over the whole call",
+            "traffic": traffic_from_profiles("topk.hip"),
+            "note": "algorithmic 3 d flop per (query, key) pair; timed over the whole call; traffic = "
+                    "counter-measured bytes per call (the codes are read once per 256-query tile)",
         },
         "roofline_quantize": {
             "kernel": "quantize_gemm (tq_quantize, d=1536)",
             "bound": "mfma", "achieved": q_tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": q_tflops / BF16_MFMA_PEAK_TFLOPS,
-            "traffic": None,
-            "note": "algorithmic 4 d^2 flop/vector; float32 inputs execute 3 + 3 bf16 MFMA passes",
+            "traffic": traffic_from_profiles("quantize_gemm.hip"),
+            "note": "algorithmic 4 d^2 flop/vector; float32 inputs execute 3 + 3 bf16 MFMA passes; "
+                    "traffic = counter-measured bytes per call, including the per-chunk scratch round "
+                    "trips of the bf16 split rows and the residual",
         },
         "quantize": {"ms": q_ms, "vectors_per_s": n / (q_ms * 1e-3),
                      "hbm_gbs": q_bytes / (q_ms * 1e-3) / 1e9},
