@@ -231,6 +231,30 @@ __device__ __forceinline__ void kstage(f32x16 (&acc)[4][2], Frags<ALO>& f0, Frag
   }
 }
 
+// Residual rows of one 32 x 64 wave tile through LDS (sb: 32 rows of 144 bytes, padded
+// against bank conflicts), so that every global store is 16 bytes and eight lanes write a
+// row's whole 128-byte segment.  Lane (row l % 32, half h) holds, per 32-column tile j and
+// group g, the bf16 pairs of columns 32 j + 8 g + 4 h .. +3.
+__device__ __forceinline__ void store_residual(char* sb, const uint32_t (&v)[2][4][2], int lane,
+                                               uint16_t* dst, long row0, long rows_left, int d,
+                                               int col0, bool okc0, bool okc1) {
+  const int vr = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<uint2*>(sb + vr * 144 + 64 * j + 16 * g + 8 * h) = make_uint2(v[j][g][0], v[j][g][1]);
+  const int piece = lane & 7;                   // 16-byte piece: columns 8 piece .. +7
+  const bool okc = piece < 4 ? okc0 : okc1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = 8 * k + (lane >> 3);
+    const uint4 w = *reinterpret_cast<const uint4*>(sb + row * 144 + 16 * piece);
+    if (okc && row < rows_left)
+      *reinterpret_cast<uint4*>(dst + size_t(row0 + row) * d + col0 + 8 * piece) = w;
+  }
+}
+
 // PHASE 1: A = x (hi[/lo]) bf16 rows, B = Pi (hi/lo). PHASE 2: A = r' (hi/lo), B = S' (hi/lo).
 template <int PHASE, int BITS, bool ALO>
 __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
@@ -332,6 +356,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
 #pragma unroll
     for (int k = 0; k < L / 2; ++k) M[k] = hdr->mpos[k];
     float* gsum = reinterpret_cast<float*>(buf0);   // [4 wn][256 rows] partial |r'|^2
+    static_assert(WAVES * 32 * 144 <= StageShape<ALO>::U4 * 16, "transpose areas fit in buf1");
+    char* sb = reinterpret_cast<char*>(buf1) + wave * (32 * 144);   // residual transpose area
     const int h = lane >> 5;
     // one row tile at a time (a compile-time index keeps the accumulators in registers)
     auto row_tile = [&](auto it) {
@@ -340,6 +366,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
       const bool okr = r0 + vr < rows;
       const float rs = rowscale[vr];
       float g2 = 0.f;
+      uint32_t hq[2][4][2], lq[2][4][2];         // residual bf16 pairs, stored after both tiles
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int cb = c0 + 64 * wn + 32 * j;    // first coordinate of this 32-column tile
@@ -386,11 +413,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
             for (int p = 0; p < BITS - 1; ++p) word[p] |= uint32_t(bit[p]) << (8 * g + e);
           }
           // 4 consecutive coordinates: lanes l and l + 32 write 16 contiguous bytes of a row
-          if (okc && okr) {
-            const size_t ro = size_t(r0 + vr) * d + cb + 8 * g + 4 * h;
-            *reinterpret_cast<uint2*>(rhi + ro) = make_uint2(hp[0], hp[1]);
-            *reinterpret_cast<uint2*>(rlo + ro) = make_uint2(lp[0], lp[1]);
-          }
+          hq[j][g][0] = hp[0];
+          hq[j][g][1] = hp[1];
+          lq[j][g][0] = lp[0];
+          lq[j][g][1] = lp[1];
         }
         // lanes l and l + 32 hold the two nibble halves of each byte of the vector's words
 #pragma unroll
@@ -402,6 +428,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
 #pragma unroll
           for (int p = 0; p < BITS - 1; ++p) codes[(size_t(v0 + r0 + vr) * groups + w) * BITS + p] = word[p];
         }
+      }
+      // residual rows 128 wm + 32 i .. +31, columns 64 wn .. +63 of the tile
+      {
+        const long row0 = r0 + 128 * wm + 32 * i;
+        const int col0 = c0 + 64 * wn;
+        store_residual(sb, hq, lane, rhi, row0, rows - row0, d, col0, col0 < d, col0 + 32 < d);
+        store_residual(sb, lq, lane, rlo, row0, rows - row0, d, col0, col0 < d, col0 + 32 < d);
       }
       // row sum over this wave's 64 columns: lanes l and l + 32 share the row
       g2 += __shfl_xor(g2, 32);
