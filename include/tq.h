@@ -107,9 +107,11 @@ int tq_prepare(int d, int b, const float* Pi, const float* S, const double* cent
  *   nu       out [n] float32, |x|
  *   gamma    out [n] float32, norm of the residual of x/|x| after the Lloyd-Max stage
  * Integer decisions (index, sign) are taken in float32 against float32 thresholds.
- * d = 128 runs one fused kernel; other multiples of 128 run two tiled kernels per chunk of
- * 16384 vectors and take a stream-ordered scratch buffer of 16384 * d * 4 bytes
- * (hipMallocAsync / hipFreeAsync on `stream`, released when the call's work completes).
+ * d = 128 runs one fused kernel; other multiples of 128 run a split pass and two tiled
+ * kernels per chunk of 32768 vectors and take a stream-ordered scratch buffer of
+ * 32768 * d * 8 bytes for float32 input, 32768 * d * 4 bytes for bfloat16, plus
+ * 32768 * ceil(d / 256) * 4 bytes (hipMallocAsync / hipFreeAsync on `stream`, released when
+ * the call's work completes).
  * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EUNSUPPORTED (d not a multiple of 128),
  * TQ_EHIP (launch or scratch allocation failed).
  */

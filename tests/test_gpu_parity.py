@@ -167,14 +167,43 @@ def test_dequantize_parity(b, mode):
 
 @pytest.mark.parametrize("b,n", [(2, 3000), (4, 16384 + 300)])
 def test_quantize_d1536_lowrank_f32(b, n):
-    # embedding-search law (low rank + noise, unit norm, fp32), d = 1536; n crosses the
-    # 16384-vector chunk of the tiled encoder in the second case
+    # embedding-search law (low rank + noise, unit norm, fp32), d = 1536; one chunk of the
+    # tiled encoder with a ragged last row block
     st = U.make_setup(1536, b, cfg=3)
     x = gen.lowrank_vectors(n, 1536, 64, 3.0, cfg=3)
     codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
     rep = U.compare_codes(st, U.host64(x, False), U.codes_np(codes, n, 1536, b),
                           nu.cpu().numpy(), gamma.cpu().numpy())
     _report(f"d1536 b={b} n={n}", rep)
+    U.assert_codes_ok(rep)
+
+
+def test_quantize_d1536_three_chunks_sampled():
+    # 32768-vector chunks: the split rows of chunk 2 reuse chunk 0's buffers while chunk 1 is
+    # encoded; rows on both sides of each chunk boundary and the ragged end are checked
+    n = 2 * 32768 + 300
+    st = U.make_setup(1536, 4, cfg=3)
+    x = gen.lowrank_vectors(n, 1536, 64, 3.0, cfg=3)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    rows = np.r_[0:256, 32768 - 256:32768 + 256, 65536 - 256:n]
+    rep = U.compare_codes(st, U.host64(x[rows], False), U.codes_np(codes, n, 1536, 4)[rows],
+                          nu.cpu().numpy()[rows], gamma.cpu().numpy()[rows])
+    _report(f"d1536 b=4 n={n} sampled", rep)
+    U.assert_codes_ok(rep)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_quantize_d256_four_chunks(bf16):
+    # four chunks of the tiled encoder, the last one ragged, every row checked
+    n = 3 * 32768 + 123
+    st = U.make_setup(256, 4, cfg=5)
+    x = gen.lowrank_vectors(n, 256, 32, 3.0, cfg=5)
+    if bf16:
+        x = gen.f32_to_bf16_bits(x)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, bf16))
+    rep = U.compare_codes(st, U.host64(x, bf16), U.codes_np(codes, n, 256, 4),
+                          nu.cpu().numpy(), gamma.cpu().numpy())
+    _report(f"d256 b=4 n={n} {'bf16' if bf16 else 'f32'}", rep)
     U.assert_codes_ok(rep)
 
 
