@@ -107,13 +107,12 @@ int tq_prepare(int d, int b, const float* Pi, const float* S, const double* cent
  *   nu       out [n] float32, |x|
  *   gamma    out [n] float32, norm of the residual of x/|x| after the Lloyd-Max stage
  * Integer decisions (index, sign) are taken in float32 against float32 thresholds.
- * d = 128 runs one fused kernel; other multiples of 128 run a split pass and two tiled
+ * d = 128 runs one fused kernel; every other d runs a split pass and two tiled
  * kernels per chunk of 32768 vectors and take a stream-ordered scratch buffer of
  * 32768 * d * 8 bytes for float32 input, 32768 * d * 4 bytes for bfloat16, plus
  * 32768 * ceil(d / 256) * 4 bytes (hipMallocAsync / hipFreeAsync on `stream`, released when
  * the call's work completes).
- * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EUNSUPPORTED (d not a multiple of 128),
- * TQ_EHIP (launch or scratch allocation failed).
+ * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EHIP (launch or scratch allocation failed).
  */
 int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
                 uint32_t* codes, float* nu, float* gamma, void* stream);
@@ -143,7 +142,9 @@ size_t tq_score_ws_bytes(int d, int b, int64_t groups, int64_t G, int64_t T);
  *   logits   out [groups][G][T] float32
  *   ws       workspace of at least tq_score_ws_bytes(d, b, groups, G, T) bytes, 256-aligned;
  *            its contents are scratch (overwritten by this call)
- * Errors: TQ_EINVAL, TQ_EUNSUPPORTED (d != 128 or G not a multiple of 4 for now),
+ * d = 128 with G a multiple of 4 runs the tuned kernel (int8 MFMA over the key bit planes);
+ * every other shape runs a general path (float32 query prep, one lane per key).
+ * Errors: TQ_EINVAL, TQ_EUNSUPPORTED (groups * G * T beyond one launch of the general path),
  *         TQ_EWORKSPACE, TQ_EHIP.
  */
 int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,

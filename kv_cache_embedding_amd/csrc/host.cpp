@@ -325,8 +325,6 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
   if (!aligned(params, 256) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(nu, 4) ||
       !aligned(gamma, 4))
     return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x and codes 16 B)");
-  if (d % 128 != 0)
-    return fail(TQ_EUNSUPPORTED, "tq_quantize: d must be a multiple of 128 (got %d)", d);
   hipError_t e = d == 128 ? tq::launch_quantize_d128(params, b, x, x_dtype, n, codes, nu, gamma,
                                                      static_cast<hipStream_t>(stream))
                           : tq::launch_quantize_gemm(params, d, b, x, x_dtype, n, codes, nu, gamma,
@@ -350,12 +348,15 @@ int tq_dequantize(const void* params, int d, int b, const uint32_t* codes, const
   return ok();
 }
 
+// The d = 128 kernel scores quads of query heads; every other shape takes the general path.
+static bool score_uses_d128(int d, int64_t G) { return d == 128 && G % 4 == 0; }
+
 size_t tq_score_ws_bytes(int d, int b, int64_t groups, int64_t G, int64_t T) {
-  (void)d;
   (void)T;
-  if (b < 2 || b > 4 || groups < 0 || G < 0) return 0;
-  // one operand block per quad of query heads
-  return tq::align256(size_t(groups) * size_t((G + 3) / 4) * tq::score_ws_per_group(b));
+  if (!valid_shape(d, b) || groups < 0 || G < 0) return 0;
+  if (score_uses_d128(d, G))   // one operand block per quad of query heads
+    return tq::align256(size_t(groups) * size_t(G / 4) * tq::score_ws_per_group(b));
+  return tq::align256(tq::score_generic_ws_bytes(d, groups, G));
 }
 
 int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
@@ -373,15 +374,17 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
   if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(codes, 16) || !aligned(q, 4) ||
       !aligned(logits, 4))
     return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; codes 16 B)");
-  if (d != 128 || G % 4 != 0)
-    return fail(TQ_EUNSUPPORTED,
-                "tq_score_ip: implemented for d=128 and G a multiple of 4 (got d=%d G=%lld)", d,
-                (long long)G);
+  const bool d128 = score_uses_d128(d, G);
+  if (!d128 && !tq::score_generic_grid_fits(groups, G, T))
+    return fail(TQ_EUNSUPPORTED, "tq_score_ip: groups * G * T too large for one launch");
   if (ws_bytes < tq_score_ws_bytes(d, b, groups, G, T))
     return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
                 tq_score_ws_bytes(d, b, groups, G, T));
-  hipError_t e = tq::launch_score_d128(params, b, q, q_dtype, codes, nu, gamma, groups, G, T,
-                                       mode, logits, ws, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = d128 ? tq::launch_score_d128(params, b, q, q_dtype, codes, nu, gamma, groups, G, T,
+                                              mode, logits, ws, s)
+                      : tq::launch_score_generic(params, d, b, q, q_dtype, codes, nu, gamma, groups,
+                                                 G, T, mode, logits, ws, s);
   if (e != hipSuccess) return hip_fail(e, "tq_score_ip launch");
   return ok();
 }

@@ -1,4 +1,5 @@
-// TurboQuant encoder for any d that is a multiple of 128 (e.g. 1536-dimensional embeddings)
+// TurboQuant encoder for any d != 128 that is a multiple of 64 (e.g. 1536-dimensional
+// embeddings)
 // ([review, inner-product paragraph]; [tldr, steps 1-2]), per chunk of vectors:
 //   split:    nu = |x| per vector; float32 x is split into bf16 rows x_hi + x_lo (RNE);
 //   phase 1:  U = X Pi^T (rows = vectors, columns = rotated coordinates); its epilogue
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   // K loop: stage s is read from buffer s % 2 while stage s + 1 lands in the other one.
-  // d is a multiple of 128, so the number of stages is a multiple of 4.
+  // d is a multiple of 64, so the number of stages is even (at least 2).
   const int ns = d / BK;
   stage_dma(plan, 0, buf0, wave);
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));

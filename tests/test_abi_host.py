@@ -59,8 +59,15 @@ def test_params_bytes_and_workspace_helpers(lib):
     assert tq.tq_params_bytes(128, 4) > 2 * 128 * 128 * 4
     assert tq.tq_params_bytes(100, 4) == 0
     assert tq.tq_params_bytes(128, 5) == 0
+    # d != 128 carries the bf16 hi/lo rows of Pi and S' (4 d^2 x 2 bytes) for the tiled encoder
+    for d in (64, 192, 256):
+        assert tq.tq_params_bytes(d, 4) >= 2 * d * d * 4 + 4 * d * d * 2
     assert tq.tq_score_ws_bytes(128, 4, 8, 4, 32768) % 256 == 0
     assert tq.tq_score_ws_bytes(128, 4, 8, 8, 32768) == 2 * tq.tq_score_ws_bytes(128, 4, 8, 4, 32768)
+    for d, G in ((64, 4), (128, 3), (1536, 1)):
+        need = 8 * G * (2 * d + 1) * 4
+        assert need <= tq.tq_score_ws_bytes(d, 4, 8, G, 100) < need + 256
+    assert tq.tq_score_ws_bytes(100, 4, 8, 4, 100) == 0
 
 
 def _raw(lib):
@@ -82,14 +89,16 @@ def test_invalid_arguments_return_status_without_launch(lib):
     assert lib.tq_quantize(fake, 128, 4, P(0x1002), 0, 10, fake, fake, fake, None) == tq.TQ_EINVAL
     # n == 0 is a no-op even with NULL pointers
     assert lib.tq_quantize(None, 128, 4, None, 0, 0, None, None, None, None) == tq.TQ_OK
-    # a valid dimension that no encoder implements (not a multiple of 128)
-    assert lib.tq_quantize(fake, 192, 4, fake, 0, 10, fake, fake, fake, None) == tq.TQ_EUNSUPPORTED
+    # every multiple of 64 in range is a valid dimension: d = 192 fails on the pointer, not the shape
+    assert lib.tq_quantize(fake, 192, 4, P(0x1002), 0, 10, fake, fake, fake, None) == tq.TQ_EINVAL
+    assert "misaligned" in tq.tq_last_error()
     # scoring: bad mode, workspace too small, unsupported G
     args = (fake, 128, 4, fake, 1, fake, fake, fake, 8, 4, 1024)
     assert lib.tq_score_ip(*args, 9, fake, fake, 1 << 30, None) == tq.TQ_EINVAL
     assert lib.tq_score_ip(*args, 0, fake, fake, 16, None) == tq.TQ_EWORKSPACE
+    # G = 3 (and any d) takes the general path, whose workspace is [groups * G] x (2 d + 1) floats
     args3 = (fake, 128, 4, fake, 1, fake, fake, fake, 8, 3, 1024)
-    assert lib.tq_score_ip(*args3, 0, fake, fake, 1 << 30, None) == tq.TQ_EUNSUPPORTED
+    assert lib.tq_score_ip(*args3, 0, fake, fake, 16, None) == tq.TQ_EWORKSPACE
     assert lib.tq_score_ip(fake, 128, 4, fake, 1, fake, fake, fake, 0, 4, 1024, 0, None, None, 0,
                            None) == tq.TQ_OK
     # top-k: k out of range, k > n

@@ -135,6 +135,30 @@ def test_score_wide_group_f32_queries():
     assert err <= U.LOGIT_TOL
 
 
+@pytest.mark.parametrize("d,b,G,T,bf16", [
+    (64, 4, 4, 300, True), (192, 3, 3, 257, False), (256, 2, 5, 1000, True),
+    (128, 4, 3, 513, True), (128, 3, 1, 77, False), (1024, 4, 2, 260, False)])
+@pytest.mark.parametrize("mode", [tq.TQ_EST_PROD, tq.TQ_EST_MSE])
+def test_score_general_shapes(d, b, G, T, bf16, mode):
+    # shapes outside the tuned kernel (d != 128, or G not a multiple of 4): the general path
+    groups = 3
+    st = U.make_setup(d, b, cfg=14)
+    chans = gen.outlier_channels(14, groups, d)
+    keys = np.concatenate([gen.kv_keys_chunk(14, 0, h, T, d, chans[h]) for h in range(groups)])
+    q = gen.kv_queries(14, 1, groups * G, d)[0]
+    if not bf16:
+        q = gen.bf16_bits_to_f32(q)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(keys, True))
+    idx, z = oracle.unpack_codes(U.codes_np(codes, groups * T, d, b), b)
+    lg = U.gpu_score(st, U.to_device(q, bf16), codes, nu, gamma, groups, G, T, mode)
+    q64 = U.host64(q, bf16).reshape(groups, G, d)
+    err = U.logit_errors(st, q64, idx, z, nu.cpu().numpy(), gamma.cpu().numpy(), lg,
+                         "prod" if mode == tq.TQ_EST_PROD else "mse")
+    print(f"[score general d={d} b={b} G={G} T={T} mode={mode}] max err {err:.2e}", flush=True)
+    assert np.all(np.isfinite(lg))
+    assert err <= U.LOGIT_TOL
+
+
 def test_score_zero_keys_give_zero_logits():
     st = U.make_setup(128, 3, cfg=13)
     x = gen.unit_sphere(64, 128, cfg=13, role=gen.ROLE_DATA)
@@ -204,6 +228,22 @@ def test_quantize_d256_four_chunks(bf16):
     rep = U.compare_codes(st, U.host64(x, bf16), U.codes_np(codes, n, 256, 4),
                           nu.cpu().numpy(), gamma.cpu().numpy())
     _report(f"d256 b=4 n={n} {'bf16' if bf16 else 'f32'}", rep)
+    U.assert_codes_ok(rep)
+
+
+@pytest.mark.parametrize("d,b,bf16", [(64, 4, False), (64, 2, True), (192, 3, False), (192, 4, True)])
+def test_quantize_d64_multiples(d, b, bf16):
+    # dimensions that are multiples of 64 but not of 128 (two and six K stages of the tiled
+    # encoder, one column tile mostly padding); ragged row count
+    n = 2000 + 37
+    st = U.make_setup(d, b, cfg=6)
+    x = gen.unit_sphere(n, d, 6, 0)
+    if bf16:
+        x = gen.f32_to_bf16_bits(x)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, bf16))
+    rep = U.compare_codes(st, U.host64(x, bf16), U.codes_np(codes, n, d, b),
+                          nu.cpu().numpy(), gamma.cpu().numpy())
+    _report(f"d{d} b={b} {'bf16' if bf16 else 'f32'}", rep)
     U.assert_codes_ok(rep)
 
 
