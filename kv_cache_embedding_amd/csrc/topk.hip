@@ -673,13 +673,17 @@ hipError_t launch_scan(bool prod, dim3 grid, const unsigned char* params, const 
 
 size_t topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k) {
   (void)b;
+  if (k > KMAX) return topk_large_ws_bytes(d, nq, n);
   return plan(d, nq, n, k).total;
 }
 
 hipError_t launch_topk(const void* params_v, int d, int b, const void* q, int q_dtype, int64_t nq,
                        const uint32_t* codes, const float* nu, const float* gamma, int64_t n,
                        int k, int mode, int32_t* idx, float* score, void* ws, hipStream_t s) {
-  if (k > KMAX || d % 32 != 0) return hipErrorNotSupported;
+  if (d % 32 != 0) return hipErrorNotSupported;
+  if (k > KMAX)
+    return launch_topk_large(params_v, d, b, q, q_dtype, nq, codes, nu, gamma, n, k, mode, idx, score,
+                             ws, s);
   const unsigned char* params = static_cast<const unsigned char*>(params_v);
   const Layout lay(d, b);
   const Plan p = plan(d, nq, n, k);

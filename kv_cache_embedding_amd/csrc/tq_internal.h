@@ -95,6 +95,13 @@ hipError_t launch_topk(const void* params, int d, int b, const void* q, int q_dt
                        const uint32_t* codes, const float* nu, const float* gamma, int64_t n,
                        int k, int mode, int32_t* idx, float* score, void* ws, hipStream_t s);
 size_t topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k);
+// k beyond the fused scan's lists: batches of queries scored by the general path, then
+// one selection workgroup per query
+hipError_t launch_topk_large(const void* params, int d, int b, const void* q, int q_dtype,
+                             int64_t nq, const uint32_t* codes, const float* nu, const float* gamma,
+                             int64_t n, int k, int mode, int32_t* idx, float* score, void* ws,
+                             hipStream_t s);
+size_t topk_large_ws_bytes(int d, int64_t nq, int64_t n);
 
 // vmcnt-only s_waitcnt immediate for gfx9 (expcnt and lgkmcnt left unconstrained).  Direct
 // global -> LDS loads count in vmcnt, and the compiler does not order later LDS reads after

@@ -93,13 +93,51 @@ def test_topk_d1536_oracle_codes(b):
     assert worst <= U.LOGIT_TOL
 
 
-def test_topk_rejects_large_k():
+def test_topk_rejects_k_beyond_1024():
     st = U.make_setup(128, 4, cfg=0)
-    x = gen.unit_sphere(100, 128, cfg=0, role=gen.ROLE_DATA)
+    x = gen.unit_sphere(2000, 128, cfg=0, role=gen.ROLE_DATA)
     codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
     with pytest.raises(tq.TQError) as e:
-        U.gpu_topk(st, U.to_device(x[:2], False), codes, nu, gamma, 100, 33, tq.TQ_EST_PROD)
-    assert e.value.status == tq.TQ_EUNSUPPORTED
+        U.gpu_topk(st, U.to_device(x[:2], False), codes, nu, gamma, 2000, 1025, tq.TQ_EST_PROD)
+    assert e.value.status == tq.TQ_EINVAL
+
+
+@pytest.mark.parametrize("d,n,nq,k,mode", [(128, 5000, 40, 33, tq.TQ_EST_PROD),
+                                           (128, 3000, 7, 1024, tq.TQ_EST_MSE),
+                                           (192, 2000, 5, 100, tq.TQ_EST_PROD)])
+def test_topk_large_k(d, n, nq, k, mode):
+    # k beyond the fused scan's lists: scores of every key, then a radix select per query;
+    # query 0 is all zero, so its k results are the k smallest indices with score 0
+    st = U.make_setup(d, 4, cfg=33)
+    x = gen.unit_sphere(n, d, cfg=33, role=gen.ROLE_DATA)
+    q = gen.unit_sphere(nq, d, cfg=33, role=gen.ROLE_QUERY)
+    q[0] = 0.0
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    idx_g, sc_g = U.gpu_topk(st, U.to_device(q, False), codes, nu, gamma, n, k, mode)
+    idx, z = oracle.unpack_codes(U.codes_np(codes, n, d, 4), 4)
+    name = "prod" if mode == tq.TQ_EST_PROD else "mse"
+    ref, scale = _oracle_scores(st, q.astype(np.float64), idx, z, nu.cpu().numpy(), gamma.cpu().numpy(),
+                                name)
+    assert idx_g[0].tolist() == list(range(k)) and np.all(sc_g[0] == 0.0)
+    worst, swapped = U.check_topk(idx_g[1:], sc_g[1:], ref[1:], scale[1:])
+    print(f"[topk large k d={d} n={n} nq={nq} k={k} {name}] max err {worst:.2e} swaps {swapped}",
+          flush=True)
+    assert worst <= U.LOGIT_TOL
+
+
+def test_topk_large_k_two_query_batches():
+    # 600000 keys: 256 MiB of scores hold 111 queries, so 150 queries run as two batches
+    st = U.make_setup(128, 3, cfg=34)
+    n, nq, k = 600000, 150, 50
+    x = gen.unit_sphere(n, 128, cfg=34, role=gen.ROLE_DATA)
+    q = gen.unit_sphere(nq, 128, cfg=34, role=gen.ROLE_QUERY)
+    codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
+    idx_g, sc_g = U.gpu_topk(st, U.to_device(q, False), codes, nu, gamma, n, k, tq.TQ_EST_PROD)
+    idx, z = oracle.unpack_codes(U.codes_np(codes, n, 128, 3), 3)
+    ref, scale = _oracle_scores(st, q.astype(np.float64), idx, z, nu.cpu().numpy(), gamma.cpu().numpy())
+    worst, swapped = U.check_topk(idx_g, sc_g, ref, scale)
+    print(f"[topk large k two batches] max err {worst:.2e} swaps {swapped}", flush=True)
+    assert worst <= U.LOGIT_TOL
 
 
 @pytest.mark.parametrize("b", [2, 4])
