@@ -22,7 +22,10 @@ The pages give the method in prose only.  Readings taken where they are silent:
   * sign(0) is +1 (z = [y >= 0]);
   * vectors are normalised and their norm nu is stored next to gamma (no other constant);
   * integer decisions (bucket index, sign bit) are taken in float32, the precision of the
-    GPU kernels: the pages fix none.
+    GPU kernels: the pages fix none;
+  * decode attention: values are quantized by the MSE stage alone (index and nu, no QJL
+    bit: they are reconstructed, not inner-producted) and the softmax is over the raw
+    estimated logits times a caller-given scale.
 """
 from __future__ import annotations
 
@@ -34,6 +37,8 @@ __all__ = [
     "gauss_cell_prob", "gauss_cell_mean", "lloyd_max_gaussian", "gaussian_distortion",
     "codebook", "normalize_rotate", "bucketize", "residual", "qjl_signs", "quantize",
     "pack_codes", "unpack_codes", "estimate_ip", "dequantize", "topk", "qjl_alpha",
+    "quantize_mse", "pack_index_planes", "unpack_index_planes", "dequantize_mse",
+    "attention_decode",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -297,3 +302,72 @@ def topk(scores: np.ndarray, k: int, index_offset: int = 0):
         ids[a] = order + index_offset
         vals[a] = scores[a, order]
     return ids, vals
+
+
+# ------------------------------------------------------------- decode attention (values)
+# [review, problem statement]: the MSE-optimal quantizer rotates the vector with a random
+# orthogonal matrix and applies Lloyd-Max at the target bit width.  Values of a KV cache
+# are reconstructed (not inner-producted), so they take this quantizer alone: the MSE stage
+# of the same encoder, its (b-1)-bit index and the norm nu, without the QJL bit.
+
+def quantize_mse(x, Pi, centroids, thresholds):
+    """TurboQuant-mse encoding of each row of x: idx [n][d] (Lloyd-Max cell of u = Pi x/nu)
+    and nu [n].  The centroids are not used by the encoding; they are taken for symmetry
+    with quantize()."""
+    del centroids
+    nu, _, u = normalize_rotate(x, Pi)
+    return {"idx": bucketize(u, thresholds), "nu": nu, "u": u}
+
+
+def pack_index_planes(idx: np.ndarray, bits: int) -> np.ndarray:
+    """Pack idx [n][d] (values < 2**bits) into uint32 [n][d/32][bits]: plane p holds bit p
+    of every coordinate's index, coordinate t in word t // 32, bit t % 32."""
+    idx = np.asarray(idx, dtype=np.int64)
+    n, d = idx.shape
+    assert d % 32 == 0
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    out = np.empty((n, d // 32, bits), dtype=np.uint32)
+    for p in range(bits):
+        grouped = ((idx >> p) & 1).reshape(n, d // 32, 32).astype(np.uint64)
+        out[:, :, p] = np.sum(grouped * weights, axis=-1).astype(np.uint32)
+    return out
+
+
+def unpack_index_planes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_index_planes: uint32 [n][d/32][bits] -> idx [n][d]."""
+    codes = np.asarray(codes, dtype=np.uint32)
+    n, groups, bb = codes.shape
+    assert bb == bits
+    shifts = np.arange(32, dtype=np.uint32)
+    bitsarr = ((codes[:, :, :, None] >> shifts) & 1).transpose(0, 2, 1, 3).reshape(n, bits, groups * 32)
+    idx = np.zeros((n, groups * 32), dtype=np.int64)
+    for p in range(bits):
+        idx |= bitsarr[:, p].astype(np.int64) << p
+    return idx
+
+
+def dequantize_mse(Pi, idx, nu, centroids) -> np.ndarray:
+    """Value reconstruction v~ = nu Pi^T chat [n][d] ([review, QJL paragraph]: inverse
+    rotation and renormalisation)."""
+    Pi = np.asarray(Pi, dtype=np.float64)
+    chat = np.asarray(centroids, dtype=np.float64)[np.asarray(idx)]
+    return np.asarray(nu, dtype=np.float64)[:, None] * (chat @ Pi)
+
+
+def attention_decode(logits: np.ndarray, values: np.ndarray, scale: float) -> np.ndarray:
+    """One decode step of attention per group: for every query head h of group g,
+        o[g][h] = sum_t softmax_t(scale * logits[g][h][t]) * values[g][t].
+    logits [groups][G][T] (the estimated <q, k>), values [groups][T][d] (reconstructed
+    values) -> o [groups][G][d].  The softmax is taken as exp(w - max w) / sum, which is the
+    same function for finite w."""
+    logits = np.asarray(logits, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    groups, G, T = logits.shape
+    out = np.empty((groups, G, values.shape[2]), dtype=np.float64)
+    for g in range(groups):
+        w = scale * logits[g]
+        w = w - np.max(w, axis=1, keepdims=True)
+        p = np.exp(w)
+        p /= np.sum(p, axis=1, keepdims=True)
+        out[g] = p @ values[g]
+    return out

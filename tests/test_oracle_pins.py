@@ -388,3 +388,81 @@ def test_topk_matches_python_sort_with_index_tiebreak():
         ref = sorted(range(300), key=lambda j: (-s[a, j], j))[:10]
         assert ids[a].tolist() == [j + 1000 for j in ref]
         assert vals[a].tolist() == [s[a, j] for j in ref]
+
+
+# ------------------------------------------------------- value quantizer and attention pins
+
+@pytest.mark.parametrize("b,expect", [(2, 0.36089), (3, 0.11601), (4, 0.03398)])
+def test_mse_value_reconstruction_error_is_sphere_distortion(b, expect):
+    # |x - v~|^2 for unit x equals |u - chat|^2 (the rotation keeps norms), whose mean is
+    # the sphere distortion of the (b-1)-bit Lloyd-Max quantizer (same quadrature values as
+    # the gamma pin); a transposed Pi in dequantize_mse or a wrong centroid index fails it.
+    d = 128
+    Pi = gen.haar_orthogonal(d, cfg=905)
+    c, t = oracle.codebook(b - 1, d)
+    x = gen.unit_sphere(4000, d, cfg=905, role=gen.ROLE_DATA).astype(np.float64)
+    r = oracle.quantize_mse(x * 2.5, Pi, c, t)
+    assert np.allclose(r["nu"], 2.5, rtol=1e-6)
+    v = oracle.dequantize_mse(Pi, r["idx"], r["nu"], c) / 2.5
+    e2 = np.sum((x - v) ** 2, axis=1)
+    se = e2.std(ddof=1) / math.sqrt(len(e2))
+    assert abs(e2.mean() - expect) < 5 * se + 2e-5
+
+
+def test_mse_value_index_matches_prod_encoder_index():
+    # the MSE stage of the inner-product encoder is the same bucketization
+    Pi, S, c, t, x, _ = _setup(d=64, b=4, n=200, cfg=906, scale=0.7)
+    assert np.array_equal(oracle.quantize_mse(x, Pi, c, t)["idx"], oracle.quantize(x, Pi, S, c, t)["idx"])
+
+
+def test_index_planes_hand_built_and_roundtrip():
+    idx = np.zeros((1, 64), dtype=np.int64)
+    idx[0, 37] = 5                   # bits 0 and 2 of coordinate 37: word 1, bit 5
+    idx[0, 0] = 2                    # bit 1 of coordinate 0: word 0, bit 0
+    idx[0, 63] = 7
+    codes = oracle.pack_index_planes(idx, 3)
+    assert codes.shape == (1, 2, 3) and codes.dtype == np.uint32
+    assert codes[0, 0].tolist() == [0, 1, 0]
+    assert codes[0, 1].tolist() == [(1 << 5) | (1 << 31), 1 << 31, (1 << 5) | (1 << 31)]
+    g = np.random.default_rng(11)
+    r = g.integers(0, 8, size=(9, 128))
+    assert np.array_equal(oracle.unpack_index_planes(oracle.pack_index_planes(r, 3), 3), r)
+
+
+def test_attention_constant_logits_give_the_mean_value():
+    g = np.random.default_rng(12)
+    vals = g.standard_normal((2, 37, 16))
+    logits = np.full((2, 3, 37), 4.25)
+    out = oracle.attention_decode(logits, vals, scale=0.3)
+    for h in range(3):
+        assert np.allclose(out[:, h], vals.mean(axis=1), rtol=1e-13, atol=1e-13)
+
+
+def test_attention_single_key_and_dominant_key():
+    g = np.random.default_rng(13)
+    vals = g.standard_normal((1, 1, 8))
+    assert np.allclose(oracle.attention_decode(g.standard_normal((1, 2, 1)), vals, 1.0)[0],
+                       vals[0, 0], rtol=0, atol=0)
+    vals = g.standard_normal((1, 50, 8))
+    logits = g.standard_normal((1, 1, 50))
+    logits[0, 0, 17] = 5.0
+    out = oracle.attention_decode(logits, vals, scale=200.0)   # exp(-200 * gap) vanishes
+    assert np.allclose(out[0, 0], vals[0, 17], rtol=0, atol=1e-12)
+
+
+def test_attention_brute_force_tiny_and_shift_invariance():
+    # pure-Python softmax sums on a tiny case; adding a constant per head changes nothing
+    g = np.random.default_rng(14)
+    vals = g.standard_normal((2, 5, 3))
+    logits = g.standard_normal((2, 2, 5)) * 3.0
+    scale = 0.7
+    out = oracle.attention_decode(logits, vals, scale)
+    for gi in range(2):
+        for h in range(2):
+            w = [math.exp(scale * float(logits[gi, h, t])) for t in range(5)]
+            tot = sum(w)
+            for c in range(3):
+                ref = sum(w[t] * float(vals[gi, t, c]) for t in range(5)) / tot
+                assert abs(out[gi, h, c] - ref) < 1e-12
+    shifted = logits + np.array([[[100.0], [-40.0]], [[3.0], [0.5]]])
+    assert np.allclose(oracle.attention_decode(shifted, vals, scale), out, rtol=1e-12, atol=1e-12)
