@@ -118,6 +118,24 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
                 uint32_t* codes, float* nu, float* gamma, void* stream);
 
 /*
+ * tq_quantize_mse — the MSE quantizer alone ([review, problem statement]: MSE-optimal
+ * TurboQuant is the random rotation followed by Lloyd-Max at the target bit width), for
+ * vectors that are reconstructed rather than inner-producted (attention values).
+ *   params   from tq_prepare(d, b, ...): its codebook has 2^(b-1) levels, so the codes carry
+ *            b-1 index bits per coordinate (values at v bits take a block prepared for v + 1)
+ *   x        [n][d] float32 or bfloat16, row-major, 16-byte aligned
+ *   codes    out [n][d/32][b-1] uint32: plane p holds bit p of each coordinate's index,
+ *            coordinate t in word t/32, bit t%32
+ *   nu       out [n] float32, |x|
+ * The decisions are those of tq_quantize's index planes. It runs the split pass and the
+ * first tiled GEMM of the d != 128 encoder for every d (float32 input takes a
+ * stream-ordered scratch of 32768 * d * 4 bytes).
+ * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EHIP.
+ */
+int tq_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
+                    uint32_t* codes, float* nu, void* stream);
+
+/*
  * tq_dequantize — reconstruction ([review, QJL paragraph]: inverse rotation and
  * renormalisation).
  *   TQ_EST_PROD: xhat = nu (Pi^T chat + sqrt(pi/2)/m * gamma * S^T (2z - 1))
@@ -151,6 +169,32 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
                 const uint32_t* codes, const float* nu, const float* gamma, int64_t groups,
                 int64_t G, int64_t T, int mode, float* logits, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* Workspace bytes needed by tq_attention for these sizes. */
+size_t tq_attention_ws_bytes(int d, int b_k, int64_t groups, int64_t G, int64_t T);
+
+/*
+ * tq_attention — one decode step of attention over a TurboQuant KV cache ([review, problem
+ * statement]: keys take the unbiased inner-product quantizer, values the MSE one; [news,
+ * KV-cache paragraph]):
+ *   out[g][h] = sum_t softmax_t(scale * l[g][h][t]) * nu_v[g][t] Pi_v^T chat_v[g][t]
+ * with l the keys' logit estimate of tq_score_ip (mode TQ_EST_PROD or TQ_EST_MSE).
+ *   params_k, b_k  keys' parameter block and bits; codes_k [groups][T][d/32][b_k], nu_k and
+ *                  gamma_k [groups][T] from tq_quantize
+ *   params_v, b_v  values' parameter block and its b; codes_v [groups][T][d/32][b_v - 1] and
+ *                  nu_v [groups][T] from tq_quantize_mse
+ *   q     [groups][G][d] float32 or bfloat16; scale: multiplies the logits (e.g. 1/sqrt(d))
+ *   out   [groups][G][d] float32
+ *   ws    tq_attention_ws_bytes(d, b_k, groups, G, T) bytes, 256-aligned, scratch (logits,
+ *         the scoring workspace and per-256-key-block partial sums)
+ * Errors: TQ_EINVAL (T = 0 with groups * G > 0, non-finite scale, ...), TQ_EUNSUPPORTED,
+ *         TQ_EWORKSPACE, TQ_EHIP.
+ */
+int tq_attention(const void* params_k, const void* params_v, int d, int b_k, int b_v,
+                 const void* q, int q_dtype, const uint32_t* codes_k, const float* nu_k,
+                 const float* gamma_k, const uint32_t* codes_v, const float* nu_v, int64_t groups,
+                 int64_t G, int64_t T, float scale, int mode, float* out, void* ws,
+                 size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by tq_topk for these sizes. */
 size_t tq_topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k);

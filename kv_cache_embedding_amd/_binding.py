@@ -45,6 +45,10 @@ def load_library():
         "tq_dequantize": (I, [P, I, I, P, P, P, I64, I, P, P]),
         "tq_score_ws_bytes": (SZ, [I, I, I64, I64, I64]),
         "tq_score_ip": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P, SZ, P]),
+        "tq_quantize_mse": (I, [P, I, I, P, I, I64, P, P, P]),
+        "tq_attention_ws_bytes": (SZ, [I, I, I64, I64, I64]),
+        "tq_attention": (I, [P, P, I, I, I, P, I, P, P, P, P, P, I64, I64, I64, ctypes.c_float, I,
+                             P, P, SZ, P]),
         "tq_topk_ws_bytes": (SZ, [I, I, I64, I64, I]),
         "tq_topk": (I, [P, I, I, P, I, I64, P, P, P, I64, I, I, P, P, P, SZ, P]),
         "tq_last_error": (ctypes.c_char_p, []),
@@ -163,6 +167,21 @@ def tq_quantize(params, d: int, b: int, x, codes, nu, gamma, stream=None):
                                       _stream(stream, x.device)))
 
 
+def tq_quantize_mse(params, d: int, b: int, x, codes, nu, stream=None):
+    """MSE quantizer alone: x [n][d] -> codes [n][d/32][b-1] uint32 (index planes), nu[n]."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError(f"x must be [n][{d}]")
+    n = x.shape[0]
+    for tname, t in (("codes", codes), ("nu", nu), ("params", params)):
+        _dev(t, tname)
+    _need(codes, "codes", n * (d // 32) * (b - 1), torch.int32)
+    _need(nu, "nu", n, torch.float32)
+    _check(load_library().tq_quantize_mse(_ptr(params), d, b, _ptr(x), _dtype_code(x, "x"), n,
+                                          _ptr(codes), _ptr(nu), _stream(stream, x.device)))
+
+
 def tq_dequantize(params, d: int, b: int, codes, nu, gamma, mode: int, xhat, stream=None):
     """Reconstruct xhat [n][d] float32 from codes/nu/gamma (n = nu.numel())."""
     torch = _torch()
@@ -197,6 +216,34 @@ def tq_score_ip(params, d: int, b: int, q, codes, nu, gamma, groups: int, G: int
                                       _ptr(nu), _ptr(gamma), groups, G, T, int(mode), _ptr(logits),
                                       _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(stream, q.device)))
+
+
+def tq_attention_ws_bytes(d: int, b_k: int, groups: int, G: int, T: int) -> int:
+    return int(load_library().tq_attention_ws_bytes(d, b_k, groups, G, T))
+
+
+def tq_attention(params_k, params_v, d: int, b_k: int, b_v: int, q, codes_k, nu_k, gamma_k,
+                 codes_v, nu_v, groups: int, G: int, T: int, scale: float, mode: int, out, ws,
+                 stream=None):
+    """out[groups][G][d] = softmax(scale * estimated logits) times the MSE-reconstructed values."""
+    torch = _torch()
+    for tname, t in (("q", q), ("codes_k", codes_k), ("nu_k", nu_k), ("gamma_k", gamma_k),
+                     ("codes_v", codes_v), ("nu_v", nu_v), ("out", out), ("ws", ws),
+                     ("params_k", params_k), ("params_v", params_v)):
+        _dev(t, tname)
+    if q.numel() < groups * G * d:
+        raise ValueError("q holds fewer than groups*G*d elements")
+    _need(codes_k, "codes_k", groups * T * (d // 32) * b_k, torch.int32)
+    _need(nu_k, "nu_k", groups * T, torch.float32)
+    _need(gamma_k, "gamma_k", groups * T, torch.float32)
+    _need(codes_v, "codes_v", groups * T * (d // 32) * (b_v - 1), torch.int32)
+    _need(nu_v, "nu_v", groups * T, torch.float32)
+    _need(out, "out", groups * G * d, torch.float32)
+    _check(load_library().tq_attention(_ptr(params_k), _ptr(params_v), d, b_k, b_v, _ptr(q),
+                                       _dtype_code(q, "q"), _ptr(codes_k), _ptr(nu_k), _ptr(gamma_k),
+                                       _ptr(codes_v), _ptr(nu_v), groups, G, T, float(scale),
+                                       int(mode), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream, q.device)))
 
 
 def tq_topk_ws_bytes(d: int, b: int, nq: int, n: int, k: int) -> int:

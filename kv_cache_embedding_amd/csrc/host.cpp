@@ -333,6 +333,21 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
   return ok();
 }
 
+int tq_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
+                    uint32_t* codes, float* nu, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad x_dtype %d", x_dtype);
+  if (n < 0) return fail(TQ_EINVAL, "n=%lld < 0", (long long)n);
+  if (n == 0) return ok();
+  if (!params || !x || !codes || !nu) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(x, 16) || !aligned(codes, 4) || !aligned(nu, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x 16 B)");
+  hipError_t e = tq::launch_quantize_mse(params, d, b, x, x_dtype, n, codes, nu,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize_mse launch");
+  return ok();
+}
+
 int tq_dequantize(const void* params, int d, int b, const uint32_t* codes, const float* nu,
                   const float* gamma, int64_t n, int mode, float* xhat, void* stream) {
   if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
@@ -350,6 +365,21 @@ int tq_dequantize(const void* params, int d, int b, const uint32_t* codes, const
 
 // The d = 128 kernel scores quads of query heads; every other shape takes the general path.
 static bool score_uses_d128(int d, int64_t G) { return d == 128 && G % 4 == 0; }
+
+static bool score_grid_fits(int d, int64_t groups, int64_t G, int64_t T) {
+  return score_uses_d128(d, G) || tq::score_generic_grid_fits(groups, G, T);
+}
+
+static hipError_t launch_score_any(const void* params, int d, int b, const void* q, int q_dtype,
+                                   const uint32_t* codes, const float* nu, const float* gamma,
+                                   int64_t groups, int64_t G, int64_t T, int mode, float* logits,
+                                   void* ws, hipStream_t s) {
+  return score_uses_d128(d, G)
+             ? tq::launch_score_d128(params, b, q, q_dtype, codes, nu, gamma, groups, G, T, mode,
+                                     logits, ws, s)
+             : tq::launch_score_generic(params, d, b, q, q_dtype, codes, nu, gamma, groups, G, T,
+                                        mode, logits, ws, s);
+}
 
 size_t tq_score_ws_bytes(int d, int b, int64_t groups, int64_t G, int64_t T) {
   (void)T;
@@ -374,18 +404,58 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
   if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(codes, 16) || !aligned(q, 4) ||
       !aligned(logits, 4))
     return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; codes 16 B)");
-  const bool d128 = score_uses_d128(d, G);
-  if (!d128 && !tq::score_generic_grid_fits(groups, G, T))
+  if (!score_grid_fits(d, groups, G, T))
     return fail(TQ_EUNSUPPORTED, "tq_score_ip: groups * G * T too large for one launch");
   if (ws_bytes < tq_score_ws_bytes(d, b, groups, G, T))
     return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes,
                 tq_score_ws_bytes(d, b, groups, G, T));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = d128 ? tq::launch_score_d128(params, b, q, q_dtype, codes, nu, gamma, groups, G, T,
-                                              mode, logits, ws, s)
-                      : tq::launch_score_generic(params, d, b, q, q_dtype, codes, nu, gamma, groups,
-                                                 G, T, mode, logits, ws, s);
+  hipError_t e = launch_score_any(params, d, b, q, q_dtype, codes, nu, gamma, groups, G, T, mode,
+                                  logits, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tq_score_ip launch");
+  return ok();
+}
+
+size_t tq_attention_ws_bytes(int d, int b_k, int64_t groups, int64_t G, int64_t T) {
+  if (!valid_shape(d, b_k) || groups < 0 || G < 0 || T < 0) return 0;
+  return tq::align256(size_t(groups) * G * T * 4) + tq_score_ws_bytes(d, b_k, groups, G, T) +
+         tq::align256(tq::attention_part_bytes(d, groups, G, T));
+}
+
+int tq_attention(const void* params_k, const void* params_v, int d, int b_k, int b_v,
+                 const void* q, int q_dtype, const uint32_t* codes_k, const float* nu_k,
+                 const float* gamma_k, const uint32_t* codes_v, const float* nu_v, int64_t groups,
+                 int64_t G, int64_t T, float scale, int mode, float* out, void* ws,
+                 size_t ws_bytes, void* stream) {
+  if (!valid_shape(d, b_k) || !valid_shape(d, b_v))
+    return fail(TQ_EINVAL, "unsupported shape d=%d b_k=%d b_v=%d", d, b_k, b_v);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad q_dtype %d", q_dtype);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (!std::isfinite(scale)) return fail(TQ_EINVAL, "scale must be finite");
+  if (groups < 0 || G < 0 || T < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0 || G == 0) return ok();
+  if (T == 0) return fail(TQ_EINVAL, "T = 0: a softmax needs at least one key");
+  if (T >= (int64_t(1) << 31)) return fail(TQ_EINVAL, "T must be < 2^31");
+  if (!params_k || !params_v || !q || !codes_k || !nu_k || !gamma_k || !codes_v || !nu_v || !out ||
+      !ws)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params_k, 256) || !aligned(params_v, 256) || !aligned(ws, 256) ||
+      !aligned(codes_k, 16) || !aligned(codes_v, 4) || !aligned(q, 4) || !aligned(out, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; key codes 16 B)");
+  if (!score_grid_fits(d, groups, G, T) || !tq::attention_grid_fits(groups, G, T))
+    return fail(TQ_EUNSUPPORTED, "tq_attention: groups * G * T too large for one launch");
+  const size_t need = tq_attention_ws_bytes(d, b_k, groups, G, T);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  float* logits = reinterpret_cast<float*>(w);
+  void* sws = w + tq::align256(size_t(groups) * G * T * 4);
+  void* part = static_cast<unsigned char*>(sws) + tq_score_ws_bytes(d, b_k, groups, G, T);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_score_any(params_k, d, b_k, q, q_dtype, codes_k, nu_k, gamma_k, groups, G, T,
+                                  mode, logits, sws, s);
+  if (e == hipSuccess)
+    e = tq::launch_attention_values(params_v, d, b_v, logits, codes_v, nu_v, groups, G, T, scale, out,
+                                    part, s);
+  if (e != hipSuccess) return hip_fail(e, "tq_attention launch");
   return ok();
 }
 

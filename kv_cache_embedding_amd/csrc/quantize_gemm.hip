@@ -257,6 +257,8 @@ __device__ __forceinline__ void store_residual(char* sb, const uint32_t (&v)[2][
 }
 
 // PHASE 1: A = x (hi[/lo]) bf16 rows, B = Pi (hi/lo). PHASE 2: A = r' (hi/lo), B = S' (hi/lo).
+// PHASE 3: phase 1 for the MSE quantizer alone: the b-1 index planes (a code stride of b-1
+// words per coordinate group) and nothing for a phase 2.
 template <int PHASE, int BITS, bool ALO>
 __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
     const unsigned char* __restrict__ params, const uint16_t* __restrict__ ahi,
@@ -342,7 +344,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
   kstage<ALO, false, false>(acc, f0, f1, buf1, buf0, plan, off, wm, wn, wave, ns - 1);
 
   const int groups = d / 32;
-  if constexpr (PHASE == 1) {
+  if constexpr (PHASE == 1 || PHASE == 3) {
+    constexpr bool MSE = PHASE == 3;
+    constexpr int CB = MSE ? BITS - 1 : BITS;   // code words per coordinate group
     if (tid < WT) {
       const long row = r0 + tid < rows ? r0 + tid : rows - 1;
       const float nrm = nu[v0 + row];
@@ -427,28 +431,32 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
         }
         if (okc && lane < 32 && okr) {
 #pragma unroll
-          for (int p = 0; p < BITS - 1; ++p) codes[(size_t(v0 + r0 + vr) * groups + w) * BITS + p] = word[p];
+          for (int p = 0; p < BITS - 1; ++p) codes[(size_t(v0 + r0 + vr) * groups + w) * CB + p] = word[p];
         }
       }
       // residual rows 128 wm + 32 i .. +31, columns 64 wn .. +63 of the tile
-      {
+      if constexpr (!MSE) {
         const long row0 = r0 + 128 * wm + 32 * i;
         const int col0 = c0 + 64 * wn;
         store_residual(sb, hq, lane, rhi, row0, rows - row0, d, col0, col0 < d, col0 + 32 < d);
         store_residual(sb, lq, lane, rlo, row0, rows - row0, d, col0, col0 < d, col0 + 32 < d);
       }
       // row sum over this wave's 64 columns: lanes l and l + 32 share the row
-      g2 += __shfl_xor(g2, 32);
-      if (lane < 32) gsum[wn * WT + vr] = g2;
+      if constexpr (!MSE) {
+        g2 += __shfl_xor(g2, 32);
+        if (lane < 32) gsum[wn * WT + vr] = g2;
+      }
     };
     row_tile(std::integral_constant<int, 0>{});
     row_tile(std::integral_constant<int, 1>{});
     row_tile(std::integral_constant<int, 2>{});
     row_tile(std::integral_constant<int, 3>{});
-    __syncthreads();
-    if (tid < WT && r0 + tid < rows)
-      gpart[size_t(r0 + tid) * nct + ct] =
-          gsum[tid] + gsum[WT + tid] + gsum[2 * WT + tid] + gsum[3 * WT + tid];
+    if constexpr (!MSE) {
+      __syncthreads();
+      if (tid < WT && r0 + tid < rows)
+        gpart[size_t(r0 + tid) * nct + ct] =
+            gsum[tid] + gsum[WT + tid] + gsum[2 * WT + tid] + gsum[3 * WT + tid];
+    }
   } else {
     const int h = lane >> 5;
 #pragma unroll
@@ -519,6 +527,46 @@ hipError_t run(const unsigned char* params, const Layout& lay, const void* x, in
   return e != hipSuccess ? e : f;
 }
 
+// The MSE quantizer alone: per chunk the split pass (nu, x hi/lo) and phase 1 without the
+// residual.
+template <int BITS, bool F32IN>
+hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x, int64_t n,
+                   uint32_t* codes, float* nu, hipStream_t s) {
+  const int d = lay.d;
+  const uint16_t* pih = reinterpret_cast<const uint16_t*>(params + lay.off_gmat);
+  const uint16_t* pil = pih + size_t(d) * d;
+  const long ch = n < CHUNK ? long(n) : CHUNK;
+  const int nct = (d + WT - 1) / WT;
+  const size_t plane = size_t(CHUNK) * d;
+  uint16_t* scratch = nullptr;
+  hipError_t e = hipSuccess;
+  if (F32IN) {
+    e = hipMallocAsync(reinterpret_cast<void**>(&scratch), plane * 2 * 2, s);
+    if (e != hipSuccess) return e;
+  }
+  uint16_t* xh = F32IN ? scratch : nullptr;
+  uint16_t* xl = F32IN ? scratch + plane : nullptr;
+  for (long c0 = 0; c0 < n; c0 += ch) {
+    const long rows = (n - c0) < ch ? (n - c0) : ch;
+    const int nrb = int((rows + WT - 1) / WT);
+    const dim3 grid(unsigned((nrb + NXCD - 1) / NXCD * NXCD * nct));
+    const void* xs = F32IN ? static_cast<const void*>(static_cast<const float*>(x) + size_t(c0) * d)
+                           : static_cast<const void*>(static_cast<const uint16_t*>(x) + size_t(c0) * d);
+    hipLaunchKernelGGL((qsplit_kernel<F32IN>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, xs,
+                       rows, d, xh, xl, c0, nu);
+    const uint16_t* a1 = F32IN ? xh : static_cast<const uint16_t*>(xs);
+    hipLaunchKernelGGL((qgemm_kernel<3, BITS, F32IN>), grid, dim3(WAVES * 64), 0, s, params, a1, xl,
+                       rows, pih, pil, d, c0, nrb, codes, nu, nullptr, nullptr, nullptr, nullptr);
+    e = hipGetLastError();
+    if (e != hipSuccess) break;
+  }
+  if (F32IN) {
+    const hipError_t f = hipFreeAsync(scratch, s);
+    if (e == hipSuccess) e = f;
+  }
+  return e;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_gemm(const void* params_v, int d, int b, const void* x, int x_dtype,
@@ -534,6 +582,26 @@ hipError_t launch_quantize_gemm(const void* params_v, int d, int b, const void* 
                        : run<3, false>(params, lay, x, n, codes, nu, gamma, s);
     case 4: return f32 ? run<4, true>(params, lay, x, n, codes, nu, gamma, s)
                        : run<4, false>(params, lay, x, n, codes, nu, gamma, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tq
+
+namespace tq {
+
+hipError_t launch_quantize_mse(const void* params_v, int d, int b, const void* x, int x_dtype,
+                               int64_t n, uint32_t* codes, float* nu, hipStream_t s) {
+  const unsigned char* params = static_cast<const unsigned char*>(params_v);
+  const Layout lay(d, b);
+  const bool f32 = x_dtype == 0;
+  switch (b) {
+    case 2: return f32 ? run_mse<2, true>(params, lay, x, n, codes, nu, s)
+                       : run_mse<2, false>(params, lay, x, n, codes, nu, s);
+    case 3: return f32 ? run_mse<3, true>(params, lay, x, n, codes, nu, s)
+                       : run_mse<3, false>(params, lay, x, n, codes, nu, s);
+    case 4: return f32 ? run_mse<4, true>(params, lay, x, n, codes, nu, s)
+                       : run_mse<4, false>(params, lay, x, n, codes, nu, s);
     default: return hipErrorInvalidValue;
   }
 }

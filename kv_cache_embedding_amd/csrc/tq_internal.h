@@ -38,7 +38,7 @@ struct Layout {
   size_t off_s = 0;       // S   [d][d] fp32 row-major
   size_t off_qfrag = 0;   // d == 128: quantize MFMA fragments (2 x 64 KiB), else 0 bytes
   size_t qfrag_bytes = 0;
-  size_t off_gmat = 0;    // d != 128: bf16 Pi_hi, Pi_lo, S'_hi, S'_lo [d][d]
+  size_t off_gmat = 0;    // bf16 Pi_hi, Pi_lo, S'_hi, S'_lo [d][d] (tiled encoders, every d)
   size_t gmat_bytes = 0;
   size_t off_tr = 0;      // d == 128: Pi^T and S^T fp32 [2][d][d] (column k of Pi at k * d)
   size_t tr_bytes = 0;
@@ -55,7 +55,7 @@ inline Layout::Layout(int d_, int b_) : d(d_), b(b_) {
   off_qfrag = align256(off_s + size_t(d) * d * 4);
   qfrag_bytes = (d == 128) ? size_t(2) * 64 * 1024 : 0;
   off_gmat = align256(off_qfrag + qfrag_bytes);
-  gmat_bytes = (d != 128) ? size_t(4) * d * d * 2 : 0;
+  gmat_bytes = size_t(4) * d * d * 2;
   off_tr = align256(off_gmat + gmat_bytes);
   tr_bytes = (d == 128) ? size_t(2) * d * d * 4 : 0;
   total = align256(off_tr + tr_bytes);
@@ -88,6 +88,17 @@ hipError_t launch_score_generic(const void* params, int d, int b, const void* q,
                                 void* ws, hipStream_t s);
 size_t score_generic_ws_bytes(int d, int64_t groups, int64_t G);
 bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T);
+// The MSE stage alone (b-1 index planes and nu), any d: the tiled encoder's phase 1.
+hipError_t launch_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype,
+                               int64_t n, uint32_t* codes, float* nu, hipStream_t s);
+// Decode attention after the logits: block partials of the softmax-weighted value sum, then
+// their merge and the inverse rotation.
+size_t attention_part_bytes(int d, int64_t groups, int64_t G, int64_t T);
+bool attention_grid_fits(int64_t groups, int64_t G, int64_t T);
+hipError_t launch_attention_values(const void* params_v, int d, int b_v, const float* logits,
+                                   const uint32_t* vcodes, const float* vnu, int64_t groups,
+                                   int64_t G, int64_t T, float scale, float* out, void* part,
+                                   hipStream_t s);
 hipError_t launch_dequantize(const void* params, int d, int b, const uint32_t* codes,
                              const float* nu, const float* gamma, int64_t n, int mode,
                              float* xhat, hipStream_t s);

@@ -108,6 +108,22 @@ def test_invalid_arguments_return_status_without_launch(lib):
                        1 << 30, None) == tq.TQ_EINVAL
     # dequantize: bad mode
     assert lib.tq_dequantize(fake, 128, 4, fake, fake, fake, 10, 3, fake, None) == tq.TQ_EINVAL
+    # quantize_mse: bad b, misaligned x, n == 0
+    assert lib.tq_quantize_mse(fake, 128, 5, fake, 0, 10, fake, fake, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize_mse(fake, 128, 4, P(0x1002), 0, 10, fake, fake, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize_mse(None, 128, 4, None, 0, 0, None, None, None) == tq.TQ_OK
+    # attention: T == 0, non-finite scale, bad mode, small workspace, empty groups
+    F = ctypes.c_float
+    def att(T, scale, mode, ws_bytes, groups=2, G=4):
+        return lib.tq_attention(fake, fake, 128, 4, 4, fake, 1, fake, fake, fake, fake, fake,
+                                groups, G, T, F(scale), mode, fake, fake, ws_bytes, None)
+    assert att(0, 0.1, 0, 1 << 30) == tq.TQ_EINVAL
+    assert att(100, float("nan"), 0, 1 << 30) == tq.TQ_EINVAL
+    assert att(100, float("inf"), 0, 1 << 30) == tq.TQ_EINVAL
+    assert att(100, 0.1, 7, 1 << 30) == tq.TQ_EINVAL
+    assert att(100, 0.1, 0, 256) == tq.TQ_EWORKSPACE
+    assert att(100, 0.1, 0, 0, groups=0) == tq.TQ_OK
+    assert tq.tq_attention_ws_bytes(128, 4, 2, 4, 100) >= 2 * 4 * 100 * 4 + tq.tq_score_ws_bytes(128, 4, 2, 4, 100)
 
 
 def test_prepare_rejects_bad_codebook_and_rotation(lib):
