@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_layer",
-                    choices=["decode_layer", "long_context", "embedding_search"])
+                    choices=["decode_layer", "long_context", "embedding_search", "decode_attention"])
     ap.add_argument("--bits", type=int, default=0, help="embedding_search: b (default 4)")
     ap.add_argument("--replicas", type=int, default=8, help="resident input copies cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU baseline budget")
@@ -272,6 +272,174 @@ def bench_search(args):
     print(json.dumps(result), flush=True)
 
 
+def cpu_baseline_attention(w, b_k, b_v, seconds: float):
+    """The oracle on a bounded sample of the decode-attention workload: whole KV heads (keys
+    and values quantized, logits, softmax, values aggregated), until the budget is spent."""
+    import oracle
+    from workloads import gen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    d = w.d
+    Pk, Sk = gen.haar_orthogonal(d, w.cfg), gen.gaussian_matrix(d, d, w.cfg)
+    Pv, Sv = gen.haar_orthogonal(d, w.cfg, rep=1), gen.gaussian_matrix(d, d, w.cfg, rep=1)
+    ck, tk = oracle.codebook(b_k - 1, d)
+    cv, tv = oracle.codebook(b_v - 1, d)
+    del Sv
+    chans = gen.outlier_channels(w.cfg, w.n_kv, d)
+    q = gen.bf16_bits_to_f32(gen.kv_queries(w.cfg, 1, w.n_q_heads, d)[0]).astype(np.float64)
+    heads, pairs, elapsed = 0, 0, 0.0
+    while heads < w.n_kv and elapsed < seconds:
+        keys = gen.bf16_bits_to_f32(gen.kv_keys_chunk(w.cfg, 0, heads, w.T, d, chans[heads]))
+        vals = gen.bf16_bits_to_f32(gen.kv_keys_chunk(w.cfg, w.n_seq, heads, w.T, d, chans[heads], scale=1.0))
+        t0 = time.perf_counter()
+        rk = oracle.quantize(keys.astype(np.float64), Pk, Sk, ck, tk)
+        rv = oracle.quantize_mse(vals.astype(np.float64), Pv, cv, tv)
+        qh = q[heads * w.G:(heads + 1) * w.G]
+        lg = oracle.estimate_ip(qh, Pk, Sk, rk["idx"], rk["z"], rk["nu"], rk["gamma"], ck)
+        vh = oracle.dequantize_mse(Pv, rv["idx"], rv["nu"], cv)
+        oracle.attention_decode(lg[None], vh[None], 1.0 / np.sqrt(d))
+        elapsed += time.perf_counter() - t0
+        heads += 1
+        pairs += lg.size
+    return {
+        "value": pairs / elapsed, "unit": "pairs/s", "cores": int(cores), "kind": "oracle",
+        "sample": f"{heads} of {w.n_kv} KV heads ({heads * w.T} keys and values quantized, {pairs} "
+                  f"(query head, key) pairs attended), float64 NumPy oracle, {elapsed:.1f} s",
+    }
+
+
+def bench_attention(args):
+    """One decode step of attention over a quantized KV cache at the decode-layer shapes:
+    keys b = 4 (TurboQuant-prod), values 3 index bits (TurboQuant-mse, a block prepared for
+    b = 4); a step is one tq_attention call (logits, softmax, value aggregation)."""
+    import torch
+
+    import kv_cache_embedding_amd as tq
+    from workloads import gen
+
+    w = gen.DECODE_LAYER
+    dev = torch.device("cuda:0")
+    d, b_k, b_v = w.d, 4, 4
+    groups, G, T = w.groups, w.G, w.T
+    n = w.n_keys
+    scale = 1.0 / float(np.sqrt(d))
+
+    def prep(bits, rep):
+        Pi = gen.haar_orthogonal(d, w.cfg, rep=rep)
+        S = gen.gaussian_matrix(d, d, w.cfg, rep=rep)
+        c, t = tq.tq_codebook_build(bits - 1, d)
+        prm = torch.empty(tq.tq_params_bytes(d, bits), dtype=torch.uint8, device=dev)
+        tq.tq_prepare(d, bits, Pi, S, c, t, prm)
+        return prm
+
+    pk, pv = prep(b_k, 0), prep(b_v, 1)
+    chans = gen.outlier_channels(w.cfg, w.n_kv, d)
+    keys = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
+    vals = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
+    for s in range(w.n_seq):
+        for h in range(w.n_kv):
+            gi = s * w.n_kv + h
+            kc = gen.kv_keys_chunk(w.cfg, s, h, T, d, chans[h])
+            vc = gen.kv_keys_chunk(w.cfg, w.n_seq + s, h, T, d, chans[h], scale=1.0)
+            keys[gi * T:(gi + 1) * T] = torch.from_numpy(kc.view(np.int16)).to(dev).view(torch.bfloat16)
+            vals[gi * T:(gi + 1) * T] = torch.from_numpy(vc.view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(gen.kv_queries(w.cfg, w.n_seq, w.n_q_heads, d).reshape(-1, d).view(np.int16))
+    q = q.to(dev).view(torch.bfloat16)
+
+    per_key = d // 8 * b_k + 8 + d // 8 * (b_v - 1) + 4     # key codes, nu, gamma, value codes, nu
+    R = max(1, min(max(args.replicas, 12), int(2 * 1024**3 // (n * per_key))))
+    ck = [torch.empty(n * (d // 32) * b_k, dtype=torch.int32, device=dev) for _ in range(R)]
+    nk = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
+    gk = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
+    cv = [torch.empty(n * (d // 32) * (b_v - 1), dtype=torch.int32, device=dev) for _ in range(R)]
+    nv = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
+    for r in range(R):
+        tq.tq_quantize(pk, d, b_k, keys, ck[r], nk[r], gk[r])
+        tq.tq_quantize_mse(pv, d, b_v, vals, cv[r], nv[r])
+    out = torch.empty(groups * G * d, dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_attention_ws_bytes(d, b_k, groups, G, T), dtype=torch.uint8, device=dev)
+
+    def attend(r):
+        tq.tq_attention(pk, pv, d, b_k, b_v, q, ck[r], nk[r], gk[r], cv[r], nv[r], groups, G, T, scale,
+                        tq.TQ_EST_PROD, out, ws)
+
+    def vquant(r):
+        tq.tq_quantize_mse(pv, d, b_v, vals, cv[r], nv[r])
+
+    for i in range(max(args.warmup, 1)):
+        attend(i % R)
+    torch.cuda.synchronize()
+
+    def capture(fn, r):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(r)
+        return g
+
+    g_att = [capture(attend, r) for r in range(R)]
+    g_vq = [capture(vquant, r) for r in range(R)]
+    for r in range(R):
+        g_att[r].replay()
+    torch.cuda.synchronize()
+    K = args.steps
+
+    def timed(gs):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(K):
+            gs[i % R].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        g_att[i % R].replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    a_ms = timed(g_att)
+    vq_ms = timed(g_vq)
+    pairs = groups * G * T
+    a_bytes = n * per_key + groups * G * d * 4
+    a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+    vq_bytes = n * (d * 2 + d // 8 * (b_v - 1) + 4)
+    result = {
+        "metric": "decode attention over a TurboQuant KV cache: (query head, key) pairs/s "
+                  "(GB/s vs HBM peak), 1 MI355X",
+        "value": pairs / (ms_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) keys with outlier channels and N(0,1) values, bf16; "
+                "random rotations and QJL matrix)",
+        "config": {
+            "workload": f"decode_attention: {w.n_kv} KV heads x {T} tokens x d={d}, keys b={b_k} "
+                        f"(prod), values {b_v - 1} index bits (mse), {w.n_q_heads} query heads "
+                        f"(GQA {G}), softmax scale 1/sqrt(d)",
+            "keys": n, "d": d, "key_bits": b_k, "value_index_bits": b_v - 1, "replicas": R,
+        },
+        "roofline": {
+            "kernel": "tq_attention (score qprep + score + attention blocks + combine)",
+            "bound": "hbm", "achieved": a_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": a_gbs / HBM_PEAK_GBS, "traffic": None,
+            "note": f"algorithmic bytes per key: {d // 8 * b_k} B key codes + 8 B nu, gamma + "
+                    f"{d // 8 * (b_v - 1)} B value codes + 4 B nu; the logits and block partials "
+                    "in the workspace are implementation traffic; timed over the whole call",
+        },
+        "value_quantize": {"ms": vq_ms, "vectors_per_s": n / (vq_ms * 1e-3),
+                           "hbm_gbs": vq_bytes / (vq_ms * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_attention(w, b_k, b_v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -280,6 +448,9 @@ def main():
         sys.exit(2)
     if args.workload == "embedding_search":
         bench_search(args)
+        return
+    if args.workload == "decode_attention":
+        bench_attention(args)
         return
 
     import torch

@@ -184,7 +184,7 @@ size_t tq_attention_ws_bytes(int d, int b_k, int64_t groups, int64_t G, int64_t 
  *   params_v, b_v  values' parameter block and its b; codes_v [groups][T][d/32][b_v - 1] and
  *                  nu_v [groups][T] from tq_quantize_mse
  *   q     [groups][G][d] float32 or bfloat16; scale: multiplies the logits (e.g. 1/sqrt(d))
- *   out   [groups][G][d] float32
+ *   out   [groups][G][d] float32, 16-byte aligned
  *   ws    tq_attention_ws_bytes(d, b_k, groups, G, T) bytes, 256-aligned, scratch (logits,
  *         the scoring workspace and per-256-key-block partial sums)
  * Errors: TQ_EINVAL (T = 0 with groups * G > 0, non-finite scale, ...), TQ_EUNSUPPORTED,

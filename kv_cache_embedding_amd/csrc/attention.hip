@@ -9,12 +9,13 @@
 // attn_block_kernel: one workgroup per (group, pass of AH heads, block of KB keys).  Lanes
 //   first hold one key each: scaled logits, the block maximum per head, the weights
 //   p = exp(l - max) and p nu.  Then each wave walks its 64 keys with the lanes over the
-//   coordinates (64 per step): the value's plane words are the same for every lane (scalar
-//   loads), a lane picks its word and bit, looks the centroid up in LDS and accumulates it
-//   times the key's weight for every head.  Out: per block and head the maximum, the sum of
+//   coordinates (64 per step): the plane words of the wave's keys are first staged in LDS
+//   (lane j loads key j's), a lane reads its word, takes its bit, looks the centroid up in
+//   LDS and accumulates it times the key's weight for every head.  Out: per block and head the maximum, the sum of
 //   p and the weighted sum of centroids.
 // attn_combine_kernel: one workgroup per (group, head): merges the blocks (log-sum-exp) and
-//   applies Pi_v^T (a row of Pi_v is contiguous, so thread j reads column j coalesced).
+//   applies Pi_v^T; threads split both sums into slices of independent float4 loads (rows
+//   of Pi_v are contiguous, so a slice reads coalesced columns).
 #include "tq_internal.h"
 
 #include <cmath>
@@ -24,7 +25,6 @@ namespace {
 
 constexpr int AH = 4;      // query heads per pass
 constexpr int KB = 256;    // keys per workgroup (64 per wave)
-constexpr int CPL = 4;     // coordinates per lane per chunk (a chunk is 256 coordinates)
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -38,7 +38,8 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int BV>   // index planes of a value
+// BV: index planes of a value; NC: 64-coordinate steps per chunk (NC divides d / 64)
+template <int BV, int NC>
 __global__ __launch_bounds__(256) void attn_block_kernel(
     const unsigned char* __restrict__ params_v, const float* __restrict__ logits,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnu, int d, long G, long T,
@@ -48,7 +49,8 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
   const Header* hdr = reinterpret_cast<const Header*>(params_v);
   __shared__ float cen[L];
   __shared__ float red[4][AH];
-  __shared__ float accs[4][AH][64 * CPL];
+  __shared__ float accs[4][AH][64 * NC];
+  __shared__ uint32_t kw[4][64][2 * NC * BV];    // words of a chunk for the wave's 64 keys
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar code loads
   if (tid < L) cen[tid] = hdr->cen[tid];
@@ -96,29 +98,37 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
     }
   }
 
-  // weighted sum of the centroids of the wave's keys, 256 coordinates per chunk
+  // weighted sum of the centroids of the wave's keys, 64 NC coordinates per chunk
   const int W = d / 32;
   const long nk = T - tw0 < 64 ? (T - tw0 > 0 ? T - tw0 : 0) : 64;
-  for (int c0 = 0; c0 < d; c0 += 64 * CPL) {
-    float acc[AH][CPL];
+  for (int c0 = 0; c0 < d; c0 += 64 * NC) {
+    // the chunk's plane words of the wave's keys: lane j loads those of key j (one pass of
+    // contiguous loads instead of a dependent scalar load per key)
+    if (lane < nk) {
+      const uint32_t* kc = vcodes + (size_t(g * T + tw0 + lane) * W + c0 / 32) * BV;
+#pragma unroll
+      for (int e = 0; e < 2 * NC * BV; ++e) kw[wave][lane][e] = kc[e];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    float acc[AH][NC];
 #pragma unroll
     for (int hh = 0; hh < AH; ++hh)
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[hh][i] = 0.f;
+      for (int i = 0; i < NC; ++i) acc[hh][i] = 0.f;
+#pragma unroll 4
     for (int j = 0; j < nk; ++j) {
       float wj[AH];
 #pragma unroll
       for (int hh = 0; hh < AH; ++hh)
         wj[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[hh]), j));
-      const uint32_t* kc = vcodes + (size_t(g * T + tw0 + j) * W + c0 / 32) * BV;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        if (c0 + 64 * i >= d) break;            // uniform
+      for (int i = 0; i < NC; ++i) {
         uint32_t idx = 0;
 #pragma unroll
         for (int p = 0; p < BV; ++p) {
-          const uint32_t wlo = kc[(2 * i) * BV + p], whi = kc[(2 * i + 1) * BV + p];
-          const uint32_t word = lane < 32 ? wlo : whi;
+          const uint32_t word = kw[wave][j][(2 * i + (lane >> 5)) * BV + p];
           idx |= ((word >> (lane & 31)) & 1u) << p;
         }
         const float c = cen[idx];
@@ -129,11 +139,11 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
 #pragma unroll
     for (int hh = 0; hh < AH; ++hh)
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) accs[wave][hh][64 * i + lane] = acc[hh][i];
+      for (int i = 0; i < NC; ++i) accs[wave][hh][64 * i + lane] = acc[hh][i];
     __syncthreads();
-    for (int e = tid; e < AH * 64 * CPL; e += 256) {
-      const int hh = e / (64 * CPL), c = e % (64 * CPL);
-      if (hh < nh && c0 + c < d)
+    for (int e = tid; e < AH * 64 * NC; e += 256) {
+      const int hh = e / (64 * NC), c = e % (64 * NC);
+      if (hh < nh)
         part_acc[((prow + hh) * nkb + kb) * d + c0 + c] =
             (accs[0][hh][c] + accs[1][hh][c]) + (accs[2][hh][c] + accs[3][hh][c]);
     }
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     const unsigned char* __restrict__ params_v, size_t off_pi, int d, long nkb,
     const float* __restrict__ part_m, const float* __restrict__ part_s,
     const float* __restrict__ part_acc, float* __restrict__ out) {
-  extern __shared__ float a[];   // the head's combined rotated-space sum, d floats
+  extern __shared__ float4 lds4[];   // [slices][d / 4] partial sums, then a[d / 4]
   __shared__ float red[4];
   const long row = blockIdx.x;   // group * G + head
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -164,25 +174,78 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   if (lane == 0) red[wave] = sum;
   __syncthreads();
   const float inv = 1.f / ((red[0] + red[1]) + (red[2] + red[3]));
-  for (int c = tid; c < d; c += 256) {
-    float v = 0.f;
-    for (long k = 0; k < nkb; ++k) v = fmaf(__expf(pm[k] - M), part_acc[(row * nkb + k) * d + c], v);
-    a[c] = v * inv;
+
+  // threads = (float4 column q4, slice): a slice sums every nsl-th block, the slices are
+  // then added in LDS; all loads of a thread are independent
+  const int d4 = d / 4;
+  const int cols = d4 < 256 ? d4 : 256;
+  const int nsl = 256 / cols;
+  const int q4 = tid % cols, sl = tid / cols;
+  float4* part = lds4;                 // [nsl][d4]
+  float4* av = lds4 + size_t(nsl) * d4;   // a / sum, d4 float4
+  const float4* pa = reinterpret_cast<const float4*>(part_acc) + row * nkb * d4;
+  if (sl < nsl) {
+    for (int c4 = q4; c4 < d4; c4 += cols) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+      for (long k = sl; k < nkb; k += nsl) {
+        const float e = __expf(pm[k] - M);
+        const float4 x = pa[k * d4 + c4];
+        v.x = fmaf(e, x.x, v.x);
+        v.y = fmaf(e, x.y, v.y);
+        v.z = fmaf(e, x.z, v.z);
+        v.w = fmaf(e, x.w, v.w);
+      }
+      part[sl * d4 + c4] = v;
+    }
   }
   __syncthreads();
-  const float* Pi = reinterpret_cast<const float*>(params_v + off_pi);
-  for (int j = tid; j < d; j += 256) {
-    float v = 0.f;
-    for (int i = 0; i < d; ++i) v = fmaf(Pi[size_t(i) * d + j], a[i], v);
-    out[row * d + j] = v;
+  for (int c4 = tid; c4 < d4; c4 += 256) {
+    float4 v = part[c4];
+    for (int t = 1; t < nsl; ++t) {
+      const float4 x = part[t * d4 + c4];
+      v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+    }
+    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
+    av[c4] = v;
+  }
+  __syncthreads();
+  // out = Pi_v^T a: thread (float4 of outputs j4, slice of rows i); rows of Pi_v contiguous
+  const float* a = reinterpret_cast<const float*>(av);
+  const float4* P4 = reinterpret_cast<const float4*>(params_v + off_pi);
+  if (sl < nsl) {
+    for (int j4 = q4; j4 < d4; j4 += cols) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+      for (int i = sl; i < d; i += nsl) {
+        const float ai = a[i];
+        const float4 x = P4[size_t(i) * d4 + j4];
+        v.x = fmaf(x.x, ai, v.x);
+        v.y = fmaf(x.y, ai, v.y);
+        v.z = fmaf(x.z, ai, v.z);
+        v.w = fmaf(x.w, ai, v.w);
+      }
+      part[sl * d4 + j4] = v;
+    }
+  }
+  __syncthreads();
+  float4* o4 = reinterpret_cast<float4*>(out) + row * d4;
+  for (int j4 = tid; j4 < d4; j4 += 256) {
+    float4 v = part[j4];
+    for (int t = 1; t < nsl; ++t) {
+      const float4 x = part[t * d4 + j4];
+      v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+    }
+    o4[j4] = v;
   }
 }
 
 }  // namespace
 
+// Block partials in the workspace: maxima, sums, weighted centroid sums, each 256-aligned.
 size_t attention_part_bytes(int d, int64_t groups, int64_t G, int64_t T) {
-  const size_t nkb = size_t((T + KB - 1) / KB);
-  return size_t(groups) * G * nkb * (2 + size_t(d)) * 4;
+  const size_t rk = size_t(groups) * G * size_t((T + KB - 1) / KB);
+  return 2 * align256(rk * 4) + align256(rk * size_t(d) * 4);
 }
 
 hipError_t launch_attention_values(const void* params_v, int d, int b_v, const float* logits,
@@ -193,24 +256,38 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
   const long nkb = (T + KB - 1) / KB;
   const long passes = (G + AH - 1) / AH;
   const size_t rows = size_t(groups) * G;
-  float* part_m = static_cast<float*>(part);
-  float* part_s = part_m + rows * nkb;
-  float* part_acc = part_s + rows * nkb;
+  unsigned char* pb = static_cast<unsigned char*>(part);
+  float* part_m = reinterpret_cast<float*>(pb);
+  float* part_s = reinterpret_cast<float*>(pb + align256(rows * nkb * 4));
+  float* part_acc = reinterpret_cast<float*>(pb + 2 * align256(rows * nkb * 4));
   const dim3 grid(unsigned(groups * passes * nkb));
+  const int steps = d / 64;
+  const int nc = steps % 4 == 0 ? 4 : steps % 3 == 0 ? 3 : steps % 2 == 0 ? 2 : 1;
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, pv, logits, vcodes, vnu, d, long(G), long(T), nkb,
+                       passes, scale, part_m, part_s, part_acc);
+  };
+#define TQ_ATTN_NC(BV)                                      \
+  switch (nc) {                                             \
+    case 4: launch(attn_block_kernel<BV, 4>); break;       \
+    case 3: launch(attn_block_kernel<BV, 3>); break;       \
+    case 2: launch(attn_block_kernel<BV, 2>); break;       \
+    default: launch(attn_block_kernel<BV, 1>); break;      \
+  }
   switch (b_v) {
-    case 2: hipLaunchKernelGGL(attn_block_kernel<1>, grid, dim3(256), 0, s, pv, logits, vcodes, vnu, d,
-                               long(G), long(T), nkb, passes, scale, part_m, part_s, part_acc); break;
-    case 3: hipLaunchKernelGGL(attn_block_kernel<2>, grid, dim3(256), 0, s, pv, logits, vcodes, vnu, d,
-                               long(G), long(T), nkb, passes, scale, part_m, part_s, part_acc); break;
-    case 4: hipLaunchKernelGGL(attn_block_kernel<3>, grid, dim3(256), 0, s, pv, logits, vcodes, vnu, d,
-                               long(G), long(T), nkb, passes, scale, part_m, part_s, part_acc); break;
+    case 2: TQ_ATTN_NC(1) break;
+    case 3: TQ_ATTN_NC(2) break;
+    case 4: TQ_ATTN_NC(3) break;
     default: return hipErrorInvalidValue;
   }
+#undef TQ_ATTN_NC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const Layout lay(d, b_v);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(256), size_t(d) * 4, s, pv,
-                     lay.off_pi, d, nkb, part_m, part_s, part_acc, out);
+  const int d4 = d / 4, cols = d4 < 256 ? d4 : 256, nsl = 256 / cols;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(256),
+                     (size_t(nsl) * d4 + d4) * 16, s, pv, lay.off_pi, d, nkb, part_m, part_s,
+                     part_acc, out);
   return hipGetLastError();
 }
 

@@ -439,8 +439,8 @@ int tq_attention(const void* params_k, const void* params_v, int d, int b_k, int
       !ws)
     return fail(TQ_EINVAL, "NULL pointer");
   if (!aligned(params_k, 256) || !aligned(params_v, 256) || !aligned(ws, 256) ||
-      !aligned(codes_k, 16) || !aligned(codes_v, 4) || !aligned(q, 4) || !aligned(out, 4))
-    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; key codes 16 B)");
+      !aligned(codes_k, 16) || !aligned(codes_v, 4) || !aligned(q, 4) || !aligned(out, 16))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; key codes, out 16 B)");
   if (!score_grid_fits(d, groups, G, T) || !tq::attention_grid_fits(groups, G, T))
     return fail(TQ_EUNSUPPORTED, "tq_attention: groups * G * T too large for one launch");
   const size_t need = tq_attention_ws_bytes(d, b_k, groups, G, T);
