@@ -342,8 +342,9 @@ int tq_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype
   if (!params || !x || !codes || !nu) return fail(TQ_EINVAL, "NULL pointer");
   if (!aligned(params, 256) || !aligned(x, 16) || !aligned(codes, 4) || !aligned(nu, 4))
     return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x 16 B)");
-  hipError_t e = tq::launch_quantize_mse(params, d, b, x, x_dtype, n, codes, nu,
-                                         static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = d == 128 ? tq::launch_quantize_d128_mse(params, b, x, x_dtype, n, codes, nu, s)
+                          : tq::launch_quantize_mse(params, d, b, x, x_dtype, n, codes, nu, s);
   if (e != hipSuccess) return hip_fail(e, "tq_quantize_mse launch");
   return ok();
 }

@@ -41,7 +41,9 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int BITS, bool F32IN>
+// MSE: the MSE quantizer alone (attention values): GEMM1 and the index planes only, b-1
+// planes per coordinate group, nu but no gamma.
+template <int BITS, bool F32IN, bool MSE>
 __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     const unsigned char* __restrict__ params, size_t frag_off, const void* __restrict__ xin,
     long n, uint32_t* __restrict__ codes, float* __restrict__ nu_out,
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     // ---- GEMM2: Y^T = S'~ R'^T, one 32-row tile of projections at a time; the sign
     //      bits of y are shifted in the same way (y is never -0 either)
 #pragma unroll
-    for (int mp = 0; mp < 4; mp += 2) {
+    for (int mp = 0; mp < (MSE ? 0 : 4); mp += 2) {
       f32x16 Y[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -274,31 +276,30 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- assemble whole words: half h = 0 finishes row tiles 0,1; h = 1 tiles 2,3
-    uint32_t out[2 * BITS];
+    constexpr int P = MSE ? BITS - 1 : BITS;   // planes stored per coordinate group
+    uint32_t out[2 * P];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
 #pragma unroll
-      for (int p = 0; p < BITS; ++p) {
+      for (int p = 0; p < P; ++p) {
         const uint32_t send = kh == 0 ? hb[p][2 + k] : hb[p][k];
         const uint32_t recv = __shfl_xor(send, 32);
-        out[k * BITS + p] = kh == 0 ? (hb[p][k] | (recv << 16)) : (recv | (hb[p][2 + k] << 16));
+        out[k * P + p] = kh == 0 ? (hb[p][k] | (recv << 16)) : (recv | (hb[p][2 + k] << 16));
       }
     }
     if (valid) {
-      uint32_t* dst = codes + (vec * 4 + 2 * kh) * BITS;
-      if constexpr (BITS == 4) {
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
-        reinterpret_cast<uint4*>(dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
-      } else if constexpr (BITS == 3) {
-        reinterpret_cast<uint2*>(dst)[0] = make_uint2(out[0], out[1]);
-        reinterpret_cast<uint2*>(dst)[1] = make_uint2(out[2], out[3]);
-        reinterpret_cast<uint2*>(dst)[2] = make_uint2(out[4], out[5]);
+      uint32_t* dst = codes + (vec * 4 + 2 * kh) * P;
+      if constexpr (P % 2 == 0) {   // 16-byte aligned: 2 P words at a multiple of 8 P words
+#pragma unroll
+        for (int i = 0; i < P / 2; ++i)
+          reinterpret_cast<uint4*>(dst)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
       } else {
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+#pragma unroll
+        for (int i = 0; i < P; ++i) reinterpret_cast<uint2*>(dst)[i] = make_uint2(out[2 * i], out[2 * i + 1]);
       }
       if (kh == 0) {
         nu_out[vec] = nu;
-        gamma_out[vec] = gamma;
+        if constexpr (!MSE) gamma_out[vec] = gamma;
       }
     }
     tile = next;
@@ -318,14 +319,14 @@ int cu_count() {
   return cached;
 }
 
-template <int BITS, bool F32IN>
+template <int BITS, bool F32IN, bool MSE = false>
 hipError_t launch(const void* params, const void* x, int64_t n, uint32_t* codes, float* nu,
                   float* gamma, hipStream_t s) {
 
   const long ntiles = (n + VPW - 1) / VPW;
   const long need = (ntiles + WAVES - 1) / WAVES;
   const int grid = int(need < cu_count() ? need : cu_count());
-  hipLaunchKernelGGL((quantize_d128_kernel<BITS, F32IN>), dim3(grid), dim3(WAVES * 64), 0, s,
+  hipLaunchKernelGGL((quantize_d128_kernel<BITS, F32IN, MSE>), dim3(grid), dim3(WAVES * 64), 0, s,
                      static_cast<const unsigned char*>(params), Layout(D, BITS).off_qfrag, x,
                      long(n), codes, nu, gamma);
   return hipGetLastError();
@@ -343,6 +344,24 @@ hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_
                        : launch<3, false>(params, x, n, codes, nu, gamma, s);
     case 4: return f32 ? launch<4, true>(params, x, n, codes, nu, gamma, s)
                        : launch<4, false>(params, x, n, codes, nu, gamma, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tq
+
+namespace tq {
+
+hipError_t launch_quantize_d128_mse(const void* params, int b, const void* x, int x_dtype,
+                                    int64_t n, uint32_t* codes, float* nu, hipStream_t s) {
+  const bool f32 = x_dtype == 0;
+  switch (b) {
+    case 2: return f32 ? launch<2, true, true>(params, x, n, codes, nu, nullptr, s)
+                       : launch<2, false, true>(params, x, n, codes, nu, nullptr, s);
+    case 3: return f32 ? launch<3, true, true>(params, x, n, codes, nu, nullptr, s)
+                       : launch<3, false, true>(params, x, n, codes, nu, nullptr, s);
+    case 4: return f32 ? launch<4, true, true>(params, x, n, codes, nu, nullptr, s)
+                       : launch<4, false, true>(params, x, n, codes, nu, nullptr, s);
     default: return hipErrorInvalidValue;
   }
 }

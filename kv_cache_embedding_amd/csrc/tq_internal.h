@@ -88,7 +88,10 @@ hipError_t launch_score_generic(const void* params, int d, int b, const void* q,
                                 void* ws, hipStream_t s);
 size_t score_generic_ws_bytes(int d, int64_t groups, int64_t G);
 bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T);
-// The MSE stage alone (b-1 index planes and nu), any d: the tiled encoder's phase 1.
+// The MSE stage alone (b-1 index planes and nu): d = 128 on the fused encoder without its
+// GEMM2, every other d on the tiled encoder's phase 1.
+hipError_t launch_quantize_d128_mse(const void* params, int b, const void* x, int x_dtype,
+                                    int64_t n, uint32_t* codes, float* nu, hipStream_t s);
 hipError_t launch_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype,
                                int64_t n, uint32_t* codes, float* nu, hipStream_t s);
 // Decode attention after the logits: block partials of the softmax-weighted value sum, then
