@@ -369,6 +369,16 @@ def bench_attention(args):
     def vquant(r):
         tq.tq_quantize_mse(pv, d, b_v, vals, cv[r], nv[r])
 
+    # one decode step's cache write: the newest token of every group, key and value
+    k_tok = keys.view(groups, T, d)[:, T - 1, :].contiguous()
+    v_tok = vals.view(groups, T, d)[:, T - 1, :].contiguous()
+    ws_app = torch.empty(max(tq.tq_append_ws_bytes(d, b_k, groups), tq.tq_append_ws_bytes(d, b_v, groups)),
+                         dtype=torch.uint8, device=dev)
+
+    def append(r):
+        tq.tq_append(pk, d, b_k, tq.TQ_EST_PROD, k_tok, T, T - 1, ck[r], nk[r], gk[r], ws_app)
+        tq.tq_append(pv, d, b_v, tq.TQ_EST_MSE, v_tok, T, T - 1, cv[r], nv[r], None, ws_app)
+
     for i in range(max(args.warmup, 1)):
         attend(i % R)
     torch.cuda.synchronize()
@@ -381,6 +391,7 @@ def bench_attention(args):
 
     g_att = [capture(attend, r) for r in range(R)]
     g_vq = [capture(vquant, r) for r in range(R)]
+    g_app = [capture(append, r) for r in range(R)]
     for r in range(R):
         g_att[r].replay()
     torch.cuda.synchronize()
@@ -405,6 +416,7 @@ def bench_attention(args):
     ms_step = (time.perf_counter() - t0) * 1e3 / K
     a_ms = timed(g_att)
     vq_ms = timed(g_vq)
+    app_ms = timed(g_app)
     pairs = groups * G * T
     a_bytes = n * per_key + groups * G * d * 4
     a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
@@ -434,6 +446,9 @@ def bench_attention(args):
         },
         "value_quantize": {"ms": vq_ms, "vectors_per_s": n / (vq_ms * 1e-3),
                            "hbm_gbs": vq_bytes / (vq_ms * 1e-3) / 1e9},
+        "append": {"us": app_ms * 1e3,
+                   "note": f"tq_append of one token per group ({groups} groups): key (prod) + value "
+                           "(mse), as one decode step writes them"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_attention(w, b_k, b_v, args.cpu_seconds)

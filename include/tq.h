@@ -109,8 +109,8 @@ int tq_prepare(int d, int b, const float* Pi, const float* S, const double* cent
  * Integer decisions (index, sign) are taken in float32 against float32 thresholds.
  * d = 128 runs one fused kernel; every other d runs a split pass and two tiled
  * kernels per chunk of 32768 vectors and take a stream-ordered scratch buffer of
- * 32768 * d * 8 bytes for float32 input, 32768 * d * 4 bytes for bfloat16, plus
- * 32768 * ceil(d / 256) * 4 bytes (hipMallocAsync / hipFreeAsync on `stream`, released when
+ * c * d * 8 bytes for float32 input, c * d * 4 bytes for bfloat16, plus c * ceil(d / 256) * 4
+ * bytes, c = min(n, 32768) (hipMallocAsync / hipFreeAsync on `stream`, released when
  * the call's work completes).
  * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EHIP (launch or scratch allocation failed).
  */
@@ -128,12 +128,32 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
  *            coordinate t in word t/32, bit t%32
  *   nu       out [n] float32, |x|
  * The decisions are those of tq_quantize's index planes. It runs the split pass and the
- * first tiled GEMM of the d != 128 encoder for every d (float32 input takes a
- * stream-ordered scratch of 32768 * d * 4 bytes).
+ * first tiled GEMM of the tiled encoder for d != 128 (float32 input takes a stream-ordered
+ * scratch of min(n, 32768) * d * 4 bytes) and the fused encoder without its QJL GEMM at
+ * d = 128.
  * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EHIP.
  */
 int tq_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
                     uint32_t* codes, float* nu, void* stream);
+
+/* Workspace bytes needed by tq_append for these sizes. */
+size_t tq_append_ws_bytes(int d, int b, int64_t groups);
+
+/*
+ * tq_append — quantize-on-write of one new token per group into existing caches ([explainer,
+ * step 1]: the grid is fixed ahead of time, so a token is encoded on arrival without
+ * calibration or other tokens): x[g] is encoded as tq_quantize (mode TQ_EST_PROD: keys, b
+ * planes, nu and gamma) or tq_quantize_mse (mode TQ_EST_MSE: values, b-1 planes and nu) would
+ * encode it, and written to slot (g, pos) of caches laid out [groups][cap]:
+ *   codes[g][pos][d/32][planes], nu[g][pos], gamma[g][pos] (gamma unused and may be NULL for
+ *   TQ_EST_MSE).  0 <= pos < cap; the other slots are not touched.
+ *   x    [groups][d] float32 or bfloat16, 16-byte aligned
+ *   ws   tq_append_ws_bytes(d, b, groups) bytes, 256-aligned, scratch
+ * Errors: TQ_EINVAL (pos outside [0, cap), NULL, misalignment, ...), TQ_EWORKSPACE, TQ_EHIP.
+ */
+int tq_append(const void* params, int d, int b, int mode, const void* x, int x_dtype,
+              int64_t groups, int64_t cap, int64_t pos, uint32_t* codes, float* nu, float* gamma,
+              void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tq_dequantize — reconstruction ([review, QJL paragraph]: inverse rotation and

@@ -46,6 +46,8 @@ def load_library():
         "tq_score_ws_bytes": (SZ, [I, I, I64, I64, I64]),
         "tq_score_ip": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P, SZ, P]),
         "tq_quantize_mse": (I, [P, I, I, P, I, I64, P, P, P]),
+        "tq_append_ws_bytes": (SZ, [I, I, I64]),
+        "tq_append": (I, [P, I, I, I, P, I, I64, I64, I64, P, P, P, P, SZ, P]),
         "tq_attention_ws_bytes": (SZ, [I, I, I64, I64, I64]),
         "tq_attention": (I, [P, P, I, I, I, P, I, P, P, P, P, P, I64, I64, I64, ctypes.c_float, I,
                              P, P, SZ, P]),
@@ -180,6 +182,32 @@ def tq_quantize_mse(params, d: int, b: int, x, codes, nu, stream=None):
     _need(nu, "nu", n, torch.float32)
     _check(load_library().tq_quantize_mse(_ptr(params), d, b, _ptr(x), _dtype_code(x, "x"), n,
                                           _ptr(codes), _ptr(nu), _stream(stream, x.device)))
+
+
+def tq_append_ws_bytes(d: int, b: int, groups: int) -> int:
+    return int(load_library().tq_append_ws_bytes(d, b, groups))
+
+
+def tq_append(params, d: int, b: int, mode: int, x, cap: int, pos: int, codes, nu, gamma, ws,
+              stream=None):
+    """Encode x [groups][d] and write vector g to slot (g, pos) of [groups][cap] caches."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError(f"x must be [groups][{d}]")
+    groups = x.shape[0]
+    planes = b if mode == TQ_EST_PROD else b - 1
+    for tname, t in (("codes", codes), ("nu", nu), ("ws", ws), ("params", params)):
+        _dev(t, tname)
+    _need(codes, "codes", groups * cap * (d // 32) * planes, torch.int32)
+    _need(nu, "nu", groups * cap, torch.float32)
+    if mode == TQ_EST_PROD:
+        _dev(gamma, "gamma")
+        _need(gamma, "gamma", groups * cap, torch.float32)
+    _check(load_library().tq_append(_ptr(params), d, b, int(mode), _ptr(x), _dtype_code(x, "x"), groups,
+                                    cap, pos, _ptr(codes), _ptr(nu),
+                                    _ptr(gamma) if gamma is not None else None, _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream, x.device)))
 
 
 def tq_dequantize(params, d: int, b: int, codes, nu, gamma, mode: int, xhat, stream=None):

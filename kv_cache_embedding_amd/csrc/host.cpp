@@ -349,6 +349,49 @@ int tq_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype
   return ok();
 }
 
+size_t tq_append_ws_bytes(int d, int b, int64_t groups) {
+  if (!valid_shape(d, b) || groups < 0) return 0;
+  return tq::align256(size_t(groups) * (d / 32) * b * 4) + 2 * tq::align256(size_t(groups) * 4);
+}
+
+int tq_append(const void* params, int d, int b, int mode, const void* x, int x_dtype,
+              int64_t groups, int64_t cap, int64_t pos, uint32_t* codes, float* nu, float* gamma,
+              void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad x_dtype %d", x_dtype);
+  if (groups < 0 || cap < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0) return ok();
+  if (pos < 0 || pos >= cap) return fail(TQ_EINVAL, "pos=%lld outside [0, cap=%lld)", (long long)pos,
+                                        (long long)cap);
+  if (groups >= (int64_t(1) << 31)) return fail(TQ_EINVAL, "groups must be < 2^31");
+  const bool prod = mode == TQ_EST_PROD;
+  if (!params || !x || !codes || !nu || (prod && !gamma) || !ws) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(x, 16) || !aligned(ws, 256) || !aligned(codes, 4) ||
+      !aligned(nu, 4) || (gamma && !aligned(gamma, 4)))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; x 16 B)");
+  const size_t need = tq_append_ws_bytes(d, b, groups);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const int planes = prod ? b : b - 1;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  uint32_t* tc = reinterpret_cast<uint32_t*>(w);
+  float* tn = reinterpret_cast<float*>(w + tq::align256(size_t(groups) * (d / 32) * b * 4));
+  float* tg = tn + tq::align256(size_t(groups) * 4) / 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (prod)
+    e = d == 128 ? tq::launch_quantize_d128(params, b, x, x_dtype, groups, tc, tn, tg, s)
+                 : tq::launch_quantize_gemm(params, d, b, x, x_dtype, groups, tc, tn, tg, s);
+  else
+    e = d == 128 ? tq::launch_quantize_d128_mse(params, b, x, x_dtype, groups, tc, tn, s)
+                 : tq::launch_quantize_mse(params, d, b, x, x_dtype, groups, tc, tn, s);
+  if (e == hipSuccess)
+    e = tq::launch_scatter_slot(tc, tn, prod ? tg : nullptr, (d / 32) * planes, groups, cap, pos, codes,
+                                nu, prod ? gamma : nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "tq_append launch");
+  return ok();
+}
+
 int tq_dequantize(const void* params, int d, int b, const uint32_t* codes, const float* nu,
                   const float* gamma, int64_t n, int mode, float* xhat, void* stream) {
   if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);

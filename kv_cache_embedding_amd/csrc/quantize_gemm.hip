@@ -495,10 +495,10 @@ hipError_t run(const unsigned char* params, const Layout& lay, const void* x, in
   const uint16_t* spl = sph + size_t(d) * d;
   const long ch = n < CHUNK ? long(n) : CHUNK;
   const int nct = (d + WT - 1) / WT;
-  // scratch: r' hi, r' lo and (float32 input) x hi, x lo, each CHUNK x d bf16; then the
-  // partial sums of |r'|^2, CHUNK x (d / 256) float32
-  const size_t plane = size_t(CHUNK) * d;
-  const size_t bytes = plane * 2 * (F32IN ? 4 : 2) + size_t(CHUNK) * nct * 4;
+  // scratch: r' hi, r' lo and (float32 input) x hi, x lo, each (chunk rows) x d bf16; then
+  // the partial sums of |r'|^2, (chunk rows) x (d / 256) float32
+  const size_t plane = size_t(ch) * d;
+  const size_t bytes = plane * 2 * (F32IN ? 4 : 2) + size_t(ch) * nct * 4;
   uint16_t* scratch = nullptr;
   hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), bytes, s);
   if (e != hipSuccess) return e;
@@ -537,7 +537,7 @@ hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x
   const uint16_t* pil = pih + size_t(d) * d;
   const long ch = n < CHUNK ? long(n) : CHUNK;
   const int nct = (d + WT - 1) / WT;
-  const size_t plane = size_t(CHUNK) * d;
+  const size_t plane = size_t(ch) * d;
   uint16_t* scratch = nullptr;
   hipError_t e = hipSuccess;
   if (F32IN) {

@@ -102,6 +102,12 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
                                    const uint32_t* vcodes, const float* vnu, int64_t groups,
                                    int64_t G, int64_t T, float scale, float* out, void* part,
                                    hipStream_t s);
+// Cache append: copies vector g's words, nu and gamma (gamma may be NULL) of a contiguous
+// batch to slot (g, pos) of [groups][cap] caches.
+hipError_t launch_scatter_slot(const uint32_t* src_codes, const float* src_nu,
+                               const float* src_gamma, int words, int64_t groups, int64_t cap,
+                               int64_t pos, uint32_t* codes, float* nu, float* gamma,
+                               hipStream_t s);
 hipError_t launch_dequantize(const void* params, int d, int b, const uint32_t* codes,
                              const float* nu, const float* gamma, int64_t n, int mode,
                              float* xhat, hipStream_t s);

@@ -124,6 +124,16 @@ def test_invalid_arguments_return_status_without_launch(lib):
     assert att(100, 0.1, 0, 256) == tq.TQ_EWORKSPACE
     assert att(100, 0.1, 0, 0, groups=0) == tq.TQ_OK
     assert tq.tq_attention_ws_bytes(128, 4, 2, 4, 100) >= 2 * 4 * 100 * 4 + tq.tq_score_ws_bytes(128, 4, 2, 4, 100)
+    # append: pos outside [0, cap), bad mode, small workspace, gamma needed for keys, no groups
+    def app(pos, cap=16, mode=0, ws_bytes=1 << 20, gamma=fake, groups=8):
+        return lib.tq_append(fake, 128, 4, mode, fake, 1, groups, cap, pos, fake, fake, gamma, fake,
+                             ws_bytes, None)
+    assert app(16) == tq.TQ_EINVAL and app(-1) == tq.TQ_EINVAL
+    assert app(3, mode=5) == tq.TQ_EINVAL
+    assert app(3, ws_bytes=64) == tq.TQ_EWORKSPACE
+    assert app(3, gamma=None) == tq.TQ_EINVAL
+    assert app(3, groups=0) == tq.TQ_OK
+    assert tq.tq_append_ws_bytes(128, 4, 8) >= 8 * 4 * 4 * 4 + 2 * 8 * 4
 
 
 def test_prepare_rejects_bad_codebook_and_rotation(lib):

@@ -161,3 +161,40 @@ def test_attention_long_sequence_many_blocks():
     err = float(np.max(np.abs(out - ref)))
     print(f"[attention long T={T}] own-logit err {err / vmax:.2e}", flush=True)
     assert err <= 2e-5 * vmax
+
+
+@pytest.mark.parametrize("d,bf16", [(128, True), (192, False)])
+def test_append_matches_bulk_encoding(d, bf16):
+    # a cache filled token by token through tq_append holds the bulk encoders' bytes, for keys
+    # (prod) and values (mse); slots not yet written keep their contents
+    groups, T, b = 3, 40, 4
+    st = U.make_setup(d, b, cfg=44)
+    x = gen.unit_sphere(groups * T, d, cfg=44, role=gen.ROLE_DATA) * 2.0
+    if bf16:
+        x = gen.f32_to_bf16_bits(x)
+    xd = U.to_device(x, bf16).reshape(groups, T, d)
+    bulk_c, bulk_n, bulk_g = U.gpu_quantize(st, U.to_device(x, bf16))
+    bulk_vc, bulk_vn = _mse_quantize(st, U.to_device(x, bf16), groups * T)
+    W = d // 32
+    ck = torch.full((groups * T * W * b,), -1, dtype=torch.int32, device=DEV)
+    nk = torch.full((groups * T,), -1.0, dtype=torch.float32, device=DEV)
+    gk = torch.full((groups * T,), -1.0, dtype=torch.float32, device=DEV)
+    cv = torch.full((groups * T * W * (b - 1),), -1, dtype=torch.int32, device=DEV)
+    nv = torch.full((groups * T,), -1.0, dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.tq_append_ws_bytes(d, b, groups), dtype=torch.uint8, device=DEV)
+    filled = [t for t in range(T) if t != 17]      # slot 17 stays empty
+    for t in filled:
+        tok = xd[:, t, :].contiguous()
+        tq.tq_append(st.params, d, b, tq.TQ_EST_PROD, tok, T, t, ck, nk, gk, ws)
+        tq.tq_append(st.params, d, b, tq.TQ_EST_MSE, tok, T, t, cv, nv, None, ws)
+    torch.cuda.synchronize()
+    rows = np.array([g * T + t for g in range(groups) for t in filled])
+    empty = np.array([g * T + 17 for g in range(groups)])
+    ckn = ck.cpu().numpy().reshape(groups * T, W * b)
+    cvn = cv.cpu().numpy().reshape(groups * T, W * (b - 1))
+    assert np.array_equal(ckn[rows], bulk_c.cpu().numpy().reshape(groups * T, W * b)[rows])
+    assert np.array_equal(cvn[rows], bulk_vc.cpu().numpy().reshape(groups * T, W * (b - 1))[rows])
+    for got, ref in ((nk, bulk_n), (gk, bulk_g), (nv, bulk_vn)):
+        assert np.array_equal(got.cpu().numpy()[rows], ref.cpu().numpy()[rows])
+        assert np.all(got.cpu().numpy()[empty] == -1.0)
+    assert np.all(ckn[empty] == -1) and np.all(cvn[empty] == -1)
