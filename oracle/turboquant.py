@@ -23,6 +23,9 @@ The pages give the method in prose only.  Readings taken where they are silent:
   * vectors are normalised and their norm nu is stored next to gamma (no other constant);
   * integer decisions (bucket index, sign bit) are taken in float32, the precision of the
     GPU kernels: the pages fix none;
+  * variants ([review, QJL paragraph]: an orthogonal QJL matrix; the exact sphere law of a
+    rotated coordinate): codebook_sphere is Lloyd-Max on that law, and an orthogonal S
+    takes the scale 1/(m E|w_1|);
   * decode attention: values are quantized by the MSE stage alone (index and nu, no QJL
     bit: they are reconstructed, not inner-producted) and the softmax is over the raw
     estimated logits times a caller-given scale.
@@ -38,7 +41,8 @@ __all__ = [
     "codebook", "normalize_rotate", "bucketize", "residual", "qjl_signs", "quantize",
     "pack_codes", "unpack_codes", "estimate_ip", "dequantize", "topk", "qjl_alpha",
     "quantize_mse", "pack_index_planes", "unpack_index_planes", "dequantize_mse",
-    "attention_decode",
+    "attention_decode", "sphere_cell_prob", "sphere_cell_moment", "codebook_sphere",
+    "qjl_alpha_orthogonal",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -113,6 +117,60 @@ def gaussian_distortion(centroids: np.ndarray, thresholds: np.ndarray) -> float:
         m2 = p + ea - eb
         total += m2 - 2.0 * c * m1 + c * c * p
     return total
+
+
+def sphere_cell_prob(a: float, b: float, d: int) -> float:
+    """P(a < u < b) for u one coordinate of a uniform point of the unit sphere in R^d.
+
+    u^2 ~ Beta(1/2, (d-1)/2), so P(|u| < t) is the regularized incomplete beta function
+    I_{t^2}(1/2, (d-1)/2) (taken from SciPy as a library primitive)."""
+    from scipy.special import betainc
+
+    def cdf(t):
+        if t <= -1.0:
+            return 0.0
+        if t >= 1.0:
+            return 1.0
+        half = 0.5 * float(betainc(0.5, 0.5 * (d - 1), t * t))
+        return 0.5 + half if t >= 0.0 else 0.5 - half
+    return cdf(b) - cdf(a)
+
+
+def sphere_cell_moment(a: float, b: float, d: int) -> float:
+    """Integral of u f(u) over (a, b), f the sphere marginal density
+    f(u) = Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)) (1 - u^2)^((d-3)/2): the antiderivative of
+    u (1 - u^2)^((d-3)/2) is -(1 - u^2)^((d-1)/2) / (d - 1)."""
+    logc = math.lgamma(0.5 * d) - math.lgamma(0.5 * (d - 1)) - 0.5 * math.log(math.pi)
+
+    def g(t):
+        t = min(max(t, -1.0), 1.0)
+        return 0.0 if abs(t) >= 1.0 else math.exp(0.5 * (d - 1) * math.log1p(-t * t))
+    return math.exp(logc) * (g(a) - g(b)) / (d - 1)
+
+
+def codebook_sphere(bits_mse: int, d: int, tol: float = 1e-15, max_iter: int = 200000):
+    """Lloyd-Max quantizer with 2**bits_mse levels for the exact law of a rotated coordinate
+    of a unit vector in R^d (the sphere marginal, which the Gaussian N(0, 1/d) approximates):
+    the same two optimality conditions as lloyd_max_gaussian, iterated from the scaled
+    Gaussian grid, then symmetrised exactly.  Returns (centroids, thresholds) in the units of
+    u."""
+    c, _ = lloyd_max_gaussian(bits_mse)
+    c = list(np.clip(c / math.sqrt(d), -0.999, 0.999))
+    L = 1 << bits_mse
+    for _ in range(max_iter):
+        t = [0.5 * (c[i] + c[i + 1]) for i in range(L - 1)]
+        edges = [-1.0] + t + [1.0]
+        new_c = [sphere_cell_moment(edges[i], edges[i + 1], d) / sphere_cell_prob(edges[i], edges[i + 1], d)
+                 for i in range(L)]
+        delta = max(abs(new_c[i] - c[i]) for i in range(L))
+        c = new_c
+        if delta < tol:
+            break
+    else:
+        raise RuntimeError("Lloyd-Max (sphere) did not converge")
+    c = np.array(c, dtype=np.float64)
+    c = 0.5 * (c - c[::-1])
+    return c, 0.5 * (c[:-1] + c[1:])
 
 
 def codebook(bits_mse: int, d: int):
@@ -239,7 +297,18 @@ def qjl_alpha(m: int) -> float:
     return math.sqrt(math.pi / 2.0) / m
 
 
-def estimate_ip(q, Pi, S, idx, z, nu, gamma, centroids, mode: str = "prod") -> np.ndarray:
+def qjl_alpha_orthogonal(m: int, d: int) -> float:
+    """Scale of the QJL term for a matrix with m orthonormal rows: 1 / (m E|w_1|), w_1 one
+    coordinate of a uniform unit vector in R^d, E|w_1| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)).
+
+    For a unit row s uniform on the sphere, E[sign<s, rho> <s, q>] = E|w_1| <q, rho>, so m
+    rows times gamma / (m E|w_1|) give <q, r> in expectation."""
+    ew = math.exp(math.lgamma(0.5 * d) - math.lgamma(0.5 * (d + 1))) / math.sqrt(math.pi)
+    return 1.0 / (m * ew)
+
+
+def estimate_ip(q, Pi, S, idx, z, nu, gamma, centroids, mode: str = "prod",
+                alpha: float | None = None) -> np.ndarray:
     """Estimated inner products <q_a, x_k> for every query row a and key row k -> [nq][n].
 
     [review, problem statement]: one vector of the pair (the key) is quantized, the other
@@ -262,10 +331,12 @@ def estimate_ip(q, Pi, S, idx, z, nu, gamma, centroids, mode: str = "prod") -> n
     sh = q @ S.T
     sgn = 2.0 * np.asarray(z, dtype=np.float64) - 1.0
     qjl = sh @ sgn.T
-    return nu[None, :] * (mse + qjl_alpha(S.shape[0]) * gamma[None, :] * qjl)
+    a = qjl_alpha(S.shape[0]) if alpha is None else alpha
+    return nu[None, :] * (mse + a * gamma[None, :] * qjl)
 
 
-def dequantize(Pi, S, idx, z, nu, gamma, centroids, mode: str = "prod") -> np.ndarray:
+def dequantize(Pi, S, idx, z, nu, gamma, centroids, mode: str = "prod",
+               alpha: float | None = None) -> np.ndarray:
     """Reconstruction x~ [n][d].
 
     [review, QJL paragraph]: dequantization is the inverse rotation and a renormalisation.
@@ -279,7 +350,8 @@ def dequantize(Pi, S, idx, z, nu, gamma, centroids, mode: str = "prod") -> np.nd
     xt = chat @ Pi
     if mode == "prod":
         sgn = 2.0 * np.asarray(z, dtype=np.float64) - 1.0
-        xt = xt + qjl_alpha(S.shape[0]) * gamma[:, None] * (sgn @ S)
+        a = qjl_alpha(S.shape[0]) if alpha is None else alpha
+        xt = xt + a * gamma[:, None] * (sgn @ S)
     elif mode != "mse":
         raise ValueError(mode)
     return nu[:, None] * xt

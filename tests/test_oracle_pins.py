@@ -466,3 +466,118 @@ def test_attention_brute_force_tiny_and_shift_invariance():
                 assert abs(out[gi, h, c] - ref) < 1e-12
     shifted = logits + np.array([[[100.0], [-40.0]], [[3.0], [0.5]]])
     assert np.allclose(oracle.attention_decode(shifted, vals, scale), out, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ variants: sphere codebook
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_sphere_codebook_is_uniform_grid_at_d3(bits):
+    # In R^3 a coordinate of a uniform unit vector is uniform on [-1, 1] (Archimedes), and the
+    # Lloyd-Max quantizer of a uniform law is the uniform grid of cell midpoints.
+    L = 1 << bits
+    c, t = oracle.codebook_sphere(bits, 3)
+    np.testing.assert_allclose(c, [-1 + (2 * i + 1) / L for i in range(L)], atol=1e-9)
+    np.testing.assert_allclose(t, [-1 + 2 * (i + 1) / L for i in range(L - 1)], atol=1e-9)
+
+
+@pytest.mark.parametrize("d,bits", [(4, 2), (16, 3), (128, 3), (64, 2)])
+def test_sphere_codebook_is_a_fixed_point_by_quadrature(d, bits):
+    # both Lloyd-Max conditions, with the cell means by numerical integration of the sphere
+    # marginal density (independent of the incomplete-beta and closed-form moments)
+    c, t = oracle.codebook_sphere(bits, d)
+    np.testing.assert_allclose(t, 0.5 * (c[:-1] + c[1:]), rtol=0, atol=1e-15)
+    f = _sphere_marginal_pdf(d)
+    edges = [-1.0] + list(t) + [1.0]
+    for i in range(len(c)):
+        mass = integrate.quad(f, edges[i], edges[i + 1], epsabs=1e-14, epsrel=1e-13)[0]
+        mom = integrate.quad(lambda x: x * f(x), edges[i], edges[i + 1], epsabs=1e-14,
+                             epsrel=1e-13)[0]
+        assert abs(mom / mass - c[i]) < 1e-9, (i, mom / mass, c[i])
+
+
+@pytest.mark.parametrize("d", [3, 7, 64, 1000])
+def test_sphere_cell_functions_against_quadrature(d):
+    f = _sphere_marginal_pdf(d)
+    assert abs(oracle.sphere_cell_prob(-1.0, 1.0, d) - 1.0) < 1e-14
+    for a, b in [(-0.3, 0.1), (0.05, 0.2), (-1.0, -0.01), (0.5, 1.0)]:
+        p = integrate.quad(f, a, b, epsabs=1e-14, epsrel=1e-13)[0]
+        m = integrate.quad(lambda x: x * f(x), a, b, epsabs=1e-14, epsrel=1e-13)[0]
+        assert abs(oracle.sphere_cell_prob(a, b, d) - p) < 1e-11
+        assert abs(oracle.sphere_cell_moment(a, b, d) - m) < 1e-11
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_sphere_codebook_tends_to_scaled_gaussian(bits):
+    # the sphere marginal tends to N(0, 1/d); the gap in sigma units shrinks like 1/d
+    gaps = []
+    for d in (256, 4096):
+        cs, _ = oracle.codebook_sphere(bits, d)
+        cg, _ = oracle.codebook(bits, d)
+        gaps.append(np.max(np.abs(cs - cg)) * math.sqrt(d))
+    assert gaps[1] < 3.0 / 4096
+    assert 15.0 < gaps[0] / gaps[1] < 17.0
+
+
+@pytest.mark.parametrize("d", [2, 3, 5, 64, 1536])
+def test_sphere_one_bit_centroid_is_mean_absolute_coordinate(d):
+    # with two cells split at 0 the centroid is E[u | u > 0] = E|w_1|
+    # = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)), which the orthogonal QJL scale also uses
+    ew = math.exp(math.lgamma(d / 2) - math.lgamma((d + 1) / 2)) / math.sqrt(math.pi)
+    c, t = oracle.codebook_sphere(1, d)
+    assert t[0] == 0.0
+    assert abs(c[1] - ew) < 1e-12 and c[0] == -c[1]
+
+
+@pytest.mark.parametrize("d,bits", [(3, 2), (8, 2), (32, 3)])
+def test_sphere_codebook_has_lower_distortion_on_the_sphere(d, bits):
+    # optimal for the exact law, so its mean squared error on sphere coordinates is below the
+    # Gaussian-approximation codebook's (Monte Carlo with one shared sample)
+    u = gen.unit_sphere(20000, d, cfg=931, role=gen.ROLE_DATA).astype(np.float64).ravel()
+
+    def mse(c, t):
+        return float(np.mean((u - c[np.searchsorted(t, u, side="right")]) ** 2))
+    cs, ts = oracle.codebook_sphere(bits, d)
+    cg, tg = oracle.codebook(bits, d)
+    assert mse(cs, ts) < mse(cg, tg)
+
+
+# ------------------------------------------------------------------ variants: orthogonal QJL
+
+@pytest.mark.parametrize("d,expect", [(2, 2.0 / math.pi), (3, 0.5), (4, 4.0 / (3.0 * math.pi))])
+def test_orthogonal_qjl_scale_closed_forms(d, expect):
+    # E|w_1| for a uniform unit vector: 2/pi on the circle, 1/2 in R^3 (uniform coordinate),
+    # 4/(3 pi) in R^4; alpha = 1 / (m E|w_1|)
+    assert abs(oracle.qjl_alpha_orthogonal(5, d) - 1.0 / (5 * expect)) < 1e-14
+    f = _sphere_marginal_pdf(d) if d > 2 else None
+    if f is not None:
+        ew = 2 * integrate.quad(lambda x: x * f(x), 0, 1, epsabs=1e-14)[0]
+        assert abs(ew - expect) < 1e-10
+
+
+def test_orthogonal_qjl_estimator_is_unbiased_over_S():
+    # every row of a Haar orthogonal S is a uniform unit vector, so with alpha = 1/(m E|w_1|)
+    # the estimate is unbiased over S; the Gaussian scale on these unit rows would be off by
+    # a factor of about sqrt(d), a transposed S or a wrong sign shifts the mean too
+    d, b, N = 32, 3, 4000
+    Pi = gen.haar_orthogonal(d, cfg=907)
+    c, t = oracle.codebook_sphere(b - 1, d)
+    x = gen.unit_sphere(1, d, cfg=907, role=gen.ROLE_DATA) * 1.7
+    q0 = gen.unit_sphere(1, d, cfg=907, role=gen.ROLE_QUERY)
+    xh = x[0] / np.linalg.norm(x[0])
+    perp = q0[0] - (q0[0] @ xh) * xh
+    perp /= np.linalg.norm(perp)
+    q = (0.5 * xh + math.sqrt(0.75) * perp)[None, :] * 0.9
+    truth = float(q[0].astype(np.float64) @ x[0].astype(np.float64))
+    alpha = oracle.qjl_alpha_orthogonal(d, d)
+    ests = np.empty(N)
+    for s in range(N):
+        S = gen.haar_orthogonal(d, cfg=907, rep=s + 1, role=gen.ROLE_S)
+        r = oracle.quantize(x, Pi, S, c, t)
+        ests[s] = oracle.estimate_ip(q, Pi, S, r["idx"], r["z"], r["nu"], r["gamma"], c,
+                                     alpha=alpha)[0, 0]
+    se = ests.std(ddof=1) / math.sqrt(N)
+    assert abs(ests.mean() - truth) < 4 * se, (ests.mean(), truth, se)
+    # the same S used through dequantize gives the same numbers
+    r = oracle.quantize(x, Pi, S, c, t)
+    xh_ = oracle.dequantize(Pi, S, r["idx"], r["z"], r["nu"], r["gamma"], c, alpha=alpha)
+    assert abs(float(q[0].astype(np.float64) @ xh_[0]) - ests[-1]) < 1e-9

@@ -63,14 +63,15 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------------ method parameters
 
-def haar_orthogonal(d: int, cfg: int, rep: int = 0) -> np.ndarray:
+def haar_orthogonal(d: int, cfg: int, rep: int = 0, role: int = ROLE_PI) -> np.ndarray:
     """Random orthogonal d x d matrix, Haar distributed, as float32.
 
     Drawn as the Q factor of a QR factorisation of a standard Gaussian matrix, with each
     column multiplied by the sign of the matching diagonal entry of R (this sign fix is
-    what makes the distribution uniform over the orthogonal group).
+    what makes the distribution uniform over the orthogonal group).  ``role`` picks the
+    random stream (ROLE_S for an orthogonal QJL matrix).
     """
-    g = rng(cfg, ROLE_PI, rep).standard_normal((d, d))
+    g = rng(cfg, role, rep).standard_normal((d, d))
     q, r = np.linalg.qr(g)
     q = q * np.sign(np.diag(r))[None, :]
     return np.ascontiguousarray(q.astype(np.float32))
