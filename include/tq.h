@@ -79,6 +79,20 @@ typedef enum {
  */
 int tq_codebook_build(int bits_mse, int d, double* centroids, double* thresholds);
 
+/*
+ * tq_codebook_build_sphere — HOST only, float64. The same Lloyd-Max quantizer for the exact
+ * law of a rotated coordinate of a unit vector in R^d, density proportional to
+ * (1 - u^2)^((d-3)/2) on (-1, 1) ([explainer, per-component reduction]: N(0, 1/d) is its
+ * large-d limit; at d = 3 the law is uniform).  Cell masses and first moments by quadrature;
+ * fixed point to |change| < 1e-14 / sqrt(d).  The result differs from tq_codebook_build's by
+ * O(1/d) in sigma units and can be passed to tq_prepare in its place.
+ *   bits_mse   1..8
+ *   d          dimension, >= 2
+ *   centroids, thresholds  as for tq_codebook_build
+ * Errors: TQ_EINVAL for bits_mse or d out of range, NULL outputs, or no convergence.
+ */
+int tq_codebook_build_sphere(int bits_mse, int d, double* centroids, double* thresholds);
+
 /* Size in bytes of the device parameter block that tq_prepare fills for (d, b). 0 if invalid. */
 size_t tq_params_bytes(int d, int b);
 
@@ -98,6 +112,19 @@ size_t tq_params_bytes(int d, int b);
  */
 int tq_prepare(int d, int b, const float* Pi, const float* S, const double* centroids,
                const double* thresholds, void* params, void* stream);
+
+/*
+ * tq_prepare_orthogonal_qjl — tq_prepare for a QJL matrix S with orthonormal rows
+ * (S S^T = I, e.g. a second random rotation) in place of Gaussian entries ([review, QJL
+ * paragraph]: the sign sketch works with orthogonalised rows).  Every row of such a random S
+ * is a uniform unit vector, for which E[sign<s, rho> <s, q>] = E|w_1| <q, rho>,
+ * E|w_1| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)), so the QJL term is scaled by 1/(d E|w_1|)
+ * instead of sqrt(pi/2)/d; every other call is unchanged.  Arguments and behaviour as for
+ * tq_prepare.
+ * Errors: as tq_prepare, plus TQ_EINVAL when max |S S^T - I| > 1e-4.
+ */
+int tq_prepare_orthogonal_qjl(int d, int b, const float* Pi, const float* S, const double* centroids,
+                              const double* thresholds, void* params, void* stream);
 
 /*
  * tq_quantize — encodes n vectors ([review, inner-product paragraph]; [tldr, steps 1-2]).

@@ -40,7 +40,9 @@ def load_library():
     sig = {
         "tq_codebook_build": (I, [I, I, ctypes.POINTER(D), ctypes.POINTER(D)]),
         "tq_params_bytes": (SZ, [I, I]),
+        "tq_codebook_build_sphere": (I, [I, I, ctypes.POINTER(D), ctypes.POINTER(D)]),
         "tq_prepare": (I, [I, I, P, P, P, P, P, P]),
+        "tq_prepare_orthogonal_qjl": (I, [I, I, P, P, P, P, P, P]),
         "tq_quantize": (I, [P, I, I, P, I, I64, P, P, P, P]),
         "tq_dequantize": (I, [P, I, I, P, P, P, I64, I, P, P]),
         "tq_score_ws_bytes": (SZ, [I, I, I64, I64, I64]),
@@ -119,15 +121,23 @@ def _stream(stream, device) -> ctypes.c_void_p:
 
 # ---------------------------------------------------------------------- C calls
 
-def tq_codebook_build(bits_mse: int, d: int):
-    """Host float64 Lloyd-Max codebook for N(0, 1/d): (centroids[L], thresholds[L-1])."""
+def _codebook_call(fn, bits_mse: int, d: int):
     L = 1 << bits_mse if 0 < bits_mse <= 8 else 2
     c = np.zeros(L, dtype=np.float64)
     t = np.zeros(max(L - 1, 1), dtype=np.float64)
-    _check(load_library().tq_codebook_build(
-        int(bits_mse), int(d), c.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-        t.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    _check(fn(int(bits_mse), int(d), c.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+              t.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
     return c, t[:L - 1]
+
+
+def tq_codebook_build(bits_mse: int, d: int):
+    """Host float64 Lloyd-Max codebook for N(0, 1/d): (centroids[L], thresholds[L-1])."""
+    return _codebook_call(load_library().tq_codebook_build, bits_mse, d)
+
+
+def tq_codebook_build_sphere(bits_mse: int, d: int):
+    """Host float64 Lloyd-Max codebook for the exact sphere-coordinate law in R^d."""
+    return _codebook_call(load_library().tq_codebook_build_sphere, bits_mse, d)
 
 
 def tq_params_bytes(d: int, b: int) -> int:
@@ -137,6 +147,16 @@ def tq_params_bytes(d: int, b: int) -> int:
 def tq_prepare(d: int, b: int, Pi: np.ndarray, S: np.ndarray, centroids: np.ndarray,
                thresholds: np.ndarray, params, stream=None):
     """Fill the device parameter block `params` (uint8 tensor of tq_params_bytes(d, b))."""
+    _prepare_call("tq_prepare", d, b, Pi, S, centroids, thresholds, params, stream)
+
+
+def tq_prepare_orthogonal_qjl(d: int, b: int, Pi: np.ndarray, S: np.ndarray, centroids: np.ndarray,
+                              thresholds: np.ndarray, params, stream=None):
+    """tq_prepare for a QJL matrix S with orthonormal rows."""
+    _prepare_call("tq_prepare_orthogonal_qjl", d, b, Pi, S, centroids, thresholds, params, stream)
+
+
+def _prepare_call(name, d, b, Pi, S, centroids, thresholds, params, stream):
     torch = _torch()
     Pi = np.ascontiguousarray(Pi, dtype=np.float32)
     S = np.ascontiguousarray(S, dtype=np.float32)
@@ -148,8 +168,8 @@ def tq_prepare(d: int, b: int, Pi: np.ndarray, S: np.ndarray, centroids: np.ndar
         raise ValueError("codebook size does not match b")
     _dev(params, "params")
     _need(params, "params", tq_params_bytes(d, b), torch.uint8)
-    _check(load_library().tq_prepare(int(d), int(b), Pi.ctypes.data, S.ctypes.data, c.ctypes.data,
-                                     t.ctypes.data, _ptr(params), _stream(stream, params.device)))
+    _check(getattr(load_library(), name)(int(d), int(b), Pi.ctypes.data, S.ctypes.data, c.ctypes.data,
+                                         t.ctypes.data, _ptr(params), _stream(stream, params.device)))
 
 
 def tq_quantize(params, d: int, b: int, x, codes, nu, gamma, stream=None):

@@ -43,32 +43,112 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // [review, MSE paragraph]: optimal grid by the Max-Lloyd algorithm; [tldr, step 1]: 1-D
 // k-means for the known bell-shaped law, solved once.  The quantizer of a symmetric law
 // is odd-symmetric, so only the positive half is iterated here: positive centroids
-// c_1 < ... < c_H (H = L/2) over cells [t_0 = 0, t_1), ..., [t_{H-1}, +inf), where
-// t_i = (c_i + c_{i+1}) / 2 and c_i = (phi(t_{i-1}) - phi(t_i)) / (Q(t_{i-1}) - Q(t_i)),
-// Q the upper tail of N(0, 1).  L = 2 has the closed form c_1 = phi(0)/Q(0) = sqrt(2/pi).
+// c_1 < ... < c_H (H = L/2) over cells [t_0 = 0, t_1), ..., [t_{H-1}, end), where
+// t_i = (c_i + c_{i+1}) / 2 and c_i is the mean of the law over its cell.  Cell masses and
+// first moments are integrated by 8-point Gauss-Legendre on panels no wider than a quarter
+// of the law's scale (no differences of nearly equal tail values, so the fixed point is
+// resolved to 1e-14 of the scale even with 128 cells a side).
 
-double std_pdf(double t) { return std::isinf(t) ? 0.0 : std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI); }
-double std_upper_tail(double t) { return std::isinf(t) ? 0.0 : 0.5 * std::erfc(t / std::sqrt(2.0)); }
+const double kGL8x[4] = {0.1834346424956498, 0.5255324099163290, 0.7966664774136267, 0.9602898564975363};
+const double kGL8w[4] = {0.3626837833783620, 0.3137066458778873, 0.2223810344533745, 0.1012285362903763};
 
-bool lloyd_max_positive_half(int H, std::vector<double>& c) {
-  c.assign(H, 0.0);
-  for (int i = 0; i < H; ++i) c[i] = (i + 0.5) * 3.0 / H;   // any increasing start
+// mass += int_a^b w(x) dx, moment += int_a^b w(x) m(x) dx, where dens(x) returns w(x) and
+// sets m(x).
+template <class Dens>
+void gl_cell(double a, double b, double width, Dens dens, double& mass, double& moment) {
+  mass = moment = 0.0;
+  if (!(b > a)) return;
+  const int np = std::max(1, int(std::ceil((b - a) / width)));
+  const double h = (b - a) / np;
+  for (int p = 0; p < np; ++p) {
+    const double mid = a + (p + 0.5) * h;
+    for (int k = 0; k < 4; ++k)
+      for (int sgn = -1; sgn <= 1; sgn += 2) {
+        double m;
+        const double w = 0.5 * h * kGL8w[k] * dens(mid + sgn * 0.5 * h * kGL8x[k], m);
+        mass += w;
+        moment += w * m;
+      }
+  }
+}
+
+// Fixed-point iteration of the positive half: cell(lo, hi, mass, moment) integrates over
+// the cell between two thresholds; edge(t) maps a threshold to the integration variable.
+template <class Cell, class Edge>
+bool lloyd_iterate(std::vector<double>& c, double top, double tol, Cell cell, Edge edge) {
+  const int H = int(c.size());
   std::vector<double> t(H + 1);
   for (int it = 0; it < 1000000; ++it) {
-    t[0] = 0.0;
-    for (int i = 1; i < H; ++i) t[i] = 0.5 * (c[i - 1] + c[i]);
-    t[H] = INFINITY;
+    t[0] = edge(0.0);
+    for (int i = 1; i < H; ++i) t[i] = edge(0.5 * (c[i - 1] + c[i]));
+    t[H] = top;
     double delta = 0.0;
     for (int i = 0; i < H; ++i) {
-      double num = std_pdf(t[i]) - std_pdf(t[i + 1]);
-      double den = std_upper_tail(t[i]) - std_upper_tail(t[i + 1]);
-      double nc = num / den;
+      double m0, m1;
+      cell(t[i], t[i + 1], m0, m1);
+      if (!(m0 > 0.0)) return false;
+      const double nc = m1 / m0;
       delta = std::fmax(delta, std::fabs(nc - c[i]));
       c[i] = nc;
     }
-    if (delta < 1e-14) return true;
+    if (delta < tol) return true;
   }
   return false;
+}
+
+double std_pdf(double t) { return std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI); }
+double std_upper_tail(double t) { return 0.5 * std::erfc(t / std::sqrt(2.0)); }
+
+// Inverse of std_upper_tail on (0, 1/2], by bisection.
+double std_upper_tail_inv(double p) {
+  double lo = 0.0, hi = 40.0;
+  for (int it = 0; it < 200; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    (std_upper_tail(mid) > p ? lo : hi) = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+// N(0, 1).  Starts from the high-resolution optimum (level density proportional to
+// pdf^(1/3): the quantiles of N(0, 3)); the last cell is cut 12 sigma past its threshold,
+// where the density has fallen by more than e^-72.  L = 2 has the closed form
+// c_1 = sqrt(2/pi).
+bool lloyd_max_positive_half(int H, std::vector<double>& c) {
+  const int L = 2 * H;
+  c.assign(H, 0.0);
+  for (int i = 0; i < H; ++i) c[i] = std::sqrt(3.0) * std_upper_tail_inv((H - i - 0.5) / L);
+  auto dens = [](double x, double& m) { m = x; return std_pdf(x); };
+  auto cell = [&](double lo, double hi, double& m0, double& m1) {
+    gl_cell(lo, std::isinf(hi) ? lo + 12.0 : hi, 0.25, dens, m0, m1);
+  };
+  return lloyd_iterate(c, INFINITY, 1e-14, cell, [](double t) { return t; });
+}
+
+// Exact law of a rotated coordinate u of a unit vector in R^d: density proportional to
+// (1 - u^2)^((d-3)/2) on (-1, 1) ([explainer, per-component reduction]: its large-d limit is
+// N(0, 1/d)).  Integrated in theta = asin(u), where the density becomes cos^(d-2)(theta) and
+// the moment weight sin(theta); the normalizer cancels in the centroid.  Past
+// theta = sqrt(1600 / (d - 2)) the integrand is below e^-800 and is dropped.
+bool lloyd_max_sphere_positive_half(int H, int d, std::vector<double>& c) {
+  std::vector<double> g;
+  if (!lloyd_max_positive_half(H, g)) return false;
+  const double sigma = 1.0 / std::sqrt(double(d));
+  c.assign(H, 0.0);
+  if (g[H - 1] * sigma < 0.9) {
+    for (int i = 0; i < H; ++i) c[i] = g[i] * sigma;   // start at the Gaussian limit
+  } else {
+    for (int i = 0; i < H; ++i) c[i] = (i + 0.5) / H;  // broad law: start uniform
+  }
+  const double tmax = d > 2 ? std::fmin(M_PI / 2, std::sqrt(1600.0 / (d - 2))) : M_PI / 2;
+  const double width = std::fmin(M_PI / 64, 0.25 * sigma);
+  auto dens = [d](double th, double& m) {
+    m = std::sin(th);
+    return d == 2 ? 1.0 : std::exp((d - 2) * std::log(std::cos(th)));
+  };
+  auto cell = [&](double lo, double hi, double& m0, double& m1) {
+    gl_cell(lo, std::fmin(hi, tmax), width, dens, m0, m1);
+  };
+  return lloyd_iterate(c, M_PI / 2, 1e-14 * sigma, cell, [](double u) { return std::asin(u); });
 }
 
 // ------------------------------------------------------------------ bf16 helpers (host)
@@ -184,13 +264,50 @@ int tq_codebook_build(int bits_mse, int d, double* centroids, double* thresholds
   return ok();
 }
 
+int tq_codebook_build_sphere(int bits_mse, int d, double* centroids, double* thresholds) {
+  if (bits_mse < 1 || bits_mse > 8) return fail(TQ_EINVAL, "bits_mse=%d outside 1..8", bits_mse);
+  if (d < 2) return fail(TQ_EINVAL, "d=%d must be at least 2", d);
+  if (!centroids || !thresholds) return fail(TQ_EINVAL, "NULL output pointer");
+  const int L = 1 << bits_mse, H = L / 2;
+  std::vector<double> c;
+  if (!lloyd_max_sphere_positive_half(H, d, c)) return fail(TQ_EINVAL, "Lloyd-Max (sphere) did not converge");
+  for (int i = 0; i < H; ++i) {
+    centroids[H + i] = c[i];
+    centroids[H - 1 - i] = -c[i];
+  }
+  for (int i = 0; i < L - 1; ++i) thresholds[i] = 0.5 * (centroids[i] + centroids[i + 1]);
+  thresholds[H - 1] = 0.0;
+  return ok();
+}
+
 size_t tq_params_bytes(int d, int b) {
   if (!valid_shape(d, b)) return 0;
   return tq::Layout(d, b).total;
 }
 
-int tq_prepare(int d, int b, const float* Pi, const float* S, const double* centroids,
-               const double* thresholds, void* params, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Largest |M M^T - I| over the rows of a d x d matrix (float64 copy).
+double gram_defect(const std::vector<double>& M, int d) {
+  std::vector<double> row_worst(d, 0.0);
+  parallel_for(d, [&](int i) {
+    double w = 0.0;
+    for (int j = i; j < d; ++j) {
+      double g = dot(&M[size_t(i) * d], &M[size_t(j) * d], d) - (i == j ? 1.0 : 0.0);
+      w = std::fmax(w, std::fabs(g));
+    }
+    row_worst[i] = w;
+  });
+  double worst = 0.0;
+  for (double w : row_worst) worst = std::fmax(worst, w);
+  return worst;
+}
+
+// s_orthonormal: S has orthonormal rows, else Gaussian entries; sets the QJL scale.
+int prepare_params(int d, int b, const float* Pi, const float* S, const double* centroids,
+                   const double* thresholds, bool s_orthonormal, void* params, void* stream) {
   if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
   if (!Pi || !S || !centroids || !thresholds || !params) return fail(TQ_EINVAL, "NULL pointer");
   if (!aligned(params, 256)) return fail(TQ_EINVAL, "params must be 256-byte aligned");
@@ -251,7 +368,11 @@ int tq_prepare(int d, int b, const float* Pi, const float* S, const double* cent
     h.esum += float(e);
     h.emax = std::fmax(h.emax, std::fabs(float(e)));
   }
-  h.alpha = float(std::sqrt(M_PI / 2.0) / d);
+  // QJL scale ([review, QJL paragraph]; m = d rows): a Gaussian row s has
+  // E[sign<s, rho> <s, q>] = sqrt(2/pi) <q, rho>, a uniform unit row E|w_1| <q, rho> with
+  // E|w_1| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)); the scale is the reciprocal over m.
+  const double mean_abs = std::exp(std::lgamma(0.5 * d) - std::lgamma(0.5 * (d + 1))) / std::sqrt(M_PI);
+  h.alpha = s_orthonormal ? float(1.0 / (d * mean_abs)) : float(std::sqrt(M_PI / 2.0) / d);
   std::memcpy(blob.data() + lay.off_hdr, &h, sizeof(h));
 
   // Pi and S in float32 (row-major), and float64 copies for host products
@@ -275,18 +396,12 @@ int tq_prepare(int d, int b, const float* Pi, const float* S, const double* cent
       return fail(TQ_EINVAL, "non-finite entry in Pi or S");
   }
   // Pi must be orthogonal: the kernels form the residual in the rotated space.
-  std::vector<double> row_worst(d, 0.0);
-  parallel_for(d, [&](int i) {
-    double w = 0.0;
-    for (int j = i; j < d; ++j) {
-      double g = dot(&P64[size_t(i) * d], &P64[size_t(j) * d], d) - (i == j ? 1.0 : 0.0);
-      w = std::fmax(w, std::fabs(g));
-    }
-    row_worst[i] = w;
-  });
-  double worst = 0.0;
-  for (double w : row_worst) worst = std::fmax(worst, w);
+  const double worst = gram_defect(P64, d);
   if (worst > 1e-4) return fail(TQ_EINVAL, "Pi is not orthogonal (max |Pi Pi^T - I| = %g)", worst);
+  if (s_orthonormal) {
+    const double sw = gram_defect(S64, d);
+    if (sw > 1e-4) return fail(TQ_EINVAL, "S rows are not orthonormal (max |S S^T - I| = %g)", sw);
+  }
 
   if (lay.qfrag_bytes || lay.gmat_bytes) {
     // S' = S Pi^T, so that S r = S' (Pi r) for the residual r (rotated-space residual)
@@ -313,6 +428,20 @@ int tq_prepare(int d, int b, const float* Pi, const float* S, const double* cent
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "tq_prepare: synchronize");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_prepare(int d, int b, const float* Pi, const float* S, const double* centroids,
+               const double* thresholds, void* params, void* stream) {
+  return prepare_params(d, b, Pi, S, centroids, thresholds, false, params, stream);
+}
+
+int tq_prepare_orthogonal_qjl(int d, int b, const float* Pi, const float* S, const double* centroids,
+                              const double* thresholds, void* params, void* stream) {
+  return prepare_params(d, b, Pi, S, centroids, thresholds, true, params, stream);
 }
 
 int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,

@@ -198,7 +198,7 @@ template <int B, bool PROD, int KM>
 __global__ __launch_bounds__(256, 1) void topk_scan_kernel(
     const unsigned char* __restrict__ params, const _Float16* __restrict__ qf,
     const uint32_t* __restrict__ codes, const float* __restrict__ nu,
-    const float* __restrict__ gamma, int G, float ag_scale, long n, int QT, long RB,
+    const float* __restrict__ gamma, int G, float s_unscale, long n, int QT, long RB,
     long nsplit, int k, long nq, const float* __restrict__ qn, int* __restrict__ cand_idx,
     float* __restrict__ cand_score, float2* __restrict__ ovf_all) {
   // two operand buffers as distinct objects, selected at compile time, so the compiler can
@@ -228,6 +228,7 @@ __global__ __launch_bounds__(256, 1) void topk_scan_kernel(
 
   // positive half of the codebook as fp16 bytes (v_perm_b32 table)
   const Header* hdr = reinterpret_cast<const Header*>(params);
+  const float ag_unit = s_unscale * hdr->alpha;                 // key side: ag_unit gamma_j (2 z - 1)
   constexpr int L = 1 << (B - 1);
   uint32_t tab_lo = 0, tab_hi = 0;
   if constexpr (B == 2) {
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void topk_scan_kernel(
     for (int kt = 0; kt < KT; ++kt) {
       jk[kt] = blk * KEYS + wave * 32 * KT + 32 * kt + nl;
       ok[kt] = jk[kt] < n;
-      const uint32_t hv = (PROD && ok[kt]) ? f16_bits(ag_scale * gamma[jk[kt]]) : 0u;
+      const uint32_t hv = (PROD && ok[kt]) ? f16_bits(ag_unit * gamma[jk[kt]]) : 0u;
       agp[kt] = hv | (hv << 16);
     }
     f32x16 acc[RT][KT];
@@ -641,16 +642,16 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(int* __restrict__ cand_
 template <int B, int KM>
 hipError_t launch_scan_km(bool prod, dim3 grid, const unsigned char* params, const _Float16* qf,
                           const uint32_t* codes, const float* nu, const float* gamma, int G,
-                          float ag_scale, long n, int QT, long RB, long nsplit, int k, long nq,
+                          float s_unscale, long n, int QT, long RB, long nsplit, int k, long nq,
                           const float* qn, int* cand_idx, float* cand_score, float2* ovf,
                           hipStream_t s) {
   if (prod)
     hipLaunchKernelGGL((topk_scan_kernel<B, true, KM>), grid, dim3(256), 0, s, params, qf, codes,
-                       nu, gamma, G, ag_scale, n, QT, RB, nsplit, k, nq, qn, cand_idx, cand_score,
+                       nu, gamma, G, s_unscale, n, QT, RB, nsplit, k, nq, qn, cand_idx, cand_score,
                        ovf);
   else
     hipLaunchKernelGGL((topk_scan_kernel<B, false, KM>), grid, dim3(256), 0, s, params, qf, codes,
-                       nu, gamma, G, ag_scale, n, QT, RB, nsplit, k, nq, qn, cand_idx, cand_score,
+                       nu, gamma, G, s_unscale, n, QT, RB, nsplit, k, nq, qn, cand_idx, cand_score,
                        ovf);
   return hipGetLastError();
 }
@@ -658,14 +659,14 @@ hipError_t launch_scan_km(bool prod, dim3 grid, const unsigned char* params, con
 template <int B>
 hipError_t launch_scan(bool prod, dim3 grid, const unsigned char* params, const _Float16* qf,
                        const uint32_t* codes, const float* nu, const float* gamma, int G,
-                       float ag_scale, long n, int QT, long RB, long nsplit, int k, long nq,
+                       float s_unscale, long n, int QT, long RB, long nsplit, int k, long nq,
                        const float* qn, int* cand_idx, float* cand_score, float2* ovf,
                        hipStream_t s) {
   // lists of 16 entries leave room for more candidate slots (fewer merges)
   if (k <= 16)
-    return launch_scan_km<B, 16>(prod, grid, params, qf, codes, nu, gamma, G, ag_scale, n, QT, RB,
+    return launch_scan_km<B, 16>(prod, grid, params, qf, codes, nu, gamma, G, s_unscale, n, QT, RB,
                                  nsplit, k, nq, qn, cand_idx, cand_score, ovf, s);
-  return launch_scan_km<B, KMAX>(prod, grid, params, qf, codes, nu, gamma, G, ag_scale, n, QT, RB,
+  return launch_scan_km<B, KMAX>(prod, grid, params, qf, codes, nu, gamma, G, s_unscale, n, QT, RB,
                                  nsplit, k, nq, qn, cand_idx, cand_score, ovf, s);
 }
 
@@ -705,15 +706,17 @@ hipError_t launch_topk(const void* params_v, int d, int b, const void* q, int q_
 
   // workgroup x -> (query tile x % QT, key range x / QT): consecutive workgroups land on
   // different XCDs, so with QT dividing 8 each XCD keeps reading one query tile from its L2
-  const float ag_scale = std::sqrt(float(d)) * std::sqrt(float(M_PI) / 2.0f) / float(d);
+  // the query operand carries S q / sqrt(d); the kernel multiplies the key side back by
+  // sqrt(d) alpha gamma_j, alpha from the parameter header
+  const float s_unscale = std::sqrt(float(d));
   const dim3 grid(unsigned(p.qt * p.nsplit));
   const bool prod = mode == 0;
   switch (b) {
-    case 2: e = launch_scan<2>(prod, grid, params, qf, codes, nu, gamma, G, ag_scale, n, int(p.qt), p.rb,
+    case 2: e = launch_scan<2>(prod, grid, params, qf, codes, nu, gamma, G, s_unscale, n, int(p.qt), p.rb,
                                p.nsplit, k, nq, qn, cand_idx, cand_score, ovf, s); break;
-    case 3: e = launch_scan<3>(prod, grid, params, qf, codes, nu, gamma, G, ag_scale, n, int(p.qt), p.rb,
+    case 3: e = launch_scan<3>(prod, grid, params, qf, codes, nu, gamma, G, s_unscale, n, int(p.qt), p.rb,
                                p.nsplit, k, nq, qn, cand_idx, cand_score, ovf, s); break;
-    default: e = launch_scan<4>(prod, grid, params, qf, codes, nu, gamma, G, ag_scale, n, int(p.qt), p.rb,
+    default: e = launch_scan<4>(prod, grid, params, qf, codes, nu, gamma, G, s_unscale, n, int(p.qt), p.rb,
                                 p.nsplit, k, nq, qn, cand_idx, cand_score, ovf, s); break;
   }
   if (e != hipSuccess) return e;

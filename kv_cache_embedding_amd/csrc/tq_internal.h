@@ -25,7 +25,7 @@ struct Header {
   int32_t ne;                 // number of Walsh terms used (1, 2 or 4)
   float esum;                 // sum of e[]
   float emax;                 // max |e|
-  float alpha;                // sqrt(pi/2) / m
+  float alpha;                // QJL scale: sqrt(pi/2) / m (Gaussian S), 1 / (m E|w_1|) (orthonormal rows)
   float pad[4];
 };
 static_assert(sizeof(Header) <= 256, "header must fit in 256 bytes");

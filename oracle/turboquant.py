@@ -148,15 +148,22 @@ def sphere_cell_moment(a: float, b: float, d: int) -> float:
     return math.exp(logc) * (g(a) - g(b)) / (d - 1)
 
 
-def codebook_sphere(bits_mse: int, d: int, tol: float = 1e-15, max_iter: int = 200000):
+def codebook_sphere(bits_mse: int, d: int, tol: float | None = None, max_iter: int = 200000):
     """Lloyd-Max quantizer with 2**bits_mse levels for the exact law of a rotated coordinate
     of a unit vector in R^d (the sphere marginal, which the Gaussian N(0, 1/d) approximates):
     the same two optimality conditions as lloyd_max_gaussian, iterated from the scaled
-    Gaussian grid, then symmetrised exactly.  Returns (centroids, thresholds) in the units of
-    u."""
-    c, _ = lloyd_max_gaussian(bits_mse)
-    c = list(np.clip(c / math.sqrt(d), -0.999, 0.999))
+    Gaussian grid (from the uniform grid when that one reaches past 0.9), then symmetrised
+    exactly.  Stops once no centroid moves by more than ``tol`` (default 1e-14 / sqrt(d), the
+    noise floor of the incomplete-beta masses).  Returns (centroids, thresholds) in the units
+    of u."""
+    if tol is None:
+        tol = 1e-14 / math.sqrt(d)
+    g, _ = lloyd_max_gaussian(bits_mse)
     L = 1 << bits_mse
+    if g[-1] / math.sqrt(d) < 0.9:
+        c = list(g / math.sqrt(d))                        # near the Gaussian limit
+    else:
+        c = [-1.0 + (2 * i + 1) / L for i in range(L)]    # broad law (small d): uniform start
     for _ in range(max_iter):
         t = [0.5 * (c[i] + c[i + 1]) for i in range(L - 1)]
         edges = [-1.0] + t + [1.0]

@@ -46,7 +46,35 @@ def test_codebook_matches_oracle(lib, bits, d):
     assert t[len(t) // 2] == 0.0
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [3, 64, 128, 1536])
+def test_sphere_codebook_matches_oracle(lib, bits, d):
+    c, t = tq.tq_codebook_build_sphere(bits, d)
+    co, to = oracle.codebook_sphere(bits, d)
+    assert np.allclose(c, co, rtol=0, atol=1e-10 / np.sqrt(d))
+    assert np.allclose(t, to, rtol=0, atol=1e-10 / np.sqrt(d))
+    assert t[len(t) // 2] == 0.0 and np.array_equal(c, -c[::-1])
+
+
+def test_codebooks_at_many_levels_are_lloyd_max_fixed_points(lib):
+    # 8 bits (128 cells a side) converges; the Gaussian cell means in closed form
+    # (pdf difference over tail difference), checked to what that form resolves
+    from scipy import stats
+    c, t = tq.tq_codebook_build(8, 1)
+    assert np.all(np.diff(c) > 0) and np.array_equal(c, -c[::-1])
+    edges = np.concatenate([[-np.inf], t, [np.inf]])
+    mean = (stats.norm.pdf(edges[:-1]) - stats.norm.pdf(edges[1:])) / (
+        stats.norm.sf(edges[:-1]) - stats.norm.sf(edges[1:]))
+    assert np.max(np.abs(mean - c)) < 1e-8
+    cs, ts = tq.tq_codebook_build_sphere(6, 1536)
+    assert np.all(np.diff(cs) > 0) and np.max(np.abs(cs * np.sqrt(1536) - tq.tq_codebook_build(6, 1)[0])) < 0.05
+
+
 def test_codebook_rejects_bad_arguments(lib):
+    for bad in ((0, 128), (9, 128), (3, 1)):
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_codebook_build_sphere(*bad)
+        assert e.value.status == tq.TQ_EINVAL
     with pytest.raises(tq.TQError) as e:
         tq.tq_codebook_build(0, 128)
     assert e.value.status == tq.TQ_EINVAL
@@ -155,3 +183,10 @@ def test_prepare_rejects_bad_codebook_and_rotation(lib):
     assert "orthogonal" in tq.tq_last_error()
     assert lib.tq_prepare(d, b, Pi.ctypes.data, S.ctypes.data, c.ctypes.data, t.ctypes.data,
                           ctypes.c_void_p(0x100010), None) == tq.TQ_EINVAL   # misaligned params
+    # the orthogonal-QJL preparation also checks the rows of S (all ones: not orthonormal)
+    assert lib.tq_prepare_orthogonal_qjl(d, b, Pi.ctypes.data, S.ctypes.data, c.ctypes.data,
+                                         t.ctypes.data, fake, None) == tq.TQ_EINVAL
+    assert "orthonormal" in tq.tq_last_error()
+    S2 = np.ascontiguousarray(np.eye(d, dtype=np.float32) * 1.01)
+    assert lib.tq_prepare_orthogonal_qjl(d, b, Pi.ctypes.data, S2.ctypes.data, c.ctypes.data,
+                                         t.ctypes.data, fake, None) == tq.TQ_EINVAL

@@ -65,9 +65,11 @@ def test_quantize_mse_parity(d, b, bf16):
         assert np.array_equal(idx_k, idx_g)
 
 
-def _kv_case(d, b_k, b_v, groups, G, T, cfg, q_bf16=True, zero_values=()):
-    stk = U.make_setup(d, b_k, cfg=cfg)
-    stv = U.make_setup(d, b_v, cfg=cfg + 1)
+def _kv_case(d, b_k, b_v, groups, G, T, cfg, q_bf16=True, zero_values=(), variant=""):
+    # variant "sphere": exact sphere-law codebooks for keys and values; "orth": orthogonal
+    # QJL matrix for the keys
+    stk = U.make_setup(d, b_k, cfg=cfg, sphere="sphere" in variant, orthogonal_s="orth" in variant)
+    stv = U.make_setup(d, b_v, cfg=cfg + 1, sphere="sphere" in variant)
     chans = gen.outlier_channels(cfg, groups, d)
     keys = np.concatenate([gen.kv_keys_chunk(cfg, 0, h, T, d, chans[h]) for h in range(groups)])
     vals = np.concatenate([gen.kv_keys_chunk(cfg, 1, h, T, d, chans[h], scale=1.0) for h in range(groups)])
@@ -98,24 +100,27 @@ def _oracle_parts(stk, stv, d, q, q_bf16, ck, nk, gk, cv, nv, groups, G, T, mode
     name = "prod" if mode == tq.TQ_EST_PROD else "mse"
     logits = np.stack([oracle.estimate_ip(q64[g], stk.Pi, stk.S, idx_k[g * T:(g + 1) * T],
                                           z_k[g * T:(g + 1) * T], nuk[g * T:(g + 1) * T],
-                                          gak[g * T:(g + 1) * T], stk.c_or, name) for g in range(groups)])
+                                          gak[g * T:(g + 1) * T], stk.c_or, name, alpha=stk.alpha)
+                       for g in range(groups)])
     idx_v = oracle.unpack_index_planes(cv.cpu().numpy().view(np.uint32).reshape(n, d // 32, stv.b - 1),
                                        stv.b - 1)
     vhat = oracle.dequantize_mse(stv.Pi, idx_v, nv.cpu().numpy(), stv.c_or).reshape(groups, T, d)
     return logits, vhat, q64
 
 
-@pytest.mark.parametrize("d,b_k,b_v,G,T,q_bf16,mode", [
-    (128, 4, 4, 4, 1000, True, tq.TQ_EST_PROD),
-    (128, 3, 3, 4, 257, False, tq.TQ_EST_MSE),
-    (128, 4, 2, 5, 600, True, tq.TQ_EST_PROD),
-    (64, 3, 4, 3, 300, True, tq.TQ_EST_PROD),
-    (256, 2, 3, 4, 513, False, tq.TQ_EST_PROD)])
-def test_attention_parity(d, b_k, b_v, G, T, q_bf16, mode):
+@pytest.mark.parametrize("d,b_k,b_v,G,T,q_bf16,mode,variant", [
+    (128, 4, 4, 4, 1000, True, tq.TQ_EST_PROD, ""),
+    (128, 3, 3, 4, 257, False, tq.TQ_EST_MSE, ""),
+    (128, 4, 2, 5, 600, True, tq.TQ_EST_PROD, ""),
+    (64, 3, 4, 3, 300, True, tq.TQ_EST_PROD, ""),
+    (256, 2, 3, 4, 513, False, tq.TQ_EST_PROD, ""),
+    (128, 4, 3, 4, 700, True, tq.TQ_EST_PROD, "sphere+orth"),
+    (192, 3, 4, 2, 333, True, tq.TQ_EST_PROD, "sphere+orth")])
+def test_attention_parity(d, b_k, b_v, G, T, q_bf16, mode, variant):
     groups = 3
     scale = 1.0 / math.sqrt(d)
     stk, stv, q, ck, nk, gk, cv, nv = _kv_case(d, b_k, b_v, groups, G, T, cfg=41, q_bf16=q_bf16,
-                                               zero_values=(5, T + 7))
+                                               zero_values=(5, T + 7), variant=variant)
     out = _gpu_attention(stk, stv, d, q, q_bf16, ck, nk, gk, cv, nv, groups, G, T, scale, mode)
     assert np.all(np.isfinite(out))
     logits, vhat, q64 = _oracle_parts(stk, stv, d, q, q_bf16, ck, nk, gk, cv, nv, groups, G, T, mode)

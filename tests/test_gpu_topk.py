@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _oracle_scores(st, q64, idx, z, nu, gamma, mode="prod"):
-    ref = oracle.estimate_ip(q64, st.Pi, st.S, idx, z, nu, gamma, st.c_or, mode)
+    ref = oracle.estimate_ip(q64, st.Pi, st.S, idx, z, nu, gamma, st.c_or, mode, alpha=st.alpha)
     scale = np.linalg.norm(q64, axis=1)[:, None] * np.maximum(nu[None, :], 1e-30)
     return ref, scale
 

@@ -39,16 +39,26 @@ class Setup:
     c_or: np.ndarray
     t_or: np.ndarray
     params: torch.Tensor
+    alpha: float | None = None     # QJL scale for the oracle (None: Gaussian S)
 
 
-def make_setup(d: int, b: int, cfg: int, rep: int = 0) -> Setup:
+def make_setup(d: int, b: int, cfg: int, rep: int = 0, sphere: bool = False,
+               orthogonal_s: bool = False) -> Setup:
+    """Parameters of one configuration.  sphere: Lloyd-Max on the exact sphere law instead of
+    N(0, 1/d); orthogonal_s: a Haar orthogonal QJL matrix instead of Gaussian entries."""
     Pi = gen.haar_orthogonal(d, cfg, rep)
-    S = gen.gaussian_matrix(d, d, cfg, rep)
-    c, t = tq.tq_codebook_build(b - 1, d)
+    if orthogonal_s:
+        S = gen.haar_orthogonal(d, cfg, rep, role=gen.ROLE_S)
+    else:
+        S = gen.gaussian_matrix(d, d, cfg, rep)
+    build = tq.tq_codebook_build_sphere if sphere else tq.tq_codebook_build
+    c, t = build(b - 1, d)
     params = torch.empty(tq.tq_params_bytes(d, b), dtype=torch.uint8, device=DEV)
-    tq.tq_prepare(d, b, Pi, S, c, t, params)
-    c_or, t_or = oracle.codebook(b - 1, d)
-    return Setup(d, b, Pi, S, c_or, t_or, params)
+    prepare = tq.tq_prepare_orthogonal_qjl if orthogonal_s else tq.tq_prepare
+    prepare(d, b, Pi, S, c, t, params)
+    c_or, t_or = (oracle.codebook_sphere if sphere else oracle.codebook)(b - 1, d)
+    alpha = oracle.qjl_alpha_orthogonal(d, d) if orthogonal_s else None
+    return Setup(d, b, Pi, S, c_or, t_or, params, alpha)
 
 
 def to_device(x: np.ndarray, bf16: bool) -> torch.Tensor:
@@ -137,7 +147,7 @@ def logit_errors(st: Setup, q64: np.ndarray, idx, z, nu, gamma, logits: np.ndarr
     for g in range(groups):
         sl = slice(g * T, (g + 1) * T)
         ref = oracle.estimate_ip(q64[g], st.Pi, st.S, idx[sl], z[sl], nu[sl], gamma[sl], st.c_or,
-                                 mode)
+                                 mode, alpha=st.alpha)
         scale = np.linalg.norm(q64[g], axis=1)[:, None] * np.maximum(nu[sl][None, :], 1e-30)
         err = np.abs(logits[g].astype(np.float64) - ref) / scale
         worst = max(worst, float(np.max(err)))
