@@ -7,6 +7,11 @@ removes the bias).  For each seed s the slope beta_s = sum_p e_p l_s(p) / sum_p 
 all (query head, key) pairs p, with e_p the exact <q, k>.  For a Haar rotation the rotated
 key is uniform on the sphere whatever the key, so E[beta] = kappa = d E[u Q(u)] for the
 MSE-only estimate (sphere quadrature below) and exactly 1 for MSE+QJL.
+
+The QJL variants are compared on the same keys and rotations: a Gaussian S (sqrt(pi/2)/m
+scale) and a Haar orthogonal S (1/(m E|w_1|) scale, [review, QJL paragraph]).  Both must be
+unbiased; the mean squared logit error sum_p (l_s(p) - e_p)^2 / sum_p e_p^2 over the seeds
+measures their variance.
 """
 import math
 
@@ -53,7 +58,8 @@ def test_bias_over_100_seeds():
     lines = []
     for b in w.bits:
         kappa = _kappa(d, b - 1)
-        slopes = {tq.TQ_EST_MSE: [], tq.TQ_EST_PROD: []}
+        slopes = {tq.TQ_EST_MSE: [], tq.TQ_EST_PROD: [], "orth": []}
+        err2 = {tq.TQ_EST_PROD: [], "orth": []}
         codes = torch.empty(n * (d // 32) * b, dtype=torch.int32, device=U.DEV)
         nu = torch.empty(n, device=U.DEV)
         gamma = torch.empty(n, device=U.DEV)
@@ -63,14 +69,21 @@ def test_bias_over_100_seeds():
         params = torch.empty(tq.tq_params_bytes(d, b), dtype=torch.uint8, device=U.DEV)
         for rep in range(SEEDS):
             Pi = gen.haar_orthogonal(d, w.cfg, rep)
-            S = gen.gaussian_matrix(d, d, w.cfg, rep)
-            tq.tq_prepare(d, b, Pi, S, c, t, params)
-            tq.tq_quantize(params, d, b, xd, codes, nu, gamma)
-            for mode in slopes:
-                tq.tq_score_ip(params, d, b, qd, codes, nu, gamma, w.groups, G, T, mode, logits, ws)
-                num = float((exact.double() * logits.view(w.groups, G, T).double()).sum())
-                slopes[mode].append(num / ee)
-        for mode, name in ((tq.TQ_EST_MSE, "MSE-only"), (tq.TQ_EST_PROD, "MSE+QJL")):
+            for kind in ("gauss", "orth"):
+                if kind == "gauss":
+                    tq.tq_prepare(d, b, Pi, gen.gaussian_matrix(d, d, w.cfg, rep), c, t, params)
+                else:
+                    tq.tq_prepare_orthogonal_qjl(d, b, Pi, gen.haar_orthogonal(d, w.cfg, rep, role=gen.ROLE_S),
+                                                 c, t, params)
+                tq.tq_quantize(params, d, b, xd, codes, nu, gamma)
+                for mode in ((tq.TQ_EST_MSE, tq.TQ_EST_PROD) if kind == "gauss" else (tq.TQ_EST_PROD,)):
+                    tq.tq_score_ip(params, d, b, qd, codes, nu, gamma, w.groups, G, T, mode, logits, ws)
+                    lv = logits.view(w.groups, G, T).double()
+                    key = "orth" if kind == "orth" else mode
+                    slopes[key].append(float((exact.double() * lv).sum()) / ee)
+                    if mode == tq.TQ_EST_PROD:
+                        err2[key].append(float(((lv - exact.double()) ** 2).sum()) / ee)
+        for mode, name in ((tq.TQ_EST_MSE, "MSE-only"), (tq.TQ_EST_PROD, "MSE+QJL"), ("orth", "MSE+QJL orthogonal S")):
             s = np.array(slopes[mode])
             mean, se = s.mean(), s.std(ddof=1) / math.sqrt(len(s))
             expect = kappa if mode == tq.TQ_EST_MSE else 1.0
@@ -79,3 +92,9 @@ def test_bias_over_100_seeds():
             assert abs(mean - expect) <= 4 * se + 1e-4, (b, name, mean, se, expect)
         ms = np.array(slopes[tq.TQ_EST_MSE])
         assert 1.0 - ms.mean() > 20 * ms.std(ddof=1) / math.sqrt(SEEDS)   # clearly biased
+        eg, eo = np.array(err2[tq.TQ_EST_PROD]), np.array(err2["orth"])
+        lines.append(f"b={b} relative mean squared logit error: Gaussian S {eg.mean():.5f} +- "
+                     f"{eg.std(ddof=1) / math.sqrt(SEEDS):.5f}, orthogonal S {eo.mean():.5f} +- "
+                     f"{eo.std(ddof=1) / math.sqrt(SEEDS):.5f} (ratio {eo.mean() / eg.mean():.3f})")
+        print(lines[-1], flush=True)
+        assert eo.mean() < eg.mean()

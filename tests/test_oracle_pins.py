@@ -577,6 +577,15 @@ def test_orthogonal_qjl_estimator_is_unbiased_over_S():
                                      alpha=alpha)[0, 0]
     se = ests.std(ddof=1) / math.sqrt(N)
     assert abs(ests.mean() - truth) < 4 * se, (ests.mean(), truth, se)
+    # variance below the Gaussian S's (predicted in closed form, as in the Gaussian test):
+    # orthonormal rows do not repeat directions, so the signs carry more of <q, r>
+    nu, gamma = r["nu"][0], r["gamma"][0]
+    _, xn, _ = oracle.normalize_rotate(x, Pi)
+    resid, _ = oracle.residual(xn, Pi, c[r["idx"]])
+    q64 = q[0].astype(np.float64)
+    rho = resid[0] / gamma
+    var_gauss = (math.pi / 2) * nu ** 2 * gamma ** 2 / d * (q64 @ q64 - (2 / math.pi) * (q64 @ rho) ** 2)
+    assert ests.var(ddof=1) < 0.8 * var_gauss, (ests.var(ddof=1), var_gauss)
     # the same S used through dequantize gives the same numbers
     r = oracle.quantize(x, Pi, S, c, t)
     xh_ = oracle.dequantize(Pi, S, r["idx"], r["z"], r["nu"], r["gamma"], c, alpha=alpha)
