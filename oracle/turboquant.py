@@ -28,7 +28,11 @@ The pages give the method in prose only.  Readings taken where they are silent:
     takes the scale 1/(m E|w_1|);
   * decode attention: values are quantized by the MSE stage alone (index and nu, no QJL
     bit: they are reconstructed, not inner-producted) and the softmax is over the raw
-    estimated logits times a caller-given scale.
+    estimated logits times a caller-given scale;
+  * fractional rates ([review, experiments paragraph] and [news, results paragraph]: 2.5 and
+    3.5 bits per channel, mechanism not given): two channel groups, each its own TurboQuant
+    instance (rotation, QJL matrix, nu, gamma) at its own b, the estimate being the sum of
+    the groups' estimates; half the channels at b + 1 and half at b give b + 1/2.
 """
 from __future__ import annotations
 
@@ -42,7 +46,7 @@ __all__ = [
     "pack_codes", "unpack_codes", "estimate_ip", "dequantize", "topk", "qjl_alpha",
     "quantize_mse", "pack_index_planes", "unpack_index_planes", "dequantize_mse",
     "attention_decode", "sphere_cell_prob", "sphere_cell_moment", "codebook_sphere",
-    "qjl_alpha_orthogonal",
+    "qjl_alpha_orthogonal", "quantize_split", "estimate_ip_split",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -450,3 +454,34 @@ def attention_decode(logits: np.ndarray, values: np.ndarray, scale: float) -> np
         p /= np.sum(p, axis=1, keepdims=True)
         out[g] = p @ values[g]
     return out
+
+
+# ---------------------------------------------------------------- fractional rates
+# [review, experiments paragraph], [news, results paragraph]: KV caches at 2.5 and 3.5 bits per
+# channel.  Reading: the channels form groups, given as (first channel, width) pairs that
+# tile [0, d); each group is a separate TurboQuant instance with its own rotation, QJL
+# matrix, codebook and bit budget, and the inner product is the sum over groups.  Each
+# group's estimate is unbiased, so the sum is.
+
+def quantize_split(x, groups):
+    """Encode the channel groups of x [n][d] separately.
+
+    groups: list of dicts with keys off, width, Pi, S, centroids, thresholds (the group's
+    instance).  Returns the list of quantize() results, one per group."""
+    x = np.asarray(x)
+    return [quantize(x[:, g["off"]:g["off"] + g["width"]], g["Pi"], g["S"], g["centroids"],
+                     g["thresholds"]) for g in groups]
+
+
+def estimate_ip_split(q, groups, codes, mode: str = "prod") -> np.ndarray:
+    """Sum over channel groups of estimate_ip on the query's matching channels -> [nq][n].
+
+    codes: per group a dict with idx, z, nu, gamma (as quantize_split returns); each group
+    may carry its own QJL scale under the key alpha (None or absent: Gaussian S)."""
+    q = np.asarray(q, dtype=np.float64)
+    total = None
+    for g, c in zip(groups, codes):
+        est = estimate_ip(q[:, g["off"]:g["off"] + g["width"]], g["Pi"], g["S"], c["idx"], c["z"],
+                          c["nu"], c["gamma"], g["centroids"], mode, alpha=g.get("alpha"))
+        total = est if total is None else total + est
+    return total

@@ -590,3 +590,82 @@ def test_orthogonal_qjl_estimator_is_unbiased_over_S():
     r = oracle.quantize(x, Pi, S, c, t)
     xh_ = oracle.dequantize(Pi, S, r["idx"], r["z"], r["nu"], r["gamma"], c, alpha=alpha)
     assert abs(float(q[0].astype(np.float64) @ xh_[0]) - ests[-1]) < 1e-9
+
+
+# -------------------------------------------------------- fractional rates: channel groups
+
+def _split_groups(d_a, b_a, d_b, b_b, cfg, rep=0):
+    gs = []
+    for k, (off, w, b) in enumerate(((0, d_a, b_a), (d_a, d_b, b_b))):
+        if w == 0:
+            continue
+        c, t = oracle.codebook(b - 1, w)
+        gs.append({"off": off, "width": w, "b": b, "Pi": gen.haar_orthogonal(w, cfg + k, rep),
+                   "S": gen.gaussian_matrix(w, w, cfg + k, rep), "centroids": c, "thresholds": t})
+    return gs
+
+
+def test_split_with_one_group_is_the_plain_quantizer():
+    d, b = 32, 3
+    x = gen.unit_sphere(50, d, cfg=940, role=gen.ROLE_DATA) * 2.0
+    q = gen.unit_sphere(4, d, cfg=940, role=gen.ROLE_QUERY)
+    g = _split_groups(d, b, 0, 2, 940)
+    r = oracle.quantize_split(x, g)[0]
+    r0 = oracle.quantize(x, g[0]["Pi"], g[0]["S"], g[0]["centroids"], g[0]["thresholds"])
+    assert np.array_equal(r["idx"], r0["idx"]) and np.array_equal(r["z"], r0["z"])
+    e = oracle.estimate_ip_split(q, g, [r])
+    e0 = oracle.estimate_ip(q, g[0]["Pi"], g[0]["S"], r0["idx"], r0["z"], r0["nu"], r0["gamma"],
+                            g[0]["centroids"])
+    assert np.array_equal(e, e0)
+
+
+@pytest.mark.parametrize("mode", ["prod", "mse"])
+def test_split_estimate_is_inner_product_with_concatenated_reconstruction(mode):
+    # each group reconstructs its own channels; the split estimate is <q, [xhat_A; xhat_B]>
+    x = gen.unit_sphere(40, 24, cfg=941, role=gen.ROLE_DATA) * 1.5
+    q = gen.unit_sphere(3, 24, cfg=941, role=gen.ROLE_QUERY)
+    g = _split_groups(16, 4, 8, 2, 941)
+    codes = oracle.quantize_split(x, g)
+    xhat = np.concatenate([oracle.dequantize(gg["Pi"], gg["S"], c["idx"], c["z"], c["nu"], c["gamma"],
+                                             gg["centroids"], mode) for gg, c in zip(g, codes)], axis=1)
+    est = oracle.estimate_ip_split(q, g, codes, mode)
+    np.testing.assert_allclose(est, q.astype(np.float64) @ xhat.T, rtol=0, atol=1e-12)
+    # the groups see only their own channels: changing group B's channels leaves group A's codes
+    x2 = x.copy()
+    x2[:, 16:] *= -3.0
+    c2 = oracle.quantize_split(x2, g)
+    assert np.array_equal(c2[0]["idx"], codes[0]["idx"]) and np.array_equal(c2[0]["z"], codes[0]["z"])
+
+
+def test_split_estimate_is_unbiased_over_both_instances():
+    # 2.5 bits per channel on 16 channels: 8 at b = 3, 8 at b = 2
+    d, N = 16, 3000
+    x = gen.unit_sphere(1, d, cfg=942, role=gen.ROLE_DATA) * 2.0
+    q = gen.unit_sphere(1, d, cfg=942, role=gen.ROLE_QUERY) * 1.2
+    truth = float(q[0].astype(np.float64) @ x[0].astype(np.float64))
+    ests = np.empty(N)
+    for s in range(N):
+        g = _split_groups(8, 3, 8, 2, 942, rep=s)
+        ests[s] = oracle.estimate_ip_split(q, g, oracle.quantize_split(x, g))[0, 0]
+    se = ests.std(ddof=1) / math.sqrt(N)
+    assert abs(ests.mean() - truth) < 4 * se, (ests.mean(), truth, se)
+
+
+def test_split_mse_distortion_is_the_sum_of_the_groups():
+    # MSE-only reconstruction over Haar rotations: E|x - xhat|^2 = sum_g nu_g^2 D(d_g, b_g - 1),
+    # D from the sphere law by quadrature; groups at different norms and bit widths, so a group
+    # run at the other's codebook or bit width moves the mean by many SE
+    d_a, d_b, N = 8, 8, 3000
+    xa = gen.unit_sphere(1, d_a, cfg=943, role=gen.ROLE_DATA) * 3.0
+    xb = gen.unit_sphere(1, d_b, cfg=944, role=gen.ROLE_DATA) * 1.0
+    x = np.concatenate([xa, xb], axis=1)
+    errs = np.empty(N)
+    for s in range(N):
+        g = _split_groups(d_a, 4, d_b, 2, 943, rep=s)
+        codes = oracle.quantize_split(x, g)
+        xhat = np.concatenate([oracle.dequantize(gg["Pi"], gg["S"], c["idx"], c["z"], c["nu"], c["gamma"],
+                                                 gg["centroids"], "mse") for gg, c in zip(g, codes)], axis=1)
+        errs[s] = float(np.sum((x[0].astype(np.float64) - xhat[0]) ** 2))
+    expect = 9.0 * _sphere_expectations(d_a, 3)[1] + 1.0 * _sphere_expectations(d_b, 1)[1]
+    se = errs.std(ddof=1) / math.sqrt(N)
+    assert abs(errs.mean() - expect) < 4 * se, (errs.mean(), expect, se)
