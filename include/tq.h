@@ -185,7 +185,8 @@ int tq_append(const void* params, int d, int b, int mode, const void* x, int x_d
 /*
  * tq_dequantize — reconstruction ([review, QJL paragraph]: inverse rotation and
  * renormalisation).
- *   TQ_EST_PROD: xhat = nu (Pi^T chat + sqrt(pi/2)/m * gamma * S^T (2z - 1))
+ *   TQ_EST_PROD: xhat = nu (Pi^T chat + alpha * gamma * S^T (2z - 1)), alpha = sqrt(pi/2)/m
+ *                (1/(m E|w_1|) for a block from tq_prepare_orthogonal_qjl)
  *   TQ_EST_MSE : xhat = nu Pi^T chat
  *   codes/nu/gamma as written by tq_quantize; xhat out [n][d] float32.
  * Errors: TQ_EINVAL, TQ_EHIP.
@@ -199,7 +200,8 @@ size_t tq_score_ws_bytes(int d, int b, int64_t groups, int64_t G, int64_t T);
 /*
  * tq_score_ip — attention logits over a quantized key cache: for every group g (a KV head
  * of one sequence), each of its G query heads and each of its T keys
- *   logits[g][h][t] = nu_k (<Pi q, chat_k> + sqrt(pi/2)/m * gamma_k * <S q, 2 z_k - 1>)
+ *   logits[g][h][t] = nu_k (<Pi q, chat_k> + alpha * gamma_k * <S q, 2 z_k - 1>)
+ * (alpha as for tq_dequantize)
  * (TQ_EST_MSE drops the second term). The raw inner product, no softmax scale
  * ([review, problem statement]: one side quantized, unbiased; [news, 8x logit paragraph]).
  *   q        [groups][G][d] float32 or bfloat16 (q_dtype), unquantized
@@ -216,6 +218,44 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
                 const uint32_t* codes, const float* nu, const float* gamma, int64_t groups,
                 int64_t G, int64_t T, int mode, float* logits, void* ws, size_t ws_bytes,
                 void* stream);
+
+/*
+ * Fractional bit rates ([review, experiments paragraph] and [news, results paragraph]: KV
+ * caches at 2.5 and 3.5 bits per channel; the pages give no mechanism).  Each row of d
+ * channels is two channel groups, [0, d0) and [d0, d), each a TurboQuant instance of its
+ * own: a parameter block from tq_prepare(d0, b0, ...) and one from tq_prepare(d - d0, b1, ...)
+ * (own rotation, QJL matrix and codebook), its own codes, nu and gamma.  The estimate of
+ * <q, x> is the sum of the two groups' estimates, each unbiased.  Half the channels at b + 1
+ * and half at b give b + 1/2 bits per channel (d = 128: d0 = 64, b0 = b + 1, b1 = b).  Any
+ * other assignment of channels to groups is a permutation applied to both queries and keys,
+ * which leaves <q, x> unchanged, so the producer of q and x can apply it.
+ * Both groups run the tiled encoder and the general scoring path, reading their channels in
+ * place (rows d apart).
+ *
+ * tq_quantize_split — encode x [n][d] (x_dtype as for tq_quantize) into
+ *   codes0 [n][d0/32][b0], nu0, gamma0 [n]     (channels 0 .. d0-1, params0)
+ *   codes1 [n][(d-d0)/32][b1], nu1, gamma1 [n] (channels d0 .. d-1, params1)
+ * Errors: TQ_EINVAL (d0 or d - d0 not a valid d, bits out of 2..4, NULL, misaligned), TQ_EHIP.
+ */
+int tq_quantize_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                      const void* x, int x_dtype, int64_t n, uint32_t* codes0, float* nu0,
+                      float* gamma0, uint32_t* codes1, float* nu1, float* gamma1, void* stream);
+
+/* Workspace bytes needed by tq_score_ip_split for these sizes. */
+size_t tq_score_split_ws_bytes(int d, int d0, int b0, int b1, int64_t groups, int64_t G, int64_t T);
+
+/*
+ * tq_score_ip_split — logits[g][h][t] = estimate over channels [0, d0) + estimate over
+ * channels [d0, d), each as tq_score_ip computes it (same mode for both), for queries
+ * q [groups][G][d] and the two groups' codes laid out [groups][T] as for tq_score_ip.
+ *   ws  at least tq_score_split_ws_bytes(...) bytes, 256-aligned, scratch.
+ * Errors: as tq_score_ip.
+ */
+int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                      const void* q, int q_dtype, const uint32_t* codes0, const float* nu0,
+                      const float* gamma0, const uint32_t* codes1, const float* nu1,
+                      const float* gamma1, int64_t groups, int64_t G, int64_t T, int mode,
+                      float* logits, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by tq_attention for these sizes. */
 size_t tq_attention_ws_bytes(int d, int b_k, int64_t groups, int64_t G, int64_t T);

@@ -48,6 +48,10 @@ def load_library():
         "tq_score_ws_bytes": (SZ, [I, I, I64, I64, I64]),
         "tq_score_ip": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P, SZ, P]),
         "tq_quantize_mse": (I, [P, I, I, P, I, I64, P, P, P]),
+        "tq_quantize_split": (I, [P, P, I, I, I, I, P, I, I64, P, P, P, P, P, P, P]),
+        "tq_score_split_ws_bytes": (SZ, [I, I, I, I, I64, I64, I64]),
+        "tq_score_ip_split": (I, [P, P, I, I, I, I, P, I, P, P, P, P, P, P, I64, I64, I64, I, P, P, SZ,
+                                  P]),
         "tq_append_ws_bytes": (SZ, [I, I, I64]),
         "tq_append": (I, [P, I, I, I, P, I, I64, I64, I64, P, P, P, P, SZ, P]),
         "tq_attention_ws_bytes": (SZ, [I, I, I64, I64, I64]),
@@ -264,6 +268,54 @@ def tq_score_ip(params, d: int, b: int, q, codes, nu, gamma, groups: int, G: int
                                       _ptr(nu), _ptr(gamma), groups, G, T, int(mode), _ptr(logits),
                                       _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(stream, q.device)))
+
+
+def tq_quantize_split(params0, params1, d: int, d0: int, b0: int, b1: int, x, codes0, nu0, gamma0,
+                      codes1, nu1, gamma1, stream=None):
+    """Fractional rate: channels [0, d0) of x [n][d] at b0 bits (params0), [d0, d) at b1."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError(f"x must be [n][{d}]")
+    n = x.shape[0]
+    for tname, t in (("codes0", codes0), ("nu0", nu0), ("gamma0", gamma0), ("codes1", codes1),
+                     ("nu1", nu1), ("gamma1", gamma1), ("params0", params0), ("params1", params1)):
+        _dev(t, tname)
+    _need(codes0, "codes0", n * (d0 // 32) * b0, torch.int32)
+    _need(codes1, "codes1", n * ((d - d0) // 32) * b1, torch.int32)
+    for tname, t in (("nu0", nu0), ("gamma0", gamma0), ("nu1", nu1), ("gamma1", gamma1)):
+        _need(t, tname, n, torch.float32)
+    _check(load_library().tq_quantize_split(_ptr(params0), _ptr(params1), d, d0, b0, b1, _ptr(x),
+                                            _dtype_code(x, "x"), n, _ptr(codes0), _ptr(nu0),
+                                            _ptr(gamma0), _ptr(codes1), _ptr(nu1), _ptr(gamma1),
+                                            _stream(stream, x.device)))
+
+
+def tq_score_split_ws_bytes(d: int, d0: int, b0: int, b1: int, groups: int, G: int, T: int) -> int:
+    return int(load_library().tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, T))
+
+
+def tq_score_ip_split(params0, params1, d: int, d0: int, b0: int, b1: int, q, codes0, nu0, gamma0,
+                      codes1, nu1, gamma1, groups: int, G: int, T: int, mode: int, logits, ws,
+                      stream=None):
+    """logits[groups][G][T] = the two channel groups' estimates summed (tq_quantize_split codes)."""
+    torch = _torch()
+    for tname, t in (("q", q), ("codes0", codes0), ("nu0", nu0), ("gamma0", gamma0),
+                     ("codes1", codes1), ("nu1", nu1), ("gamma1", gamma1), ("logits", logits),
+                     ("ws", ws), ("params0", params0), ("params1", params1)):
+        _dev(t, tname)
+    if q.numel() < groups * G * d:
+        raise ValueError("q holds fewer than groups*G*d elements")
+    _need(codes0, "codes0", groups * T * (d0 // 32) * b0, torch.int32)
+    _need(codes1, "codes1", groups * T * ((d - d0) // 32) * b1, torch.int32)
+    for tname, t in (("nu0", nu0), ("gamma0", gamma0), ("nu1", nu1), ("gamma1", gamma1)):
+        _need(t, tname, groups * T, torch.float32)
+    _need(logits, "logits", groups * G * T, torch.float32)
+    _check(load_library().tq_score_ip_split(_ptr(params0), _ptr(params1), d, d0, b0, b1, _ptr(q),
+                                            _dtype_code(q, "q"), _ptr(codes0), _ptr(nu0), _ptr(gamma0),
+                                            _ptr(codes1), _ptr(nu1), _ptr(gamma1), groups, G, T,
+                                            int(mode), _ptr(logits), _ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(stream, q.device)))
 
 
 def tq_attention_ws_bytes(d: int, b_k: int, groups: int, G: int, T: int) -> int:

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -585,6 +586,80 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
   hipError_t e = launch_score_any(params, d, b, q, q_dtype, codes, nu, gamma, groups, G, T, mode,
                                   logits, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tq_score_ip launch");
+  return ok();
+}
+
+// ------------------------------------------------------------- fractional rates
+// Two channel groups of each row: [0, d0) and [d0, d), each a TurboQuant instance of its own
+// width and bit budget; the logits are the sum of the groups' estimates.
+
+static bool valid_split(int d, int d0, int b0, int b1) {
+  return d0 > 0 && d0 < d && valid_shape(d0, b0) && valid_shape(d - d0, b1);
+}
+
+int tq_quantize_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                      const void* x, int x_dtype, int64_t n, uint32_t* codes0, float* nu0,
+                      float* gamma0, uint32_t* codes1, float* nu1, float* gamma1, void* stream) {
+  if (!valid_split(d, d0, b0, b1))
+    return fail(TQ_EINVAL, "unsupported split d=%d d0=%d b0=%d b1=%d", d, d0, b0, b1);
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad x_dtype %d", x_dtype);
+  if (n < 0) return fail(TQ_EINVAL, "n=%lld < 0", (long long)n);
+  if (n == 0) return ok();
+  if (!params0 || !params1 || !x || !codes0 || !nu0 || !gamma0 || !codes1 || !nu1 || !gamma1)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params0, 256) || !aligned(params1, 256) || !aligned(x, 16) || !aligned(codes0, 16) ||
+      !aligned(codes1, 16) || !aligned(nu0, 4) || !aligned(gamma0, 4) || !aligned(nu1, 4) ||
+      !aligned(gamma1, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x and codes 16 B)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
+  const void* x1 = static_cast<const unsigned char*>(x) + size_t(d0) * esz;
+  hipError_t e = tq::launch_quantize_gemm(params0, d0, b0, x, x_dtype, n, codes0, nu0, gamma0, s, d);
+  if (e == hipSuccess)
+    e = tq::launch_quantize_gemm(params1, d - d0, b1, x1, x_dtype, n, codes1, nu1, gamma1, s, d);
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize_split launch");
+  return ok();
+}
+
+size_t tq_score_split_ws_bytes(int d, int d0, int b0, int b1, int64_t groups, int64_t G, int64_t T) {
+  (void)T;
+  if (!valid_split(d, d0, b0, b1) || groups < 0 || G < 0) return 0;
+  return tq::align256(std::max(tq::score_generic_ws_bytes(d0, groups, G),
+                               tq::score_generic_ws_bytes(d - d0, groups, G)));
+}
+
+int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                      const void* q, int q_dtype, const uint32_t* codes0, const float* nu0,
+                      const float* gamma0, const uint32_t* codes1, const float* nu1,
+                      const float* gamma1, int64_t groups, int64_t G, int64_t T, int mode,
+                      float* logits, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_split(d, d0, b0, b1))
+    return fail(TQ_EINVAL, "unsupported split d=%d d0=%d b0=%d b1=%d", d, d0, b0, b1);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad q_dtype %d", q_dtype);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (groups < 0 || G < 0 || T < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0 || G == 0 || T == 0) return ok();
+  if (T >= (int64_t(1) << 31)) return fail(TQ_EINVAL, "T must be < 2^31");
+  if (!params0 || !params1 || !q || !codes0 || !nu0 || !gamma0 || !codes1 || !nu1 || !gamma1 ||
+      !logits || !ws)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params0, 256) || !aligned(params1, 256) || !aligned(ws, 256) || !aligned(codes0, 16) ||
+      !aligned(codes1, 16) || !aligned(q, 4) || !aligned(logits, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; codes 16 B)");
+  if (!tq::score_generic_grid_fits(groups, G, T))
+    return fail(TQ_EUNSUPPORTED, "tq_score_ip_split: groups * G * T too large for one launch");
+  const size_t need = tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, T);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = q_dtype == TQ_F32 ? 4 : 2;
+  const void* q1 = static_cast<const unsigned char*>(q) + size_t(d0) * esz;
+  // the second launch adds to the first one's logits (same stream, so in order; both reuse ws)
+  hipError_t e = tq::launch_score_generic(params0, d0, b0, q, q_dtype, codes0, nu0, gamma0, groups, G, T,
+                                          mode, logits, ws, s, d, false);
+  if (e == hipSuccess)
+    e = tq::launch_score_generic(params1, d - d0, b1, q1, q_dtype, codes1, nu1, gamma1, groups, G, T,
+                                 mode, logits, ws, s, d, true);
+  if (e != hipSuccess) return hip_fail(e, "tq_score_ip_split launch");
   return ok();
 }
 

@@ -66,9 +66,11 @@ __device__ __forceinline__ uint32_t bf16_bits(float v) {
 // ------------------------------------------------------------------------------ split
 // One wave per vector: nu = |x| (float32 sum of squares), and for float32 inputs the bf16
 // rows x_hi = RNE(x), x_lo = RNE(x - x_hi).  Lane l covers coordinates 8 (l + 64 i) .. +7.
+// Input rows are xpitch elements apart (a channel group of wider rows); x_hi, x_lo are
+// written d apart.
 template <bool F32IN>
 __global__ __launch_bounds__(256) void qsplit_kernel(const void* __restrict__ x, long rows, int d,
-                                                      uint16_t* __restrict__ xh,
+                                                      long xpitch, uint16_t* __restrict__ xh,
                                                       uint16_t* __restrict__ xl, long v0,
                                                       float* __restrict__ nu_out) {
   const int lane = threadIdx.x & 63;
@@ -77,9 +79,10 @@ __global__ __launch_bounds__(256) void qsplit_kernel(const void* __restrict__ x,
   float ss = 0.f;
   for (int c = 8 * lane; c < d; c += 512) {
     const size_t off = size_t(row) * d + c;
+    const size_t in = size_t(row) * xpitch + c;
     if constexpr (F32IN) {
-      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
-      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off + 4);
+      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + in);
+      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + in + 4);
       const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       uint32_t h[4], l[4];
 #pragma unroll
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(256) void qsplit_kernel(const void* __restrict__ x,
       *reinterpret_cast<uint4*>(xh + off) = make_uint4(h[0], h[1], h[2], h[3]);
       *reinterpret_cast<uint4*>(xl + off) = make_uint4(l[0], l[1], l[2], l[3]);
     } else {
-      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + in);
       const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -257,13 +260,14 @@ __device__ __forceinline__ void store_residual(char* sb, const uint32_t (&v)[2][
 }
 
 // PHASE 1: A = x (hi[/lo]) bf16 rows, B = Pi (hi/lo). PHASE 2: A = r' (hi/lo), B = S' (hi/lo).
+// A rows are apitch elements apart (d, or the caller's row pitch for bf16 rows read in place).
 // PHASE 3: phase 1 for the MSE quantizer alone: the b-1 index planes (a code stride of b-1
 // words per coordinate group) and nothing for a phase 2.
 template <int PHASE, int BITS, bool ALO>
 __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
     const unsigned char* __restrict__ params, const uint16_t* __restrict__ ahi,
     const uint16_t* __restrict__ alo, long rows, const uint16_t* __restrict__ bhi,
-    const uint16_t* __restrict__ blo, int d, long v0, int nrb, uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ blo, int d, long apitch, long v0, int nrb, uint32_t* __restrict__ codes,
     const float* __restrict__ nu, float* __restrict__ gamma_out, uint16_t* __restrict__ rhi,
     uint16_t* __restrict__ rlo, float* __restrict__ gpart) {
   __shared__ uint4 buf0[StageShape<ALO>::U4];
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
   plan.a[0] = const_cast<uint16_t*>(ahi);
   if constexpr (ALO) plan.a[1] = const_cast<uint16_t*>(alo);
   plan.bbytes = int(size_t(d) * d * 2);
-  plan.abytes = int(size_t(rows) * d * 2);
+  plan.abytes = int((size_t(rows - 1) * apitch + d) * 2);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int f = WAVES * m + wave;
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
     const int fa = WAVES * m + wave;
     long row = r0 + 16 * (fa & 15) + q;
     row = row < rows ? row : rows - 1;
-    plan.ao[m] = uint32_t((size_t(row) * d + 8 * piece) * 2);
+    plan.ao[m] = uint32_t((size_t(row) * apitch + 8 * piece) * 2);
   }
   // fragment read offsets: lane l reads row l % 32 of a 32-row pair of blocks, piece
   // 2 ks + l / 32
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
 }
 
 template <int BITS, bool F32IN>
-hipError_t run(const unsigned char* params, const Layout& lay, const void* x, int64_t n,
+hipError_t run(const unsigned char* params, const Layout& lay, const void* x, long xpitch, int64_t n,
                uint32_t* codes, float* nu, float* gamma, hipStream_t s) {
   const int d = lay.d;
   const uint16_t* pih = reinterpret_cast<const uint16_t*>(params + lay.off_gmat);
@@ -511,15 +515,16 @@ hipError_t run(const unsigned char* params, const Layout& lay, const void* x, in
     const long rows = (n - c0) < ch ? (n - c0) : ch;
     const int nrb = int((rows + WT - 1) / WT);
     const dim3 grid(unsigned((nrb + NXCD - 1) / NXCD * NXCD * nct));
-    const void* xs = F32IN ? static_cast<const void*>(static_cast<const float*>(x) + size_t(c0) * d)
-                           : static_cast<const void*>(static_cast<const uint16_t*>(x) + size_t(c0) * d);
+    const void* xs = F32IN ? static_cast<const void*>(static_cast<const float*>(x) + size_t(c0) * xpitch)
+                           : static_cast<const void*>(static_cast<const uint16_t*>(x) + size_t(c0) * xpitch);
     hipLaunchKernelGGL((qsplit_kernel<F32IN>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, xs,
-                       rows, d, xh, xl, c0, nu);
+                       rows, d, xpitch, xh, xl, c0, nu);
     const uint16_t* a1 = F32IN ? xh : static_cast<const uint16_t*>(xs);
+    const long ap = F32IN ? long(d) : xpitch;
     hipLaunchKernelGGL((qgemm_kernel<1, BITS, F32IN>), grid, dim3(WAVES * 64), 0, s, params, a1, xl,
-                       rows, pih, pil, d, c0, nrb, codes, nu, gamma, rhi, rlo, gpart);
+                       rows, pih, pil, d, ap, c0, nrb, codes, nu, gamma, rhi, rlo, gpart);
     hipLaunchKernelGGL((qgemm_kernel<2, BITS, true>), grid, dim3(WAVES * 64), 0, s, params, rhi, rlo,
-                       rows, sph, spl, d, c0, nrb, codes, nu, gamma, nullptr, nullptr, gpart);
+                       rows, sph, spl, d, long(d), c0, nrb, codes, nu, gamma, nullptr, nullptr, gpart);
     e = hipGetLastError();
     if (e != hipSuccess) break;
   }
@@ -530,8 +535,8 @@ hipError_t run(const unsigned char* params, const Layout& lay, const void* x, in
 // The MSE quantizer alone: per chunk the split pass (nu, x hi/lo) and phase 1 without the
 // residual.
 template <int BITS, bool F32IN>
-hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x, int64_t n,
-                   uint32_t* codes, float* nu, hipStream_t s) {
+hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x, long xpitch,
+                   int64_t n, uint32_t* codes, float* nu, hipStream_t s) {
   const int d = lay.d;
   const uint16_t* pih = reinterpret_cast<const uint16_t*>(params + lay.off_gmat);
   const uint16_t* pil = pih + size_t(d) * d;
@@ -550,13 +555,14 @@ hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x
     const long rows = (n - c0) < ch ? (n - c0) : ch;
     const int nrb = int((rows + WT - 1) / WT);
     const dim3 grid(unsigned((nrb + NXCD - 1) / NXCD * NXCD * nct));
-    const void* xs = F32IN ? static_cast<const void*>(static_cast<const float*>(x) + size_t(c0) * d)
-                           : static_cast<const void*>(static_cast<const uint16_t*>(x) + size_t(c0) * d);
+    const void* xs = F32IN ? static_cast<const void*>(static_cast<const float*>(x) + size_t(c0) * xpitch)
+                           : static_cast<const void*>(static_cast<const uint16_t*>(x) + size_t(c0) * xpitch);
     hipLaunchKernelGGL((qsplit_kernel<F32IN>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, xs,
-                       rows, d, xh, xl, c0, nu);
+                       rows, d, xpitch, xh, xl, c0, nu);
     const uint16_t* a1 = F32IN ? xh : static_cast<const uint16_t*>(xs);
+    const long ap = F32IN ? long(d) : xpitch;
     hipLaunchKernelGGL((qgemm_kernel<3, BITS, F32IN>), grid, dim3(WAVES * 64), 0, s, params, a1, xl,
-                       rows, pih, pil, d, c0, nrb, codes, nu, nullptr, nullptr, nullptr, nullptr);
+                       rows, pih, pil, d, ap, c0, nrb, codes, nu, nullptr, nullptr, nullptr, nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) break;
   }
@@ -571,17 +577,18 @@ hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x
 
 hipError_t launch_quantize_gemm(const void* params_v, int d, int b, const void* x, int x_dtype,
                                 int64_t n, uint32_t* codes, float* nu, float* gamma,
-                                hipStream_t s) {
+                                hipStream_t s, int64_t xpitch) {
   const unsigned char* params = static_cast<const unsigned char*>(params_v);
   const Layout lay(d, b);
   const bool f32 = x_dtype == 0;
+  const long xp = xpitch > 0 ? long(xpitch) : long(d);
   switch (b) {
-    case 2: return f32 ? run<2, true>(params, lay, x, n, codes, nu, gamma, s)
-                       : run<2, false>(params, lay, x, n, codes, nu, gamma, s);
-    case 3: return f32 ? run<3, true>(params, lay, x, n, codes, nu, gamma, s)
-                       : run<3, false>(params, lay, x, n, codes, nu, gamma, s);
-    case 4: return f32 ? run<4, true>(params, lay, x, n, codes, nu, gamma, s)
-                       : run<4, false>(params, lay, x, n, codes, nu, gamma, s);
+    case 2: return f32 ? run<2, true>(params, lay, x, xp, n, codes, nu, gamma, s)
+                       : run<2, false>(params, lay, x, xp, n, codes, nu, gamma, s);
+    case 3: return f32 ? run<3, true>(params, lay, x, xp, n, codes, nu, gamma, s)
+                       : run<3, false>(params, lay, x, xp, n, codes, nu, gamma, s);
+    case 4: return f32 ? run<4, true>(params, lay, x, xp, n, codes, nu, gamma, s)
+                       : run<4, false>(params, lay, x, xp, n, codes, nu, gamma, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -591,17 +598,19 @@ hipError_t launch_quantize_gemm(const void* params_v, int d, int b, const void* 
 namespace tq {
 
 hipError_t launch_quantize_mse(const void* params_v, int d, int b, const void* x, int x_dtype,
-                               int64_t n, uint32_t* codes, float* nu, hipStream_t s) {
+                               int64_t n, uint32_t* codes, float* nu, hipStream_t s,
+                               int64_t xpitch) {
   const unsigned char* params = static_cast<const unsigned char*>(params_v);
   const Layout lay(d, b);
   const bool f32 = x_dtype == 0;
+  const long xp = xpitch > 0 ? long(xpitch) : long(d);
   switch (b) {
-    case 2: return f32 ? run_mse<2, true>(params, lay, x, n, codes, nu, s)
-                       : run_mse<2, false>(params, lay, x, n, codes, nu, s);
-    case 3: return f32 ? run_mse<3, true>(params, lay, x, n, codes, nu, s)
-                       : run_mse<3, false>(params, lay, x, n, codes, nu, s);
-    case 4: return f32 ? run_mse<4, true>(params, lay, x, n, codes, nu, s)
-                       : run_mse<4, false>(params, lay, x, n, codes, nu, s);
+    case 2: return f32 ? run_mse<2, true>(params, lay, x, xp, n, codes, nu, s)
+                       : run_mse<2, false>(params, lay, x, xp, n, codes, nu, s);
+    case 3: return f32 ? run_mse<3, true>(params, lay, x, xp, n, codes, nu, s)
+                       : run_mse<3, false>(params, lay, x, xp, n, codes, nu, s);
+    case 4: return f32 ? run_mse<4, true>(params, lay, x, xp, n, codes, nu, s)
+                       : run_mse<4, false>(params, lay, x, xp, n, codes, nu, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -23,7 +23,7 @@ constexpr int HB = 4;        // query heads per pass of the scoring kernel
 constexpr int KEYS = 256;    // keys per workgroup (one per lane)
 
 __global__ __launch_bounds__(256) void generic_qprep_kernel(
-    const unsigned char* __restrict__ params, size_t off_pi, size_t off_s, int d,
+    const unsigned char* __restrict__ params, size_t off_pi, size_t off_s, int d, long qpitch,
     const void* __restrict__ q, int q_f32, float* __restrict__ qs, float* __restrict__ ssum) {
   extern __shared__ float qv[];            // the query row, d floats
   __shared__ float red[4];
@@ -31,9 +31,9 @@ __global__ __launch_bounds__(256) void generic_qprep_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int k = tid; k < d; k += 256) {
     if (q_f32) {
-      qv[k] = static_cast<const float*>(q)[row * d + k];
+      qv[k] = static_cast<const float*>(q)[row * qpitch + k];
     } else {
-      const uint32_t hbits = static_cast<const uint16_t*>(q)[row * d + k];
+      const uint32_t hbits = static_cast<const uint16_t*>(q)[row * qpitch + k];
       qv[k] = __uint_as_float(hbits << 16);
     }
   }
@@ -57,8 +57,9 @@ __global__ __launch_bounds__(256) void generic_qprep_kernel(
   if (tid == 0) ssum[row] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// grid: one workgroup per (group, head pass, block of KEYS keys), flattened into x.
-template <int BITS, bool PROD>
+// grid: one workgroup per (group, head pass, block of KEYS keys), flattened into x.  ACC adds
+// the estimate to the logits already there (the channel groups of a fractional rate).
+template <int BITS, bool PROD, bool ACC>
 __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     const unsigned char* __restrict__ params, const float* __restrict__ qs,
     const float* __restrict__ ssum, const uint32_t* __restrict__ codes,
@@ -120,12 +121,13 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     const long h = h0 + hh;
     float l = mse[hh];
     if constexpr (PROD) l = fmaf(alpha * g_k, 2.f * zsum[hh] - ssum[g * G + h], l);
-    logits[size_t(g * G + h) * T + t] = n_k * l;
+    float* dst = logits + size_t(g * G + h) * T + t;
+    *dst = ACC ? *dst + n_k * l : n_k * l;
   }
 }
 
-template <int BITS>
-hipError_t launch_b(const void* params_v, int d, const void* q, int q_dtype,
+template <int BITS, bool ACC>
+hipError_t launch_b(const void* params_v, int d, const void* q, int q_dtype, long qpitch,
                     const uint32_t* codes, const float* nu, const float* gamma, int64_t groups,
                     int64_t G, int64_t T, int mode, float* logits, void* ws, hipStream_t s) {
   const unsigned char* params = static_cast<const unsigned char*>(params_v);
@@ -134,17 +136,17 @@ hipError_t launch_b(const void* params_v, int d, const void* q, int q_dtype,
   float* ssum = qs + size_t(groups) * G * 2 * d;
   const long rows = long(groups) * G;
   hipLaunchKernelGGL(generic_qprep_kernel, dim3(unsigned(rows)), dim3(256), size_t(d) * 4, s, params,
-                     lay.off_pi, lay.off_s, d, q, q_dtype == 0 ? 1 : 0, qs, ssum);
+                     lay.off_pi, lay.off_s, d, qpitch, q, q_dtype == 0 ? 1 : 0, qs, ssum);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long kblocks = (T + KEYS - 1) / KEYS;
   const long passes = (G + HB - 1) / HB;
   const dim3 grid(unsigned(groups * passes * kblocks));
   if (mode == 0)
-    hipLaunchKernelGGL((generic_score_kernel<BITS, true>), grid, dim3(KEYS), 0, s, params, qs, ssum,
+    hipLaunchKernelGGL((generic_score_kernel<BITS, true, ACC>), grid, dim3(KEYS), 0, s, params, qs, ssum,
                        codes, nu, gamma, d, long(G), long(T), kblocks, passes, logits);
   else
-    hipLaunchKernelGGL((generic_score_kernel<BITS, false>), grid, dim3(KEYS), 0, s, params, qs, ssum,
+    hipLaunchKernelGGL((generic_score_kernel<BITS, false, ACC>), grid, dim3(KEYS), 0, s, params, qs, ssum,
                        codes, nu, gamma, d, long(G), long(T), kblocks, passes, logits);
   return hipGetLastError();
 }
@@ -163,13 +165,22 @@ bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T) {
 hipError_t launch_score_generic(const void* params, int d, int b, const void* q, int q_dtype,
                                 const uint32_t* codes, const float* nu, const float* gamma,
                                 int64_t groups, int64_t G, int64_t T, int mode, float* logits,
-                                void* ws, hipStream_t s) {
+                                void* ws, hipStream_t s, int64_t qpitch, bool accumulate) {
+  const long qp = qpitch > 0 ? long(qpitch) : long(d);
+#define TQ_GEN_CASE(B)                                                                            \
+  case B:                                                                                         \
+    return accumulate                                                                             \
+               ? launch_b<B, true>(params, d, q, q_dtype, qp, codes, nu, gamma, groups, G, T, mode, \
+                                   logits, ws, s)                                                 \
+               : launch_b<B, false>(params, d, q, q_dtype, qp, codes, nu, gamma, groups, G, T,      \
+                                    mode, logits, ws, s);
   switch (b) {
-    case 2: return launch_b<2>(params, d, q, q_dtype, codes, nu, gamma, groups, G, T, mode, logits, ws, s);
-    case 3: return launch_b<3>(params, d, q, q_dtype, codes, nu, gamma, groups, G, T, mode, logits, ws, s);
-    case 4: return launch_b<4>(params, d, q, q_dtype, codes, nu, gamma, groups, G, T, mode, logits, ws, s);
+    TQ_GEN_CASE(2)
+    TQ_GEN_CASE(3)
+    TQ_GEN_CASE(4)
     default: return hipErrorInvalidValue;
   }
+#undef TQ_GEN_CASE
 }
 
 }  // namespace tq

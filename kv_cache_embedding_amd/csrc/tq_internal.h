@@ -73,19 +73,23 @@ constexpr size_t score_ws_per_group(int b) {
 // ---- kernel launchers (defined in the .hip files), return hipError_t
 hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_dtype, int64_t n,
                                 uint32_t* codes, float* nu, float* gamma, hipStream_t s);
+// Tiled encoder, any valid d.  xpitch: elements between input rows (0: d), so that a
+// channel group of wider rows is read in place.
 hipError_t launch_quantize_gemm(const void* params, int d, int b, const void* x, int x_dtype,
                                 int64_t n, uint32_t* codes, float* nu, float* gamma,
-                                hipStream_t s);
+                                hipStream_t s, int64_t xpitch = 0);
 hipError_t launch_score_d128(const void* params, int b, const void* q, int q_dtype,
                              const uint32_t* codes, const float* nu, const float* gamma,
                              int64_t groups, int64_t G, int64_t T, int mode, float* logits,
                              void* ws, hipStream_t s);
 // Scoring for shapes the d = 128 kernel does not take (any d, any G): fp32 query prep into
-// ws ([groups * G][2][d] floats, then [groups * G] sums), then one lane per key.
+// ws ([groups * G][2][d] floats, then [groups * G] sums), then one lane per key.  qpitch:
+// elements between query rows (0: d); accumulate: add to logits instead of overwriting.
 hipError_t launch_score_generic(const void* params, int d, int b, const void* q, int q_dtype,
                                 const uint32_t* codes, const float* nu, const float* gamma,
                                 int64_t groups, int64_t G, int64_t T, int mode, float* logits,
-                                void* ws, hipStream_t s);
+                                void* ws, hipStream_t s, int64_t qpitch = 0,
+                                bool accumulate = false);
 size_t score_generic_ws_bytes(int d, int64_t groups, int64_t G);
 bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T);
 // The MSE stage alone (b-1 index planes and nu): d = 128 on the fused encoder without its
@@ -93,7 +97,8 @@ bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T);
 hipError_t launch_quantize_d128_mse(const void* params, int b, const void* x, int x_dtype,
                                     int64_t n, uint32_t* codes, float* nu, hipStream_t s);
 hipError_t launch_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype,
-                               int64_t n, uint32_t* codes, float* nu, hipStream_t s);
+                               int64_t n, uint32_t* codes, float* nu, hipStream_t s,
+                               int64_t xpitch = 0);
 // Decode attention after the logits: block partials of the softmax-weighted value sum, then
 // their merge and the inverse rotation.
 size_t attention_part_bytes(int d, int64_t groups, int64_t G, int64_t T);

@@ -190,3 +190,25 @@ def test_prepare_rejects_bad_codebook_and_rotation(lib):
     S2 = np.ascontiguousarray(np.eye(d, dtype=np.float32) * 1.01)
     assert lib.tq_prepare_orthogonal_qjl(d, b, Pi.ctypes.data, S2.ctypes.data, c.ctypes.data,
                                          t.ctypes.data, fake, None) == tq.TQ_EINVAL
+
+
+def test_split_calls_validate_without_launch(lib):
+    fake = ctypes.c_void_p(0x100000)
+    P = fake
+    # channel groups must each be a valid d (multiple of 64, 64..4096) with bits in 2..4
+    for d, d0, b0, b1 in ((128, 32, 3, 2), (128, 128, 3, 2), (128, 0, 3, 2), (192, 64, 5, 2),
+                          (192, 64, 3, 1)):
+        assert lib.tq_quantize_split(P, P, d, d0, b0, b1, P, tq.TQ_BF16, 10, P, P, P, P, P, P,
+                                     None) == tq.TQ_EINVAL
+        assert lib.tq_score_split_ws_bytes(d, d0, b0, b1, 2, 4, 100) == 0
+    assert "split" in tq.tq_last_error()
+    assert lib.tq_quantize_split(P, None, 128, 64, 3, 2, P, tq.TQ_BF16, 10, P, P, P, P, P, P,
+                                 None) == tq.TQ_EINVAL
+    assert lib.tq_quantize_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, 0, None, None, None, None, None,
+                                 None, None) == tq.TQ_OK                       # n = 0: nothing to do
+    need = lib.tq_score_split_ws_bytes(128, 64, 3, 2, 2, 4, 100)
+    assert need >= 2 * 4 * (2 * 64 + 1) * 4 and need % 256 == 0
+    assert lib.tq_score_ip_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, P, P, P, P, P, P, 2, 4, 100,
+                                 tq.TQ_EST_PROD, P, P, need - 256, None) == tq.TQ_EWORKSPACE
+    assert lib.tq_score_ip_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, P, P, P, P, P, P, 2, 4, 100,
+                                 7, P, P, need, None) == tq.TQ_EINVAL          # bad mode
