@@ -135,10 +135,11 @@ int tq_prepare_orthogonal_qjl(int d, int b, const float* Pi, const float* S, con
  *   gamma    out [n] float32, norm of the residual of x/|x| after the Lloyd-Max stage
  * Integer decisions (index, sign) are taken in float32 against float32 thresholds.
  * d = 128 runs one fused kernel; every other d runs a split pass and two tiled
- * kernels per chunk of 32768 vectors and take a stream-ordered scratch buffer of
+ * kernels per chunk of c vectors and takes a stream-ordered scratch buffer of
  * c * d * 8 bytes for float32 input, c * d * 4 bytes for bfloat16, plus c * ceil(d / 256) * 4
- * bytes, c = min(n, 32768) (hipMallocAsync / hipFreeAsync on `stream`, released when
- * the call's work completes).
+ * bytes (hipMallocAsync / hipFreeAsync on `stream`, released when the call's work
+ * completes).  c = min(n, max(32768, 384 MiB / (d * 8) for float32 or / (d * 4) for
+ * bfloat16)): about 384 MiB of scratch whatever d is (more for float32 d > 1536).
  * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EHIP (launch or scratch allocation failed).
  */
 int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
@@ -156,8 +157,8 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
  *   nu       out [n] float32, |x|
  * The decisions are those of tq_quantize's index planes. It runs the split pass and the
  * first tiled GEMM of the tiled encoder for d != 128 (float32 input takes a stream-ordered
- * scratch of min(n, 32768) * d * 4 bytes) and the fused encoder without its QJL GEMM at
- * d = 128.
+ * scratch of c * d * 4 bytes, c = min(n, max(32768, 384 MiB / (d * 4)))) and the fused
+ * encoder without its QJL GEMM at d = 128.
  * Errors: TQ_EINVAL (shape, NULL, misalignment), TQ_EHIP.
  */
 int tq_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,

@@ -38,7 +38,22 @@ typedef __attribute__((address_space(3))) void* lptr;         // LDS
 constexpr int WT = 256;          // workgroup tile: vectors x coordinates
 constexpr int BK = 32;           // K per stage (two MFMA K steps, 64 bytes of a bf16 row)
 constexpr int WAVES = 8;
-constexpr long CHUNK = 32768;    // vectors per pass
+constexpr long CHUNK = 32768;    // vectors per pass at d = 1536 (float32 rows)
+// Scratch of one pass (bf16 hi/lo planes of r' and, for float32 rows, of x) is held to the
+// d = 1536 float32 footprint; smaller d take proportionally more vectors per pass, so that
+// one launch still fills the chip.
+constexpr size_t SCRATCH_BUDGET = size_t(CHUNK) * 1536 * 2 * 4;
+
+// Vectors per pass for rows of d (pitch xpitch) with `planes` bf16 scratch planes per row;
+// at least CHUNK, and small enough that every byte offset of a pass fits 30 bits.
+long chunk_rows(int64_t n, int d, long xpitch, int planes) {
+  long ch = long(SCRATCH_BUDGET / (size_t(d) * 2 * planes));
+  if (ch < CHUNK) ch = CHUNK;
+  const long pitch = xpitch > d ? xpitch : long(d);
+  const long cap = long((size_t(1) << 30) / size_t(pitch));
+  if (ch > cap) ch = cap;
+  return n < ch ? long(n) : ch;
+}
 constexpr int NXCD = 8;
 
 // LDS blocks (1 KiB) of one stage: 16 rows x 32 K of one operand part.  B blocks
@@ -497,7 +512,7 @@ hipError_t run(const unsigned char* params, const Layout& lay, const void* x, lo
   const uint16_t* pil = pih + size_t(d) * d;
   const uint16_t* sph = pil + size_t(d) * d;
   const uint16_t* spl = sph + size_t(d) * d;
-  const long ch = n < CHUNK ? long(n) : CHUNK;
+  const long ch = chunk_rows(n, d, xpitch, F32IN ? 4 : 2);
   const int nct = (d + WT - 1) / WT;
   // scratch: r' hi, r' lo and (float32 input) x hi, x lo, each (chunk rows) x d bf16; then
   // the partial sums of |r'|^2, (chunk rows) x (d / 256) float32
@@ -540,7 +555,7 @@ hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x
   const int d = lay.d;
   const uint16_t* pih = reinterpret_cast<const uint16_t*>(params + lay.off_gmat);
   const uint16_t* pil = pih + size_t(d) * d;
-  const long ch = n < CHUNK ? long(n) : CHUNK;
+  const long ch = chunk_rows(n, d, xpitch, 2);
   const int nct = (d + WT - 1) / WT;
   const size_t plane = size_t(ch) * d;
   uint16_t* scratch = nullptr;

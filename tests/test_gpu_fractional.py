@@ -106,3 +106,70 @@ def test_score_split_parity(d, d0, b0, b1, G, T, q_bf16):
             qg = qd.view(groups * G, d)[:, off:off + w].contiguous()
             ref_sum += U.gpu_score(st, qg, c, nu, ga, groups, G, T, mode)
         assert np.max(np.abs(lg - ref_sum) / np.maximum(scale, 1e-30)) <= 1e-6
+
+
+def _rel_logit_mse(lg, exact):
+    return float(np.sum((lg - exact) ** 2) / np.sum(exact ** 2))
+
+
+def _plain_logits(d, b, cfg, xd, qd, groups, G, T):
+    st = U.make_setup(d, b, cfg=cfg)
+    c, nu, ga = U.gpu_quantize(st, xd)
+    return U.gpu_score(st, qd, c, nu, ga, groups, G, T, tq.TQ_EST_PROD).astype(np.float64)
+
+
+def _split_logits(d, b0, b1, cfg, xd, qd, groups, G, T):
+    d0 = d // 2
+    sts = _groups(d, d0, b0, b1, cfg)
+    parts = _split_quantize(sts, d, d0, xd)
+    ws = torch.empty(tq.tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, T), dtype=torch.uint8, device=U.DEV)
+    logits = torch.empty(groups * G * T, device=U.DEV)
+    tq.tq_score_ip_split(sts[0].params, sts[1].params, d, d0, b0, b1, qd, *parts[0], *parts[1], groups, G,
+                         T, tq.TQ_EST_PROD, logits, ws)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy().reshape(groups, G, T).astype(np.float64)
+
+
+def test_fractional_rates_order_the_logit_error():
+    # isotropic keys: each half bit lowers the relative mean squared logit error
+    d, groups, G, T, cfg = 128, 4, 4, 4096, 72
+    x = gen.unit_sphere(groups * T, d, cfg=cfg, role=gen.ROLE_DATA)
+    q = gen.unit_sphere(groups * G, d, cfg=cfg, role=gen.ROLE_QUERY)
+    exact = np.einsum("ghd,gtd->ght", q.astype(np.float64).reshape(groups, G, d),
+                      x.astype(np.float64).reshape(groups, T, d))
+    xd, qd = U.to_device(x, False), U.to_device(q, False)
+    errs = {}
+    for rate in (2.0, 2.5, 3.0, 3.5, 4.0):
+        if rate == int(rate):
+            lg = _plain_logits(d, int(rate), cfg, xd, qd, groups, G, T)
+        else:
+            lg = _split_logits(d, int(rate + 0.5), int(rate - 0.5), cfg, xd, qd, groups, G, T)
+        errs[rate] = _rel_logit_mse(lg, exact)
+    print("[rate -> relative logit MSE] " + ", ".join(f"{r}: {e:.4f}" for r, e in errs.items()), flush=True)
+    rates = sorted(errs)
+    assert all(errs[a] > errs[b] for a, b in zip(rates, rates[1:])), errs
+
+
+def test_outlier_channels_belong_in_the_higher_bit_group():
+    # KV-key law: 4 channels per head x20.  A channel permutation applied to both keys and
+    # queries leaves <q, k> unchanged; sending the outliers to the 3-bit group of a 2.5-bit
+    # split beats sending them to the 2-bit group
+    d, groups, G, T, cfg = 128, 4, 4, 4096, 73
+    chans = gen.outlier_channels(cfg, groups, d)
+    keys = [gen.bf16_bits_to_f32(gen.kv_keys_chunk(cfg, 0, h, T, d, chans[h])) for h in range(groups)]
+    qs = gen.bf16_bits_to_f32(gen.kv_queries(cfg, 1, groups * G, d)[0]).reshape(groups, G, d)
+    exact = np.stack([qs[h].astype(np.float64) @ keys[h].astype(np.float64).T for h in range(groups)])
+    errs = {}
+    for where in ("high", "low"):
+        xp, qp = [], []
+        for h in range(groups):
+            rest = np.setdiff1d(np.arange(d), chans[h])
+            perm = np.concatenate([chans[h], rest]) if where == "high" else np.concatenate([rest, chans[h]])
+            xp.append(keys[h][:, perm])
+            qp.append(qs[h][:, perm])
+        xd = U.to_device(np.concatenate(xp).astype(np.float32), False)
+        qd = U.to_device(np.concatenate(qp).astype(np.float32), False)
+        errs[where] = _rel_logit_mse(_split_logits(d, 3, 2, cfg, xd, qd, groups, G, T), exact)
+    print(f"[2.5 bits, outliers in the 3-bit group: {errs['high']:.4f}, in the 2-bit group: {errs['low']:.4f}]",
+          flush=True)
+    assert errs["high"] < errs["low"]
