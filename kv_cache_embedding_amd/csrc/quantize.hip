@@ -20,6 +20,15 @@
 //   GEMM2  Y^T = S'~ R'^T, passes S'_hi r_hi + S'_lo r_hi + S'_hi r_lo; the sign of each
 //          output is shifted into half words the same way.
 //   Lanes h = 0 / 1 of a vector swap half words and store whole words (canonical layout).
+//
+// Split mode (fractional bit rates: channels 0..63 and 64..127 as two TurboQuant instances
+// of d = 64 at B0 and B1 bits): the two rotations and QJL matrices act on the 128-vector as
+// block-diagonal matrices, so the same two GEMMs run on fragments assembled in LDS from the
+// two 64-d parameter blocks (zeros off the diagonal blocks).  Lane half h already holds the
+// channels of group h, so its half of the squared norm is that group's nu^2; row tiles 0, 1
+// (coordinates of group 0) are bucketized with group 0's codebook and nu, tiles 2, 3 with
+// group 1's; the residual of each group is projected by its own block of S', whose signs
+// do not depend on the group's scale.  Lane half h stores group h's words, nu and gamma.
 #include "tq_internal.h"
 
 namespace tq {
@@ -41,13 +50,110 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Row of the 32-row tile held by MFMA output lane rho % 32 (the fragment row permutation).
+__device__ __forceinline__ int row_coord(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
+
+// Bucketize one 32-row tile of u (this lane's 16 coordinates of it) against nu-scaled
+// positive thresholds T and centroids M: the index planes' half words into hb[0 .. BITS-2]
+// (the top index bit is the sign of u; hb[BITS-1] is left for the QJL signs), the residual as
+// bf16 hi/lo B operands of GEMM2 (K steps 2 mt, 2 mt + 1) and its squared norm into g2.
+template <int BITS>
+__device__ __forceinline__ void bucketize_tile(const f32x16& Um, const float* T, const float* M,
+                                               uint32_t* hb, bf16x8* rh, bf16x8* rl, float& g2) {
+  // Index bits from |u| against the positive thresholds (a binary search over the
+  // magnitude index k of the level), the level's sign from u: for u >= 0 the index is
+  // L/2 + k, for u < 0 it is L/2 - 1 - k, i.e. the bits of k complemented.  So the index
+  // planes are the k planes xor the sign plane, applied once per 16-coordinate word.
+  uint32_t w0 = 0, w1 = 0, ws = 0;
+  float rr[16];
+#pragma unroll
+  for (int r = 15; r >= 0; --r) {
+    const float u = Um[r];
+    const float a = fabsf(u);
+    ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(u), 31);   // 1 = u < 0
+    float cm;
+    if constexpr (BITS == 2) {
+      cm = M[0];
+    } else if constexpr (BITS == 3) {
+      const bool k0 = a >= T[0];
+      cm = k0 ? M[1] : M[0];
+      w0 = (w0 << 1) | uint32_t(k0);
+    } else {
+      const bool k1 = a >= T[1];
+      const bool k0 = a >= (k1 ? T[2] : T[0]);
+      const float mlo = k0 ? M[1] : M[0];
+      const float mhi = k0 ? M[3] : M[2];
+      cm = k1 ? mhi : mlo;
+      w0 = (w0 << 1) | uint32_t(k0);
+      w1 = (w1 << 1) | uint32_t(k1);
+    }
+    const float c = __uint_as_float((__float_as_uint(cm) & 0x7fffffffu) | (__float_as_uint(u) & 0x80000000u));
+    const float rv = u - c;
+    rr[r] = rv;
+    g2 = fmaf(rv, rv, g2);
+  }
+  const uint32_t sgn = ws & 0xffffu;          // 1 = u < 0
+  const uint32_t wsign = ~ws & 0xffffu;       // sign plane: 1 = u >= 0
+  if constexpr (BITS == 2) {
+    hb[0] = wsign;
+  } else if constexpr (BITS == 3) {
+    hb[0] = w0 ^ sgn;
+    hb[1] = wsign;
+  } else {
+    hb[0] = w0 ^ sgn;
+    hb[1] = w1 ^ sgn;
+    hb[2] = wsign;
+  }
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      // hi = RNE(v); lo = RNE(v - hi): converted two at a time
+      const f32x2 v2 = {rr[8 * hf + e], rr[8 * hf + e + 1]};
+      const bf16x2 h2 = __builtin_convertvector(v2, bf16x2);
+      const uint32_t hb2 = __builtin_bit_cast(uint32_t, h2);
+      const f32x2 hf2 = {__uint_as_float(hb2 << 16), __uint_as_float(hb2 & 0xffff0000u)};
+      const bf16x2 l2 = __builtin_convertvector(v2 - hf2, bf16x2);
+      rh[hf][e] = h2[0];
+      rh[hf][e + 1] = h2[1];
+      rl[hf][e] = l2[0];
+      rl[hf][e + 1] = l2[1];
+    }
+  }
+}
+
+// 2 P words of one lane (word k P + p taken from out[k PM + p]) to dst: 16-byte stores when P
+// is even (dst is then 16-byte aligned), 8-byte ones otherwise.
+template <int P, int PM>
+__device__ __forceinline__ void store_words(uint32_t* dst, const uint32_t* out) {
+  uint32_t o[2 * P];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int p = 0; p < P; ++p) o[k * P + p] = out[k * PM + p];
+  if constexpr (P % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < P / 2; ++i)
+      reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < P; ++i) reinterpret_cast<uint2*>(dst)[i] = make_uint2(o[2 * i], o[2 * i + 1]);
+  }
+}
+
 // MSE: the MSE quantizer alone (attention values): GEMM1 and the index planes only, b-1
-// planes per coordinate group, nu but no gamma.
-template <int BITS, bool F32IN, bool MSE>
+// planes per coordinate group, nu but no gamma.  Without SPLIT, B0 == B1 is the b of params
+// and params1, codes1, nu1_out, gamma1_out are unused; with SPLIT, params / params1 are the
+// d = 64 blocks of channel groups 0 / 1 (gmat_off: their bf16 matrices) and group 1's
+// results go to codes1, nu1_out, gamma1_out.
+template <int B0, int B1, bool F32IN, bool MSE, bool SPLIT>
 __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
-    const unsigned char* __restrict__ params, size_t frag_off, const void* __restrict__ xin,
-    long n, uint32_t* __restrict__ codes, float* __restrict__ nu_out,
-    float* __restrict__ gamma_out) {
+    const unsigned char* __restrict__ params, const unsigned char* __restrict__ params1,
+    size_t frag_off, size_t gmat_off, const void* __restrict__ xin, long n,
+    uint32_t* __restrict__ codes, float* __restrict__ nu_out, float* __restrict__ gamma_out,
+    uint32_t* __restrict__ codes1, float* __restrict__ nu1_out, float* __restrict__ gamma1_out) {
+  static_assert(SPLIT || B0 == B1, "one bit width without split");
+  static_assert(!(SPLIT && MSE), "split mode encodes keys (MSE + QJL)");
   __shared__ uint4 frag[2 * FRAG_U4];  // [0, FRAG_U4): Pi~ fragments; then S'~ fragments
   __shared__ int next_tile;            // work queue of this workgroup's tile range
 
@@ -84,20 +190,49 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     for (int i = 0; i < NRAW; ++i) raw[i] = p[i];
   };
   if (tile < t_end) load_tile(tile);      // in flight while the fragments fill LDS
-  {
+  if constexpr (!SPLIT) {
     const uint4* src = reinterpret_cast<const uint4*>(params + frag_off);
     for (int i = threadIdx.x; i < 2 * FRAG_U4; i += WAVES * 64) frag[i] = src[i];
+  } else {
+    // fragment element e of lane ln: Pi~ [s][mt][pass] holds Pi[32 mt + row_coord(ln % 32)]
+    // [64 (ln / 32) + 8 s + e]; S'~ [mt][s][pass] holds S'[32 mt + row_coord(ln % 32)]
+    // [32 (s / 2) + 16 (ln / 32) + 8 (s % 2) + e]; block g of the block-diagonal matrices is
+    // group g's 64 x 64 matrix (row-major bf16 hi and lo: Pi at 0 and 4096 elements, S' at
+    // 8192 and 12288), every other block zero
+    const uint16_t* gm[2] = {reinterpret_cast<const uint16_t*>(params + gmat_off),
+                             reinterpret_cast<const uint16_t*>(params1 + gmat_off)};
+    for (int i = threadIdx.x; i < 2 * FRAG_U4; i += WAVES * 64) {
+      const bool is_s = i >= FRAG_U4;
+      const int k = is_s ? i - FRAG_U4 : i;
+      const int ln = k & 63, j = k >> 6, pass = j & 1, m = j >> 1;
+      const int mt = is_s ? m >> 3 : m & 3;
+      const int st = is_s ? m & 7 : m >> 2;
+      const int rg = mt >> 1;                               // group of the output row
+      const int cg = is_s ? st >> 2 : ln >> 5;              // group of the input column
+      const int col = is_s ? 32 * (st >> 1) + 16 * (ln >> 5) + 8 * (st & 1) - 64 * cg : 8 * st;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (rg == cg) {
+        const int row = 32 * mt + row_coord(ln & 31) - 64 * rg;
+        v = *reinterpret_cast<const uint4*>(gm[rg] + (is_s ? 8192 : 0) + pass * 4096 + row * 64 + col);
+      }
+      frag[i] = v;
+    }
   }
   __syncthreads();
 
   const Header* hdr = reinterpret_cast<const Header*>(params);
-  constexpr int L = 1 << (BITS - 1);
-  float tp[L / 2 > 1 ? L / 2 - 1 : 1];   // positive thresholds
-  float mp[L / 2];                        // positive centroids
+  const Header* hdr1 = reinterpret_cast<const Header*>(SPLIT ? params1 : params);
+  constexpr int L0 = 1 << (B0 - 1), L1 = 1 << (B1 - 1);
+  float tp0[L0 / 2 > 1 ? L0 / 2 - 1 : 1], tp1[L1 / 2 > 1 ? L1 / 2 - 1 : 1];   // positive thresholds
+  float mp0[L0 / 2], mp1[L1 / 2];                                             // positive centroids
 #pragma unroll
-  for (int k = 0; k < L / 2 - 1; ++k) tp[k] = hdr->tpos[k];
+  for (int k = 0; k < L0 / 2 - 1; ++k) tp0[k] = hdr->tpos[k];
 #pragma unroll
-  for (int k = 0; k < L / 2; ++k) mp[k] = hdr->mpos[k];
+  for (int k = 0; k < L0 / 2; ++k) mp0[k] = hdr->mpos[k];
+#pragma unroll
+  for (int k = 0; k < L1 / 2 - 1; ++k) tp1[k] = hdr1->tpos[k];
+#pragma unroll
+  for (int k = 0; k < L1 / 2; ++k) mp1[k] = hdr1->mpos[k];
 
   while (tile < t_end) {
     const long vec = tile * VPW + (lane & 31);
@@ -133,9 +268,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
         }
       }
     }
-    ss += __shfl_xor(ss, 32);
-    const float nu = sqrtf(ss);
-    const float sc = nu > 0.f ? nu : 1.f;   // zero vector: u is taken as 0, grid unscaled
+    // squared norms of group 0 (channels 0..63, lane half 0) and group 1 (half 1); without
+    // SPLIT both are the whole vector's
+    const float ss_other = __shfl_xor(ss, 32);
+    const float ssa = SPLIT ? (kh == 0 ? ss : ss_other) : ss + ss_other;
+    const float ssb = SPLIT ? (kh == 0 ? ss_other : ss) : ssa;
+    const float nu0 = sqrtf(ssa), nu1 = sqrtf(ssb);
+    const float sc0 = nu0 > 0.f ? nu0 : 1.f;   // zero vector: u is taken as 0, grid unscaled
+    const float sc1 = nu1 > 0.f ? nu1 : 1.f;
 
     // ---- GEMM1: U^T = Pi~ X^T, one 32-row tile at a time
     f32x16 U[4];
@@ -169,81 +309,33 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     // ---- bucketize + residual against nu-scaled thresholds (u is never divided by nu).
     // Bits of the sign plane are the float sign bits of u, shifted in with v_alignbit and
     // inverted at the end (u is never -0: the MFMA sum starts from +0).
-    float T[L / 2 > 1 ? L / 2 - 1 : 1], M[L / 2];
+    float T0[L0 / 2 > 1 ? L0 / 2 - 1 : 1], M0[L0 / 2], T1[L1 / 2 > 1 ? L1 / 2 - 1 : 1], M1[L1 / 2];
 #pragma unroll
-    for (int k = 0; k < L / 2 - 1; ++k) T[k] = tp[k] * sc;
+    for (int k = 0; k < L0 / 2 - 1; ++k) T0[k] = tp0[k] * sc0;
 #pragma unroll
-    for (int k = 0; k < L / 2; ++k) M[k] = mp[k] * sc;
+    for (int k = 0; k < L0 / 2; ++k) M0[k] = mp0[k] * sc0;
+#pragma unroll
+    for (int k = 0; k < L1 / 2 - 1; ++k) T1[k] = tp1[k] * sc1;
+#pragma unroll
+    for (int k = 0; k < L1 / 2; ++k) M1[k] = mp1[k] * sc1;
 
-    uint32_t hb[BITS][4];     // [plane][row tile]: this lane's 16-bit half words
+    uint32_t hb[4][4];        // [row tile][plane]: this lane's 16-bit half words
     bf16x8 rh[8], rl[8];      // GEMM2 B operands, K step 2 mt + half
-    float g2 = 0.f;
+    float g2a = 0.f, g2b = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      // Index bits from |u| against the positive thresholds (a binary search over the
-      // magnitude index k of the level), the level's sign from u: for u >= 0 the index is
-      // L/2 + k, for u < 0 it is L/2 - 1 - k, i.e. the bits of k complemented.  So the index
-      // planes are the k planes xor the sign plane, applied once per 16-coordinate word.
-      uint32_t w0 = 0, w1 = 0, ws = 0;
-      float rr[16];
-#pragma unroll
-      for (int r = 15; r >= 0; --r) {
-        const float u = U[mt][r];
-        const float a = fabsf(u);
-        ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(u), 31);   // 1 = u < 0
-        float cm;
-        if constexpr (BITS == 2) {
-          cm = M[0];
-        } else if constexpr (BITS == 3) {
-          const bool k0 = a >= T[0];
-          cm = k0 ? M[1] : M[0];
-          w0 = (w0 << 1) | uint32_t(k0);
-        } else {
-          const bool k1 = a >= T[1];
-          const bool k0 = a >= (k1 ? T[2] : T[0]);
-          const float mlo = k0 ? M[1] : M[0];
-          const float mhi = k0 ? M[3] : M[2];
-          cm = k1 ? mhi : mlo;
-          w0 = (w0 << 1) | uint32_t(k0);
-          w1 = (w1 << 1) | uint32_t(k1);
-        }
-        const float c = __uint_as_float((__float_as_uint(cm) & 0x7fffffffu) | (__float_as_uint(u) & 0x80000000u));
-        const float rv = u - c;
-        rr[r] = rv;
-        g2 = fmaf(rv, rv, g2);
-      }
-      const uint32_t sgn = ws & 0xffffu;          // 1 = u < 0
-      const uint32_t wsign = ~ws & 0xffffu;       // sign plane: 1 = u >= 0
-      if constexpr (BITS == 2) {
-        hb[0][mt] = wsign;
-      } else if constexpr (BITS == 3) {
-        hb[0][mt] = w0 ^ sgn;
-        hb[1][mt] = wsign;
-      } else {
-        hb[0][mt] = w0 ^ sgn;
-        hb[1][mt] = w1 ^ sgn;
-        hb[2][mt] = wsign;
-      }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          // hi = RNE(v); lo = RNE(v - hi): converted two at a time
-          const f32x2 v2 = {rr[8 * hf + e], rr[8 * hf + e + 1]};
-          const bf16x2 h2 = __builtin_convertvector(v2, bf16x2);
-          const uint32_t hb2 = __builtin_bit_cast(uint32_t, h2);
-          const f32x2 hf2 = {__uint_as_float(hb2 << 16), __uint_as_float(hb2 & 0xffff0000u)};
-          const bf16x2 l2 = __builtin_convertvector(v2 - hf2, bf16x2);
-          rh[2 * mt + hf][e] = h2[0];
-          rh[2 * mt + hf][e + 1] = h2[1];
-          rl[2 * mt + hf][e] = l2[0];
-          rl[2 * mt + hf][e + 1] = l2[1];
-        }
-      }
+    for (int mt = 0; mt < 2; ++mt) {
+      bucketize_tile<B0>(U[mt], T0, M0, hb[mt], rh + 2 * mt, rl + 2 * mt, g2a);
       __builtin_amdgcn_sched_barrier(0);
     }
-    g2 += __shfl_xor(g2, 32);
-    const float gamma = sqrtf(g2) / sc;
+#pragma unroll
+    for (int mt = 2; mt < 4; ++mt) {
+      bucketize_tile<B1>(U[mt], T1, M1, hb[mt], rh + 2 * mt, rl + 2 * mt, SPLIT ? g2b : g2a);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    g2a += __shfl_xor(g2a, 32);
+    if constexpr (SPLIT) g2b += __shfl_xor(g2b, 32);
+    const float gamma0 = sqrtf(g2a) / sc0;
+    const float gamma1 = SPLIT ? sqrtf(g2b) / sc1 : gamma0;
 
     // ---- GEMM2: Y^T = S'~ R'^T, one 32-row tile of projections at a time; the sign
     //      bits of y are shifted in the same way (y is never -0 either)
@@ -271,35 +363,41 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
         uint32_t w = 0;
 #pragma unroll
         for (int r = 15; r >= 0; --r) w = __builtin_amdgcn_alignbit(w, __float_as_uint(Y[t][r]), 31);
-        hb[BITS - 1][mp + t] = ~w & 0xffffu;
+        hb[mp + t][(mp + t < 2 ? B0 : B1) - 1] = ~w & 0xffffu;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- assemble whole words: half h = 0 finishes row tiles 0,1; h = 1 tiles 2,3
-    constexpr int P = MSE ? BITS - 1 : BITS;   // planes stored per coordinate group
-    uint32_t out[2 * P];
+    constexpr int P0 = MSE ? B0 - 1 : B0, P1 = MSE ? B1 - 1 : B1;   // planes per coordinate group
+    constexpr int PM = P0 > P1 ? P0 : P1;
+    uint32_t out[2 * PM];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const uint32_t send = kh == 0 ? hb[p][2 + k] : hb[p][k];
+      for (int p = 0; p < PM; ++p) {
+        // planes a group does not have are sent but not stored
+        const uint32_t send = kh == 0 ? (p < P1 ? hb[2 + k][p] : 0u) : (p < P0 ? hb[k][p] : 0u);
         const uint32_t recv = __shfl_xor(send, 32);
-        out[k * P + p] = kh == 0 ? (hb[p][k] | (recv << 16)) : (recv | (hb[p][2 + k] << 16));
+        out[k * PM + p] = kh == 0 ? ((p < P0 ? hb[k][p] : 0u) | (recv << 16))
+                                  : (recv | ((p < P1 ? hb[2 + k][p] : 0u) << 16));
       }
     }
     if (valid) {
-      uint32_t* dst = codes + (vec * 4 + 2 * kh) * P;
-      if constexpr (P % 2 == 0) {   // 16-byte aligned: 2 P words at a multiple of 8 P words
-#pragma unroll
-        for (int i = 0; i < P / 2; ++i)
-          reinterpret_cast<uint4*>(dst)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+      if constexpr (!SPLIT) {
+        // 2 P words at a multiple of 8 P words (16-byte aligned when P is even)
+        store_words<P0, PM>(codes + (vec * 4 + 2 * kh) * P0, out);
+        if (kh == 0) {
+          nu_out[vec] = nu0;
+          if constexpr (!MSE) gamma_out[vec] = gamma0;
+        }
+      } else if (kh == 0) {
+        store_words<P0, PM>(codes + vec * 2 * P0, out);
+        nu_out[vec] = nu0;
+        gamma_out[vec] = gamma0;
       } else {
-#pragma unroll
-        for (int i = 0; i < P; ++i) reinterpret_cast<uint2*>(dst)[i] = make_uint2(out[2 * i], out[2 * i + 1]);
-      }
-      if (kh == 0) {
-        nu_out[vec] = nu;
-        if constexpr (!MSE) gamma_out[vec] = gamma;
+        store_words<P1, PM>(codes1 + vec * 2 * P1, out);
+        nu1_out[vec] = nu1;
+        gamma1_out[vec] = gamma1;
       }
     }
     tile = next;
@@ -319,16 +417,30 @@ int cu_count() {
   return cached;
 }
 
+int grid_for(int64_t n) {
+  const long ntiles = (n + VPW - 1) / VPW;
+  const long need = (ntiles + WAVES - 1) / WAVES;
+  return int(need < cu_count() ? need : cu_count());
+}
+
 template <int BITS, bool F32IN, bool MSE = false>
 hipError_t launch(const void* params, const void* x, int64_t n, uint32_t* codes, float* nu,
                   float* gamma, hipStream_t s) {
+  hipLaunchKernelGGL((quantize_d128_kernel<BITS, BITS, F32IN, MSE, false>), dim3(grid_for(n)),
+                     dim3(WAVES * 64), 0, s, static_cast<const unsigned char*>(params), nullptr,
+                     Layout(D, BITS).off_qfrag, size_t(0), x, long(n), codes, nu, gamma, nullptr,
+                     nullptr, nullptr);
+  return hipGetLastError();
+}
 
-  const long ntiles = (n + VPW - 1) / VPW;
-  const long need = (ntiles + WAVES - 1) / WAVES;
-  const int grid = int(need < cu_count() ? need : cu_count());
-  hipLaunchKernelGGL((quantize_d128_kernel<BITS, F32IN, MSE>), dim3(grid), dim3(WAVES * 64), 0, s,
-                     static_cast<const unsigned char*>(params), Layout(D, BITS).off_qfrag, x,
-                     long(n), codes, nu, gamma);
+template <int B0, int B1, bool F32IN>
+hipError_t launch_split(const void* params0, const void* params1, const void* x, int64_t n,
+                        uint32_t* codes0, float* nu0, float* gamma0, uint32_t* codes1, float* nu1,
+                        float* gamma1, hipStream_t s) {
+  hipLaunchKernelGGL((quantize_d128_kernel<B0, B1, F32IN, false, true>), dim3(grid_for(n)),
+                     dim3(WAVES * 64), 0, s, static_cast<const unsigned char*>(params0),
+                     static_cast<const unsigned char*>(params1), size_t(0), Layout(64, B0).off_gmat, x,
+                     long(n), codes0, nu0, gamma0, codes1, nu1, gamma1);
   return hipGetLastError();
 }
 
@@ -364,6 +476,28 @@ hipError_t launch_quantize_d128_mse(const void* params, int b, const void* x, in
                        : launch<4, false, true>(params, x, n, codes, nu, nullptr, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace tq
+
+namespace tq {
+
+hipError_t launch_quantize_d128_split(const void* params0, const void* params1, int b0, int b1,
+                                      const void* x, int x_dtype, int64_t n, uint32_t* codes0,
+                                      float* nu0, float* gamma0, uint32_t* codes1, float* nu1,
+                                      float* gamma1, hipStream_t s) {
+  const bool f32 = x_dtype == 0;
+#define TQ_SPLIT_CASE(B0, B1)                                                                       \
+  if (b0 == B0 && b1 == B1)                                                                         \
+    return f32 ? launch_split<B0, B1, true>(params0, params1, x, n, codes0, nu0, gamma0, codes1, nu1, \
+                                            gamma1, s)                                              \
+               : launch_split<B0, B1, false>(params0, params1, x, n, codes0, nu0, gamma0, codes1,     \
+                                             nu1, gamma1, s);
+  TQ_SPLIT_CASE(2, 2) TQ_SPLIT_CASE(2, 3) TQ_SPLIT_CASE(2, 4)
+  TQ_SPLIT_CASE(3, 2) TQ_SPLIT_CASE(3, 3) TQ_SPLIT_CASE(3, 4)
+  TQ_SPLIT_CASE(4, 2) TQ_SPLIT_CASE(4, 3) TQ_SPLIT_CASE(4, 4)
+#undef TQ_SPLIT_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tq
