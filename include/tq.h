@@ -230,8 +230,10 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
  * and half at b give b + 1/2 bits per channel (d = 128: d0 = 64, b0 = b + 1, b1 = b).  Any
  * other assignment of channels to groups is a permutation applied to both queries and keys,
  * which leaves <q, x> unchanged, so the producer of q and x can apply it.
- * Both groups run the tiled encoder and the general scoring path, reading their channels in
- * place (rows d apart).
+ * A 64 + 64 split of d = 128 encodes both groups in one pass of the fused d = 128 encoder
+ * (the two rotations and QJL matrices as block-diagonal operands); other splits run the
+ * tiled encoder once per group.  Scoring runs the general path once per group, the second
+ * launch adding to the first's logits.  Channels are read in place (rows d apart).
  *
  * tq_quantize_split — encode x [n][d] (x_dtype as for tq_quantize) into
  *   codes0 [n][d0/32][b0], nu0, gamma0 [n]     (channels 0 .. d0-1, params0)

@@ -3,17 +3,17 @@
 //
 // Estimate ([review, problem statement]: the query is exact, the key quantized, unbiased;
 // [tldr, step 2]):
-//   l = nu (<Pi q, chat> + alpha gamma <S q, 2z - 1>),  alpha = sqrt(pi/2)/m,
+//   l = nu (<Pi q, chat> + alpha gamma <S q, 2z - 1>),  alpha from the parameter header,
 // with <S q, 2z - 1> = 2 sum_{t : z_t = 1} (S q)_t - sum_t (S q)_t, so per coordinate a key
 // needs one centroid times (Pi q)_t and one sign-bit-selected (S q)_t for each head.
 //
-// generic_qprep_kernel: qh = Pi q and sh = S q in float32, one workgroup per (group, head);
-//   a wave forms one output as a 64-lane strided dot product over one row of Pi or S (rows
-//   are contiguous), and the workgroup sums sh.
+// generic_qprep_kernel: qh = Pi q and sh = S q in float32, a tiled NT product of the query
+//   rows with the stacked rows of Pi and S.
 // generic_score_kernel: one lane per key and HB heads per pass.  The key's plane words of a
-//   32-coordinate group are loaded once; per coordinate the index bits pick the centroid
-//   from an LDS table and the sign bit weights sh.  The query values are the same for every
-//   lane of a workgroup, so they come in through scalar loads.
+//   32-coordinate group come in with one vector load; per coordinate the index bits pick
+//   the centroid by a register select tree and the sign bit weights sh.  The query values
+//   are the same for every lane of a workgroup: staged in LDS and read as broadcasts; the
+//   workgroup also sums the staged sh for the -sum_t (S q)_t term.
 #include "tq_internal.h"
 
 namespace tq {
@@ -22,56 +22,96 @@ namespace {
 constexpr int HB = 4;        // query heads per pass of the scoring kernel
 constexpr int KEYS = 256;    // keys per workgroup (one per lane)
 
+constexpr int QR = 16;       // query prep tile: query rows
+constexpr int QO = 64;       //                  outputs (rows of the stacked [Pi; S])
+constexpr int QK = 64;       //                  K staged per round
+
+// qs[row][o] = <M_o, q_row> for the stacked M = [Pi; S] (o < d: Pi q, o >= d: S q): an
+// NT product of the query rows with the rows of M, one workgroup per QR x QO tile (64
+// outputs never straddle Pi and S since d is a multiple of 64).  Thread t accumulates
+// output t % 64 of rows 4 (t / 64) .. +3 over K, both operands staged in LDS with padded
+// rows (the M rows are read at a stride of QK + 1 words: conflict-free).
 __global__ __launch_bounds__(256) void generic_qprep_kernel(
     const unsigned char* __restrict__ params, size_t off_pi, size_t off_s, int d, long qpitch,
-    const void* __restrict__ q, int q_f32, float* __restrict__ qs, float* __restrict__ ssum) {
-  extern __shared__ float qv[];            // the query row, d floats
-  __shared__ float red[4];
-  const long row = blockIdx.x;             // (group, head) = group * G + head
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int k = tid; k < d; k += 256) {
-    if (q_f32) {
-      qv[k] = static_cast<const float*>(q)[row * qpitch + k];
-    } else {
-      const uint32_t hbits = static_cast<const uint16_t*>(q)[row * qpitch + k];
-      qv[k] = __uint_as_float(hbits << 16);
+    const void* __restrict__ q, int q_f32, long rows, float* __restrict__ qs) {
+  __shared__ float Qs[QR][QK + 1];
+  __shared__ float Ms[QO][QK + 1];
+  const int tid = threadIdx.x;
+  const long ntile_o = 2 * d / QO;
+  const long r0 = long(blockIdx.x / ntile_o) * QR;
+  const int o0 = int(blockIdx.x % ntile_o) * QO;
+  const float* M = o0 < d ? reinterpret_cast<const float*>(params + off_pi) + size_t(o0) * d
+                          : reinterpret_cast<const float*>(params + off_s) + size_t(o0 - d) * d;
+  const int o = tid & 63, rq = tid >> 6;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < d; k0 += QK) {
+    __syncthreads();                       // the previous round's tiles are no longer read
+    for (int i = tid; i < QR * QK; i += 256) {
+      const int r = i / QK, k = i % QK;
+      const long row = r0 + r;
+      float v = 0.f;
+      if (row < rows) {
+        const size_t at = size_t(row) * qpitch + k0 + k;
+        v = q_f32 ? static_cast<const float*>(q)[at]
+                  : __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at]) << 16);
+      }
+      Qs[r][k] = v;
+    }
+    for (int i = tid; i < QO * QK; i += 256) Ms[i / QK][i % QK] = M[size_t(i / QK) * d + k0 + i % QK];
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < QK; ++k) {
+      const float m = Ms[o][k];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(m, Qs[4 * rq + j][k], acc[j]);
     }
   }
-  __syncthreads();
-  const float* Pi = reinterpret_cast<const float*>(params + off_pi);
-  const float* S = reinterpret_cast<const float*>(params + off_s);
-  float sacc = 0.f;
-  for (int o = wave; o < 2 * d; o += 4) {  // output o: row o of Pi (o < d), else row o - d of S
-    const bool is_s = o >= d;
-    const int r = is_s ? o - d : o;
-    const float* m = (is_s ? S : Pi) + size_t(r) * d;
-    float acc = 0.f;
-    for (int k = lane; k < d; k += 64) acc = fmaf(m[k], qv[k], acc);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) qs[(row * 2 + (is_s ? 1 : 0)) * d + r] = acc;
-    if (is_s) sacc += acc;
+  for (int j = 0; j < 4; ++j) {
+    const long row = r0 + 4 * rq + j;
+    if (row < rows) qs[size_t(row) * 2 * d + o0 + o] = acc[j];
   }
-  if (lane == 0) red[wave] = sacc;
-  __syncthreads();
-  if (tid == 0) ssum[row] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Centroid of the index held in bits b0 (low) .. b2 of one coordinate: a select tree over the
+// levels held in registers (no memory access on the per-coordinate path).
+template <int BITS>
+__device__ __forceinline__ float centroid(const float* C, uint32_t p0, uint32_t p1, uint32_t p2) {
+  if constexpr (BITS == 2) {
+    return p0 ? C[1] : C[0];
+  } else if constexpr (BITS == 3) {
+    const float lo = p0 ? C[1] : C[0], hi = p0 ? C[3] : C[2];
+    return p1 ? hi : lo;
+  } else {
+    const float a = p0 ? C[1] : C[0], b = p0 ? C[3] : C[2];
+    const float c = p0 ? C[5] : C[4], e = p0 ? C[7] : C[6];
+    const float lo = p1 ? b : a, hi = p1 ? e : c;
+    return p2 ? hi : lo;
+  }
 }
 
 // grid: one workgroup per (group, head pass, block of KEYS keys), flattened into x.  ACC adds
-// the estimate to the logits already there (the channel groups of a fractional rate).
+// the estimate to the logits already there (the channel groups of a fractional rate).  The
+// pass's query values (HB heads of Pi q and S q) are staged in LDS, CH coordinates at a
+// time, as one float4 per coordinate and matrix: every lane reads the same address, a
+// broadcast.
 template <int BITS, bool PROD, bool ACC>
 __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     const unsigned char* __restrict__ params, const float* __restrict__ qs,
-    const float* __restrict__ ssum, const uint32_t* __restrict__ codes,
-    const float* __restrict__ nu, const float* __restrict__ gamma, int d, long G, long T,
-    long kblocks, long passes, float* __restrict__ logits) {
+    const uint32_t* __restrict__ codes, const float* __restrict__ nu,
+    const float* __restrict__ gamma, int d, long G, long T, long kblocks, long passes,
+    float* __restrict__ logits) {
+  static_assert(HB == 4, "one float4 of query values per coordinate");
   constexpr int L = 1 << (BITS - 1);
+  constexpr int CH = KEYS;                 // coordinates staged per round (one per thread)
+  __shared__ float4 qsh[2][CH];            // [0]: Pi q, [1]: S q of the pass's 4 heads
+  __shared__ float4 red[KEYS / 64];        // sum_t (S q)_t: per-wave partial sums
   const Header* hdr = reinterpret_cast<const Header*>(params);
-  __shared__ float cen[L];
-  const int tid = threadIdx.x;
-  if (tid < L) cen[tid] = hdr->cen[tid];
+  float C[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) C[i] = hdr->cen[i];
   const float alpha = hdr->alpha;
-  __syncthreads();
+  const int tid = threadIdx.x;
 
   const long blk = blockIdx.x;
   const long kb = blk % kblocks;
@@ -91,36 +131,86 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     const long h = h0 + (hh < nh ? hh : nh - 1);
     qrow[hh] = qs + size_t(g * G + h) * 2 * d;
   }
-  float mse[HB], zsum[HB];
+  float4 mse = make_float4(0.f, 0.f, 0.f, 0.f), zs = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 spart = make_float4(0.f, 0.f, 0.f, 0.f);   // this thread's staged S q values, summed
+  for (int c0 = 0; c0 < d; c0 += CH) {
+    const int cn = d - c0 < CH ? d - c0 : CH;
+    __syncthreads();                       // the previous round's values are no longer read
+    if (tid < cn) {
+      const int c = c0 + tid;
+      qsh[0][tid] = make_float4(qrow[0][c], qrow[1][c], qrow[2][c], qrow[3][c]);
+      if constexpr (PROD) {
+        const float4 sv = make_float4(qrow[0][d + c], qrow[1][d + c], qrow[2][d + c], qrow[3][d + c]);
+        qsh[1][tid] = sv;
+        spart.x += sv.x;
+        spart.y += sv.y;
+        spart.z += sv.z;
+        spart.w += sv.w;
+      }
+    }
+    __syncthreads();
+    for (int w = 0; w < cn / 32; ++w) {
+      const uint32_t* src = kc + size_t(c0 / 32 + w) * BITS;
+      uint32_t pl[4] = {0u, 0u, 0u, 0u};
+      if constexpr (BITS == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        pl[0] = v.x; pl[1] = v.y; pl[2] = v.z; pl[3] = v.w;
+      } else if constexpr (BITS == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        pl[0] = v.x; pl[1] = v.y;
+      } else {
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) mse[hh] = zsum[hh] = 0.f;
-  for (int w = 0; w < words; ++w) {
-    uint32_t pl[BITS];
-#pragma unroll
-    for (int p = 0; p < BITS; ++p) pl[p] = kc[w * BITS + p];
-#pragma unroll 4
-    for (int e = 0; e < 32; ++e) {
-      const int c0 = 32 * w + e;
-      uint32_t idx = 0;
-#pragma unroll
-      for (int p = 0; p < BITS - 1; ++p) idx |= ((pl[p] >> e) & 1u) << p;
-      const float c = cen[idx];
-      const float zf = float((pl[BITS - 1] >> e) & 1u);
-#pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        mse[hh] = fmaf(qrow[hh][c0], c, mse[hh]);
-        if constexpr (PROD) zsum[hh] = fmaf(qrow[hh][d + c0], zf, zsum[hh]);
+        for (int p = 0; p < BITS; ++p) pl[p] = src[p];
+      }
+#pragma unroll 8
+      for (int e = 0; e < 32; ++e) {
+        const uint32_t p0 = (pl[0] >> e) & 1u;
+        const uint32_t p1 = BITS > 2 ? (pl[1] >> e) & 1u : 0u;
+        const uint32_t p2 = BITS > 3 ? (pl[2] >> e) & 1u : 0u;
+        const float c = centroid<BITS>(C, p0, p1, p2);
+        const float4 a = qsh[0][32 * w + e];
+        mse.x = fmaf(a.x, c, mse.x);
+        mse.y = fmaf(a.y, c, mse.y);
+        mse.z = fmaf(a.z, c, mse.z);
+        mse.w = fmaf(a.w, c, mse.w);
+        if constexpr (PROD) {
+          const float zf = float((pl[BITS - 1] >> e) & 1u);
+          const float4 b = qsh[1][32 * w + e];
+          zs.x = fmaf(b.x, zf, zs.x);
+          zs.y = fmaf(b.y, zf, zs.y);
+          zs.z = fmaf(b.z, zf, zs.z);
+          zs.w = fmaf(b.w, zf, zs.w);
+        }
       }
     }
   }
+  float s4[HB] = {0.f, 0.f, 0.f, 0.f};    // sum_t (S q)_t of the 4 heads (same order everywhere)
+  if constexpr (PROD) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      spart.x += __shfl_xor(spart.x, off);
+      spart.y += __shfl_xor(spart.y, off);
+      spart.z += __shfl_xor(spart.z, off);
+      spart.w += __shfl_xor(spart.w, off);
+    }
+    if ((tid & 63) == 0) red[tid >> 6] = spart;
+    __syncthreads();
+    const float4 a = red[0], b = red[1], c = red[2], e = red[3];
+    s4[0] = (a.x + b.x) + (c.x + e.x);
+    s4[1] = (a.y + b.y) + (c.y + e.y);
+    s4[2] = (a.z + b.z) + (c.z + e.z);
+    s4[3] = (a.w + b.w) + (c.w + e.w);
+  }
   if (!valid) return;
   const float n_k = nu[key], g_k = gamma[key];
+  const float m4[HB] = {mse.x, mse.y, mse.z, mse.w};
+  const float z4[HB] = {zs.x, zs.y, zs.z, zs.w};
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     if (hh >= nh) break;
     const long h = h0 + hh;
-    float l = mse[hh];
-    if constexpr (PROD) l = fmaf(alpha * g_k, 2.f * zsum[hh] - ssum[g * G + h], l);
+    float l = m4[hh];
+    if constexpr (PROD) l = fmaf(alpha * g_k, 2.f * z4[hh] - s4[hh], l);
     float* dst = logits + size_t(g * G + h) * T + t;
     *dst = ACC ? *dst + n_k * l : n_k * l;
   }
@@ -133,20 +223,20 @@ hipError_t launch_b(const void* params_v, int d, const void* q, int q_dtype, lon
   const unsigned char* params = static_cast<const unsigned char*>(params_v);
   const Layout lay(d, BITS);
   float* qs = static_cast<float*>(ws);
-  float* ssum = qs + size_t(groups) * G * 2 * d;
   const long rows = long(groups) * G;
-  hipLaunchKernelGGL(generic_qprep_kernel, dim3(unsigned(rows)), dim3(256), size_t(d) * 4, s, params,
-                     lay.off_pi, lay.off_s, d, qpitch, q, q_dtype == 0 ? 1 : 0, qs, ssum);
+  const long qblocks = (rows + QR - 1) / QR * (2 * d / QO);
+  hipLaunchKernelGGL(generic_qprep_kernel, dim3(unsigned(qblocks)), dim3(256), 0, s, params, lay.off_pi,
+                     lay.off_s, d, qpitch, q, q_dtype == 0 ? 1 : 0, rows, qs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long kblocks = (T + KEYS - 1) / KEYS;
   const long passes = (G + HB - 1) / HB;
   const dim3 grid(unsigned(groups * passes * kblocks));
   if (mode == 0)
-    hipLaunchKernelGGL((generic_score_kernel<BITS, true, ACC>), grid, dim3(KEYS), 0, s, params, qs, ssum,
+    hipLaunchKernelGGL((generic_score_kernel<BITS, true, ACC>), grid, dim3(KEYS), 0, s, params, qs,
                        codes, nu, gamma, d, long(G), long(T), kblocks, passes, logits);
   else
-    hipLaunchKernelGGL((generic_score_kernel<BITS, false, ACC>), grid, dim3(KEYS), 0, s, params, qs, ssum,
+    hipLaunchKernelGGL((generic_score_kernel<BITS, false, ACC>), grid, dim3(KEYS), 0, s, params, qs,
                        codes, nu, gamma, d, long(G), long(T), kblocks, passes, logits);
   return hipGetLastError();
 }
@@ -154,12 +244,13 @@ hipError_t launch_b(const void* params_v, int d, const void* q, int q_dtype, lon
 }  // namespace
 
 size_t score_generic_ws_bytes(int d, int64_t groups, int64_t G) {
-  return size_t(groups) * G * (2 * size_t(d) + 1) * 4;
+  return size_t(groups) * G * 2 * size_t(d) * 4;
 }
 
 bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T) {
   const int64_t blocks = groups * ((G + HB - 1) / HB) * ((T + KEYS - 1) / KEYS);
-  return groups * G < (int64_t(1) << 31) && blocks < (int64_t(1) << 31);
+  const int64_t qblocks = (groups * G + QR - 1) / QR * (2 * 4096 / QO);
+  return groups * G < (int64_t(1) << 31) && blocks < (int64_t(1) << 31) && qblocks < (int64_t(1) << 31);
 }
 
 hipError_t launch_score_generic(const void* params, int d, int b, const void* q, int q_dtype,

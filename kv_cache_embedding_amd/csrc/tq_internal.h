@@ -88,7 +88,7 @@ hipError_t launch_score_d128(const void* params, int b, const void* q, int q_dty
                              int64_t groups, int64_t G, int64_t T, int mode, float* logits,
                              void* ws, hipStream_t s);
 // Scoring for shapes the d = 128 kernel does not take (any d, any G): fp32 query prep into
-// ws ([groups * G][2][d] floats, then [groups * G] sums), then one lane per key.  qpitch:
+// ws ([groups * G][2][d] floats: Pi q, S q), then one lane per key.  qpitch:
 // elements between query rows (0: d); accumulate: add to logits instead of overwriting.
 hipError_t launch_score_generic(const void* params, int d, int b, const void* q, int q_dtype,
                                 const uint32_t* codes, const float* nu, const float* gamma,

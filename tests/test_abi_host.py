@@ -93,7 +93,7 @@ def test_params_bytes_and_workspace_helpers(lib):
     assert tq.tq_score_ws_bytes(128, 4, 8, 4, 32768) % 256 == 0
     assert tq.tq_score_ws_bytes(128, 4, 8, 8, 32768) == 2 * tq.tq_score_ws_bytes(128, 4, 8, 4, 32768)
     for d, G in ((64, 4), (128, 3), (1536, 1)):
-        need = 8 * G * (2 * d + 1) * 4
+        need = 8 * G * 2 * d * 4          # Pi q and S q of every query row, float32
         assert need <= tq.tq_score_ws_bytes(d, 4, 8, G, 100) < need + 256
     assert tq.tq_score_ws_bytes(100, 4, 8, 4, 100) == 0
 
@@ -207,7 +207,7 @@ def test_split_calls_validate_without_launch(lib):
     assert lib.tq_quantize_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, 0, None, None, None, None, None,
                                  None, None) == tq.TQ_OK                       # n = 0: nothing to do
     need = lib.tq_score_split_ws_bytes(128, 64, 3, 2, 2, 4, 100)
-    assert need >= 2 * 4 * (2 * 64 + 1) * 4 and need % 256 == 0
+    assert need >= 2 * 4 * 2 * 64 * 4 and need % 256 == 0
     assert lib.tq_score_ip_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, P, P, P, P, P, P, 2, 4, 100,
                                  tq.TQ_EST_PROD, P, P, need - 256, None) == tq.TQ_EWORKSPACE
     assert lib.tq_score_ip_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, P, P, P, P, P, P, 2, 4, 100,
