@@ -260,6 +260,40 @@ int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, i
                       const float* gamma1, int64_t groups, int64_t G, int64_t T, int mode,
                       float* logits, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * tq_quantize_mse_split — the MSE quantizer alone (as tq_quantize_mse) on the two channel
+ * groups of x [n][d]: channels [0, d0) with params0 (b0 - 1 index bits) into codes0
+ * [n][d0/32][b0-1], nu0 [n]; channels [d0, d) with params1 into codes1, nu1.  Values of a
+ * fractional-rate KV cache.  Runs the tiled encoder's first pass once per group, reading
+ * the channels in place.
+ * Errors: as tq_quantize_split.
+ */
+int tq_quantize_mse_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                          const void* x, int x_dtype, int64_t n, uint32_t* codes0, float* nu0,
+                          uint32_t* codes1, float* nu1, void* stream);
+
+/* Workspace bytes needed by tq_attention_split for these sizes. */
+size_t tq_attention_split_ws_bytes(int d, int d0, int bk0, int bk1, int64_t groups, int64_t G, int64_t T);
+
+/*
+ * tq_attention_split — tq_attention over a fractional-rate KV cache: the logits are
+ * tq_score_ip_split's (key groups [0, d0) and [d0, d) at bk0, bk1 bits), and each value group
+ * g (params_v0 / params_v1 from tq_prepare(d_g, bv_g, ...), codes from tq_quantize_mse_split)
+ * yields its channels of the output under the same softmax weights:
+ *   out[g][h][channels of group v] = Pi_v^T sum_t p_t nu_v,t chat_v,t / sum_t p_t.
+ *   out  [groups][G][d] float32, 16-byte aligned
+ *   ws   at least tq_attention_split_ws_bytes(...) bytes, 256-aligned, scratch.
+ * Errors: as tq_attention.
+ */
+int tq_attention_split(const void* params_k0, const void* params_k1, const void* params_v0,
+                       const void* params_v1, int d, int d0, int bk0, int bk1, int bv0, int bv1,
+                       const void* q, int q_dtype, const uint32_t* codes_k0, const float* nu_k0,
+                       const float* gamma_k0, const uint32_t* codes_k1, const float* nu_k1,
+                       const float* gamma_k1, const uint32_t* codes_v0, const float* nu_v0,
+                       const uint32_t* codes_v1, const float* nu_v1, int64_t groups, int64_t G,
+                       int64_t T, float scale, int mode, float* out, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* Workspace bytes needed by tq_attention for these sizes. */
 size_t tq_attention_ws_bytes(int d, int b_k, int64_t groups, int64_t G, int64_t T);
 

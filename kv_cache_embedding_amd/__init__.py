@@ -11,7 +11,7 @@ from ._binding import (  # noqa: F401
     TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_EWORKSPACE, TQ_F32, TQ_BF16, TQ_EST_PROD,
     TQ_EST_MSE, TQError, lib_path, load_library, tq_codebook_build, tq_codebook_build_sphere,
     tq_params_bytes, tq_prepare, tq_prepare_orthogonal_qjl, tq_quantize_split, tq_score_split_ws_bytes,
-    tq_score_ip_split,
+    tq_score_ip_split, tq_quantize_mse_split, tq_attention_split_ws_bytes, tq_attention_split,
     tq_quantize, tq_quantize_mse, tq_append_ws_bytes, tq_append, tq_dequantize, tq_score_ws_bytes, tq_score_ip,
     tq_attention_ws_bytes, tq_attention, tq_topk_ws_bytes, tq_topk, tq_last_error,
 )
@@ -20,7 +20,8 @@ __all__ = [
     "TQ_OK", "TQ_EINVAL", "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_EWORKSPACE", "TQ_F32", "TQ_BF16",
     "TQ_EST_PROD", "TQ_EST_MSE", "TQError", "lib_path", "load_library", "tq_codebook_build",
     "tq_codebook_build_sphere", "tq_params_bytes", "tq_prepare", "tq_prepare_orthogonal_qjl",
-    "tq_quantize_split", "tq_score_split_ws_bytes", "tq_score_ip_split", "tq_quantize", "tq_quantize_mse", "tq_append_ws_bytes", "tq_append",
+    "tq_quantize_split", "tq_score_split_ws_bytes", "tq_score_ip_split", "tq_quantize_mse_split",
+    "tq_attention_split_ws_bytes", "tq_attention_split", "tq_quantize", "tq_quantize_mse", "tq_append_ws_bytes", "tq_append",
     "tq_dequantize",
     "tq_score_ws_bytes", "tq_score_ip", "tq_attention_ws_bytes", "tq_attention",
     "tq_topk_ws_bytes", "tq_topk", "tq_last_error",

@@ -50,6 +50,10 @@ def load_library():
         "tq_quantize_mse": (I, [P, I, I, P, I, I64, P, P, P]),
         "tq_quantize_split": (I, [P, P, I, I, I, I, P, I, I64, P, P, P, P, P, P, P]),
         "tq_score_split_ws_bytes": (SZ, [I, I, I, I, I64, I64, I64]),
+        "tq_quantize_mse_split": (I, [P, P, I, I, I, I, P, I, I64, P, P, P, P, P]),
+        "tq_attention_split_ws_bytes": (SZ, [I, I, I, I, I64, I64, I64]),
+        "tq_attention_split": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P, P, P, P, P, P, P, P, P, P, I64, I64,
+                                   I64, ctypes.c_float, I, P, P, SZ, P]),
         "tq_score_ip_split": (I, [P, P, I, I, I, I, P, I, P, P, P, P, P, P, I64, I64, I64, I, P, P, SZ,
                                   P]),
         "tq_append_ws_bytes": (SZ, [I, I, I64]),
@@ -316,6 +320,62 @@ def tq_score_ip_split(params0, params1, d: int, d0: int, b0: int, b1: int, q, co
                                             _ptr(codes1), _ptr(nu1), _ptr(gamma1), groups, G, T,
                                             int(mode), _ptr(logits), _ptr(ws),
                                             ws.numel() * ws.element_size(), _stream(stream, q.device)))
+
+
+def tq_quantize_mse_split(params0, params1, d: int, d0: int, b0: int, b1: int, x, codes0, nu0, codes1,
+                          nu1, stream=None):
+    """Values of a fractional-rate cache: channels [0, d0) of x [n][d] by params0, the rest by params1."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError(f"x must be [n][{d}]")
+    n = x.shape[0]
+    for tname, t in (("codes0", codes0), ("nu0", nu0), ("codes1", codes1), ("nu1", nu1),
+                     ("params0", params0), ("params1", params1)):
+        _dev(t, tname)
+    _need(codes0, "codes0", n * (d0 // 32) * (b0 - 1), torch.int32)
+    _need(codes1, "codes1", n * ((d - d0) // 32) * (b1 - 1), torch.int32)
+    _need(nu0, "nu0", n, torch.float32)
+    _need(nu1, "nu1", n, torch.float32)
+    _check(load_library().tq_quantize_mse_split(_ptr(params0), _ptr(params1), d, d0, b0, b1, _ptr(x),
+                                                _dtype_code(x, "x"), n, _ptr(codes0), _ptr(nu0),
+                                                _ptr(codes1), _ptr(nu1), _stream(stream, x.device)))
+
+
+def tq_attention_split_ws_bytes(d: int, d0: int, bk0: int, bk1: int, groups: int, G: int, T: int) -> int:
+    return int(load_library().tq_attention_split_ws_bytes(d, d0, bk0, bk1, groups, G, T))
+
+
+def tq_attention_split(params_k0, params_k1, params_v0, params_v1, d: int, d0: int, bk0: int, bk1: int,
+                       bv0: int, bv1: int, q, codes_k0, nu_k0, gamma_k0, codes_k1, nu_k1, gamma_k1,
+                       codes_v0, nu_v0, codes_v1, nu_v1, groups: int, G: int, T: int, scale: float,
+                       mode: int, out, ws, stream=None):
+    """Decode attention over a fractional-rate KV cache -> out [groups][G][d] float32."""
+    torch = _torch()
+    named = (("q", q), ("codes_k0", codes_k0), ("nu_k0", nu_k0), ("gamma_k0", gamma_k0),
+             ("codes_k1", codes_k1), ("nu_k1", nu_k1), ("gamma_k1", gamma_k1), ("codes_v0", codes_v0),
+             ("nu_v0", nu_v0), ("codes_v1", codes_v1), ("nu_v1", nu_v1), ("out", out), ("ws", ws),
+             ("params_k0", params_k0), ("params_k1", params_k1), ("params_v0", params_v0),
+             ("params_v1", params_v1))
+    for tname, t in named:
+        _dev(t, tname)
+    if q.numel() < groups * G * d:
+        raise ValueError("q holds fewer than groups*G*d elements")
+    n = groups * T
+    _need(codes_k0, "codes_k0", n * (d0 // 32) * bk0, torch.int32)
+    _need(codes_k1, "codes_k1", n * ((d - d0) // 32) * bk1, torch.int32)
+    _need(codes_v0, "codes_v0", n * (d0 // 32) * (bv0 - 1), torch.int32)
+    _need(codes_v1, "codes_v1", n * ((d - d0) // 32) * (bv1 - 1), torch.int32)
+    for tname, t in (("nu_k0", nu_k0), ("gamma_k0", gamma_k0), ("nu_k1", nu_k1), ("gamma_k1", gamma_k1),
+                     ("nu_v0", nu_v0), ("nu_v1", nu_v1)):
+        _need(t, tname, n, torch.float32)
+    _need(out, "out", groups * G * d, torch.float32)
+    _check(load_library().tq_attention_split(
+        _ptr(params_k0), _ptr(params_k1), _ptr(params_v0), _ptr(params_v1), d, d0, bk0, bk1, bv0, bv1,
+        _ptr(q), _dtype_code(q, "q"), _ptr(codes_k0), _ptr(nu_k0), _ptr(gamma_k0), _ptr(codes_k1),
+        _ptr(nu_k1), _ptr(gamma_k1), _ptr(codes_v0), _ptr(nu_v0), _ptr(codes_v1), _ptr(nu_v1), groups, G, T,
+        float(scale), int(mode), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream, q.device)))
 
 
 def tq_attention_ws_bytes(d: int, b_k: int, groups: int, G: int, T: int) -> int:

@@ -151,10 +151,11 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
   }
 }
 
+// out rows are opitch floats apart (a channel group of wider output rows: its columns only)
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const unsigned char* __restrict__ params_v, size_t off_pi, int d, long nkb,
     const float* __restrict__ part_m, const float* __restrict__ part_s,
-    const float* __restrict__ part_acc, float* __restrict__ out) {
+    const float* __restrict__ part_acc, float* __restrict__ out, long opitch) {
   extern __shared__ float4 lds4[];   // [slices][d / 4] partial sums, then a[d / 4]
   __shared__ float red[4];
   const long row = blockIdx.x;   // group * G + head
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     }
   }
   __syncthreads();
-  float4* o4 = reinterpret_cast<float4*>(out) + row * d4;
+  float4* o4 = reinterpret_cast<float4*>(out + row * opitch);
   for (int j4 = tid; j4 < d4; j4 += 256) {
     float4 v = part[j4];
     for (int t = 1; t < nsl; ++t) {
@@ -251,7 +252,7 @@ size_t attention_part_bytes(int d, int64_t groups, int64_t G, int64_t T) {
 hipError_t launch_attention_values(const void* params_v, int d, int b_v, const float* logits,
                                    const uint32_t* vcodes, const float* vnu, int64_t groups,
                                    int64_t G, int64_t T, float scale, float* out, void* part,
-                                   hipStream_t s) {
+                                   hipStream_t s, int64_t opitch) {
   const unsigned char* pv = static_cast<const unsigned char*>(params_v);
   const long nkb = (T + KB - 1) / KB;
   const long passes = (G + AH - 1) / AH;
@@ -287,7 +288,7 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
   const int d4 = d / 4, cols = d4 < 256 ? d4 : 256, nsl = 256 / cols;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(256),
                      (size_t(nsl) * d4 + d4) * 16, s, pv, lay.off_pi, d, nkb, part_m, part_s,
-                     part_acc, out);
+                     part_acc, out, long(opitch > 0 ? opitch : d));
   return hipGetLastError();
 }
 

@@ -669,6 +669,85 @@ int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, i
   return ok();
 }
 
+int tq_quantize_mse_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                          const void* x, int x_dtype, int64_t n, uint32_t* codes0, float* nu0,
+                          uint32_t* codes1, float* nu1, void* stream) {
+  if (!valid_split(d, d0, b0, b1))
+    return fail(TQ_EINVAL, "unsupported split d=%d d0=%d b0=%d b1=%d", d, d0, b0, b1);
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad x_dtype %d", x_dtype);
+  if (n < 0) return fail(TQ_EINVAL, "n=%lld < 0", (long long)n);
+  if (n == 0) return ok();
+  if (!params0 || !params1 || !x || !codes0 || !nu0 || !codes1 || !nu1)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params0, 256) || !aligned(params1, 256) || !aligned(x, 16) || !aligned(codes0, 4) ||
+      !aligned(codes1, 4) || !aligned(nu0, 4) || !aligned(nu1, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x 16 B)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
+  const void* x1 = static_cast<const unsigned char*>(x) + size_t(d0) * esz;
+  hipError_t e = tq::launch_quantize_mse(params0, d0, b0, x, x_dtype, n, codes0, nu0, s, d);
+  if (e == hipSuccess) e = tq::launch_quantize_mse(params1, d - d0, b1, x1, x_dtype, n, codes1, nu1, s, d);
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize_mse_split launch");
+  return ok();
+}
+
+size_t tq_attention_split_ws_bytes(int d, int d0, int bk0, int bk1, int64_t groups, int64_t G, int64_t T) {
+  if (!valid_split(d, d0, bk0, bk1) || groups < 0 || G < 0 || T < 0) return 0;
+  const int dmax = std::max(d0, d - d0);
+  return tq::align256(size_t(groups) * G * T * 4) + tq_score_split_ws_bytes(d, d0, bk0, bk1, groups, G, T) +
+         tq::align256(tq::attention_part_bytes(dmax, groups, G, T));
+}
+
+int tq_attention_split(const void* params_k0, const void* params_k1, const void* params_v0,
+                       const void* params_v1, int d, int d0, int bk0, int bk1, int bv0, int bv1,
+                       const void* q, int q_dtype, const uint32_t* codes_k0, const float* nu_k0,
+                       const float* gamma_k0, const uint32_t* codes_k1, const float* nu_k1,
+                       const float* gamma_k1, const uint32_t* codes_v0, const float* nu_v0,
+                       const uint32_t* codes_v1, const float* nu_v1, int64_t groups, int64_t G,
+                       int64_t T, float scale, int mode, float* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!valid_split(d, d0, bk0, bk1) || !valid_split(d, d0, bv0, bv1))
+    return fail(TQ_EINVAL, "unsupported split d=%d d0=%d keys b=%d,%d values b=%d,%d", d, d0, bk0, bk1,
+                bv0, bv1);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad q_dtype %d", q_dtype);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (!std::isfinite(scale)) return fail(TQ_EINVAL, "scale must be finite");
+  if (groups < 0 || G < 0 || T < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0 || G == 0) return ok();
+  if (T == 0) return fail(TQ_EINVAL, "T = 0: a softmax needs at least one key");
+  if (T >= (int64_t(1) << 31)) return fail(TQ_EINVAL, "T must be < 2^31");
+  if (!params_k0 || !params_k1 || !params_v0 || !params_v1 || !q || !codes_k0 || !nu_k0 || !gamma_k0 ||
+      !codes_k1 || !nu_k1 || !gamma_k1 || !codes_v0 || !nu_v0 || !codes_v1 || !nu_v1 || !out || !ws)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params_k0, 256) || !aligned(params_k1, 256) || !aligned(params_v0, 256) ||
+      !aligned(params_v1, 256) || !aligned(ws, 256) || !aligned(codes_k0, 16) || !aligned(codes_k1, 16) ||
+      !aligned(codes_v0, 4) || !aligned(codes_v1, 4) || !aligned(q, 4) || !aligned(out, 16))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; key codes, out 16 B)");
+  if (!tq::score_generic_grid_fits(groups, G, T) || !tq::attention_grid_fits(groups, G, T))
+    return fail(TQ_EUNSUPPORTED, "tq_attention_split: groups * G * T too large for one launch");
+  const size_t need = tq_attention_split_ws_bytes(d, d0, bk0, bk1, groups, G, T);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  float* logits = reinterpret_cast<float*>(w);
+  const size_t sws_bytes = tq_score_split_ws_bytes(d, d0, bk0, bk1, groups, G, T);
+  void* sws = w + tq::align256(size_t(groups) * G * T * 4);
+  void* part = static_cast<unsigned char*>(sws) + sws_bytes;
+  // logits of the split keys, then each value group's softmax-weighted sum into its columns
+  // of out (the partials are reused by the second group: same stream, in order)
+  const int rc = tq_score_ip_split(params_k0, params_k1, d, d0, bk0, bk1, q, q_dtype, codes_k0, nu_k0,
+                                   gamma_k0, codes_k1, nu_k1, gamma_k1, groups, G, T, mode, logits, sws,
+                                   sws_bytes, stream);
+  if (rc != TQ_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = tq::launch_attention_values(params_v0, d0, bv0, logits, codes_v0, nu_v0, groups, G, T,
+                                             scale, out, part, s, d);
+  if (e == hipSuccess)
+    e = tq::launch_attention_values(params_v1, d - d0, bv1, logits, codes_v1, nu_v1, groups, G, T, scale,
+                                    out + d0, part, s, d);
+  if (e != hipSuccess) return hip_fail(e, "tq_attention_split launch");
+  return ok();
+}
+
 size_t tq_attention_ws_bytes(int d, int b_k, int64_t groups, int64_t G, int64_t T) {
   if (!valid_shape(d, b_k) || groups < 0 || G < 0 || T < 0) return 0;
   return tq::align256(size_t(groups) * G * T * 4) + tq_score_ws_bytes(d, b_k, groups, G, T) +

@@ -111,7 +111,7 @@ bool attention_grid_fits(int64_t groups, int64_t G, int64_t T);
 hipError_t launch_attention_values(const void* params_v, int d, int b_v, const float* logits,
                                    const uint32_t* vcodes, const float* vnu, int64_t groups,
                                    int64_t G, int64_t T, float scale, float* out, void* part,
-                                   hipStream_t s);
+                                   hipStream_t s, int64_t opitch = 0);
 // Cache append: copies vector g's words, nu and gamma (gamma may be NULL) of a contiguous
 // batch to slot (g, pos) of [groups][cap] caches.
 hipError_t launch_scatter_slot(const uint32_t* src_codes, const float* src_nu,

@@ -195,3 +195,92 @@ def test_outlier_channels_belong_in_the_higher_bit_group():
     print(f"[2.5 bits, outliers in the 3-bit group: {errs['high']:.4f}, in the 2-bit group: {errs['low']:.4f}]",
           flush=True)
     assert errs["high"] < errs["low"]
+
+
+# ------------------------------------------------------- fractional-rate values + attention
+
+def _mse_split(svs, d, d0, xd):
+    n = xd.shape[0]
+    out = []
+    for st, w in zip(svs, (d0, d - d0)):
+        out.append((torch.full((n * (w // 32) * (st.b - 1),), -1, dtype=torch.int32, device=U.DEV),
+                    torch.full((n,), float("nan"), device=U.DEV)))
+    tq.tq_quantize_mse_split(svs[0].params, svs[1].params, d, d0, svs[0].b, svs[1].b, xd, *out[0], *out[1])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("d,d0,bk0,bk1,bv0,bv1,G,T,q_bf16", [
+    (128, 64, 3, 2, 4, 3, 4, 700, True),      # 2.5-bit keys, 2.5-bit values (b - 1 index bits)
+    (128, 64, 4, 3, 4, 3, 3, 257, False),
+    (192, 128, 4, 2, 3, 4, 2, 300, True)])
+def test_attention_split_parity(d, d0, bk0, bk1, bv0, bv1, G, T, q_bf16):
+    import math
+    groups, cfg = 3, 75
+    sks = _groups(d, d0, bk0, bk1, cfg)
+    svs = [U.make_setup(d0, bv0, cfg=cfg + 10), U.make_setup(d - d0, bv1, cfg=cfg + 11)]
+    chans = gen.outlier_channels(cfg, groups, d)
+    keys = np.concatenate([gen.kv_keys_chunk(cfg, 0, h, T, d, chans[h]) for h in range(groups)])
+    vals = np.concatenate([gen.kv_keys_chunk(cfg, 1, h, T, d, chans[h], scale=1.0) for h in range(groups)])
+    vals[5, :d0] = 0                       # a value whose group 0 is zero
+    q = gen.kv_queries(cfg, 1, groups * G, d)[0]
+    if not q_bf16:
+        q = gen.bf16_bits_to_f32(q)
+    kp = _split_quantize(sks, d, d0, U.to_device(keys, True))
+    vp = _mse_split(svs, d, d0, U.to_device(vals, True))
+    n = groups * T
+    # value codes against the oracle's MSE quantizer, group by group
+    v64 = U.host64(vals, True)
+    for st, (c, nu), off, w in zip(svs, vp, (0, d0), (d0, d - d0)):
+        idx_g = oracle.unpack_index_planes(c.cpu().numpy().view(np.uint32).reshape(n, w // 32, st.b - 1), st.b - 1)
+        ro = oracle.quantize_mse(v64[:, off:off + w], st.Pi, st.c_or, st.t_or)
+        mism = idx_g != ro["idx"]
+        if mism.any():   # only within 1e-5 of a threshold between the two indices
+            rr, cc = np.nonzero(mism)
+            for r, c_ in zip(rr, cc):
+                lo, hi = sorted((idx_g[r, c_], ro["idx"][r, c_]))
+                assert np.min(np.abs(ro["u"][r, c_] - st.t_or[lo:hi])) <= U.EXCUSE_U
+        assert mism.sum() <= 1e-4 * mism.size
+        np.testing.assert_allclose(nu.cpu().numpy(), ro["nu"], rtol=1e-5, atol=0)
+    qd = U.to_device(q, q_bf16)
+    scale = 1.0 / math.sqrt(d)
+    out = torch.full((groups * G * d,), float("nan"), device=U.DEV)
+    ws = torch.empty(tq.tq_attention_split_ws_bytes(d, d0, bk0, bk1, groups, G, T), dtype=torch.uint8,
+                     device=U.DEV)
+    tq.tq_attention_split(sks[0].params, sks[1].params, svs[0].params, svs[1].params, d, d0, bk0, bk1, bv0,
+                          bv1, qd, *kp[0], *kp[1], *vp[0], *vp[1], groups, G, T, scale, tq.TQ_EST_PROD,
+                          out, ws)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(groups, G, d)
+    assert np.all(np.isfinite(out))
+    # oracle fed the GPU's codes: split logits, per-group reconstructions side by side
+    q64 = U.host64(q, q_bf16).reshape(groups, G, d)
+    gdefs = [{"off": off, "width": w, "Pi": st.Pi, "S": st.S, "centroids": st.c_or}
+             for st, off, w in zip(sks, (0, d0), (d0, d - d0))]
+    gcodes = []
+    for st, (c, nu, ga), w in zip(sks, kp, (d0, d - d0)):
+        idx, z = oracle.unpack_codes(U.codes_np(c, n, w, st.b), st.b)
+        gcodes.append({"idx": idx, "z": z, "nu": nu.cpu().numpy(), "gamma": ga.cpu().numpy()})
+    logits = np.stack([oracle.estimate_ip_split(q64[g], gdefs, [{k: v[g * T:(g + 1) * T] for k, v in c.items()}
+                                                                for c in gcodes]) for g in range(groups)])
+    vhat = np.concatenate([
+        oracle.dequantize_mse(st.Pi, oracle.unpack_index_planes(
+            c.cpu().numpy().view(np.uint32).reshape(n, w // 32, st.b - 1), st.b - 1), nu.cpu().numpy(), st.c_or)
+        for st, (c, nu), w in zip(svs, vp, (d0, d - d0))], axis=1).reshape(groups, T, d)
+    ref = oracle.attention_decode(logits, vhat, scale)
+    vmax = float(np.max(np.sqrt(vp[0][1].cpu().numpy() ** 2 + vp[1][1].cpu().numpy() ** 2)))
+    # the GPU's own logits (the same kernels as tq_score_ip_split)
+    lg_t = torch.empty(groups * G * T, device=U.DEV)
+    sws = torch.empty(tq.tq_score_split_ws_bytes(d, d0, bk0, bk1, groups, G, T), dtype=torch.uint8, device=U.DEV)
+    tq.tq_score_ip_split(sks[0].params, sks[1].params, d, d0, bk0, bk1, qd, *kp[0], *kp[1], groups, G, T,
+                         tq.TQ_EST_PROD, lg_t, sws)
+    torch.cuda.synchronize()
+    lg = lg_t.cpu().numpy().reshape(groups, G, T).astype(np.float64)
+    dl = float(np.max(np.abs(lg - logits)))
+    tol = (math.exp(2 * scale * dl) - 1.0) * vmax + 2e-5 * vmax
+    err = float(np.max(np.abs(out - ref)))
+    err_own = float(np.max(np.abs(out - oracle.attention_decode(lg, vhat, scale))))
+    print(f"[attention split d={d} keys {d0}@{bk0}+{d - d0}@{bk1} values {d0}@{bv0 - 1}+{d - d0}@{bv1 - 1} "
+          f"idx bits] err {err / vmax:.2e} (bound {tol / vmax:.2e}), own-logit err {err_own / vmax:.2e}", flush=True)
+    assert err <= tol
+    assert err_own <= 2e-5 * vmax
