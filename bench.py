@@ -606,6 +606,48 @@ def bench_fractional(args):
           "note": f"algorithmic bytes per key: {code_bytes} B codes, nu and gamma of both groups in; "
                   f"fp32 logits written and, by the second group, read back"}
     dominant, other = (rq, rs) if q_ms >= s_ms else (rs, rq)
+
+    # the value side of the same cache: values as two channel groups through the MSE quantizer,
+    # each group at the key group's bit count in index bits, capped at 3 (a block prepared for
+    # b carries b - 1 of them), and one decode step of attention over the split keys and values
+    bv = [min(b0 + 1, 4), min(b1 + 1, 4)]
+    pvs = []
+    for k, (wd, b) in enumerate(((d0, bv[0]), (d - d0, bv[1]))):
+        c, t = tq.tq_codebook_build(b - 1, wd)
+        p = torch.empty(tq.tq_params_bytes(wd, b), dtype=torch.uint8, device=dev)
+        tq.tq_prepare(wd, b, gen.haar_orthogonal(wd, w.cfg + 2 + k), gen.gaussian_matrix(wd, wd, w.cfg + 2 + k),
+                      c, t, p)
+        pvs.append(p)
+    vals = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
+    for s_ in range(w.n_seq):
+        for h in range(w.n_kv):
+            gi = s_ * w.n_kv + h
+            vc = gen.kv_keys_chunk(w.cfg, w.n_seq + s_, h, T, d, chans[h], scale=1.0)
+            vals[gi * T:(gi + 1) * T] = torch.from_numpy(vc.view(np.int16)).to(dev).view(torch.bfloat16)
+    cv = [[torch.empty(n * (wd // 32) * (b - 1), dtype=torch.int32, device=dev) for _ in range(R)]
+          for wd, b in ((d0, bv[0]), (d - d0, bv[1]))]
+    nv = [[torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)] for _ in range(2)]
+    scale = 1.0 / float(np.sqrt(d))
+    out = torch.empty(groups * G * d, dtype=torch.float32, device=dev)
+    wsa = torch.empty(tq.tq_attention_split_ws_bytes(d, d0, b0, b1, groups, G, T), dtype=torch.uint8, device=dev)
+
+    def vquant(r):
+        tq.tq_quantize_mse_split(pvs[0], pvs[1], d, d0, bv[0], bv[1], vals, cv[0][r], nv[0][r], cv[1][r], nv[1][r])
+
+    def attend(r):
+        tq.tq_attention_split(params[0], params[1], pvs[0], pvs[1], d, d0, b0, b1, bv[0], bv[1], q, g0[0][r],
+                              g0[1][r], g0[2][r], g1[0][r], g1[1][r], g1[2][r], cv[0][r], nv[0][r], cv[1][r],
+                              nv[1][r], groups, G, T, scale, tq.TQ_EST_PROD, out, wsa)
+
+    for r in range(R):
+        vquant(r)
+        attend(r)
+    torch.cuda.synchronize()
+    g_vq = [capture(vquant, r) for r in range(R)]
+    g_att = [capture(attend, r) for r in range(R)]
+    vq_ms = timed(g_vq)
+    a_ms = timed(g_att)
+
     result = {
         "metric": "quantized-key logits/s at a fractional rate (two channel groups), 1 MI355X",
         "value": n_logits / (ms_step * 1e-3),
@@ -629,6 +671,10 @@ def bench_fractional(args):
         "roofline_other": other,
         "quantize": {"ms": q_ms, "vectors_per_s": n / (q_ms * 1e-3), "hbm_gbs": q_gbs},
         "score": {"ms": s_ms, "logits_per_s": n_logits / (s_ms * 1e-3), "hbm_gbs": s_gbs},
+        "value_quantize": {"ms": vq_ms, "vectors_per_s": n / (vq_ms * 1e-3),
+                           "index_bits": [[d0, bv[0] - 1], [d - d0, bv[1] - 1]]},
+        "attention": {"ms": a_ms, "pairs_per_s": n_logits / (a_ms * 1e-3),
+                      "note": "tq_attention_split: split-key logits, softmax, per-group value sums"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_fractional(w, b0, b1, args.cpu_seconds)

@@ -264,8 +264,9 @@ int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, i
  * tq_quantize_mse_split — the MSE quantizer alone (as tq_quantize_mse) on the two channel
  * groups of x [n][d]: channels [0, d0) with params0 (b0 - 1 index bits) into codes0
  * [n][d0/32][b0-1], nu0 [n]; channels [d0, d) with params1 into codes1, nu1.  Values of a
- * fractional-rate KV cache.  Runs the tiled encoder's first pass once per group, reading
- * the channels in place.
+ * fractional-rate KV cache.  A 64 + 64 split of d = 128 runs one pass of the fused
+ * encoder (no QJL stage); other splits run the tiled encoder's first pass once per group,
+ * reading the channels in place.
  * Errors: as tq_quantize_split.
  */
 int tq_quantize_mse_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,

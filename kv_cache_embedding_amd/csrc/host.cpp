@@ -685,8 +685,14 @@ int tq_quantize_mse_split(const void* params0, const void* params1, int d, int d
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
   const void* x1 = static_cast<const unsigned char*>(x) + size_t(d0) * esz;
-  hipError_t e = tq::launch_quantize_mse(params0, d0, b0, x, x_dtype, n, codes0, nu0, s, d);
-  if (e == hipSuccess) e = tq::launch_quantize_mse(params1, d - d0, b1, x1, x_dtype, n, codes1, nu1, s, d);
+  hipError_t e;
+  if (d == 128 && d0 == 64) {   // both groups in one pass of the fused encoder
+    e = tq::launch_quantize_d128_split(params0, params1, b0, b1, x, x_dtype, n, codes0, nu0, nullptr, codes1,
+                                       nu1, nullptr, s, true);
+  } else {
+    e = tq::launch_quantize_mse(params0, d0, b0, x, x_dtype, n, codes0, nu0, s, d);
+    if (e == hipSuccess) e = tq::launch_quantize_mse(params1, d - d0, b1, x1, x_dtype, n, codes1, nu1, s, d);
+  }
   if (e != hipSuccess) return hip_fail(e, "tq_quantize_mse_split launch");
   return ok();
 }

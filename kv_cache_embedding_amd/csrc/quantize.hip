@@ -142,7 +142,7 @@ __device__ __forceinline__ void store_words(uint32_t* dst, const uint32_t* out) 
 }
 
 // MSE: the MSE quantizer alone (attention values): GEMM1 and the index planes only, b-1
-// planes per coordinate group, nu but no gamma.  Without SPLIT, B0 == B1 is the b of params
+// planes per coordinate group, nu but no gamma (also in split mode).  Without SPLIT, B0 == B1 is the b of params
 // and params1, codes1, nu1_out, gamma1_out are unused; with SPLIT, params / params1 are the
 // d = 64 blocks of channel groups 0 / 1 (gmat_off: their bf16 matrices) and group 1's
 // results go to codes1, nu1_out, gamma1_out.
@@ -153,7 +153,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     uint32_t* __restrict__ codes, float* __restrict__ nu_out, float* __restrict__ gamma_out,
     uint32_t* __restrict__ codes1, float* __restrict__ nu1_out, float* __restrict__ gamma1_out) {
   static_assert(SPLIT || B0 == B1, "one bit width without split");
-  static_assert(!(SPLIT && MSE), "split mode encodes keys (MSE + QJL)");
   __shared__ uint4 frag[2 * FRAG_U4];  // [0, FRAG_U4): Pi~ fragments; then S'~ fragments
   __shared__ int next_tile;            // work queue of this workgroup's tile range
 
@@ -393,11 +392,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
       } else if (kh == 0) {
         store_words<P0, PM>(codes + vec * 2 * P0, out);
         nu_out[vec] = nu0;
-        gamma_out[vec] = gamma0;
+        if constexpr (!MSE) gamma_out[vec] = gamma0;
       } else {
         store_words<P1, PM>(codes1 + vec * 2 * P1, out);
         nu1_out[vec] = nu1;
-        gamma1_out[vec] = gamma1;
+        if constexpr (!MSE) gamma1_out[vec] = gamma1;
       }
     }
     tile = next;
@@ -433,11 +432,11 @@ hipError_t launch(const void* params, const void* x, int64_t n, uint32_t* codes,
   return hipGetLastError();
 }
 
-template <int B0, int B1, bool F32IN>
+template <int B0, int B1, bool F32IN, bool MSE = false>
 hipError_t launch_split(const void* params0, const void* params1, const void* x, int64_t n,
                         uint32_t* codes0, float* nu0, float* gamma0, uint32_t* codes1, float* nu1,
                         float* gamma1, hipStream_t s) {
-  hipLaunchKernelGGL((quantize_d128_kernel<B0, B1, F32IN, false, true>), dim3(grid_for(n)),
+  hipLaunchKernelGGL((quantize_d128_kernel<B0, B1, F32IN, MSE, true>), dim3(grid_for(n)),
                      dim3(WAVES * 64), 0, s, static_cast<const unsigned char*>(params0),
                      static_cast<const unsigned char*>(params1), size_t(0), Layout(64, B0).off_gmat, x,
                      long(n), codes0, nu0, gamma0, codes1, nu1, gamma1);
@@ -485,14 +484,20 @@ namespace tq {
 hipError_t launch_quantize_d128_split(const void* params0, const void* params1, int b0, int b1,
                                       const void* x, int x_dtype, int64_t n, uint32_t* codes0,
                                       float* nu0, float* gamma0, uint32_t* codes1, float* nu1,
-                                      float* gamma1, hipStream_t s) {
+                                      float* gamma1, hipStream_t s, bool mse) {
   const bool f32 = x_dtype == 0;
-#define TQ_SPLIT_CASE(B0, B1)                                                                       \
-  if (b0 == B0 && b1 == B1)                                                                         \
-    return f32 ? launch_split<B0, B1, true>(params0, params1, x, n, codes0, nu0, gamma0, codes1, nu1, \
-                                            gamma1, s)                                              \
-               : launch_split<B0, B1, false>(params0, params1, x, n, codes0, nu0, gamma0, codes1,     \
-                                             nu1, gamma1, s);
+#define TQ_SPLIT_CASE(B0, B1)                                                                         \
+  if (b0 == B0 && b1 == B1) {                                                                         \
+    if (mse)                                                                                          \
+      return f32 ? launch_split<B0, B1, true, true>(params0, params1, x, n, codes0, nu0, nullptr, codes1, \
+                                                    nu1, nullptr, s)                                  \
+                 : launch_split<B0, B1, false, true>(params0, params1, x, n, codes0, nu0, nullptr,      \
+                                                     codes1, nu1, nullptr, s);                        \
+    return f32 ? launch_split<B0, B1, true>(params0, params1, x, n, codes0, nu0, gamma0, codes1, nu1,   \
+                                            gamma1, s)                                                \
+               : launch_split<B0, B1, false>(params0, params1, x, n, codes0, nu0, gamma0, codes1,       \
+                                             nu1, gamma1, s);                                         \
+  }
   TQ_SPLIT_CASE(2, 2) TQ_SPLIT_CASE(2, 3) TQ_SPLIT_CASE(2, 4)
   TQ_SPLIT_CASE(3, 2) TQ_SPLIT_CASE(3, 3) TQ_SPLIT_CASE(3, 4)
   TQ_SPLIT_CASE(4, 2) TQ_SPLIT_CASE(4, 3) TQ_SPLIT_CASE(4, 4)

@@ -44,20 +44,29 @@ __global__ __launch_bounds__(256) void generic_qprep_kernel(
                           : reinterpret_cast<const float*>(params + off_s) + size_t(o0 - d) * d;
   const int o = tid & 63, rq = tid >> 6;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int NQ = QR * QK / 256, NM = QO * QK / 256;   // staged values per thread
   for (int k0 = 0; k0 < d; k0 += QK) {
-    __syncthreads();                       // the previous round's tiles are no longer read
-    for (int i = tid; i < QR * QK; i += 256) {
-      const int r = i / QK, k = i % QK;
+    // all of this round's loads are issued before the first LDS store
+    float qv[NQ], mv[NM];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int i = tid + 256 * j, r = i / QK, k = i % QK;
       const long row = r0 + r;
-      float v = 0.f;
-      if (row < rows) {
-        const size_t at = size_t(row) * qpitch + k0 + k;
-        v = q_f32 ? static_cast<const float*>(q)[at]
-                  : __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at]) << 16);
-      }
-      Qs[r][k] = v;
+      const size_t at = size_t(row < rows ? row : rows - 1) * qpitch + k0 + k;
+      const float v = q_f32 ? static_cast<const float*>(q)[at]
+                            : __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at]) << 16);
+      qv[j] = row < rows ? v : 0.f;
     }
-    for (int i = tid; i < QO * QK; i += 256) Ms[i / QK][i % QK] = M[size_t(i / QK) * d + k0 + i % QK];
+#pragma unroll
+    for (int j = 0; j < NM; ++j) {
+      const int i = tid + 256 * j;
+      mv[j] = M[size_t(i / QK) * d + k0 + i % QK];
+    }
+    __syncthreads();                       // the previous round's tiles are no longer read
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) Qs[(tid + 256 * j) / QK][(tid + 256 * j) % QK] = qv[j];
+#pragma unroll
+    for (int j = 0; j < NM; ++j) Ms[(tid + 256 * j) / QK][(tid + 256 * j) % QK] = mv[j];
     __syncthreads();
 #pragma unroll 8
     for (int k = 0; k < QK; ++k) {

@@ -73,11 +73,12 @@ constexpr size_t score_ws_per_group(int b) {
 // ---- kernel launchers (defined in the .hip files), return hipError_t
 hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_dtype, int64_t n,
                                 uint32_t* codes, float* nu, float* gamma, hipStream_t s);
-// Fused d = 128 encoder on two 64-channel groups (each its own d = 64 parameter block).
+// Fused d = 128 encoder on two 64-channel groups (each its own d = 64 parameter block);
+// mse: the MSE quantizer alone (b - 1 index planes per group, no gamma).
 hipError_t launch_quantize_d128_split(const void* params0, const void* params1, int b0, int b1,
                                       const void* x, int x_dtype, int64_t n, uint32_t* codes0,
                                       float* nu0, float* gamma0, uint32_t* codes1, float* nu1,
-                                      float* gamma1, hipStream_t s);
+                                      float* gamma1, hipStream_t s, bool mse = false);
 // Tiled encoder, any valid d.  xpitch: elements between input rows (0: d), so that a
 // channel group of wider rows is read in place.
 hipError_t launch_quantize_gemm(const void* params, int d, int b, const void* x, int x_dtype,
