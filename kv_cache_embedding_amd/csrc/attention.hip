@@ -8,11 +8,14 @@
 //
 // attn_block_kernel: one workgroup per (group, pass of AH heads, block of KB keys).  Lanes
 //   first hold one key each: scaled logits, the block maximum per head, the weights
-//   p = exp(l - max) and p nu.  Then each wave walks its 64 keys with the lanes over the
-//   coordinates (64 per step): the plane words of the wave's keys are first staged in LDS
-//   (lane j loads key j's), a lane reads its word, takes its bit, looks the centroid up in
-//   LDS and accumulates it times the key's weight for every head.  Out: per block and head the maximum, the sum of
-//   p and the weighted sum of centroids.
+//   p = exp(l - max) and p nu, which go to LDS as one float4 per key.  Then each wave walks
+//   its 64 keys with the lanes over the coordinates (64 per step): the wave's keys are first
+//   staged in LDS, lane j turning key j's plane words of each 32-coordinate group into one
+//   16-byte slot of 4-bit indices (coordinate 8 q + i in bits 4 i .. of dword q), so that
+//   per key a lane reads the weights (a broadcast) and its coordinate's dword, extracts the
+//   index with one bit-field op, looks the centroid up in LDS and accumulates it times the
+//   key's weight for every head.  Out: per block and head the maximum, the sum of p and the
+//   weighted sum of centroids.
 // attn_combine_kernel: one workgroup per (group, head): merges the blocks (log-sum-exp) and
 //   applies Pi_v^T; threads split both sums into slices of independent float4 loads (rows
 //   of Pi_v are contiguous, so a slice reads coalesced columns).
@@ -38,19 +41,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// BV: index planes of a value; NC: 64-coordinate steps per chunk (NC divides d / 64)
+// Bits 0..7 of x to bits 0, 4, .., 28.
+__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
+  x &= 0xffu;
+  x = (x | (x << 12)) & 0x000f000fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  return (x | (x << 3)) & 0x11111111u;
+}
+
+// BV: index planes of a value (1..3); NC: 64-coordinate steps per chunk (NC divides d / 64)
 template <int BV, int NC>
 __global__ __launch_bounds__(256) void attn_block_kernel(
     const unsigned char* __restrict__ params_v, const float* __restrict__ logits,
     const uint32_t* __restrict__ vcodes, const float* __restrict__ vnu, int d, long G, long T,
     long nkb, long passes, float scale, float* __restrict__ part_m, float* __restrict__ part_s,
     float* __restrict__ part_acc) {
+  static_assert(BV >= 1 && BV <= 3, "a value's index fits one 4-bit field");
   constexpr int L = 1 << BV;
   const Header* hdr = reinterpret_cast<const Header*>(params_v);
   __shared__ float cen[L];
   __shared__ float red[4][AH];
   __shared__ float accs[4][AH][64 * NC];
-  __shared__ uint32_t kw[4][64][2 * NC * BV];    // words of a chunk for the wave's 64 keys
+  __shared__ uint4 kw[4][64][2 * NC];   // a chunk's 4-bit indices: [wave][key][32-coordinate group]
+  __shared__ float4 wsh[4][64];         // p nu of the wave's keys for the 4 heads
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar code loads
   if (tid < L) cen[tid] = hdr->cen[tid];
@@ -88,6 +101,7 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
     const float sp = wave_sum(p);
     if (lane == 0) red[wave][hh] = sp;
   }
+  wsh[wave][lane] = make_float4(w[0], w[1], w[2], w[3]);
   __syncthreads();
   const long prow = g * G + h0;                 // partial rows of this pass: prow + hh
 #pragma unroll
@@ -107,7 +121,15 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
     if (lane < nk) {
       const uint32_t* kc = vcodes + (size_t(g * T + tw0 + lane) * W + c0 / 32) * BV;
 #pragma unroll
-      for (int e = 0; e < 2 * NC * BV; ++e) kw[wave][lane][e] = kc[e];
+      for (int e = 0; e < 2 * NC; ++e) {
+        const uint32_t p0 = kc[e * BV], p1 = BV > 1 ? kc[e * BV + 1] : 0u, p2 = BV > 2 ? kc[e * BV + 2] : 0u;
+        uint32_t nib[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          nib[q] = spread_nibbles(p0 >> (8 * q)) | (spread_nibbles(p1 >> (8 * q)) << 1) |
+                   (spread_nibbles(p2 >> (8 * q)) << 2);
+        kw[wave][lane][e] = make_uint4(nib[0], nib[1], nib[2], nib[3]);
+      }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0);
@@ -117,23 +139,20 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
     for (int hh = 0; hh < AH; ++hh)
 #pragma unroll
       for (int i = 0; i < NC; ++i) acc[hh][i] = 0.f;
+    // this lane's coordinate within a 32-coordinate group: dword q of the slot, field i
+    const int q = (lane & 31) >> 3, fsh = 4 * (lane & 7);
+    const uint32_t* kwd = reinterpret_cast<const uint32_t*>(&kw[wave][0][0]) + q;
 #pragma unroll 4
     for (int j = 0; j < nk; ++j) {
-      float wj[AH];
-#pragma unroll
-      for (int hh = 0; hh < AH; ++hh)
-        wj[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[hh]), j));
+      const float4 wj = wsh[wave][j];
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        uint32_t idx = 0;
-#pragma unroll
-        for (int p = 0; p < BV; ++p) {
-          const uint32_t word = kw[wave][j][(2 * i + (lane >> 5)) * BV + p];
-          idx |= ((word >> (lane & 31)) & 1u) << p;
-        }
-        const float c = cen[idx];
-#pragma unroll
-        for (int hh = 0; hh < AH; ++hh) acc[hh][i] = fmaf(wj[hh], c, acc[hh][i]);
+        const uint32_t dw = kwd[(j * 2 * NC + 2 * i + (lane >> 5)) * 4];
+        const float c = cen[(dw >> fsh) & 0xfu];
+        acc[0][i] = fmaf(wj.x, c, acc[0][i]);
+        acc[1][i] = fmaf(wj.y, c, acc[1][i]);
+        acc[2][i] = fmaf(wj.z, c, acc[2][i]);
+        acc[3][i] = fmaf(wj.w, c, acc[3][i]);
       }
     }
 #pragma unroll
@@ -188,7 +207,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   if (sl < nsl) {
     for (int c4 = q4; c4 < d4; c4 += cols) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 8
       for (long k = sl; k < nkb; k += nsl) {
         const float e = __expf(pm[k] - M);
         const float4 x = pa[k * d4 + c4];
@@ -217,7 +236,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   if (sl < nsl) {
     for (int j4 = q4; j4 < d4; j4 += cols) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 8
       for (int i = sl; i < d; i += nsl) {
         const float ai = a[i];
         const float4 x = P4[size_t(i) * d4 + j4];
