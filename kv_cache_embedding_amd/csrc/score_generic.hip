@@ -10,10 +10,10 @@
 // generic_qprep_kernel: qh = Pi q and sh = S q in float32, a tiled NT product of the query
 //   rows with the stacked rows of Pi and S.
 // generic_score_kernel: one lane per key and HB heads per pass.  The key's plane words of a
-//   32-coordinate group come in with one vector load; per coordinate the index bits pick
-//   the centroid by a register select tree and the sign bit weights sh.  The query values
-//   are the same for every lane of a workgroup: staged in LDS and read as broadcasts; the
-//   workgroup also sums the staged sh for the -sum_t (S q)_t term.
+//   32-coordinate group come in with one vector load and are turned into 4-bit fields; per
+//   coordinate one LDS read gives the centroid and the sign bit that weights sh.  The query
+//   values are the same for every lane of a workgroup: staged in LDS and read as
+//   broadcasts; the workgroup also sums the staged sh for the -sum_t (S q)_t term.
 #include "tq_internal.h"
 
 namespace tq {
@@ -82,28 +82,21 @@ __global__ __launch_bounds__(256) void generic_qprep_kernel(
   }
 }
 
-// Centroid of the index held in bits b0 (low) .. b2 of one coordinate: a select tree over the
-// levels held in registers (no memory access on the per-coordinate path).
-template <int BITS>
-__device__ __forceinline__ float centroid(const float* C, uint32_t p0, uint32_t p1, uint32_t p2) {
-  if constexpr (BITS == 2) {
-    return p0 ? C[1] : C[0];
-  } else if constexpr (BITS == 3) {
-    const float lo = p0 ? C[1] : C[0], hi = p0 ? C[3] : C[2];
-    return p1 ? hi : lo;
-  } else {
-    const float a = p0 ? C[1] : C[0], b = p0 ? C[3] : C[2];
-    const float c = p0 ? C[5] : C[4], e = p0 ? C[7] : C[6];
-    const float lo = p1 ? b : a, hi = p1 ? e : c;
-    return p2 ? hi : lo;
-  }
+// Bits 0..7 of x to bits 0, 4, .., 28.
+__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
+  x &= 0xffu;
+  x = (x | (x << 12)) & 0x000f000fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  return (x | (x << 3)) & 0x11111111u;
 }
 
 // grid: one workgroup per (group, head pass, block of KEYS keys), flattened into x.  ACC adds
 // the estimate to the logits already there (the channel groups of a fractional rate).  The
 // pass's query values (HB heads of Pi q and S q) are staged in LDS, CH coordinates at a
 // time, as one float4 per coordinate and matrix: every lane reads the same address, a
-// broadcast.
+// broadcast.  A key's plane words of a 32-coordinate group are turned into 4-bit fields
+// (index bits, QJL sign in bit 3), so that per coordinate one bit-field op and one LDS read
+// of (centroid, sign) from a 16-entry table decode it.
 template <int BITS, bool PROD, bool ACC>
 __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     const unsigned char* __restrict__ params, const float* __restrict__ qs,
@@ -115,12 +108,11 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
   constexpr int CH = KEYS;                 // coordinates staged per round (one per thread)
   __shared__ float4 qsh[2][CH];            // [0]: Pi q, [1]: S q of the pass's 4 heads
   __shared__ float4 red[KEYS / 64];        // sum_t (S q)_t: per-wave partial sums
+  __shared__ float2 tab[16];               // field -> (centroid, QJL sign bit as 0 / 1)
   const Header* hdr = reinterpret_cast<const Header*>(params);
-  float C[L];
-#pragma unroll
-  for (int i = 0; i < L; ++i) C[i] = hdr->cen[i];
   const float alpha = hdr->alpha;
   const int tid = threadIdx.x;
+  if (tid < 16) tab[tid] = make_float2(hdr->cen[(tid & 7) < L ? (tid & 7) : L - 1], float(tid >> 3));
 
   const long blk = blockIdx.x;
   const long kb = blk % kblocks;
@@ -140,6 +132,30 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     const long h = h0 + (hh < nh ? hh : nh - 1);
     qrow[hh] = qs + size_t(g * G + h) * 2 * d;
   }
+  // a word's BITS planes (one vector load where the size allows)
+  auto load_word = [&](int wi, uint32_t* pl) {
+    const uint32_t* src = kc + size_t(wi) * BITS;
+    if constexpr (BITS == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      pl[0] = v.x; pl[1] = v.y; pl[2] = v.z; pl[3] = v.w;
+    } else if constexpr (BITS == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      pl[0] = v.x; pl[1] = v.y; pl[2] = 0u; pl[3] = 0u;
+    } else {
+      pl[0] = src[0]; pl[1] = src[1]; pl[2] = src[2]; pl[3] = 0u;
+    }
+  };
+  // loads in flight before the first barrier: the logits this launch adds to (ACC), the
+  // key's nu and gamma, and the first word; later words are loaded one word ahead
+  float prev[HB] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (ACC) {
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh)
+      if (valid && hh < nh) prev[hh] = logits[size_t(g * G + h0 + hh) * T + t];
+  }
+  const float n_k = nu[key], g_k = gamma[key];
+  uint32_t cur[4];
+  load_word(0, cur);
   float4 mse = make_float4(0.f, 0.f, 0.f, 0.f), zs = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 spart = make_float4(0.f, 0.f, 0.f, 0.f);   // this thread's staged S q values, summed
   for (int c0 = 0; c0 < d; c0 += CH) {
@@ -159,36 +175,34 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     }
     __syncthreads();
     for (int w = 0; w < cn / 32; ++w) {
-      const uint32_t* src = kc + size_t(c0 / 32 + w) * BITS;
-      uint32_t pl[4] = {0u, 0u, 0u, 0u};
-      if constexpr (BITS == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
-        pl[0] = v.x; pl[1] = v.y; pl[2] = v.z; pl[3] = v.w;
-      } else if constexpr (BITS == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
-        pl[0] = v.x; pl[1] = v.y;
-      } else {
+      const int wi = c0 / 32 + w;
+      uint32_t pl[4] = {cur[0], cur[1], cur[2], cur[3]};
+      if (wi + 1 < words) load_word(wi + 1, cur);
+      // fields: index bits 0 .. BITS-2, the QJL sign in bit 3 (coordinate 8 q + i in bits
+      // 4 i .. of nib[q])
+      uint32_t nib[4];
 #pragma unroll
-        for (int p = 0; p < BITS; ++p) pl[p] = src[p];
+      for (int q = 0; q < 4; ++q) {
+        uint32_t v = spread_nibbles(pl[0] >> (8 * q));
+        if constexpr (BITS > 2) v |= spread_nibbles(pl[1] >> (8 * q)) << 1;
+        if constexpr (BITS > 3) v |= spread_nibbles(pl[2] >> (8 * q)) << 2;
+        if constexpr (PROD) v |= spread_nibbles(pl[BITS - 1] >> (8 * q)) << 3;
+        nib[q] = v;
       }
 #pragma unroll 8
       for (int e = 0; e < 32; ++e) {
-        const uint32_t p0 = (pl[0] >> e) & 1u;
-        const uint32_t p1 = BITS > 2 ? (pl[1] >> e) & 1u : 0u;
-        const uint32_t p2 = BITS > 3 ? (pl[2] >> e) & 1u : 0u;
-        const float c = centroid<BITS>(C, p0, p1, p2);
+        const float2 cz = tab[(nib[e >> 3] >> (4 * (e & 7))) & 0xfu];
         const float4 a = qsh[0][32 * w + e];
-        mse.x = fmaf(a.x, c, mse.x);
-        mse.y = fmaf(a.y, c, mse.y);
-        mse.z = fmaf(a.z, c, mse.z);
-        mse.w = fmaf(a.w, c, mse.w);
+        mse.x = fmaf(a.x, cz.x, mse.x);
+        mse.y = fmaf(a.y, cz.x, mse.y);
+        mse.z = fmaf(a.z, cz.x, mse.z);
+        mse.w = fmaf(a.w, cz.x, mse.w);
         if constexpr (PROD) {
-          const float zf = float((pl[BITS - 1] >> e) & 1u);
           const float4 b = qsh[1][32 * w + e];
-          zs.x = fmaf(b.x, zf, zs.x);
-          zs.y = fmaf(b.y, zf, zs.y);
-          zs.z = fmaf(b.z, zf, zs.z);
-          zs.w = fmaf(b.w, zf, zs.w);
+          zs.x = fmaf(b.x, cz.y, zs.x);
+          zs.y = fmaf(b.y, cz.y, zs.y);
+          zs.z = fmaf(b.z, cz.y, zs.z);
+          zs.w = fmaf(b.w, cz.y, zs.w);
         }
       }
     }
@@ -211,7 +225,6 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     s4[3] = (a.w + b.w) + (c.w + e.w);
   }
   if (!valid) return;
-  const float n_k = nu[key], g_k = gamma[key];
   const float m4[HB] = {mse.x, mse.y, mse.z, mse.w};
   const float z4[HB] = {zs.x, zs.y, zs.z, zs.w};
 #pragma unroll
@@ -220,8 +233,7 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     const long h = h0 + hh;
     float l = m4[hh];
     if constexpr (PROD) l = fmaf(alpha * g_k, 2.f * z4[hh] - s4[hh], l);
-    float* dst = logits + size_t(g * G + h) * T + t;
-    *dst = ACC ? *dst + n_k * l : n_k * l;
+    logits[size_t(g * G + h) * T + t] = ACC ? prev[hh] + n_k * l : n_k * l;
   }
 }
 
