@@ -595,7 +595,8 @@ def bench_fractional(args):
     q_flops = n * 4.0 * (d0 * d0 + (d - d0) ** 2)
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     s_gbs = s_bytes / (s_ms * 1e-3) / 1e9
-    rq = {"kernel": "tq_quantize_split (tiled encoder, two channel groups)", "bound": "hbm",
+    rq = {"kernel": "tq_quantize_split (fused d = 128 encoder, split mode: both groups in one pass)",
+          "bound": "hbm",
           "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_gbs / HBM_PEAK_GBS,
           "traffic": None,
           "note": f"algorithmic bytes per vector: {d * 2} B bf16 key in, {code_bytes} B codes, nu and gamma "
