@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_layer",
                     choices=["decode_layer", "long_context", "embedding_search", "decode_attention",
-                             "fractional_kv"])
+                             "fractional_kv", "ubench"])
     ap.add_argument("--rate", type=float, default=3.5, help="fractional_kv: bits per channel (2.5 or 3.5)")
     ap.add_argument("--bits", type=int, default=0, help="embedding_search: b (default 4)")
     ap.add_argument("--replicas", type=int, default=8, help="resident input copies cycled per step")
@@ -57,6 +57,64 @@ def parse():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the oracle baseline's record."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_ubench(args):
+    """Achievable peaks of this MI355X next to the published ones: HBM from a 2 GiB device
+    copy (read + write bytes), dense bf16 / fp16 MFMA from a library GEMM (8192^3)."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def median_ms(fn, reps=20):
+        ts = []
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    n = (2 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    copy_ms = median_ms(lambda: b.copy_(a))
+    copy_gbs = 2 * n * 4 / (copy_ms * 1e-3) / 1e9
+    del a, b
+    out = {}
+    for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        m = 8192
+        x = torch.randn(m, m, device=dev).to(dt)
+        y = torch.randn(m, m, device=dev).to(dt)
+        ms = median_ms(lambda: torch.mm(x, y), reps=10)
+        out[name] = 2.0 * m ** 3 / (ms * 1e-3) / 1e12
+        del x, y
+    result = {
+        "metric": "achievable MI355X peaks (device copy, library GEMM), 1 MI355X",
+        "value": copy_gbs, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+        "hbm_copy_gbs": copy_gbs, "hbm_copy_frac_of_published": copy_gbs / HBM_PEAK_GBS,
+        "bf16_gemm_tflops": out["bf16"], "bf16_frac_of_published": out["bf16"] / BF16_MFMA_PEAK_TFLOPS,
+        "fp16_gemm_tflops": out["fp16"], "fp16_frac_of_published": out["fp16"] / FP16_MFMA_PEAK_TFLOPS,
+        "note": "published: HBM 8000 GB/s, dense bf16/fp16 MFMA 2500 TFLOP/s; the rooflines of the other "
+                "workloads are quoted against the published figures",
+    }
+    print(json.dumps(result), flush=True)
 
 
 def source_hash(*names) -> str:
@@ -112,7 +170,7 @@ def cpu_baseline(workload, seconds: float):
         vectors += w.T
         logits += est.size
     return {
-        "value": logits / elapsed, "unit": "logits/s", "cores": int(cores), "kind": "oracle",
+        "value": logits / elapsed, "unit": "logits/s", "cores": int(cores), "cpu_model": cpu_model(), "kind": "oracle",
         "sample": f"{heads} of {w.n_kv} KV heads ({vectors} keys quantized, {logits} logits), "
                   f"float64 NumPy oracle, {elapsed:.1f} s",
         "vectors_per_s": vectors / elapsed,
@@ -149,7 +207,7 @@ def cpu_baseline_search(w, b, seconds: float):
         vectors += x.shape[0]
         pairs += est.size
     return {
-        "value": pairs / elapsed, "unit": "scores/s", "cores": int(cores), "kind": "oracle",
+        "value": pairs / elapsed, "unit": "scores/s", "cores": int(cores), "cpu_model": cpu_model(), "kind": "oracle",
         "sample": f"{vectors} of {w.n} vectors (first 2048 of {blocks} seeded blocks) quantized and "
                   f"scored against all {w.nq} queries with top-{w.k}, float64 NumPy oracle, {elapsed:.1f} s",
         "vectors_per_s": vectors / elapsed,
@@ -311,7 +369,7 @@ def cpu_baseline_attention(w, b_k, b_v, seconds: float):
         heads += 1
         pairs += lg.size
     return {
-        "value": pairs / elapsed, "unit": "pairs/s", "cores": int(cores), "kind": "oracle",
+        "value": pairs / elapsed, "unit": "pairs/s", "cores": int(cores), "cpu_model": cpu_model(), "kind": "oracle",
         "sample": f"{heads} of {w.n_kv} KV heads ({heads * w.T} keys and values quantized, {pairs} "
                   f"(query head, key) pairs attended), float64 NumPy oracle, {elapsed:.1f} s",
     }
@@ -490,7 +548,7 @@ def cpu_baseline_fractional(w, b0, b1, seconds: float):
         vectors += w.T
         logits += est.size
     return {
-        "value": logits / elapsed, "unit": "logits/s", "cores": int(cores), "kind": "oracle",
+        "value": logits / elapsed, "unit": "logits/s", "cores": int(cores), "cpu_model": cpu_model(), "kind": "oracle",
         "sample": f"{heads} of {w.n_kv} KV heads ({vectors} keys quantized, {logits} logits), "
                   f"float64 NumPy oracle, {elapsed:.1f} s",
     }
@@ -696,6 +754,9 @@ def main():
         return
     if args.workload == "fractional_kv":
         bench_fractional(args)
+        return
+    if args.workload == "ubench":
+        bench_ubench(args)
         return
 
     import torch
