@@ -877,6 +877,34 @@ def main():
     ms_step = min(serial_ms, pipe_ms)
     n_logits = groups * G * T
 
+    # The pages' comparison (attention logits with 4-bit keys against 32-bit keys): the same
+    # logits from a float32 copy of the cache by a library batched GEMM, K q^T per group (the
+    # cache is the contiguous left operand), beside the tq_score_ip call on the 4-bit codes.
+    # long_context only: its 8.6 GB of float32 keys cannot be served from the 256 MB MALL.
+    keys32 = None
+    if args.workload == "long_context":
+        kf = xs[0].view(groups, T, d).float()
+        qt = q.view(groups, G, d).float().transpose(1, 2).contiguous()
+        o32 = torch.empty((groups, T, G), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            torch.bmm(kf, qt, out=o32)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            torch.bmm(kf, qt, out=o32)
+        e1.record()
+        torch.cuda.synchronize()
+        ms32 = e0.elapsed_time(e1) / 5
+        keys32 = {"fp32_keys_ms": ms32, "fp32_keys_gbs": n * d * 4 / (ms32 * 1e-3) / 1e9,
+                  "tq_score_ms": s_ms, "speedup": ms32 / s_ms,
+                  "note": "logits of all query heads: float32 keys through torch.bmm vs b-bit TurboQuant "
+                          "codes through tq_score_ip (query prep included); the pages report up to 8x "
+                          "for 4-bit vs 32-bit keys on another GPU"}
+        del kf, o32
+        torch.cuda.empty_cache()
+
     # algorithmic work per launch
     q_flops = n * 4.0 * d * d                       # Pi x and S' r': 2 d^2 each
     q_bytes = n * (d * 2 + d // 8 * b + 8)          # bf16 keys in, codes + nu + gamma out
@@ -936,6 +964,8 @@ def main():
         "context": "pages: up to 8x faster attention logits with 4-bit keys vs 32-bit keys on H100 "
                    "(no absolute numbers); not a target",
     }
+    if keys32 is not None:
+        result["vs_fp32_keys"] = keys32
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
