@@ -117,6 +117,27 @@ def bench_ubench(args):
     print(json.dumps(result), flush=True)
 
 
+def time_per_launch(torch, fn, R: int, K: int) -> float:
+    """Average duration (ms) of one call fn(r): the R calls r = 0 .. R-1 are captured into one
+    HIP graph (so the graph launch overhead is paid once per R calls, not per call) and the
+    graph is replayed until about K calls ran, between two events on the current stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            fn(r)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, K // R)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * R)
+
+
 def source_hash(*names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -454,7 +475,6 @@ def bench_attention(args):
         return g
 
     g_att = [capture(attend, r) for r in range(R)]
-    g_vq = [capture(vquant, r) for r in range(R)]
     g_app = [capture(append, r) for r in range(R)]
     for r in range(R):
         g_att[r].replay()
@@ -478,8 +498,8 @@ def bench_attention(args):
         g_att[i % R].replay()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / K
-    a_ms = timed(g_att)
-    vq_ms = timed(g_vq)
+    a_ms = time_per_launch(torch, attend, R, K)
+    vq_ms = time_per_launch(torch, vquant, R, K)
     app_ms = timed(g_app)
     pairs = groups * G * T
     a_bytes = n * per_key + groups * G * d * 4
@@ -618,8 +638,6 @@ def bench_fractional(args):
         return g
 
     g_step = [capture(lambda r: (quantize(r), score(r)), r) for r in range(R)]
-    g_q = [capture(quantize, r) for r in range(R)]
-    g_s = [capture(score, r) for r in range(R)]
     for r in range(R):
         g_step[r].replay()
     torch.cuda.synchronize()
@@ -632,19 +650,8 @@ def bench_fractional(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    def timed(gs):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(K):
-            gs[i % R].replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
-
-    q_ms = timed(g_q)
-    s_ms = timed(g_s)
+    q_ms = time_per_launch(torch, quantize, R, K)
+    s_ms = time_per_launch(torch, score, R, K)
     ms_step = (t1 - t0) * 1e3 / K
     n_logits = groups * G * T
     code_bytes = (d0 * b0 + (d - d0) * b1) // 8 + 16          # both groups' codes, nu, gamma
@@ -702,10 +709,8 @@ def bench_fractional(args):
         vquant(r)
         attend(r)
     torch.cuda.synchronize()
-    g_vq = [capture(vquant, r) for r in range(R)]
-    g_att = [capture(attend, r) for r in range(R)]
-    vq_ms = timed(g_vq)
-    a_ms = timed(g_att)
+    vq_ms = time_per_launch(torch, vquant, R, K)
+    a_ms = time_per_launch(torch, attend, R, K)
 
     result = {
         "metric": "quantized-key logits/s at a fractional rate (two channel groups), 1 MI355X",
@@ -825,8 +830,6 @@ def main():
         return g
 
     g_step = [capture(lambda r: (quantize(r), score(r)), r) for r in range(R)]
-    g_q = [capture(quantize, r) for r in range(R)]
-    g_s = [capture(score, r) for r in range(R)]
     for r in range(R):
         g_step[r].replay()
     torch.cuda.synchronize()
@@ -861,19 +864,8 @@ def main():
     serial_ms = wall(g_step)
     pipe_ms = wall(g_pipe)
 
-    def timed(gs):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(K):
-            gs[i % R].replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
-
-    q_ms = timed(g_q)
-    s_ms = timed(g_s)
+    q_ms = time_per_launch(torch, quantize, R, K)
+    s_ms = time_per_launch(torch, score, R, K)
     ms_step = min(serial_ms, pipe_ms)
     n_logits = groups * G * T
 
