@@ -29,7 +29,8 @@
  *     crosses the ABI.
  *   - Supported shapes: d % 64 == 0, 64 <= d <= 4096; b in {2, 3, 4} total bits
  *     (b-1 bits of Lloyd-Max index + 1 QJL bit); m = d QJL rows. Individual calls may
- *     narrow this (TQ_EUNSUPPORTED).
+ *     narrow this (TQ_EUNSUPPORTED). The fractional-rate (*_split) calls take rows of two
+ *     channel groups, each a supported d with its own b.
  *   - n == 0 (or groups/T/nq == 0) is a no-op returning TQ_OK.
  *   - NaN / Inf inputs give unspecified codes and estimates but never a fault.
  *   - A zero vector gets nu = 0, its rotated coordinates are taken as 0, and every
