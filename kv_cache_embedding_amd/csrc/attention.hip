@@ -18,7 +18,8 @@
 //   weighted sum of centroids.
 // attn_combine_kernel: one workgroup per (group, head): merges the blocks (log-sum-exp) and
 //   applies Pi_v^T; threads split both sums into slices of independent float4 loads (rows
-//   of Pi_v are contiguous, so a slice reads coalesced columns).
+//   of Pi_v are contiguous, so a slice reads coalesced columns), the first loads of both
+//   issued before the maximum and the sum are reduced.
 #include "tq_internal.h"
 
 #include <cmath>
@@ -28,6 +29,7 @@ namespace {
 
 constexpr int AH = 4;      // query heads per pass
 constexpr int KB = 256;    // keys per workgroup (64 per wave)
+constexpr int CT = 1024;   // threads of a combine workgroup (one per (group, head))
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -171,56 +173,83 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
 }
 
 // out rows are opitch floats apart (a channel group of wider output rows: its columns only)
-__global__ __launch_bounds__(256) void attn_combine_kernel(
+__global__ __launch_bounds__(CT) void attn_combine_kernel(
     const unsigned char* __restrict__ params_v, size_t off_pi, int d, long nkb,
     const float* __restrict__ part_m, const float* __restrict__ part_s,
     const float* __restrict__ part_acc, float* __restrict__ out, long opitch) {
+  constexpr int NW = CT / 64;
+  constexpr int PF = 8;              // loads of each sum issued before the reductions
   extern __shared__ float4 lds4[];   // [slices][d / 4] partial sums, then a[d / 4]
-  __shared__ float red[4];
+  __shared__ float red[NW];
   const long row = blockIdx.x;   // group * G + head
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* pm = part_m + row * nkb;
   const float* ps = part_s + row * nkb;
+  // threads = (float4 column q4, slice sl): a slice sums every nsl-th block (and, for the
+  // inverse rotation, every nsl-th row of Pi_v); d / 4 <= CT, so a thread owns one column
+  const int d4 = d / 4;
+  const int cols = d4 < CT ? d4 : CT;
+  const int nsl = CT / cols;
+  const int q4 = tid % cols, sl = tid / cols;
+  const bool act = sl < nsl;
+  const float4* pa = reinterpret_cast<const float4*>(part_acc) + row * nkb * d4;
+  const float4* P4 = reinterpret_cast<const float4*>(params_v + off_pi);
+  float4 pacc[PF], ppi[PF];
+  float pmk[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const long k = sl + long(i) * nsl;
+    const int r = sl + i * nsl;
+    const bool okk = act && k < nkb, okr = act && r < d;
+    pacc[i] = okk ? pa[k * d4 + q4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    pmk[i] = okk ? pm[k] : -INFINITY;
+    ppi[i] = okr ? P4[size_t(r) * d4 + q4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
   float mx = -INFINITY;
-  for (long k = tid; k < nkb; k += 256) mx = fmaxf(mx, pm[k]);
+  for (long k = tid; k < nkb; k += CT) mx = fmaxf(mx, pm[k]);
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
   __syncthreads();
   float sum = 0.f;
-  for (long k = tid; k < nkb; k += 256) sum += __expf(pm[k] - M) * ps[k];
+  for (long k = tid; k < nkb; k += CT) sum += __expf(pm[k] - M) * ps[k];
   sum = wave_sum(sum);
   if (lane == 0) red[wave] = sum;
   __syncthreads();
-  const float inv = 1.f / ((red[0] + red[1]) + (red[2] + red[3]));
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) tot += red[i];
+  const float inv = 1.f / tot;
 
-  // threads = (float4 column q4, slice): a slice sums every nsl-th block, the slices are
-  // then added in LDS; all loads of a thread are independent
-  const int d4 = d / 4;
-  const int cols = d4 < 256 ? d4 : 256;
-  const int nsl = 256 / cols;
-  const int q4 = tid % cols, sl = tid / cols;
-  float4* part = lds4;                 // [nsl][d4]
+  float4* part = lds4;                    // [nsl][d4]
   float4* av = lds4 + size_t(nsl) * d4;   // a / sum, d4 float4
-  const float4* pa = reinterpret_cast<const float4*>(part_acc) + row * nkb * d4;
-  if (sl < nsl) {
-    for (int c4 = q4; c4 < d4; c4 += cols) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-      for (long k = sl; k < nkb; k += nsl) {
-        const float e = __expf(pm[k] - M);
-        const float4 x = pa[k * d4 + c4];
-        v.x = fmaf(e, x.x, v.x);
-        v.y = fmaf(e, x.y, v.y);
-        v.z = fmaf(e, x.z, v.z);
-        v.w = fmaf(e, x.w, v.w);
-      }
-      part[sl * d4 + c4] = v;
+  if (act) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const float e = __expf(pmk[i] - M);   // 0 for the slots past nkb
+      v.x = fmaf(e, pacc[i].x, v.x);
+      v.y = fmaf(e, pacc[i].y, v.y);
+      v.z = fmaf(e, pacc[i].z, v.z);
+      v.w = fmaf(e, pacc[i].w, v.w);
     }
+#pragma unroll 8
+    for (long k = sl + long(PF) * nsl; k < nkb; k += nsl) {
+      const float e = __expf(pm[k] - M);
+      const float4 x = pa[k * d4 + q4];
+      v.x = fmaf(e, x.x, v.x);
+      v.y = fmaf(e, x.y, v.y);
+      v.z = fmaf(e, x.z, v.z);
+      v.w = fmaf(e, x.w, v.w);
+    }
+    part[sl * d4 + q4] = v;
   }
   __syncthreads();
-  for (int c4 = tid; c4 < d4; c4 += 256) {
+  for (int c4 = tid; c4 < d4; c4 += CT) {
     float4 v = part[c4];
     for (int t = 1; t < nsl; ++t) {
       const float4 x = part[t * d4 + c4];
@@ -230,27 +259,33 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     av[c4] = v;
   }
   __syncthreads();
-  // out = Pi_v^T a: thread (float4 of outputs j4, slice of rows i); rows of Pi_v contiguous
+  // out = Pi_v^T a: thread (float4 of outputs q4, slice of rows sl); rows of Pi_v contiguous
   const float* a = reinterpret_cast<const float*>(av);
-  const float4* P4 = reinterpret_cast<const float4*>(params_v + off_pi);
-  if (sl < nsl) {
-    for (int j4 = q4; j4 < d4; j4 += cols) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-      for (int i = sl; i < d; i += nsl) {
-        const float ai = a[i];
-        const float4 x = P4[size_t(i) * d4 + j4];
-        v.x = fmaf(x.x, ai, v.x);
-        v.y = fmaf(x.y, ai, v.y);
-        v.z = fmaf(x.z, ai, v.z);
-        v.w = fmaf(x.w, ai, v.w);
-      }
-      part[sl * d4 + j4] = v;
+  if (act) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int r = sl + i * nsl;
+      const float ai = r < d ? a[r] : 0.f;
+      v.x = fmaf(ppi[i].x, ai, v.x);
+      v.y = fmaf(ppi[i].y, ai, v.y);
+      v.z = fmaf(ppi[i].z, ai, v.z);
+      v.w = fmaf(ppi[i].w, ai, v.w);
     }
+#pragma unroll 8
+    for (int r = sl + PF * nsl; r < d; r += nsl) {
+      const float ai = a[r];
+      const float4 x = P4[size_t(r) * d4 + q4];
+      v.x = fmaf(x.x, ai, v.x);
+      v.y = fmaf(x.y, ai, v.y);
+      v.z = fmaf(x.z, ai, v.z);
+      v.w = fmaf(x.w, ai, v.w);
+    }
+    part[sl * d4 + q4] = v;
   }
   __syncthreads();
   float4* o4 = reinterpret_cast<float4*>(out + row * opitch);
-  for (int j4 = tid; j4 < d4; j4 += 256) {
+  for (int j4 = tid; j4 < d4; j4 += CT) {
     float4 v = part[j4];
     for (int t = 1; t < nsl; ++t) {
       const float4 x = part[t * d4 + j4];
@@ -304,8 +339,8 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const Layout lay(d, b_v);
-  const int d4 = d / 4, cols = d4 < 256 ? d4 : 256, nsl = 256 / cols;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(256),
+  const int d4 = d / 4, cols = d4 < CT ? d4 : CT, nsl = CT / cols;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT),
                      (size_t(nsl) * d4 + d4) * 16, s, pv, lay.off_pi, d, nkb, part_m, part_s,
                      part_acc, out, long(opitch > 0 ? opitch : d));
   return hipGetLastError();
