@@ -70,6 +70,52 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def measured_copy_gbs(torch, mib: int = 1024, reps: int = 10) -> float:
+    """Achievable HBM rate on this GPU: a device copy of `mib` MiB, read + write bytes."""
+    a = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2.0 * mib * 1024 * 1024 / (ms * 1e-3) / 1e9
+
+
+def measured_gemm_tflops(torch, dtype, m: int = 8192, reps: int = 5) -> float:
+    """Achievable dense MFMA rate on this GPU for dtype: a library GEMM of m x m x m."""
+    x = torch.randn(m, m, device="cuda:0").to(dtype)
+    y = torch.randn(m, m, device="cuda:0").to(dtype)
+    for _ in range(2):
+        torch.mm(x, y)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x, y
+    return 2.0 * m ** 3 / (ms * 1e-3) / 1e12
+
+
+def with_measured_peak(roof: dict, measured: float, what: str) -> dict:
+    """Adds the achievable rate measured in this run next to the published peak."""
+    roof["measured_peak"] = measured
+    roof["frac_of_measured_peak"] = roof["achieved"] / measured
+    roof["measured_peak_source"] = what
+    return roof
+
+
 def bench_ubench(args):
     """Achievable peaks of this MI355X next to the published ones: HBM from a 2 GiB device
     copy (read + write bytes), dense bf16 / fp16 MFMA from a library GEMM (8192^3)."""
@@ -352,6 +398,10 @@ def bench_search(args):
                      "hbm_gbs": q_bytes / (q_ms * 1e-3) / 1e9},
         "topk": {"ms": t_ms, "scores_per_s": pairs / (t_ms * 1e-3), "hbm_gbs": t_bytes / (t_ms * 1e-3) / 1e9},
     }
+    with_measured_peak(result["roofline"], measured_gemm_tflops(torch, torch.float16),
+                       "8192^3 fp16 library GEMM in this run")
+    with_measured_peak(result["roofline_quantize"], measured_gemm_tflops(torch, torch.bfloat16),
+                       "8192^3 bf16 library GEMM in this run")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_search(w, b, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -534,6 +584,7 @@ def bench_attention(args):
                    "note": f"tq_append of one token per group ({groups} groups): key (prod) + value "
                            "(mse), as one decode step writes them"},
     }
+    with_measured_peak(result["roofline"], measured_copy_gbs(torch), "1 GiB device copy in this run (read + write bytes)")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_attention(w, b_k, b_v, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -742,6 +793,9 @@ def bench_fractional(args):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_fractional(w, b0, b1, args.cpu_seconds)
+    copy_gbs = measured_copy_gbs(torch)
+    for key in ("roofline", "roofline_other"):
+        with_measured_peak(result[key], copy_gbs, "1 GiB device copy in this run (read + write bytes)")
     print(json.dumps(result), flush=True)
 
 
@@ -958,6 +1012,9 @@ def main():
     }
     if keys32 is not None:
         result["vs_fp32_keys"] = keys32
+    copy_gbs = measured_copy_gbs(torch)
+    with_measured_peak(result["roofline"], copy_gbs, "1 GiB device copy in this run (read + write bytes)")
+    with_measured_peak(result["roofline_score"], copy_gbs, "1 GiB device copy in this run (read + write bytes)")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
