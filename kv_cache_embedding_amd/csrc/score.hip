@@ -51,18 +51,21 @@ int cu_count_s() {
 // ------------------------------------------------------------------------ query prep
 // Two workgroups per virtual group (G query heads): type 0 forms qh = Pi q and the MSE rows
 // of the MFMA A operands, type 1 forms sh = S q and the QJL rows; the two halves share
-// nothing.  Thread i accumulates row i % D over half of the columns (i / D), reading
-// column k of the transposed matrix with one contiguous load per wave; all its loads are
-// issued before the first product.  Outputs: rows 4 h + part of the A operands in register
+// nothing.  Thread i accumulates row i % D over a quarter of the columns (i / D), reading
+// column k of the transposed matrix with one contiguous load per wave; its matrix loads are
+// issued before the query loads and all of them before the first product, so the kernel
+// waits on one round trip to memory.  Outputs: rows 4 h + part of the A operands in register
 // order ws[g][m][lane][16 bytes] (m = 2 word + j; lane l holds row l % 16) and the
 // epilogue constants per head.
+constexpr int QP_THREADS = 512;
+constexpr int QP_SLICES = QP_THREADS / D;     // column slices per row
 template <int BITS>
-__global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* __restrict__ params,
-                                                           size_t off_tr,
-                                                           const void* __restrict__ q, int q_f32,
-                                                           unsigned char* __restrict__ ws) {
+__global__ __launch_bounds__(QP_THREADS) void score_qprep_kernel(const unsigned char* __restrict__ params,
+                                                                 size_t off_tr,
+                                                                 const void* __restrict__ q, int q_f32,
+                                                                 unsigned char* __restrict__ ws) {
   constexpr int NW = score_words(BITS);
-  constexpr int KH = D / 2;
+  constexpr int KS = D / QP_SLICES;        // columns per slice
   const Header* hdr = reinterpret_cast<const Header*>(params);
   const long g = blockIdx.x >> 1;
   const int type = blockIdx.x & 1;         // 0: Pi (MSE rows), 1: S (QJL rows)
@@ -73,37 +76,42 @@ __global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* _
   const float emax = hdr->emax, esum = hdr->esum, alpha = hdr->alpha;
   const int ne = hdr->ne;
   __shared__ float4 qv[D];                 // q of the G heads, column-major: qv[k] = heads 0..3
-  __shared__ float part_sum[2][G][D];
+  __shared__ float part_sum[QP_SLICES][G][D];
   __shared__ float stats[G][2];            // per head: max |v|, sum v
 
-  for (int i = tid; i < G * D; i += 256) {
-    const long off = g * G * D + i;
-    reinterpret_cast<float*>(qv)[(i % D) * G + i / D] =
-        q_f32 ? static_cast<const float*>(q)[off]
-              : __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[off]) << 16);
-  }
   {
-    const int row = tid % D, half = tid / D;
+    const int row = tid % D, slice = tid / D;
     const float* col = reinterpret_cast<const float*>(params + off_tr) + size_t(type) * D * D +
-                       size_t(half) * KH * D + row;
-    float m[KH];
+                       size_t(slice) * KS * D + row;
+    float m[KS];
 #pragma unroll
-    for (int k = 0; k < KH; ++k) m[k] = col[size_t(k) * D];
+    for (int k = 0; k < KS; ++k) m[k] = col[size_t(k) * D];
+    for (int i = tid; i < G * D; i += QP_THREADS) {
+      const long off = g * G * D + i;
+      reinterpret_cast<float*>(qv)[(i % D) * G + i / D] =
+          q_f32 ? static_cast<const float*>(q)[off]
+                : __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[off]) << 16);
+    }
     __syncthreads();                       // q is in LDS
     float acc[G] = {};
 #pragma unroll
-    for (int k = 0; k < KH; ++k) {
-      const float4 qk = qv[half * KH + k];
+    for (int k = 0; k < KS; ++k) {
+      const float4 qk = qv[slice * KS + k];
       acc[0] = fmaf(m[k], qk.x, acc[0]);
       acc[1] = fmaf(m[k], qk.y, acc[1]);
       acc[2] = fmaf(m[k], qk.z, acc[2]);
       acc[3] = fmaf(m[k], qk.w, acc[3]);
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) part_sum[half][h][row] = acc[h];
+    for (int h = 0; h < G; ++h) part_sum[slice][h][row] = acc[h];
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += 256) part_sum[0][i / D][i % D] += part_sum[1][i / D][i % D];
+  for (int i = tid; i < G * D; i += QP_THREADS) {
+    float t = part_sum[0][i / D][i % D];
+#pragma unroll
+    for (int sl = 1; sl < QP_SLICES; ++sl) t += part_sum[sl][i / D][i % D];
+    part_sum[0][i / D][i % D] = t;
+  }
   __syncthreads();
   float (*v)[D] = part_sum[0];             // v[h][row]: qh (type 0) or sh (type 1)
   if (tid < G * 2 * 16) {
@@ -126,7 +134,7 @@ __global__ __launch_bounds__(256) void score_qprep_kernel(const unsigned char* _
 
   unsigned char* base = ws + size_t(g) * score_ws_per_group(BITS);
   // A operand chunks of this half: per head 2 NW MFMAs x 4 K groups x 2 rows
-  for (int item = tid; item < G * 2 * NW * 8; item += 256) {
+  for (int item = tid; item < G * 2 * NW * 8; item += QP_THREADS) {
     const int h = item / (2 * NW * 8), r = item % (2 * NW * 8);
     const int m = r / 8, part = 2 * type + (r / 4) % 2, grp = r % 4;
     const int lane = 16 * grp + 4 * h + part;
@@ -278,7 +286,7 @@ hipError_t launch_b(const void* params, const void* q, int q_dtype, const uint32
   const Layout lay(D, BITS);
   const long qpg = long(Gq / G);
   const int64_t groups = kv_groups * qpg;       // virtual groups of 4 query heads
-  hipLaunchKernelGGL((score_qprep_kernel<BITS>), dim3(unsigned(2 * groups)), dim3(256), 0, s,
+  hipLaunchKernelGGL((score_qprep_kernel<BITS>), dim3(unsigned(2 * groups)), dim3(QP_THREADS), 0, s,
                      static_cast<const unsigned char*>(params), lay.off_tr, q,
                      q_dtype == 0 ? 1 : 0, static_cast<unsigned char*>(ws));
   hipError_t e = hipGetLastError();
