@@ -630,8 +630,7 @@ int tq_quantize_split(const void* params0, const void* params1, int d, int d0, i
 size_t tq_score_split_ws_bytes(int d, int d0, int b0, int b1, int64_t groups, int64_t G, int64_t T) {
   (void)T;
   if (!valid_split(d, d0, b0, b1) || groups < 0 || G < 0) return 0;
-  return tq::align256(std::max(tq::score_generic_ws_bytes(d0, groups, G),
-                               tq::score_generic_ws_bytes(d - d0, groups, G)));
+  return tq::align256(tq::score_generic_split_ws_bytes(d0, d - d0, groups, G));
 }
 
 int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
@@ -657,14 +656,10 @@ int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, i
   const size_t need = tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, T);
   if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t esz = q_dtype == TQ_F32 ? 4 : 2;
-  const void* q1 = static_cast<const unsigned char*>(q) + size_t(d0) * esz;
-  // the second launch adds to the first one's logits (same stream, so in order; both reuse ws)
-  hipError_t e = tq::launch_score_generic(params0, d0, b0, q, q_dtype, codes0, nu0, gamma0, groups, G, T,
-                                          mode, logits, ws, s, d, false);
-  if (e == hipSuccess)
-    e = tq::launch_score_generic(params1, d - d0, b1, q1, q_dtype, codes1, nu1, gamma1, groups, G, T,
-                                 mode, logits, ws, s, d, true);
+  // one query prep launch for both groups, one scoring pass summing their estimates
+  const hipError_t e = tq::launch_score_generic_split(params0, params1, d0, d - d0, b0, b1, q, q_dtype,
+                                                      codes0, nu0, gamma0, codes1, nu1, gamma1, groups,
+                                                      G, T, mode, logits, ws, s);
   if (e != hipSuccess) return hip_fail(e, "tq_score_ip_split launch");
   return ok();
 }

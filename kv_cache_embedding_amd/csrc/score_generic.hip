@@ -27,21 +27,48 @@ constexpr int QO = 64;       //                  outputs (rows of the stacked [P
 constexpr int QK = 64;       //                  K staged per round
 
 // qs[row][o] = <M_o, q_row> for the stacked M = [Pi; S] (o < d: Pi q, o >= d: S q): an
+// Query operands of one channel group (qs[row][2][d]: Pi q then S q of each query row).
+struct QprepGroup {
+  const unsigned char* params;
+  size_t off_pi, off_s;
+  int d;
+  const void* q;          // the group's first query value (row stride qpitch elements)
+  float* qs;
+  long blocks;            // workgroups of this group: query row tiles x output tiles
+};
+
+// Codes and query operands of one channel group for the scoring kernel.
+struct ScoreGroup {
+  const unsigned char* params;
+  const float* qs;        // [groups * G][2][d] from the query prep
+  const uint32_t* codes;
+  const float* nu;
+  const float* gamma;
+  int d;
+};
+
 // NT product of the query rows with the rows of M, one workgroup per QR x QO tile (64
 // outputs never straddle Pi and S since d is a multiple of 64).  Thread t accumulates
 // output t % 64 of rows 4 (t / 64) .. +3 over K, both operands staged in LDS with padded
 // rows (the M rows are read at a stride of QK + 1 words: conflict-free).
-__global__ __launch_bounds__(256) void generic_qprep_kernel(
-    const unsigned char* __restrict__ params, size_t off_pi, size_t off_s, int d, long qpitch,
-    const void* __restrict__ q, int q_f32, long rows, float* __restrict__ qs) {
+// grid: the blocks of group 0, then those of group 1 (none for a single group)
+__global__ __launch_bounds__(256) void generic_qprep_kernel(QprepGroup g0, QprepGroup g1, long qpitch,
+                                                            int q_f32, long rows) {
   __shared__ float Qs[QR][QK + 1];
   __shared__ float Ms[QO][QK + 1];
+  const bool second = long(blockIdx.x) >= g0.blocks;
+  const QprepGroup& gr = second ? g1 : g0;
+  const long blk = second ? long(blockIdx.x) - g0.blocks : long(blockIdx.x);
+  const unsigned char* params = gr.params;
+  const int d = gr.d;
+  const void* q = gr.q;
+  float* qs = gr.qs;
   const int tid = threadIdx.x;
   const long ntile_o = 2 * d / QO;
-  const long r0 = long(blockIdx.x / ntile_o) * QR;
-  const int o0 = int(blockIdx.x % ntile_o) * QO;
-  const float* M = o0 < d ? reinterpret_cast<const float*>(params + off_pi) + size_t(o0) * d
-                          : reinterpret_cast<const float*>(params + off_s) + size_t(o0 - d) * d;
+  const long r0 = (blk / ntile_o) * QR;
+  const int o0 = int(blk % ntile_o) * QO;
+  const float* M = o0 < d ? reinterpret_cast<const float*>(params + gr.off_pi) + size_t(o0) * d
+                          : reinterpret_cast<const float*>(params + gr.off_s) + size_t(o0 - d) * d;
   const int o = tid & 63, rq = tid >> 6;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   constexpr int NQ = QR * QK / 256, NM = QO * QK / 256;   // staged values per thread
@@ -90,38 +117,28 @@ __device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
   return (x | (x << 3)) & 0x11111111u;
 }
 
-// grid: one workgroup per (group, head pass, block of KEYS keys), flattened into x.  ACC adds
-// the estimate to the logits already there (the channel groups of a fractional rate).  The
-// pass's query values (HB heads of Pi q and S q) are staged in LDS, CH coordinates at a
-// time, as one float4 per coordinate and matrix: every lane reads the same address, a
-// broadcast.  A key's plane words of a 32-coordinate group are turned into 4-bit fields
-// (index bits, QJL sign in bit 3), so that per coordinate one bit-field op and one LDS read
-// of (centroid, sign) from a 16-entry table decode it.
-template <int BITS, bool PROD, bool ACC>
-__global__ __launch_bounds__(KEYS) void generic_score_kernel(
+// One channel group's part of the estimate for this thread's key and the pass's heads:
+// l[hh] += n_k (<Pi q, chat> + alpha gamma_k <S q, 2z - 1>).  The pass's query values (HB
+// heads of Pi q and S q) are staged in LDS, CH coordinates at a time, as one float4 per
+// coordinate and matrix: every lane reads the same address, a broadcast.  A key's plane
+// words of a 32-coordinate group are turned into 4-bit fields (index bits, QJL sign in bit
+// 3), so that per coordinate one bit-field op and one LDS read of (centroid, sign) from a
+// 16-entry table decode it.  Every thread of the workgroup calls it (it synchronizes).
+template <int BITS, bool PROD>
+__device__ __forceinline__ void add_group_estimate(
     const unsigned char* __restrict__ params, const float* __restrict__ qs,
     const uint32_t* __restrict__ codes, const float* __restrict__ nu,
-    const float* __restrict__ gamma, int d, long G, long T, long kblocks, long passes,
-    float* __restrict__ logits) {
+    const float* __restrict__ gamma, int d, long G, long T, long g, long h0, long nh, long t,
+    bool valid, float4 (*qsh)[KEYS], float4* red, float2* tab, float* l) {
   static_assert(HB == 4, "one float4 of query values per coordinate");
   constexpr int L = 1 << (BITS - 1);
   constexpr int CH = KEYS;                 // coordinates staged per round (one per thread)
-  __shared__ float4 qsh[2][CH];            // [0]: Pi q, [1]: S q of the pass's 4 heads
-  __shared__ float4 red[KEYS / 64];        // sum_t (S q)_t: per-wave partial sums
-  __shared__ float2 tab[16];               // field -> (centroid, QJL sign bit as 0 / 1)
   const Header* hdr = reinterpret_cast<const Header*>(params);
   const float alpha = hdr->alpha;
   const int tid = threadIdx.x;
+  __syncthreads();                         // a previous group's table and sums are read
   if (tid < 16) tab[tid] = make_float2(hdr->cen[(tid & 7) < L ? (tid & 7) : L - 1], float(tid >> 3));
 
-  const long blk = blockIdx.x;
-  const long kb = blk % kblocks;
-  const long gp = blk / kblocks;           // group * passes + pass
-  const long g = gp / passes;
-  const long h0 = (gp % passes) * HB;
-  const long nh = G - h0 < HB ? G - h0 : HB;   // heads of this pass
-  const long t = kb * KEYS + tid;
-  const bool valid = t < T;
   const long key = g * T + (valid ? t : T - 1);  // ragged block: read a valid key, store nothing
   const int words = d / 32;
   const uint32_t* kc = codes + size_t(key) * words * BITS;
@@ -145,14 +162,8 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
       pl[0] = src[0]; pl[1] = src[1]; pl[2] = src[2]; pl[3] = 0u;
     }
   };
-  // loads in flight before the first barrier: the logits this launch adds to (ACC), the
-  // key's nu and gamma, and the first word; later words are loaded one word ahead
-  float prev[HB] = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (ACC) {
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh)
-      if (valid && hh < nh) prev[hh] = logits[size_t(g * G + h0 + hh) * T + t];
-  }
+  // loads in flight before the first barrier: the key's nu and gamma and the first word;
+  // later words are loaded one word ahead
   const float n_k = nu[key], g_k = gamma[key];
   uint32_t cur[4];
   load_word(0, cur);
@@ -224,42 +235,123 @@ __global__ __launch_bounds__(KEYS) void generic_score_kernel(
     s4[2] = (a.z + b.z) + (c.z + e.z);
     s4[3] = (a.w + b.w) + (c.w + e.w);
   }
-  if (!valid) return;
   const float m4[HB] = {mse.x, mse.y, mse.z, mse.w};
   const float z4[HB] = {zs.x, zs.y, zs.z, zs.w};
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
-    if (hh >= nh) break;
-    const long h = h0 + hh;
-    float l = m4[hh];
-    if constexpr (PROD) l = fmaf(alpha * g_k, 2.f * z4[hh] - s4[hh], l);
-    logits[size_t(g * G + h) * T + t] = ACC ? prev[hh] + n_k * l : n_k * l;
+    float v = m4[hh];
+    if constexpr (PROD) v = fmaf(alpha * g_k, 2.f * z4[hh] - s4[hh], v);
+    l[hh] += n_k * v;
   }
 }
 
-template <int BITS, bool ACC>
-hipError_t launch_b(const void* params_v, int d, const void* q, int q_dtype, long qpitch,
-                    const uint32_t* codes, const float* nu, const float* gamma, int64_t groups,
-                    int64_t G, int64_t T, int mode, float* logits, void* ws, hipStream_t s) {
-  const unsigned char* params = static_cast<const unsigned char*>(params_v);
-  const Layout lay(d, BITS);
-  float* qs = static_cast<float*>(ws);
+// grid: one workgroup per (group, head pass, block of KEYS keys), flattened into x.  B1 > 0:
+// a fractional rate's second channel group (its own parameters, codes and query operands),
+// whose estimate is added to the first one's in registers before the single store.
+template <int B0, int B1, bool PROD>
+__global__ __launch_bounds__(KEYS) void generic_score_kernel(ScoreGroup s0, ScoreGroup s1, long G, long T,
+                                                             long kblocks, long passes,
+                                                             float* __restrict__ logits) {
+  __shared__ float4 qsh[2][KEYS];          // [0]: Pi q, [1]: S q of the pass's 4 heads
+  __shared__ float4 red[KEYS / 64];        // sum_t (S q)_t: per-wave partial sums
+  __shared__ float2 tab[16];               // field -> (centroid, QJL sign bit as 0 / 1)
+  const long blk = blockIdx.x;
+  const long kb = blk % kblocks;
+  const long gp = blk / kblocks;           // group * passes + pass
+  const long g = gp / passes;
+  const long h0 = (gp % passes) * HB;
+  const long nh = G - h0 < HB ? G - h0 : HB;   // heads of this pass
+  const long t = kb * KEYS + threadIdx.x;
+  const bool valid = t < T;
+  float l[HB] = {0.f, 0.f, 0.f, 0.f};
+  add_group_estimate<B0, PROD>(s0.params, s0.qs, s0.codes, s0.nu, s0.gamma, s0.d, G, T, g, h0, nh,
+                               t, valid, qsh, red, tab, l);
+  if constexpr (B1 > 0)
+    add_group_estimate<B1, PROD>(s1.params, s1.qs, s1.codes, s1.nu, s1.gamma, s1.d, G, T, g, h0,
+                                 nh, t, valid, qsh, red, tab, l);
+  if (!valid) return;
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    if (hh >= nh) break;
+    logits[size_t(g * G + h0 + hh) * T + t] = l[hh];
+  }
+}
+
+// Query prep of one or two channel groups in one launch, then the scoring kernel.
+template <int B0, int B1>
+hipError_t launch_b(const void* params0, int d0, const void* params1, int d1, const void* q,
+                    int q_dtype, long qpitch, const uint32_t* codes0, const float* nu0,
+                    const float* gamma0, const uint32_t* codes1, const float* nu1,
+                    const float* gamma1, int64_t groups, int64_t G, int64_t T, int mode,
+                    float* logits, void* ws, hipStream_t s) {
   const long rows = long(groups) * G;
-  const long qblocks = (rows + QR - 1) / QR * (2 * d / QO);
-  hipLaunchKernelGGL(generic_qprep_kernel, dim3(unsigned(qblocks)), dim3(256), 0, s, params, lay.off_pi,
-                     lay.off_s, d, qpitch, q, q_dtype == 0 ? 1 : 0, rows, qs);
+  const size_t esz = q_dtype == 0 ? 4 : 2;
+  const Layout lay0(d0, B0);
+  float* qs0 = static_cast<float*>(ws);
+  QprepGroup g0{static_cast<const unsigned char*>(params0), lay0.off_pi, lay0.off_s, d0, q, qs0,
+                (rows + QR - 1) / QR * (2 * d0 / QO)};
+  QprepGroup g1{};
+  ScoreGroup s1{};
+  if constexpr (B1 > 0) {
+    const Layout lay1(d1, B1);
+    float* qs1 = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
+                                          align256(score_generic_ws_bytes(d0, groups, G)));
+    g1 = QprepGroup{static_cast<const unsigned char*>(params1), lay1.off_pi, lay1.off_s, d1,
+                    static_cast<const unsigned char*>(q) + size_t(d0) * esz, qs1,
+                    (rows + QR - 1) / QR * (2 * d1 / QO)};
+    s1 = ScoreGroup{g1.params, qs1, codes1, nu1, gamma1, d1};
+  }
+  hipLaunchKernelGGL(generic_qprep_kernel, dim3(unsigned(g0.blocks + g1.blocks)), dim3(256), 0, s, g0,
+                     g1, qpitch, q_dtype == 0 ? 1 : 0, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const ScoreGroup s0{g0.params, qs0, codes0, nu0, gamma0, d0};
   const long kblocks = (T + KEYS - 1) / KEYS;
   const long passes = (G + HB - 1) / HB;
   const dim3 grid(unsigned(groups * passes * kblocks));
   if (mode == 0)
-    hipLaunchKernelGGL((generic_score_kernel<BITS, true, ACC>), grid, dim3(KEYS), 0, s, params, qs,
-                       codes, nu, gamma, d, long(G), long(T), kblocks, passes, logits);
+    hipLaunchKernelGGL((generic_score_kernel<B0, B1, true>), grid, dim3(KEYS), 0, s, s0, s1, long(G),
+                       long(T), kblocks, passes, logits);
   else
-    hipLaunchKernelGGL((generic_score_kernel<BITS, false, ACC>), grid, dim3(KEYS), 0, s, params, qs,
-                       codes, nu, gamma, d, long(G), long(T), kblocks, passes, logits);
+    hipLaunchKernelGGL((generic_score_kernel<B0, B1, false>), grid, dim3(KEYS), 0, s, s0, s1, long(G),
+                       long(T), kblocks, passes, logits);
   return hipGetLastError();
+}
+
+template <int B0>
+hipError_t launch_b1(int b1, const void* params0, int d0, const void* params1, int d1, const void* q,
+                     int q_dtype, long qpitch, const uint32_t* codes0, const float* nu0,
+                     const float* gamma0, const uint32_t* codes1, const float* nu1,
+                     const float* gamma1, int64_t groups, int64_t G, int64_t T, int mode,
+                     float* logits, void* ws, hipStream_t s) {
+  switch (b1) {
+#define TQ_GEN_CASE(B1)                                                                           \
+  case B1:                                                                                        \
+    return launch_b<B0, B1>(params0, d0, params1, d1, q, q_dtype, qpitch, codes0, nu0, gamma0,    \
+                            codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+    TQ_GEN_CASE(0)
+    TQ_GEN_CASE(2)
+    TQ_GEN_CASE(3)
+    TQ_GEN_CASE(4)
+#undef TQ_GEN_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_groups(const void* params0, int d0, int b0, const void* params1, int d1, int b1,
+                         const void* q, int q_dtype, long qpitch, const uint32_t* codes0,
+                         const float* nu0, const float* gamma0, const uint32_t* codes1,
+                         const float* nu1, const float* gamma1, int64_t groups, int64_t G,
+                         int64_t T, int mode, float* logits, void* ws, hipStream_t s) {
+  switch (b0) {
+    case 2: return launch_b1<2>(b1, params0, d0, params1, d1, q, q_dtype, qpitch, codes0, nu0, gamma0,
+                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+    case 3: return launch_b1<3>(b1, params0, d0, params1, d1, q, q_dtype, qpitch, codes0, nu0, gamma0,
+                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+    case 4: return launch_b1<4>(b1, params0, d0, params1, d1, q, q_dtype, qpitch, codes0, nu0, gamma0,
+                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -268,8 +360,13 @@ size_t score_generic_ws_bytes(int d, int64_t groups, int64_t G) {
   return size_t(groups) * G * 2 * size_t(d) * 4;
 }
 
+size_t score_generic_split_ws_bytes(int d0, int d1, int64_t groups, int64_t G) {
+  return align256(score_generic_ws_bytes(d0, groups, G)) + score_generic_ws_bytes(d1, groups, G);
+}
+
 bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T) {
   const int64_t blocks = groups * ((G + HB - 1) / HB) * ((T + KEYS - 1) / KEYS);
+  // query prep of one or two channel groups, at most 4096 coordinates in all
   const int64_t qblocks = (groups * G + QR - 1) / QR * (2 * 4096 / QO);
   return groups * G < (int64_t(1) << 31) && blocks < (int64_t(1) << 31) && qblocks < (int64_t(1) << 31);
 }
@@ -277,22 +374,20 @@ bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T) {
 hipError_t launch_score_generic(const void* params, int d, int b, const void* q, int q_dtype,
                                 const uint32_t* codes, const float* nu, const float* gamma,
                                 int64_t groups, int64_t G, int64_t T, int mode, float* logits,
-                                void* ws, hipStream_t s, int64_t qpitch, bool accumulate) {
+                                void* ws, hipStream_t s, int64_t qpitch) {
   const long qp = qpitch > 0 ? long(qpitch) : long(d);
-#define TQ_GEN_CASE(B)                                                                            \
-  case B:                                                                                         \
-    return accumulate                                                                             \
-               ? launch_b<B, true>(params, d, q, q_dtype, qp, codes, nu, gamma, groups, G, T, mode, \
-                                   logits, ws, s)                                                 \
-               : launch_b<B, false>(params, d, q, q_dtype, qp, codes, nu, gamma, groups, G, T,      \
-                                    mode, logits, ws, s);
-  switch (b) {
-    TQ_GEN_CASE(2)
-    TQ_GEN_CASE(3)
-    TQ_GEN_CASE(4)
-    default: return hipErrorInvalidValue;
-  }
-#undef TQ_GEN_CASE
+  return launch_groups(params, d, b, nullptr, 0, 0, q, q_dtype, qp, codes, nu, gamma, nullptr, nullptr,
+                       nullptr, groups, G, T, mode, logits, ws, s);
+}
+
+hipError_t launch_score_generic_split(const void* params0, const void* params1, int d0, int d1, int b0,
+                                      int b1, const void* q, int q_dtype, const uint32_t* codes0,
+                                      const float* nu0, const float* gamma0, const uint32_t* codes1,
+                                      const float* nu1, const float* gamma1, int64_t groups, int64_t G,
+                                      int64_t T, int mode, float* logits, void* ws, hipStream_t s) {
+  if (b1 < 2) return hipErrorInvalidValue;
+  return launch_groups(params0, d0, b0, params1, d1, b1, q, q_dtype, long(d0) + d1, codes0, nu0,
+                       gamma0, codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
 }
 
 }  // namespace tq

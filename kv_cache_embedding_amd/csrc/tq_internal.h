@@ -90,13 +90,21 @@ hipError_t launch_score_d128(const void* params, int b, const void* q, int q_dty
                              void* ws, hipStream_t s);
 // Scoring for shapes the d = 128 kernel does not take (any d, any G): fp32 query prep into
 // ws ([groups * G][2][d] floats: Pi q, S q), then one lane per key.  qpitch:
-// elements between query rows (0: d); accumulate: add to logits instead of overwriting.
+// elements between query rows (0: d).
 hipError_t launch_score_generic(const void* params, int d, int b, const void* q, int q_dtype,
                                 const uint32_t* codes, const float* nu, const float* gamma,
                                 int64_t groups, int64_t G, int64_t T, int mode, float* logits,
-                                void* ws, hipStream_t s, int64_t qpitch = 0,
-                                bool accumulate = false);
+                                void* ws, hipStream_t s, int64_t qpitch = 0);
 size_t score_generic_ws_bytes(int d, int64_t groups, int64_t G);
+// Two channel groups (coordinates 0..d0-1 and d0..d0+d1-1 of the query rows, each group its
+// own parameter block and codes): one query prep launch for both (group 1's operands at
+// align256 of group 0's in ws), one scoring pass that sums the groups' estimates per key.
+hipError_t launch_score_generic_split(const void* params0, const void* params1, int d0, int d1, int b0,
+                                      int b1, const void* q, int q_dtype, const uint32_t* codes0,
+                                      const float* nu0, const float* gamma0, const uint32_t* codes1,
+                                      const float* nu1, const float* gamma1, int64_t groups, int64_t G,
+                                      int64_t T, int mode, float* logits, void* ws, hipStream_t s);
+size_t score_generic_split_ws_bytes(int d0, int d1, int64_t groups, int64_t G);
 bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T);
 // The MSE stage alone (b-1 index planes and nu): d = 128 on the fused encoder without its
 // GEMM2, every other d on the tiled encoder's phase 1.
