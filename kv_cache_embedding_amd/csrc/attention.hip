@@ -22,6 +22,7 @@
 //   issued before the maximum and the sum are reduced.
 #include "tq_internal.h"
 
+#include <algorithm>
 #include <cmath>
 
 namespace tq {
@@ -172,16 +173,36 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
   }
 }
 
-// out rows are opitch floats apart (a channel group of wider output rows: its columns only)
-__global__ __launch_bounds__(CT) void attn_combine_kernel(
-    const unsigned char* __restrict__ params_v, size_t off_pi, int d, long nkb,
-    const float* __restrict__ part_m, const float* __restrict__ part_s,
-    const float* __restrict__ part_acc, float* __restrict__ out, long opitch) {
+// The block partials and output columns of one value channel group.
+struct CombineGroup {
+  const unsigned char* params_v;
+  size_t off_pi;
+  int d;
+  const float* part_m;
+  const float* part_s;
+  const float* part_acc;
+  float* out;                        // the group's first output column
+};
+
+// grid: the rows (group * G + head) of channel group 0, then those of group 1 (a fractional
+// rate's second value group; none otherwise).  out rows are opitch floats apart (a channel
+// group of wider output rows: its columns only).
+__global__ __launch_bounds__(CT) void attn_combine_kernel(CombineGroup c0, CombineGroup c1, long rows0,
+                                                          long nkb, long opitch) {
   constexpr int NW = CT / 64;
   constexpr int PF = 8;              // loads of each sum issued before the reductions
   extern __shared__ float4 lds4[];   // [slices][d / 4] partial sums, then a[d / 4]
   __shared__ float red[NW];
-  const long row = blockIdx.x;   // group * G + head
+  const bool second = long(blockIdx.x) >= rows0;
+  const CombineGroup& cg = second ? c1 : c0;
+  const long row = second ? long(blockIdx.x) - rows0 : long(blockIdx.x);
+  const unsigned char* params_v = cg.params_v;
+  const size_t off_pi = cg.off_pi;
+  const int d = cg.d;
+  const float* part_m = cg.part_m;
+  const float* part_s = cg.part_s;
+  const float* part_acc = cg.part_acc;
+  float* out = cg.out;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* pm = part_m + row * nkb;
   const float* ps = part_s + row * nkb;
@@ -303,10 +324,13 @@ size_t attention_part_bytes(int d, int64_t groups, int64_t G, int64_t T) {
   return 2 * align256(rk * 4) + align256(rk * size_t(d) * 4);
 }
 
-hipError_t launch_attention_values(const void* params_v, int d, int b_v, const float* logits,
-                                   const uint32_t* vcodes, const float* vnu, int64_t groups,
-                                   int64_t G, int64_t T, float scale, float* out, void* part,
-                                   hipStream_t s, int64_t opitch) {
+namespace {
+
+// Block partials of one value channel group into part; returns the group's combine operands.
+hipError_t launch_value_blocks(const void* params_v, int d, int b_v, const float* logits,
+                               const uint32_t* vcodes, const float* vnu, int64_t groups, int64_t G,
+                               int64_t T, float scale, float* out, void* part, hipStream_t s,
+                               CombineGroup* cg) {
   const unsigned char* pv = static_cast<const unsigned char*>(params_v);
   const long nkb = (T + KB - 1) / KB;
   const long passes = (G + AH - 1) / AH;
@@ -336,13 +360,50 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
     default: return hipErrorInvalidValue;
   }
 #undef TQ_ATTN_NC
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const Layout lay(d, b_v);
+  *cg = CombineGroup{pv, lay.off_pi, d, part_m, part_s, part_acc, out};
+  return hipGetLastError();
+}
+
+size_t combine_lds_bytes(int d) {
   const int d4 = d / 4, cols = d4 < CT ? d4 : CT, nsl = CT / cols;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT),
-                     (size_t(nsl) * d4 + d4) * 16, s, pv, lay.off_pi, d, nkb, part_m, part_s,
-                     part_acc, out, long(opitch > 0 ? opitch : d));
+  return (size_t(nsl) * d4 + d4) * 16;
+}
+
+}  // namespace
+
+hipError_t launch_attention_values(const void* params_v, int d, int b_v, const float* logits,
+                                   const uint32_t* vcodes, const float* vnu, int64_t groups,
+                                   int64_t G, int64_t T, float scale, float* out, void* part,
+                                   hipStream_t s, int64_t opitch) {
+  CombineGroup cg{};
+  hipError_t e = launch_value_blocks(params_v, d, b_v, logits, vcodes, vnu, groups, G, T, scale, out,
+                                     part, s, &cg);
+  if (e != hipSuccess) return e;
+  const long rows = long(groups) * G;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT), combine_lds_bytes(d), s, cg,
+                     cg, rows, long((T + KB - 1) / KB), long(opitch > 0 ? opitch : d));
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_values_split(const void* params_v0, const void* params_v1, int d0, int d1,
+                                         int bv0, int bv1, const float* logits,
+                                         const uint32_t* vcodes0, const float* vnu0,
+                                         const uint32_t* vcodes1, const float* vnu1, int64_t groups,
+                                         int64_t G, int64_t T, float scale, float* out, void* part,
+                                         hipStream_t s) {
+  CombineGroup c0{}, c1{};
+  void* part1 = static_cast<unsigned char*>(part) + align256(attention_part_bytes(d0, groups, G, T));
+  hipError_t e = launch_value_blocks(params_v0, d0, bv0, logits, vcodes0, vnu0, groups, G, T, scale, out,
+                                     part, s, &c0);
+  if (e == hipSuccess)
+    e = launch_value_blocks(params_v1, d1, bv1, logits, vcodes1, vnu1, groups, G, T, scale, out + d0,
+                            part1, s, &c1);
+  if (e != hipSuccess) return e;
+  const long rows = long(groups) * G;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(2 * rows)), dim3(CT),
+                     std::max(combine_lds_bytes(d0), combine_lds_bytes(d1)), s, c0, c1, rows,
+                     long((T + KB - 1) / KB), long(d0) + d1);
   return hipGetLastError();
 }
 

@@ -694,9 +694,9 @@ int tq_quantize_mse_split(const void* params0, const void* params1, int d, int d
 
 size_t tq_attention_split_ws_bytes(int d, int d0, int bk0, int bk1, int64_t groups, int64_t G, int64_t T) {
   if (!valid_split(d, d0, bk0, bk1) || groups < 0 || G < 0 || T < 0) return 0;
-  const int dmax = std::max(d0, d - d0);
   return tq::align256(size_t(groups) * G * T * 4) + tq_score_split_ws_bytes(d, d0, bk0, bk1, groups, G, T) +
-         tq::align256(tq::attention_part_bytes(dmax, groups, G, T));
+         tq::align256(tq::attention_part_bytes(d0, groups, G, T)) +
+         tq::align256(tq::attention_part_bytes(d - d0, groups, G, T));
 }
 
 int tq_attention_split(const void* params_k0, const void* params_k1, const void* params_v0,
@@ -733,18 +733,16 @@ int tq_attention_split(const void* params_k0, const void* params_k1, const void*
   const size_t sws_bytes = tq_score_split_ws_bytes(d, d0, bk0, bk1, groups, G, T);
   void* sws = w + tq::align256(size_t(groups) * G * T * 4);
   void* part = static_cast<unsigned char*>(sws) + sws_bytes;
-  // logits of the split keys, then each value group's softmax-weighted sum into its columns
-  // of out (the partials are reused by the second group: same stream, in order)
+  // logits of the split keys, then each value group's block partials and one merge of both
+  // groups into their columns of out
   const int rc = tq_score_ip_split(params_k0, params_k1, d, d0, bk0, bk1, q, q_dtype, codes_k0, nu_k0,
                                    gamma_k0, codes_k1, nu_k1, gamma_k1, groups, G, T, mode, logits, sws,
                                    sws_bytes, stream);
   if (rc != TQ_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = tq::launch_attention_values(params_v0, d0, bv0, logits, codes_v0, nu_v0, groups, G, T,
-                                             scale, out, part, s, d);
-  if (e == hipSuccess)
-    e = tq::launch_attention_values(params_v1, d - d0, bv1, logits, codes_v1, nu_v1, groups, G, T, scale,
-                                    out + d0, part, s, d);
+  const hipError_t e = tq::launch_attention_values_split(params_v0, params_v1, d0, d - d0, bv0, bv1, logits,
+                                                         codes_v0, nu_v0, codes_v1, nu_v1, groups, G, T,
+                                                         scale, out, part, s);
   if (e != hipSuccess) return hip_fail(e, "tq_attention_split launch");
   return ok();
 }

@@ -121,6 +121,15 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
                                    const uint32_t* vcodes, const float* vnu, int64_t groups,
                                    int64_t G, int64_t T, float scale, float* out, void* part,
                                    hipStream_t s, int64_t opitch = 0);
+// Two value channel groups (output columns 0..d0-1 and d0..d0+d1-1): the block partials of
+// each group (group 1's at align256(attention_part_bytes(d0, ...)) in part), then one merge
+// launch for both.
+hipError_t launch_attention_values_split(const void* params_v0, const void* params_v1, int d0, int d1,
+                                         int bv0, int bv1, const float* logits,
+                                         const uint32_t* vcodes0, const float* vnu0,
+                                         const uint32_t* vcodes1, const float* vnu1, int64_t groups,
+                                         int64_t G, int64_t T, float scale, float* out, void* part,
+                                         hipStream_t s);
 // Cache append: copies vector g's words, nu and gamma (gamma may be NULL) of a contiguous
 // batch to slot (g, pos) of [groups][cap] caches.
 hipError_t launch_scatter_slot(const uint32_t* src_codes, const float* src_nu,
