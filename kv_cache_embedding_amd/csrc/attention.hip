@@ -52,27 +52,42 @@ __device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
   return (x | (x << 3)) & 0x11111111u;
 }
 
-// BV: index planes of a value (1..3); NC: 64-coordinate steps per chunk (NC divides d / 64)
+// The value operands of one channel group for the block kernel.
+struct BlockGroup {
+  const unsigned char* params_v;
+  const uint32_t* vcodes;
+  const float* vnu;
+  int d;
+  float* part_m;
+  float* part_s;
+  float* part_acc;
+};
+
+// One workgroup's block (256 keys) of one value channel group.  BV: index planes of a value
+// (1..3); NC: 64-coordinate steps per chunk (NC divides d / 64).  The LDS arrays come from
+// the kernel, sized for the largest codebook.
 template <int BV, int NC>
-__global__ __launch_bounds__(256) void attn_block_kernel(
-    const unsigned char* __restrict__ params_v, const float* __restrict__ logits,
-    const uint32_t* __restrict__ vcodes, const float* __restrict__ vnu, int d, long G, long T,
-    long nkb, long passes, float scale, float* __restrict__ part_m, float* __restrict__ part_s,
-    float* __restrict__ part_acc) {
+__device__ __forceinline__ void value_block(const BlockGroup& bg, const float* __restrict__ logits,
+                                            long G, long T, long nkb, long passes, float scale,
+                                            long blk, float* cen, float (*red)[AH],
+                                            float (*accs)[AH][64 * NC], uint4 (*kw)[64][2 * NC],
+                                            float4 (*wsh)[64]) {
   static_assert(BV >= 1 && BV <= 3, "a value's index fits one 4-bit field");
   constexpr int L = 1 << BV;
+  const unsigned char* __restrict__ params_v = bg.params_v;
+  const uint32_t* __restrict__ vcodes = bg.vcodes;
+  const float* __restrict__ vnu = bg.vnu;
+  const int d = bg.d;
+  float* __restrict__ part_m = bg.part_m;
+  float* __restrict__ part_s = bg.part_s;
+  float* __restrict__ part_acc = bg.part_acc;
   const Header* hdr = reinterpret_cast<const Header*>(params_v);
-  __shared__ float cen[L];
-  __shared__ float red[4][AH];
-  __shared__ float accs[4][AH][64 * NC];
-  __shared__ uint4 kw[4][64][2 * NC];   // a chunk's 4-bit indices: [wave][key][32-coordinate group]
-  __shared__ float4 wsh[4][64];         // p nu of the wave's keys for the 4 heads
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar code loads
   if (tid < L) cen[tid] = hdr->cen[tid];
 
-  const long kb = blockIdx.x % nkb;
-  const long gp = blockIdx.x / nkb;
+  const long kb = blk % nkb;
+  const long gp = blk / nkb;
   const long g = gp / passes;
   const long h0 = (gp % passes) * AH;
   const long nh = G - h0 < AH ? G - h0 : AH;   // heads of this pass
@@ -171,6 +186,28 @@ __global__ __launch_bounds__(256) void attn_block_kernel(
     }
     __syncthreads();
   }
+}
+
+
+// grid: the blocks of value channel group 0, then those of group 1 (BV1 > 0: a fractional
+// rate's second value group with the same chunk shape).
+template <int BV0, int BV1, int NC>
+__global__ __launch_bounds__(256) void attn_block_kernel(BlockGroup b0, BlockGroup b1, long blocks0,
+                                                         const float* __restrict__ logits, long G,
+                                                         long T, long nkb, long passes, float scale) {
+  __shared__ float cen[8];
+  __shared__ float red[4][AH];
+  __shared__ float accs[4][AH][64 * NC];
+  __shared__ uint4 kw[4][64][2 * NC];   // a chunk's 4-bit indices: [wave][key][32-coordinate group]
+  __shared__ float4 wsh[4][64];         // p nu of the wave's keys for the 4 heads
+  const long blk = blockIdx.x;
+  if constexpr (BV1 > 0) {
+    if (blk >= blocks0) {
+      value_block<BV1, NC>(b1, logits, G, T, nkb, passes, scale, blk - blocks0, cen, red, accs, kw, wsh);
+      return;
+    }
+  }
+  value_block<BV0, NC>(b0, logits, G, T, nkb, passes, scale, blk, cen, red, accs, kw, wsh);
 }
 
 // The block partials and output columns of one value channel group.
@@ -326,43 +363,82 @@ size_t attention_part_bytes(int d, int64_t groups, int64_t G, int64_t T) {
 
 namespace {
 
-// Block partials of one value channel group into part; returns the group's combine operands.
-hipError_t launch_value_blocks(const void* params_v, int d, int b_v, const float* logits,
-                               const uint32_t* vcodes, const float* vnu, int64_t groups, int64_t G,
-                               int64_t T, float scale, float* out, void* part, hipStream_t s,
-                               CombineGroup* cg) {
+// The operands of one value channel group: its partials in part, its output columns at out.
+struct ValueGroup {
+  BlockGroup blk;
+  CombineGroup comb;
+  int bv;       // index planes (b_v - 1)
+  int nc;       // 64-coordinate steps per chunk of the block kernel
+};
+
+ValueGroup value_group(const void* params_v, int d, int b_v, const uint32_t* vcodes, const float* vnu,
+                       int64_t groups, int64_t G, int64_t T, float* out, void* part) {
   const unsigned char* pv = static_cast<const unsigned char*>(params_v);
   const long nkb = (T + KB - 1) / KB;
-  const long passes = (G + AH - 1) / AH;
   const size_t rows = size_t(groups) * G;
   unsigned char* pb = static_cast<unsigned char*>(part);
   float* part_m = reinterpret_cast<float*>(pb);
   float* part_s = reinterpret_cast<float*>(pb + align256(rows * nkb * 4));
   float* part_acc = reinterpret_cast<float*>(pb + 2 * align256(rows * nkb * 4));
-  const dim3 grid(unsigned(groups * passes * nkb));
   const int steps = d / 64;
   const int nc = steps % 4 == 0 ? 4 : steps % 3 == 0 ? 3 : steps % 2 == 0 ? 2 : 1;
-  auto launch = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, pv, logits, vcodes, vnu, d, long(G), long(T), nkb,
-                       passes, scale, part_m, part_s, part_acc);
-  };
-#define TQ_ATTN_NC(BV)                                      \
-  switch (nc) {                                             \
-    case 4: launch(attn_block_kernel<BV, 4>); break;       \
-    case 3: launch(attn_block_kernel<BV, 3>); break;       \
-    case 2: launch(attn_block_kernel<BV, 2>); break;       \
-    default: launch(attn_block_kernel<BV, 1>); break;      \
+  const Layout lay(d, b_v);
+  return ValueGroup{BlockGroup{pv, vcodes, vnu, d, part_m, part_s, part_acc},
+                    CombineGroup{pv, lay.off_pi, d, part_m, part_s, part_acc, out}, b_v - 1, nc};
+}
+
+template <int BV0, int BV1, int NC>
+void launch_blocks_t(const ValueGroup& v0, const ValueGroup& v1, long blocks0, long blocks1,
+                     const float* logits, int64_t G, int64_t T, float scale, hipStream_t s) {
+  const long nkb = (T + KB - 1) / KB;
+  const long passes = (G + AH - 1) / AH;
+  hipLaunchKernelGGL((attn_block_kernel<BV0, BV1, NC>), dim3(unsigned(blocks0 + blocks1)), dim3(256), 0, s,
+                     v0.blk, v1.blk, blocks0, logits, long(G), long(T), nkb, passes, scale);
+}
+
+template <int BV0, int NC>
+hipError_t launch_blocks_b1(const ValueGroup& v0, const ValueGroup* v1, long blocks, const float* logits,
+                            int64_t G, int64_t T, float scale, hipStream_t s) {
+  if (!v1) {
+    launch_blocks_t<BV0, 0, NC>(v0, v0, blocks, 0, logits, G, T, scale, s);
+    return hipSuccess;
   }
-  switch (b_v) {
-    case 2: TQ_ATTN_NC(1) break;
-    case 3: TQ_ATTN_NC(2) break;
-    case 4: TQ_ATTN_NC(3) break;
+  if constexpr (NC <= 2) {
+    switch (v1->bv) {
+      case 1: launch_blocks_t<BV0, 1, NC>(v0, *v1, blocks, blocks, logits, G, T, scale, s); break;
+      case 2: launch_blocks_t<BV0, 2, NC>(v0, *v1, blocks, blocks, logits, G, T, scale, s); break;
+      case 3: launch_blocks_t<BV0, 3, NC>(v0, *v1, blocks, blocks, logits, G, T, scale, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
+  } else {
+    return hipErrorInvalidValue;   // two groups share a grid only with NC <= 2
+  }
+}
+
+// Block kernel launch for one group (v1 NULL) or for two groups of the same chunk shape with
+// NC <= 2 (a fractional rate's value groups of up to 128 channels each), in one grid.
+template <int NC>
+hipError_t launch_blocks_nc(const ValueGroup& v0, const ValueGroup* v1, long blocks, const float* logits,
+                            int64_t G, int64_t T, float scale, hipStream_t s) {
+  switch (v0.bv) {
+    case 1: return launch_blocks_b1<1, NC>(v0, v1, blocks, logits, G, T, scale, s);
+    case 2: return launch_blocks_b1<2, NC>(v0, v1, blocks, logits, G, T, scale, s);
+    case 3: return launch_blocks_b1<3, NC>(v0, v1, blocks, logits, G, T, scale, s);
     default: return hipErrorInvalidValue;
   }
-#undef TQ_ATTN_NC
-  const Layout lay(d, b_v);
-  *cg = CombineGroup{pv, lay.off_pi, d, part_m, part_s, part_acc, out};
-  return hipGetLastError();
+}
+
+hipError_t launch_blocks_one(const ValueGroup& v, long blocks, const float* logits, int64_t G, int64_t T,
+                             float scale, hipStream_t s) {
+  hipError_t e;
+  switch (v.nc) {
+    case 4: e = launch_blocks_nc<4>(v, nullptr, blocks, logits, G, T, scale, s); break;
+    case 3: e = launch_blocks_nc<3>(v, nullptr, blocks, logits, G, T, scale, s); break;
+    case 2: e = launch_blocks_nc<2>(v, nullptr, blocks, logits, G, T, scale, s); break;
+    default: e = launch_blocks_nc<1>(v, nullptr, blocks, logits, G, T, scale, s); break;
+  }
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 size_t combine_lds_bytes(int d) {
@@ -376,13 +452,15 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
                                    const uint32_t* vcodes, const float* vnu, int64_t groups,
                                    int64_t G, int64_t T, float scale, float* out, void* part,
                                    hipStream_t s, int64_t opitch) {
-  CombineGroup cg{};
-  hipError_t e = launch_value_blocks(params_v, d, b_v, logits, vcodes, vnu, groups, G, T, scale, out,
-                                     part, s, &cg);
+  if (b_v < 2 || b_v > 4) return hipErrorInvalidValue;
+  const ValueGroup v = value_group(params_v, d, b_v, vcodes, vnu, groups, G, T, out, part);
+  const long nkb = (T + KB - 1) / KB;
+  const long blocks = long(groups) * ((G + AH - 1) / AH) * nkb;
+  hipError_t e = launch_blocks_one(v, blocks, logits, G, T, scale, s);
   if (e != hipSuccess) return e;
   const long rows = long(groups) * G;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT), combine_lds_bytes(d), s, cg,
-                     cg, rows, long((T + KB - 1) / KB), long(opitch > 0 ? opitch : d));
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT), combine_lds_bytes(d), s, v.comb,
+                     v.comb, rows, nkb, long(opitch > 0 ? opitch : d));
   return hipGetLastError();
 }
 
@@ -392,24 +470,33 @@ hipError_t launch_attention_values_split(const void* params_v0, const void* para
                                          const uint32_t* vcodes1, const float* vnu1, int64_t groups,
                                          int64_t G, int64_t T, float scale, float* out, void* part,
                                          hipStream_t s) {
-  CombineGroup c0{}, c1{};
+  if (bv0 < 2 || bv0 > 4 || bv1 < 2 || bv1 > 4) return hipErrorInvalidValue;
   void* part1 = static_cast<unsigned char*>(part) + align256(attention_part_bytes(d0, groups, G, T));
-  hipError_t e = launch_value_blocks(params_v0, d0, bv0, logits, vcodes0, vnu0, groups, G, T, scale, out,
-                                     part, s, &c0);
-  if (e == hipSuccess)
-    e = launch_value_blocks(params_v1, d1, bv1, logits, vcodes1, vnu1, groups, G, T, scale, out + d0,
-                            part1, s, &c1);
+  const ValueGroup v0 = value_group(params_v0, d0, bv0, vcodes0, vnu0, groups, G, T, out, part);
+  const ValueGroup v1 = value_group(params_v1, d1, bv1, vcodes1, vnu1, groups, G, T, out + d0, part1);
+  const long nkb = (T + KB - 1) / KB;
+  const long blocks = long(groups) * ((G + AH - 1) / AH) * nkb;
+  hipError_t e;
+  if (v0.nc == v1.nc && v0.nc <= 2) {   // both groups' blocks in one grid
+    e = v0.nc == 2 ? launch_blocks_nc<2>(v0, &v1, blocks, logits, G, T, scale, s)
+                   : launch_blocks_nc<1>(v0, &v1, blocks, logits, G, T, scale, s);
+    if (e == hipSuccess) e = hipGetLastError();
+  } else {
+    e = launch_blocks_one(v0, blocks, logits, G, T, scale, s);
+    if (e == hipSuccess) e = launch_blocks_one(v1, blocks, logits, G, T, scale, s);
+  }
   if (e != hipSuccess) return e;
   const long rows = long(groups) * G;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(2 * rows)), dim3(CT),
-                     std::max(combine_lds_bytes(d0), combine_lds_bytes(d1)), s, c0, c1, rows,
-                     long((T + KB - 1) / KB), long(d0) + d1);
+                     std::max(combine_lds_bytes(d0), combine_lds_bytes(d1)), s, v0.comb, v1.comb, rows,
+                     nkb, long(d0) + d1);
   return hipGetLastError();
 }
 
 bool attention_grid_fits(int64_t groups, int64_t G, int64_t T) {
   const int64_t nkb = (T + KB - 1) / KB;
-  return groups * G < (int64_t(1) << 31) && groups * ((G + AH - 1) / AH) * nkb < (int64_t(1) << 31);
+  // a fractional rate's two value groups share the block and combine grids: twice the sizes
+  return 2 * groups * G < (int64_t(1) << 31) && 2 * groups * ((G + AH - 1) / AH) * nkb < (int64_t(1) << 31);
 }
 
 }  // namespace tq
