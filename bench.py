@@ -1,25 +1,29 @@
 #!/usr/bin/env python3
 """TurboQuant hot-path benchmark on one MI355X.
 
-A step is one pass of the whole path over one batch of synthetic keys: quantize the key
-cache of one decode layer (rotation, Lloyd-Max, residual, QJL signs, packing) and score
-every query head against all keys (query prep + quantized-key logits).
+A step is one pass of the whole path over one batch of synthetic keys: quantize a whole
+key cache (rotation, Lloyd-Max, residual, QJL signs, packing) and score every query head
+of one decode step against all keys (query prep + quantized-key logits).
 
-Default workload (decode_layer): 8 KV heads x 32768 tokens x d = 128, bf16 keys drawn
-N(0, 1) with 4 outlier channels per head scaled x20, b = 4 bits (3-bit Lloyd-Max + 1-bit
-QJL), 32 query heads in GQA groups of 4, batch 1.
+Default workload (long_context, the largest single-GPU configuration): 16 sequences x 8 KV
+heads x 131072 tokens x d = 128, bf16 keys drawn N(0, 1) with 4 outlier channels per head
+scaled x20, b = 3 bits (2-bit Lloyd-Max + 1-bit QJL), 32 query heads per sequence in GQA
+groups of 4.  --workload decode_layer: one sequence x 8 KV heads x 32768 tokens, b = 4;
+--workload decode_batch16: 16 sequences x 8 KV heads x 8192 tokens, b = 2 (--bits 3 for b = 3).
 
 --workload embedding_search: a step quantizes 10^6 unit vectors in R^1536 (float32, low
 rank + noise) and returns the top-10 of 1000 queries by the estimated inner product (flat
 scan over the codes); b = 4 unless --bits says otherwise.
 
+--workload decode_attention: one tq_attention decode step at the decode-layer shapes.
 --workload fractional_kv: decode_layer's keys and queries at a fractional rate (--rate 2.5
 or 3.5 bits per channel): channels 0..63 at the higher b and 64..127 at the lower one, each
 group its own TurboQuant instance; a step is tq_quantize_split + tq_score_ip_split.
+--workload ubench: achievable HBM and MFMA rates of the GPU.
 
 Prints one JSON line.  Kernel durations come from HIP events recorded on the stream the
-kernels run on; inputs cycle through several resident copies so that the 256 MB MALL
-does not serve them from cache.
+kernels run on; every per-launch timing cycles through more than 512 MB of distinct
+inputs, so that the 256 MB MALL does not serve them from cache.
 """
 from __future__ import annotations
 
@@ -46,11 +50,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_layer",
-                    choices=["decode_layer", "long_context", "embedding_search", "decode_attention",
-                             "fractional_kv", "ubench"])
+    ap.add_argument("--workload", default="long_context",
+                    choices=["long_context", "decode_layer", "decode_batch16", "embedding_search",
+                             "decode_attention", "fractional_kv", "ubench"])
     ap.add_argument("--rate", type=float, default=3.5, help="fractional_kv: bits per channel (2.5 or 3.5)")
-    ap.add_argument("--bits", type=int, default=0, help="embedding_search: b (default 4)")
+    ap.add_argument("--bits", type=int, default=0,
+                    help="b of workloads defined at several (embedding_search: 4, decode_batch16: 2)")
     ap.add_argument("--replicas", type=int, default=8, help="resident input copies cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle CPU baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -192,13 +197,14 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_file: str):
-    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current source."""
+def traffic_from_profiles(kernel_file: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json, keyed
+    "<source file>:<workload>"), if they were taken on the current source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel_file)
+        rec = json.load(open(path)).get(f"{kernel_file}:{workload}")
     except Exception:
         return None
     if not rec or rec.get("source_hash") != source_hash(kernel_file):
@@ -206,7 +212,7 @@ def traffic_from_profiles(kernel_file: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(workload, seconds: float):
+def cpu_baseline(workload, b: int, seconds: float):
     """The oracle (float64 NumPy) on a bounded sample: whole KV heads, one at a time."""
     import oracle
     from workloads import gen
@@ -216,30 +222,32 @@ def cpu_baseline(workload, seconds: float):
     except Exception:
         cores = os.cpu_count() or 1
     w = workload
-    d, b = w.d, w.bits[0]
+    d = w.d
     Pi = gen.haar_orthogonal(d, w.cfg)
     S = gen.gaussian_matrix(d, d, w.cfg)
     c, t = oracle.codebook(b - 1, d)
     chans = gen.outlier_channels(w.cfg, w.n_kv, d)
-    q = gen.bf16_bits_to_f32(gen.kv_queries(w.cfg, 1, w.n_q_heads, d)[0]).astype(np.float64)
-    heads = 0
+    q = gen.bf16_bits_to_f32(gen.kv_queries(w.cfg, w.n_seq, w.n_q_heads, d)).astype(np.float64)
+    q = q.reshape(w.groups, w.G, d)
+    groups = 0
     logits = 0
     vectors = 0
     elapsed = 0.0
-    while heads < w.n_kv and elapsed < seconds:
-        keys = gen.bf16_bits_to_f32(gen.kv_keys_chunk(w.cfg, 0, heads, w.T, d, chans[heads]))
+    # whole (sequence, KV head) groups in cache order until the time budget is spent
+    while groups < w.groups and elapsed < seconds:
+        s_, h = divmod(groups, w.n_kv)
+        keys = gen.bf16_bits_to_f32(gen.kv_keys_chunk(w.cfg, s_, h, w.T, d, chans[h]))
         t0 = time.perf_counter()
         r = oracle.quantize(keys.astype(np.float64), Pi, S, c, t)
-        est = oracle.estimate_ip(q[heads * w.G:(heads + 1) * w.G], Pi, S, r["idx"], r["z"], r["nu"],
-                                 r["gamma"], c)
+        est = oracle.estimate_ip(q[groups], Pi, S, r["idx"], r["z"], r["nu"], r["gamma"], c)
         elapsed += time.perf_counter() - t0
-        heads += 1
+        groups += 1
         vectors += w.T
         logits += est.size
     return {
         "value": logits / elapsed, "unit": "logits/s", "cores": int(cores), "cpu_model": cpu_model(), "kind": "oracle",
-        "sample": f"{heads} of {w.n_kv} KV heads ({vectors} keys quantized, {logits} logits), "
-                  f"float64 NumPy oracle, {elapsed:.1f} s",
+        "sample": f"{groups} of {w.groups} (sequence, KV head) groups ({vectors} keys quantized, {logits} "
+                  f"logits), float64 NumPy oracle, {elapsed:.1f} s",
         "vectors_per_s": vectors / elapsed,
     }
 
@@ -381,7 +389,7 @@ def bench_search(args):
             "kernel": "tq_topk (query prep + fused score/select scan + merge)",
             "bound": "mfma", "achieved": t_tflops, "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": t_tflops / FP16_MFMA_PEAK_TFLOPS,
-            "traffic": traffic_from_profiles("topk.hip"),
+            "traffic": traffic_from_profiles("topk.hip", w.name),
             "note": "algorithmic 3 d flop per (query, key) pair; timed over the whole call; traffic = "
                     "counter-measured bytes per call (the codes are read once per 256-query tile)",
         },
@@ -389,7 +397,7 @@ def bench_search(args):
             "kernel": "quantize_gemm (tq_quantize, d=1536)",
             "bound": "mfma", "achieved": q_tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": q_tflops / BF16_MFMA_PEAK_TFLOPS,
-            "traffic": traffic_from_profiles("quantize_gemm.hip"),
+            "traffic": traffic_from_profiles("quantize_gemm.hip", w.name),
             "note": "algorithmic 4 d^2 flop/vector; float32 inputs execute 3 + 3 bf16 MFMA passes; "
                     "traffic = counter-measured bytes per call, including the per-chunk scratch round "
                     "trips of the bf16 split rows and the residual",
@@ -799,33 +807,43 @@ def bench_fractional(args):
     print(json.dumps(result), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    if args.workload == "embedding_search":
-        bench_search(args)
-        return
-    if args.workload == "decode_attention":
-        bench_attention(args)
-        return
-    if args.workload == "fractional_kv":
-        bench_fractional(args)
-        return
-    if args.workload == "ubench":
-        bench_ubench(args)
-        return
+def kv_keys_on_device(torch, w, chans, dev):
+    """The whole bf16 key cache of a KV workload on the GPU, generated chunk by chunk on host
+    threads from the seeded generator."""
+    import concurrent.futures
 
+    from workloads import gen
+    x = torch.empty((w.n_keys, w.d), dtype=torch.bfloat16, device=dev)
+
+    def one(gi):
+        s_, h = divmod(gi, w.n_kv)
+        return gi, gen.kv_keys_chunk(w.cfg, s_, h, w.T, w.d, chans[h])
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        for gi, chunk in ex.map(one, range(w.groups)):
+            x[gi * w.T:(gi + 1) * w.T] = torch.from_numpy(chunk.view(np.int16)).to(dev).view(torch.bfloat16)
+    return x
+
+
+#: working set cycled by every per-launch timing: above the 256 MB MALL by a wide margin
+MIN_WORKING_SET = 640 * 1024 * 1024
+
+
+def bench_kv(args):
+    """A decode-step workload: quantize the whole key cache, then score every query head."""
     import torch
 
     import kv_cache_embedding_amd as tq
     from workloads import gen
 
-    w = gen.DECODE_LAYER if args.workload == "decode_layer" else gen.LONG_CONTEXT
+    w = {"decode_layer": gen.DECODE_LAYER, "decode_batch16": gen.DECODE_BATCH16,
+         "long_context": gen.LONG_CONTEXT}[args.workload]
     dev = torch.device("cuda:0")
-    d, b = w.d, w.bits[0]
+    d = w.d
+    b = args.bits or w.bits[0]
+    if b not in w.bits:
+        raise SystemExit(f"{w.name} is defined for b in {w.bits}")
     groups, G, T = w.groups, w.G, w.T
     n = w.n_keys
 
@@ -836,27 +854,30 @@ def main():
     params = torch.empty(tq.tq_params_bytes(d, b), dtype=torch.uint8, device=dev)
     tq.tq_prepare(d, b, Pi, S, c, t, params)
     chans = gen.outlier_channels(w.cfg, w.n_kv, d)
-    x = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
-    for s in range(w.n_seq):
-        for h in range(w.n_kv):
-            gi = s * w.n_kv + h
-            chunk = gen.kv_keys_chunk(w.cfg, s, h, T, d, chans[h])
-            x[gi * T:(gi + 1) * T] = torch.from_numpy(chunk.view(np.int16)).to(dev).view(torch.bfloat16)
+    t_gen = time.perf_counter()
+    x = kv_keys_on_device(torch, w, chans, dev)
+    print(f"# generated {n} keys in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     q = torch.from_numpy(gen.kv_queries(w.cfg, w.n_seq, w.n_q_heads, d).reshape(-1, d).view(np.int16))
     q = q.to(dev).view(torch.bfloat16)
 
+    # Replicas: the inputs of the quantize launches and the code sets of the scoring launches
+    # each cycle through more than MIN_WORKING_SET distinct bytes, so no per-launch timing is
+    # served from the MALL.  Step r quantizes input copy r % Rx into code set r.
+    n_logits = groups * G * T
     in_bytes = n * d * 2
-    R = max(1, min(args.replicas, int(2 * 1024**3 // max(in_bytes, 1))))  # cap ~2 GiB of copies
-    xs = [x] + [x.clone() for _ in range(R - 1)]
+    score_in_bytes = n * (d // 8 * b + 8) + n_logits * 4
+    Rx = max(1, min(16, -(-MIN_WORKING_SET // in_bytes)))
+    R = max(Rx, min(64, -(-MIN_WORKING_SET // score_in_bytes)))
+    xs = [x] + [x.clone() for _ in range(Rx - 1)]
     wc = d // 32 * b
     codes = [torch.empty(n * wc, dtype=torch.int32, device=dev) for _ in range(R)]
     nus = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
     gms = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
-    logits = [torch.empty(groups * G * T, dtype=torch.float32, device=dev) for _ in range(R)]
+    logits = [torch.empty(n_logits, dtype=torch.float32, device=dev) for _ in range(R)]
     ws = torch.empty(tq.tq_score_ws_bytes(d, b, groups, G, T), dtype=torch.uint8, device=dev)
 
     def quantize(r):
-        tq.tq_quantize(params, d, b, xs[r], codes[r], nus[r], gms[r])
+        tq.tq_quantize(params, d, b, xs[r % Rx], codes[r], nus[r], gms[r])
 
     def score(r):
         tq.tq_score_ip(params, d, b, q, codes[r], nus[r], gms[r], groups, G, T, tq.TQ_EST_PROD,
@@ -869,14 +890,18 @@ def main():
         torch.cuda.synchronize()
         bb.copy_(a)
         torch.cuda.synchronize()
+        del a, bb
 
-    for i in range(max(args.warmup, 1)):
+    for r in range(R):
+        quantize(r)
+        score(r)
+    for i in range(args.warmup):
         quantize(i % R)
         score(i % R)
     torch.cuda.synchronize()
 
     # Each step is replayed from a HIP graph (one node per kernel launch) so that Python
-    # launch overhead does not pace the GPU; graph r works on input copy r.
+    # launch overhead does not pace the GPU; graph r works on input copy r % Rx, code set r.
     def capture(fn, r):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -921,11 +946,10 @@ def main():
     q_ms = time_per_launch(torch, quantize, R, K)
     s_ms = time_per_launch(torch, score, R, K)
     ms_step = min(serial_ms, pipe_ms)
-    n_logits = groups * G * T
 
     # The pages' comparison (attention logits with 4-bit keys against 32-bit keys): the same
     # logits from a float32 copy of the cache by a library batched GEMM, K q^T per group (the
-    # cache is the contiguous left operand), beside the tq_score_ip call on the 4-bit codes.
+    # cache is the contiguous left operand), beside the tq_score_ip call on the b-bit codes.
     # long_context only: its 8.6 GB of float32 keys cannot be served from the 256 MB MALL.
     keys32 = None
     if args.workload == "long_context":
@@ -954,7 +978,7 @@ def main():
     # algorithmic work per launch
     q_flops = n * 4.0 * d * d                       # Pi x and S' r': 2 d^2 each
     q_bytes = n * (d * 2 + d // 8 * b + 8)          # bf16 keys in, codes + nu + gamma out
-    s_bytes = n * (d // 8 * b + 8) + n_logits * 4   # codes + nu + gamma in, fp32 logits out
+    s_bytes = score_in_bytes                        # codes + nu + gamma in, fp32 logits out
     q_tflops = q_flops / (q_ms * 1e-3) / 1e12
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     s_gbs = s_bytes / (s_ms * 1e-3) / 1e9
@@ -974,14 +998,15 @@ def main():
         "data": "synthetic (seeded N(0,1) keys with outlier channels, bf16; random rotation and QJL matrix)",
         "config": {
             "workload": f"{w.name}: {w.n_seq} seq x {w.n_kv} KV heads x {T} tokens x d={d} bf16 keys "
-                        f"(4 outlier channels x20), b={b}, {w.n_q_heads} query heads (GQA {G})",
-            "keys": n, "d": d, "bits": b, "query_heads": w.n_seq * w.n_q_heads, "replicas": R,
+                        f"(4 outlier channels x20), b={b}, {w.n_q_heads} query heads per sequence (GQA {G})",
+            "keys": n, "d": d, "bits": b, "query_heads": w.n_seq * w.n_q_heads,
+            "input_copies": Rx, "code_sets": R,
         },
         "roofline": {
             "kernel": "quantize_d128 (tq_quantize)",
             "bound": "hbm", "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": q_gbs / HBM_PEAK_GBS,
-            "traffic": traffic_from_profiles("quantize.hip"),
+            "traffic": traffic_from_profiles("quantize.hip", w.name),
             "note": f"algorithmic bytes per vector: {d * 2} B bf16 key in, {d // 8 * b} B codes and 8 B "
                     f"nu, gamma out; at 4 d^2 flop per vector the arithmetic intensity "
                     f"({4 * d * d / (d * 2 + d // 8 * b + 8):.0f} flop/B) is below the MFMA ridge "
@@ -998,13 +1023,15 @@ def main():
         "roofline_score": {
             "kernel": "score_qprep + score (tq_score_ip)",
             "bound": "hbm", "achieved": s_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": s_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profiles("score.hip"),
+            "frac": s_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profiles("score.hip", w.name),
+            "note": f"the whole call (query prep + scan) over {R} code sets of "
+                    f"{score_in_bytes / 2**20:.0f} MiB cycled per launch",
         },
         "steps_timing": {"serial_ms": serial_ms, "pipelined_ms": pipe_ms,
                          "note": "ms_per_step is the faster of: serial (quantize then score of each batch) and "
                                  "pipelined (batch i's quantize overlaps batch i-1's scoring on a second stream)"},
-        "quantize": {"ms": q_ms, "vectors_per_s": n / (q_ms * 1e-3), "hbm_gbs": q_bytes / (q_ms * 1e-3) / 1e9,
-                     "hbm_frac": q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "quantize": {"ms": q_ms, "vectors_per_s": n / (q_ms * 1e-3), "hbm_gbs": q_gbs,
+                     "hbm_frac": q_gbs / HBM_PEAK_GBS},
         "score": {"ms": s_ms, "logits_per_s": n_logits / (s_ms * 1e-3), "keys_per_s": n / (s_ms * 1e-3),
                   "hbm_gbs": s_gbs},
         "context": "pages: up to 8x faster attention logits with 4-bit keys vs 32-bit keys on H100 "
@@ -1016,8 +1043,19 @@ def main():
     with_measured_peak(result["roofline"], copy_gbs, "1 GiB device copy in this run (read + write bytes)")
     with_measured_peak(result["roofline_score"], copy_gbs, "1 GiB device copy in this run (read + write bytes)")
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, b, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    run = {"embedding_search": bench_search, "decode_attention": bench_attention,
+           "fractional_kv": bench_fractional, "ubench": bench_ubench}.get(args.workload, bench_kv)
+    run(args)
 
 
 if __name__ == "__main__":

@@ -134,7 +134,9 @@ int tq_prepare_orthogonal_qjl(int d, int b, const float* Pi, const float* S, con
  *   codes    out [n][d/32][b] uint32 (canonical layout above)
  *   nu       out [n] float32, |x|
  *   gamma    out [n] float32, norm of the residual of x/|x| after the Lloyd-Max stage
- * Integer decisions (index, sign) are taken in float32 against float32 thresholds.
+ * Integer decisions (index, sign) are taken in float32 against float32 thresholds; a
+ * coordinate exactly on a threshold goes to the cell farther from zero (u = 0 to the positive
+ * side), which keeps the quantizer odd-symmetric.
  * d = 128 runs one fused kernel; every other d runs a split pass and two tiled
  * kernels per chunk of c vectors and takes a stream-ordered scratch buffer of
  * c * d * 8 bytes for float32 input, c * d * 4 bytes for bfloat16, plus c * ceil(d / 256) * 4
@@ -147,6 +149,17 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
                 uint32_t* codes, float* nu, float* gamma, void* stream);
 
 /*
+ * tq_quantize_with_rotation — tq_quantize that also returns the rotated unit coordinates
+ * u = Pi x / |x| of step 1 ([review, MSE paragraph]: random orthogonal rotation of the
+ * normalised vector), as the encoder computed them, for checking the rotation itself.
+ *   u      out [n][d] float32, 16-byte aligned (u = 0 for a zero vector)
+ *   other arguments, results and errors as tq_quantize; codes, nu and gamma are identical to
+ *   tq_quantize's (the same kernels with one extra store).
+ */
+int tq_quantize_with_rotation(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
+                              uint32_t* codes, float* nu, float* gamma, float* u, void* stream);
+
+/*
  * tq_quantize_mse — the MSE quantizer alone ([review, problem statement]: MSE-optimal
  * TurboQuant is the random rotation followed by Lloyd-Max at the target bit width), for
  * vectors that are reconstructed rather than inner-producted (attention values).
@@ -154,7 +167,7 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
  *            b-1 index bits per coordinate (values at v bits take a block prepared for v + 1)
  *   x        [n][d] float32 or bfloat16, row-major, 16-byte aligned
  *   codes    out [n][d/32][b-1] uint32: plane p holds bit p of each coordinate's index,
- *            coordinate t in word t/32, bit t%32
+ *            coordinate t in word t/32, bit t%32; 16-byte aligned at d = 128, else 4-byte
  *   nu       out [n] float32, |x|
  * The decisions are those of tq_quantize's index planes. It runs the split pass and the
  * first tiled GEMM of the tiled encoder for d != 128 (float32 input takes a stream-ordered
@@ -233,8 +246,10 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
  * which leaves <q, x> unchanged, so the producer of q and x can apply it.
  * A 64 + 64 split of d = 128 encodes both groups in one pass of the fused d = 128 encoder
  * (the two rotations and QJL matrices as block-diagonal operands); other splits run the
- * tiled encoder once per group.  Scoring runs the general path once per group, the second
- * launch adding to the first's logits.  Channels are read in place (rows d apart).
+ * tiled encoder once per group.  Scoring runs one query-prep launch for both groups and one
+ * pass over the keys that adds the two groups' estimates in registers and stores each logit
+ * once; tq_score_split_ws_bytes covers both groups' query operands.  Channels are read in
+ * place (rows d apart).
  *
  * tq_quantize_split — encode x [n][d] (x_dtype as for tq_quantize) into
  *   codes0 [n][d0/32][b0], nu0, gamma0 [n]     (channels 0 .. d0-1, params0)
@@ -266,8 +281,8 @@ int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, i
  * groups of x [n][d]: channels [0, d0) with params0 (b0 - 1 index bits) into codes0
  * [n][d0/32][b0-1], nu0 [n]; channels [d0, d) with params1 into codes1, nu1.  Values of a
  * fractional-rate KV cache.  A 64 + 64 split of d = 128 runs one pass of the fused
- * encoder (no QJL stage); other splits run the tiled encoder's first pass once per group,
- * reading the channels in place.
+ * encoder (no QJL stage; codes0 and codes1 then 16-byte aligned); other splits run the tiled
+ * encoder's first pass once per group, reading the channels in place.
  * Errors: as tq_quantize_split.
  */
 int tq_quantize_mse_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,

@@ -44,6 +44,7 @@ def load_library():
         "tq_prepare": (I, [I, I, P, P, P, P, P, P]),
         "tq_prepare_orthogonal_qjl": (I, [I, I, P, P, P, P, P, P]),
         "tq_quantize": (I, [P, I, I, P, I, I64, P, P, P, P]),
+        "tq_quantize_with_rotation": (I, [P, I, I, P, I, I64, P, P, P, P, P]),
         "tq_dequantize": (I, [P, I, I, P, P, P, I64, I, P, P]),
         "tq_score_ws_bytes": (SZ, [I, I, I64, I64, I64]),
         "tq_score_ip": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P, SZ, P]),
@@ -195,6 +196,24 @@ def tq_quantize(params, d: int, b: int, x, codes, nu, gamma, stream=None):
     _check(load_library().tq_quantize(_ptr(params), d, b, _ptr(x), _dtype_code(x, "x"), n,
                                       _ptr(codes), _ptr(nu), _ptr(gamma),
                                       _stream(stream, x.device)))
+
+
+def tq_quantize_with_rotation(params, d: int, b: int, x, codes, nu, gamma, u, stream=None):
+    """tq_quantize plus the rotated unit coordinates u [n][d] float32 the encoder computed."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError(f"x must be [n][{d}]")
+    n = x.shape[0]
+    for tname, t in (("codes", codes), ("nu", nu), ("gamma", gamma), ("u", u), ("params", params)):
+        _dev(t, tname)
+    _need(codes, "codes", n * (d // 32) * b, torch.int32)
+    _need(nu, "nu", n, torch.float32)
+    _need(gamma, "gamma", n, torch.float32)
+    _need(u, "u", n * d, torch.float32)
+    _check(load_library().tq_quantize_with_rotation(_ptr(params), d, b, _ptr(x), _dtype_code(x, "x"), n,
+                                                    _ptr(codes), _ptr(nu), _ptr(gamma), _ptr(u),
+                                                    _stream(stream, x.device)))
 
 
 def tq_quantize_mse(params, d: int, b: int, x, codes, nu, stream=None):

@@ -463,6 +463,23 @@ int tq_quantize(const void* params, int d, int b, const void* x, int x_dtype, in
   return ok();
 }
 
+int tq_quantize_with_rotation(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
+                              uint32_t* codes, float* nu, float* gamma, float* u, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad x_dtype %d", x_dtype);
+  if (n < 0) return fail(TQ_EINVAL, "n=%lld < 0", (long long)n);
+  if (n == 0) return ok();
+  if (!params || !x || !codes || !nu || !gamma || !u) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(nu, 4) ||
+      !aligned(gamma, 4) || !aligned(u, 16))
+    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x, codes and u 16 B)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = d == 128 ? tq::launch_quantize_d128_u(params, b, x, x_dtype, n, codes, nu, gamma, u, s)
+                          : tq::launch_quantize_gemm(params, d, b, x, x_dtype, n, codes, nu, gamma, s, 0, u);
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize_with_rotation launch");
+  return ok();
+}
+
 int tq_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype, int64_t n,
                     uint32_t* codes, float* nu, void* stream) {
   if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
@@ -470,8 +487,9 @@ int tq_quantize_mse(const void* params, int d, int b, const void* x, int x_dtype
   if (n < 0) return fail(TQ_EINVAL, "n=%lld < 0", (long long)n);
   if (n == 0) return ok();
   if (!params || !x || !codes || !nu) return fail(TQ_EINVAL, "NULL pointer");
-  if (!aligned(params, 256) || !aligned(x, 16) || !aligned(codes, 4) || !aligned(nu, 4))
-    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x 16 B)");
+  // the d = 128 encoder stores each lane's words with 8- or 16-byte stores
+  if (!aligned(params, 256) || !aligned(x, 16) || !aligned(codes, d == 128 ? 16 : 4) || !aligned(nu, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x 16 B, codes 16 B at d = 128)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = d == 128 ? tq::launch_quantize_d128_mse(params, b, x, x_dtype, n, codes, nu, s)
                           : tq::launch_quantize_mse(params, d, b, x, x_dtype, n, codes, nu, s);
@@ -674,9 +692,11 @@ int tq_quantize_mse_split(const void* params0, const void* params1, int d, int d
   if (n == 0) return ok();
   if (!params0 || !params1 || !x || !codes0 || !nu0 || !codes1 || !nu1)
     return fail(TQ_EINVAL, "NULL pointer");
-  if (!aligned(params0, 256) || !aligned(params1, 256) || !aligned(x, 16) || !aligned(codes0, 4) ||
-      !aligned(codes1, 4) || !aligned(nu0, 4) || !aligned(nu1, 4))
-    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x 16 B)");
+  // the one-pass 64 + 64 split stores each lane's words with 8- or 16-byte stores
+  const size_t ca = (d == 128 && d0 == 64) ? 16 : 4;
+  if (!aligned(params0, 256) || !aligned(params1, 256) || !aligned(x, 16) || !aligned(codes0, ca) ||
+      !aligned(codes1, ca) || !aligned(nu0, 4) || !aligned(nu1, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params 256 B, x 16 B, codes 16 B for a 64 + 64 split)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
   const void* x1 = static_cast<const unsigned char*>(x) + size_t(d0) * esz;

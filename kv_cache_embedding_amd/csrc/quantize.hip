@@ -146,13 +146,17 @@ __device__ __forceinline__ void store_words(uint32_t* dst, const uint32_t* out) 
 // and params1, codes1, nu1_out, gamma1_out are unused; with SPLIT, params / params1 are the
 // d = 64 blocks of channel groups 0 / 1 (gmat_off: their bf16 matrices) and group 1's
 // results go to codes1, nu1_out, gamma1_out.
-template <int B0, int B1, bool F32IN, bool MSE, bool SPLIT>
+// UOUT (diagnostic, no split): u = Pi x / nu of every vector is also written to u_out
+// [n][128] float32, from the accumulators that the bucketize reads.
+template <int B0, int B1, bool F32IN, bool MSE, bool SPLIT, bool UOUT = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     const unsigned char* __restrict__ params, const unsigned char* __restrict__ params1,
     size_t frag_off, size_t gmat_off, const void* __restrict__ xin, long n,
     uint32_t* __restrict__ codes, float* __restrict__ nu_out, float* __restrict__ gamma_out,
-    uint32_t* __restrict__ codes1, float* __restrict__ nu1_out, float* __restrict__ gamma1_out) {
+    uint32_t* __restrict__ codes1, float* __restrict__ nu1_out, float* __restrict__ gamma1_out,
+    float* __restrict__ u_out) {
   static_assert(SPLIT || B0 == B1, "one bit width without split");
+  static_assert(!(UOUT && SPLIT), "rotation output without split only");
   __shared__ uint4 frag[2 * FRAG_U4];  // [0, FRAG_U4): Pi~ fragments; then S'~ fragments
   __shared__ int next_tile;            // work queue of this workgroup's tile range
 
@@ -301,6 +305,19 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);   // bound the fragment reads in flight
     }
+    if constexpr (UOUT) {
+      // lane half h, register r of row tile mt holds coordinate 32 mt + 16 h + r
+      if (valid) {
+        const float inv = nu0 > 0.f ? 1.f / nu0 : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<float4*>(u_out + vec * D + 32 * mt + 16 * kh + 4 * r4) =
+                make_float4(U[mt][4 * r4] * inv, U[mt][4 * r4 + 1] * inv, U[mt][4 * r4 + 2] * inv,
+                            U[mt][4 * r4 + 3] * inv);
+      }
+    }
     // the input registers are free: fetch the next tile while this one is finished
     const long next = grab();
     if (next < t_end) load_tile(next);
@@ -428,7 +445,17 @@ hipError_t launch(const void* params, const void* x, int64_t n, uint32_t* codes,
   hipLaunchKernelGGL((quantize_d128_kernel<BITS, BITS, F32IN, MSE, false>), dim3(grid_for(n)),
                      dim3(WAVES * 64), 0, s, static_cast<const unsigned char*>(params), nullptr,
                      Layout(D, BITS).off_qfrag, size_t(0), x, long(n), codes, nu, gamma, nullptr,
-                     nullptr, nullptr);
+                     nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+template <int BITS, bool F32IN>
+hipError_t launch_u(const void* params, const void* x, int64_t n, uint32_t* codes, float* nu,
+                    float* gamma, float* u, hipStream_t s) {
+  hipLaunchKernelGGL((quantize_d128_kernel<BITS, BITS, F32IN, false, false, true>), dim3(grid_for(n)),
+                     dim3(WAVES * 64), 0, s, static_cast<const unsigned char*>(params), nullptr,
+                     Layout(D, BITS).off_qfrag, size_t(0), x, long(n), codes, nu, gamma, nullptr,
+                     nullptr, nullptr, u);
   return hipGetLastError();
 }
 
@@ -439,7 +466,7 @@ hipError_t launch_split(const void* params0, const void* params1, const void* x,
   hipLaunchKernelGGL((quantize_d128_kernel<B0, B1, F32IN, MSE, true>), dim3(grid_for(n)),
                      dim3(WAVES * 64), 0, s, static_cast<const unsigned char*>(params0),
                      static_cast<const unsigned char*>(params1), size_t(0), Layout(64, B0).off_gmat, x,
-                     long(n), codes0, nu0, gamma0, codes1, nu1, gamma1);
+                     long(n), codes0, nu0, gamma0, codes1, nu1, gamma1, nullptr);
   return hipGetLastError();
 }
 
@@ -455,6 +482,20 @@ hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_
                        : launch<3, false>(params, x, n, codes, nu, gamma, s);
     case 4: return f32 ? launch<4, true>(params, x, n, codes, nu, gamma, s)
                        : launch<4, false>(params, x, n, codes, nu, gamma, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_quantize_d128_u(const void* params, int b, const void* x, int x_dtype, int64_t n,
+                                  uint32_t* codes, float* nu, float* gamma, float* u, hipStream_t s) {
+  const bool f32 = x_dtype == 0;
+  switch (b) {
+    case 2: return f32 ? launch_u<2, true>(params, x, n, codes, nu, gamma, u, s)
+                       : launch_u<2, false>(params, x, n, codes, nu, gamma, u, s);
+    case 3: return f32 ? launch_u<3, true>(params, x, n, codes, nu, gamma, u, s)
+                       : launch_u<3, false>(params, x, n, codes, nu, gamma, u, s);
+    case 4: return f32 ? launch_u<4, true>(params, x, n, codes, nu, gamma, u, s)
+                       : launch_u<4, false>(params, x, n, codes, nu, gamma, u, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -278,13 +278,17 @@ __device__ __forceinline__ void store_residual(char* sb, const uint32_t (&v)[2][
 // A rows are apitch elements apart (d, or the caller's row pitch for bf16 rows read in place).
 // PHASE 3: phase 1 for the MSE quantizer alone: the b-1 index planes (a code stride of b-1
 // words per coordinate group) and nothing for a phase 2.
-template <int PHASE, int BITS, bool ALO>
+// UOUT (diagnostic, phase 1 only): u = Pi x / nu of every vector is also written to u_out
+// [rows of the call][d] float32 (row v0 + r of the call at u_out + (v0 + r) d), the values the
+// bucketize reads.
+template <int PHASE, int BITS, bool ALO, bool UOUT = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
     const unsigned char* __restrict__ params, const uint16_t* __restrict__ ahi,
     const uint16_t* __restrict__ alo, long rows, const uint16_t* __restrict__ bhi,
     const uint16_t* __restrict__ blo, int d, long apitch, long v0, int nrb, uint32_t* __restrict__ codes,
     const float* __restrict__ nu, float* __restrict__ gamma_out, uint16_t* __restrict__ rhi,
-    uint16_t* __restrict__ rlo, float* __restrict__ gpart) {
+    uint16_t* __restrict__ rlo, float* __restrict__ gpart, float* __restrict__ u_out) {
+  static_assert(!UOUT || PHASE == 1, "rotation output from phase 1 only");
   __shared__ uint4 buf0[StageShape<ALO>::U4];
   __shared__ uint4 buf1[StageShape<ALO>::U4];
   __shared__ float rowscale[WT];
@@ -351,6 +355,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
   // would turn every partial wait for LDS reads into a full one.
   asm volatile("" ::"s"(params), "s"(codes), "s"(nu), "s"(gamma_out), "s"(rhi), "s"(rlo),
                "s"(gpart), "s"(rows), "s"(v0));
+  if constexpr (UOUT) asm volatile("" ::"s"(u_out));
   Frags<ALO> f0, f1;
   read_b(f0, reinterpret_cast<const char*>(buf0) + off[0], wn);
 #pragma unroll
@@ -402,30 +407,42 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
         for (int p = 0; p < BITS - 1; ++p) word[p] = 0u;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          if constexpr (UOUT) {
+            // coordinates cb + 8 g + 4 h + e, e = 0..3, of this lane's vector
+            if (okc && okr)
+              *reinterpret_cast<float4*>(u_out + size_t(v0 + r0 + vr) * d + cb + 8 * g + 4 * h) =
+                  make_float4(acc[i][j][4 * g] * rs, acc[i][j][4 * g + 1] * rs, acc[i][j][4 * g + 2] * rs,
+                              acc[i][j][4 * g + 3] * rs);
+          }
           uint32_t hp[2] = {0u, 0u}, lp[2] = {0u, 0u};   // bf16 pairs of coordinates 4 h + e
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float u = acc[i][j][4 * g + e] * rs;
+            // magnitude index k of |u| against the positive thresholds (a tie goes to the
+            // outer cell), the level's side from the sign of u (0 to the positive side):
+            // index = L/2 + k for u >= 0, L/2 - 1 - k for u < 0, so the low index bits are
+            // the bits of k, complemented on the negative side
+            const float a = fabsf(u);
+            const bool pos = u >= 0.f;
             bool bit[3] = {false, false, false};
-            float c;
+            float mag;
             if constexpr (BITS == 2) {
-              bit[0] = u >= 0.f;
-              c = bit[0] ? M[0] : -M[0];
+              bit[0] = pos;
+              mag = M[0];
             } else if constexpr (BITS == 3) {
-              bit[1] = u >= 0.f;
-              bit[0] = u >= (bit[1] ? T[0] : -T[0]);
-              const float mag = (bit[0] == bit[1]) ? M[1] : M[0];
-              c = bit[1] ? mag : -mag;
+              const bool k0 = a >= T[0];
+              bit[1] = pos;
+              bit[0] = k0 == pos;
+              mag = k0 ? M[1] : M[0];
             } else {
-              bit[2] = u >= 0.f;
-              bit[1] = u >= (bit[2] ? T[1] : -T[1]);
-              const bool e1 = (bit[1] == bit[2]);
-              const float t2 = e1 ? T[2] : T[0];
-              bit[0] = u >= (bit[2] ? t2 : -t2);
-              const bool e0 = (bit[0] == bit[2]);
-              const float mag = e1 ? (e0 ? M[3] : M[2]) : (e0 ? M[1] : M[0]);
-              c = bit[2] ? mag : -mag;
+              const bool k1 = a >= T[1];
+              const bool k0 = a >= (k1 ? T[2] : T[0]);
+              bit[2] = pos;
+              bit[1] = k1 == pos;
+              bit[0] = k0 == pos;
+              mag = k1 ? (k0 ? M[3] : M[2]) : (k0 ? M[1] : M[0]);
             }
+            const float c = pos ? mag : -mag;
             const float rv = u - c;
             const uint32_t hb = bf16_bits(rv);
             const uint32_t lb = bf16_bits(rv - __uint_as_float(hb << 16));
@@ -506,7 +523,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void qgemm_kernel(
 
 template <int BITS, bool F32IN>
 hipError_t run(const unsigned char* params, const Layout& lay, const void* x, long xpitch, int64_t n,
-               uint32_t* codes, float* nu, float* gamma, hipStream_t s) {
+               uint32_t* codes, float* nu, float* gamma, hipStream_t s, float* u) {
   const int d = lay.d;
   const uint16_t* pih = reinterpret_cast<const uint16_t*>(params + lay.off_gmat);
   const uint16_t* pil = pih + size_t(d) * d;
@@ -536,10 +553,15 @@ hipError_t run(const unsigned char* params, const Layout& lay, const void* x, lo
                        rows, d, xpitch, xh, xl, c0, nu);
     const uint16_t* a1 = F32IN ? xh : static_cast<const uint16_t*>(xs);
     const long ap = F32IN ? long(d) : xpitch;
-    hipLaunchKernelGGL((qgemm_kernel<1, BITS, F32IN>), grid, dim3(WAVES * 64), 0, s, params, a1, xl,
-                       rows, pih, pil, d, ap, c0, nrb, codes, nu, gamma, rhi, rlo, gpart);
+    if (u)
+      hipLaunchKernelGGL((qgemm_kernel<1, BITS, F32IN, true>), grid, dim3(WAVES * 64), 0, s, params, a1, xl,
+                         rows, pih, pil, d, ap, c0, nrb, codes, nu, gamma, rhi, rlo, gpart, u);
+    else
+      hipLaunchKernelGGL((qgemm_kernel<1, BITS, F32IN>), grid, dim3(WAVES * 64), 0, s, params, a1, xl,
+                         rows, pih, pil, d, ap, c0, nrb, codes, nu, gamma, rhi, rlo, gpart, nullptr);
     hipLaunchKernelGGL((qgemm_kernel<2, BITS, true>), grid, dim3(WAVES * 64), 0, s, params, rhi, rlo,
-                       rows, sph, spl, d, long(d), c0, nrb, codes, nu, gamma, nullptr, nullptr, gpart);
+                       rows, sph, spl, d, long(d), c0, nrb, codes, nu, gamma, nullptr, nullptr, gpart,
+                       nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) break;
   }
@@ -577,7 +599,8 @@ hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x
     const uint16_t* a1 = F32IN ? xh : static_cast<const uint16_t*>(xs);
     const long ap = F32IN ? long(d) : xpitch;
     hipLaunchKernelGGL((qgemm_kernel<3, BITS, F32IN>), grid, dim3(WAVES * 64), 0, s, params, a1, xl,
-                       rows, pih, pil, d, ap, c0, nrb, codes, nu, nullptr, nullptr, nullptr, nullptr);
+                       rows, pih, pil, d, ap, c0, nrb, codes, nu, nullptr, nullptr, nullptr, nullptr,
+                       nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) break;
   }
@@ -592,18 +615,18 @@ hipError_t run_mse(const unsigned char* params, const Layout& lay, const void* x
 
 hipError_t launch_quantize_gemm(const void* params_v, int d, int b, const void* x, int x_dtype,
                                 int64_t n, uint32_t* codes, float* nu, float* gamma,
-                                hipStream_t s, int64_t xpitch) {
+                                hipStream_t s, int64_t xpitch, float* u) {
   const unsigned char* params = static_cast<const unsigned char*>(params_v);
   const Layout lay(d, b);
   const bool f32 = x_dtype == 0;
   const long xp = xpitch > 0 ? long(xpitch) : long(d);
   switch (b) {
-    case 2: return f32 ? run<2, true>(params, lay, x, xp, n, codes, nu, gamma, s)
-                       : run<2, false>(params, lay, x, xp, n, codes, nu, gamma, s);
-    case 3: return f32 ? run<3, true>(params, lay, x, xp, n, codes, nu, gamma, s)
-                       : run<3, false>(params, lay, x, xp, n, codes, nu, gamma, s);
-    case 4: return f32 ? run<4, true>(params, lay, x, xp, n, codes, nu, gamma, s)
-                       : run<4, false>(params, lay, x, xp, n, codes, nu, gamma, s);
+    case 2: return f32 ? run<2, true>(params, lay, x, xp, n, codes, nu, gamma, s, u)
+                       : run<2, false>(params, lay, x, xp, n, codes, nu, gamma, s, u);
+    case 3: return f32 ? run<3, true>(params, lay, x, xp, n, codes, nu, gamma, s, u)
+                       : run<3, false>(params, lay, x, xp, n, codes, nu, gamma, s, u);
+    case 4: return f32 ? run<4, true>(params, lay, x, xp, n, codes, nu, gamma, s, u)
+                       : run<4, false>(params, lay, x, xp, n, codes, nu, gamma, s, u);
     default: return hipErrorInvalidValue;
   }
 }

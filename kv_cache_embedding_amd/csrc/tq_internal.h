@@ -73,6 +73,9 @@ constexpr size_t score_ws_per_group(int b) {
 // ---- kernel launchers (defined in the .hip files), return hipError_t
 hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_dtype, int64_t n,
                                 uint32_t* codes, float* nu, float* gamma, hipStream_t s);
+// The same encoder, also writing u = Pi x / nu ([n][128] float32) from its accumulators.
+hipError_t launch_quantize_d128_u(const void* params, int b, const void* x, int x_dtype, int64_t n,
+                                  uint32_t* codes, float* nu, float* gamma, float* u, hipStream_t s);
 // Fused d = 128 encoder on two 64-channel groups (each its own d = 64 parameter block);
 // mse: the MSE quantizer alone (b - 1 index planes per group, no gamma).
 hipError_t launch_quantize_d128_split(const void* params0, const void* params1, int b0, int b1,
@@ -80,10 +83,11 @@ hipError_t launch_quantize_d128_split(const void* params0, const void* params1, 
                                       float* nu0, float* gamma0, uint32_t* codes1, float* nu1,
                                       float* gamma1, hipStream_t s, bool mse = false);
 // Tiled encoder, any valid d.  xpitch: elements between input rows (0: d), so that a
-// channel group of wider rows is read in place.
+// channel group of wider rows is read in place.  u (optional): also write u = Pi x / nu
+// ([n][d] float32) from phase 1's accumulators.
 hipError_t launch_quantize_gemm(const void* params, int d, int b, const void* x, int x_dtype,
                                 int64_t n, uint32_t* codes, float* nu, float* gamma,
-                                hipStream_t s, int64_t xpitch = 0);
+                                hipStream_t s, int64_t xpitch = 0, float* u = nullptr);
 hipError_t launch_score_d128(const void* params, int b, const void* q, int q_dtype,
                              const uint32_t* codes, const float* nu, const float* gamma,
                              int64_t groups, int64_t G, int64_t T, int mode, float* logits,

@@ -15,14 +15,17 @@ Sources (web pages; cited by short name and the passage on the page):
 The pages give the method in prose only.  Readings taken where they are silent:
   * the codebook is Lloyd-Max for N(0, 1/d) (coordinates of a rotated unit vector are
     "almost normal"), with L = 2**(b-1) levels for a total budget of b bits;
-  * a coordinate lying exactly on a threshold goes to the upper cell;
+  * a coordinate lying exactly on a threshold goes to the cell farther from zero, and a
+    coordinate equal to 0 to the positive side: the quantizer of the symmetric law stays odd,
+    Q(-u) = -Q(u), at ties too;
   * the QJL matrix S is Gaussian N(0, 1) with m = d rows, separate from the rotation;
   * the QJL scale is sqrt(pi/2)/m times the residual norm gamma (the value that makes the
     estimate exactly unbiased: E|<s, r/|r|>| sign terms average sqrt(2/pi)|r|);
   * sign(0) is +1 (z = [y >= 0]);
   * vectors are normalised and their norm nu is stored next to gamma (no other constant);
-  * integer decisions (bucket index, sign bit) are taken in float32, the precision of the
-    GPU kernels: the pages fix none;
+  * integer decisions (bucket index, sign bit) are taken in float64 on the float64 values
+    (the pages fix no precision; a decision within rounding of a threshold is what the
+    parity tests excuse);
   * variants ([review, QJL paragraph]: an orthogonal QJL matrix; the exact sphere law of a
     rotated coordinate): codebook_sphere is Lloyd-Max on that law, and an orthogonal S
     takes the scale 1/(m E|w_1|);
@@ -213,16 +216,24 @@ def normalize_rotate(x: np.ndarray, Pi: np.ndarray):
     return nu, xn, u
 
 
-def bucketize(u: np.ndarray, thresholds: np.ndarray, decide_dtype=np.float32) -> np.ndarray:
-    """idx_t = number of thresholds tau_i with u_t >= tau_i.
+def bucketize(u: np.ndarray, thresholds: np.ndarray, decide_dtype=np.float64) -> np.ndarray:
+    """Lloyd-Max cell index of every coordinate: the number of thresholds below u_t.
 
     [tldr, step 1] / [explainer, step 1]: each coordinate is rounded on its own against the
-    precomputed grid.  A value equal to a threshold goes to the upper cell.  The comparison
-    is made in ``decide_dtype`` (float32 by default, the kernels' precision).
+    precomputed grid.  The grid of the symmetric law is odd-symmetric, and ties keep the
+    quantizer odd: a value equal to a threshold goes to the cell farther from zero (for
+    u >= 0 the thresholds with u >= tau count, for u < 0 those with u > tau), so u = 0
+    goes to the positive side.  The comparison is made in ``decide_dtype`` (float64 by
+    default).
     """
     uu = np.asarray(u).astype(decide_dtype)
     tt = np.asarray(thresholds).astype(decide_dtype)
-    return np.sum(uu[..., None] >= tt, axis=-1).astype(np.int64)
+    at_or_above = np.zeros(uu.shape, dtype=np.int64)       # #{tau : tau <= u}
+    strictly_above = np.zeros(uu.shape, dtype=np.int64)    # #{tau : tau < u}
+    for tau in tt.ravel():
+        at_or_above += uu >= tau
+        strictly_above += uu > tau
+    return np.where(uu >= 0, at_or_above, strictly_above)
 
 
 def residual(xn: np.ndarray, Pi: np.ndarray, chat: np.ndarray):
@@ -236,7 +247,7 @@ def residual(xn: np.ndarray, Pi: np.ndarray, chat: np.ndarray):
     return r, np.sqrt(np.sum(r * r, axis=1))
 
 
-def qjl_signs(S: np.ndarray, r: np.ndarray, decide_dtype=np.float32):
+def qjl_signs(S: np.ndarray, r: np.ndarray, decide_dtype=np.float64):
     """y = S r and z_i = [y_i >= 0] (1 bit per projected dimension).
 
     [tldr, step 2]: the residual is multiplied by another random matrix and only the sign

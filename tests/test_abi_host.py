@@ -120,6 +120,17 @@ def test_invalid_arguments_return_status_without_launch(lib):
     # every multiple of 64 in range is a valid dimension: d = 192 fails on the pointer, not the shape
     assert lib.tq_quantize(fake, 192, 4, P(0x1002), 0, 10, fake, fake, fake, None) == tq.TQ_EINVAL
     assert "misaligned" in tq.tq_last_error()
+    # the rotation diagnostic validates like tq_quantize, plus its u pointer
+    assert lib.tq_quantize_with_rotation(fake, 100, 4, fake, 0, 10, fake, fake, fake, fake, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize_with_rotation(fake, 128, 4, fake, 0, 10, fake, fake, fake, None, None) == tq.TQ_EINVAL
+    assert lib.tq_quantize_with_rotation(fake, 128, 4, fake, 0, 10, fake, fake, fake, P(0x1004), None) == tq.TQ_EINVAL
+    assert "misaligned" in tq.tq_last_error()
+    assert lib.tq_quantize_with_rotation(None, 128, 4, None, 0, 0, None, None, None, None, None) == tq.TQ_OK
+    # d = 128 MSE codes are stored 8 or 16 bytes at a time: 16-byte alignment required
+    assert lib.tq_quantize_mse(fake, 128, 3, fake, 0, 10, P(0x1004), fake, None) == tq.TQ_EINVAL
+    assert "misaligned" in tq.tq_last_error()
+    assert lib.tq_quantize_mse_split(fake, fake, 128, 64, 3, 3, fake, 0, 10, P(0x1008), fake, fake, fake,
+                                     None) == tq.TQ_EINVAL
     # scoring: bad mode, workspace too small, unsupported G
     args = (fake, 128, 4, fake, 1, fake, fake, fake, 8, 4, 1024)
     assert lib.tq_score_ip(*args, 9, fake, fake, 1 << 30, None) == tq.TQ_EINVAL

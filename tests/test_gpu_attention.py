@@ -169,9 +169,11 @@ def test_attention_long_sequence_many_blocks():
 
 
 @pytest.mark.parametrize("d,bf16", [(128, True), (192, False)])
-def test_append_matches_bulk_encoding(d, bf16):
-    # a cache filled token by token through tq_append holds the bulk encoders' bytes, for keys
-    # (prod) and values (mse); slots not yet written keep their contents
+def test_append_matches_oracle_and_bulk_encoding(d, bf16):
+    # a cache filled token by token through tq_append holds, in every written slot, the
+    # oracle's encoding of that token (keys: oracle.quantize, values: oracle.quantize_mse,
+    # under the excuse rule of the bulk parity tests) and the bulk encoders' bytes; slots not
+    # yet written keep their contents
     groups, T, b = 3, 40, 4
     st = U.make_setup(d, b, cfg=44)
     x = gen.unit_sphere(groups * T, d, cfg=44, role=gen.ROLE_DATA) * 2.0
@@ -203,3 +205,15 @@ def test_append_matches_bulk_encoding(d, bf16):
         assert np.array_equal(got.cpu().numpy()[rows], ref.cpu().numpy()[rows])
         assert np.all(got.cpu().numpy()[empty] == -1.0)
     assert np.all(ckn[empty] == -1) and np.all(cvn[empty] == -1)
+    # against the oracle, slot by slot: token t of group g sits at row g * T + t
+    x64 = U.host64(x, bf16)[rows]
+    rep = U.compare_codes(st, x64, ckn[rows].view(np.uint32).reshape(rows.size, W, b),
+                          nk.cpu().numpy()[rows], gk.cpu().numpy()[rows])
+    print(f"[append d={d}] keys vs oracle: {U.describe(rep)}", flush=True)
+    U.assert_codes_ok(rep)
+    idx_v = oracle.unpack_index_planes(cvn[rows].view(np.uint32).reshape(rows.size, W, b - 1), b - 1)
+    unexcused, mism = _idx_report(st, x64, idx_v)
+    print(f"[append d={d}] values vs oracle: index mismatches {mism}, unexcused {unexcused}", flush=True)
+    assert unexcused == 0 and mism <= 1e-4 * idx_v.size
+    nu_o = np.linalg.norm(x64, axis=1)
+    assert np.max(np.abs(nv.cpu().numpy()[rows] - nu_o) / nu_o) <= 1e-5

@@ -163,7 +163,7 @@ def test_bucketize_equals_bruteforce_nearest_product_codebook(d, bits):
     c, t = oracle.codebook(bits, d)
     g = np.random.default_rng(1000 * d + bits)
     u = g.standard_normal((40, d)) / math.sqrt(d)
-    idx = oracle.bucketize(u, t, decide_dtype=np.float64)
+    idx = oracle.bucketize(u, t)
     cands = np.array(list(itertools.product(range(len(c)), repeat=d)))
     pts = c[cands]                                             # [L^d][d]
     for row in range(u.shape[0]):
@@ -172,21 +172,39 @@ def test_bucketize_equals_bruteforce_nearest_product_codebook(d, bits):
         assert np.array_equal(best, idx[row])
 
 
-def test_bucketize_threshold_tie_goes_to_upper_cell():
+def test_bucketize_threshold_tie_goes_away_from_zero():
+    # Ties keep the quantizer odd: on a positive threshold the upper cell, on a negative one
+    # the lower cell (both farther from zero); exactly 0 (either zero) to the positive side.
     c, t = oracle.codebook(3, 128)
-    u = np.array([t, np.nextafter(t, -np.inf)])           # exactly on, and just below
-    idx = oracle.bucketize(u, t, decide_dtype=np.float64)
-    assert idx[0].tolist() == list(range(1, len(c)))
-    assert idx[1].tolist() == list(range(0, len(c) - 1))
-    # -0.0 sits on the zero threshold: upper cell
+    L = len(c)
+    on = oracle.bucketize(t[None, :].repeat(1, 0), t)[0]
+    for i, tau in enumerate(t):
+        expect = i + 1 if tau >= 0 else i
+        assert on[i] == expect, (i, tau, on[i])
+    below = oracle.bucketize(np.nextafter(t, -np.inf)[None, :], t)[0]
+    above = oracle.bucketize(np.nextafter(t, np.inf)[None, :], t)[0]
+    assert below.tolist() == list(range(0, L - 1))
+    assert above.tolist() == list(range(1, L))
     assert oracle.bucketize(np.array([-0.0]), np.array([0.0]))[0] == 1
+    assert oracle.bucketize(np.array([0.0]), np.array([0.0]))[0] == 1
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_bucketize_is_odd_symmetric_including_ties(bits):
+    # Q(-u) = -Q(u) for u != 0: index(-u) = L - 1 - index(u), also on every threshold.
+    c, t = oracle.codebook(bits, 64)
+    g = np.random.default_rng(77 + bits)
+    u = np.concatenate([g.standard_normal(500) / 8.0, t[t != 0], -t[t != 0]])
+    i_pos = oracle.bucketize(u, t)
+    i_neg = oracle.bucketize(-u, t)
+    assert np.array_equal(i_neg, len(c) - 1 - i_pos)
 
 
 def test_bucketize_float32_decision_matches_float64_away_from_thresholds():
     c, t = oracle.codebook(3, 128)
     u = np.random.default_rng(5).standard_normal((2000, 128)) / math.sqrt(128)
-    i32 = oracle.bucketize(u, t)
-    i64 = oracle.bucketize(u, t, decide_dtype=np.float64)
+    i32 = oracle.bucketize(u, t, decide_dtype=np.float32)
+    i64 = oracle.bucketize(u, t)
     near = np.min(np.abs(u[..., None] - t), axis=-1) <= 1e-7
     assert np.array_equal(i32[~near], i64[~near])
 

@@ -8,12 +8,16 @@ Acceptance rules (the pages fix no tolerances; these follow the stated targets):
   * excused rate <= 1e-4, unexcused = 0;
   * nu within 1e-5 relative, gamma within 1e-5 absolute (gamma is a norm of a unit-vector
     residual);
-  * logits with the oracle fed the GPU's codes: |l_gpu - l_oracle| <= 1e-3 |q| nu.
+  * logits with the oracle fed the GPU's codes: |l_gpu - l_oracle| <= 1e-3 |q| nu;
+  * rotated coordinates (where the encoder reports them): max |u_gpu - u_oracle| <= 1e-5
+    (u is a unit vector, so this is relative to |x|).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 import torch
@@ -26,6 +30,55 @@ EXCUSE_U = 1e-5
 EXCUSE_Y = 1e-5
 MAX_EXCUSED_RATE = 1e-4
 LOGIT_TOL = 1e-3
+ROTATION_TOL = 1e-5
+
+
+def worker_count() -> int:
+    """Host threads for the oracle side of the full-size checks (at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:   # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def parallel_map(fn, items, label: str | None = None, every: int = 16):
+    """fn over items on host threads, BLAS limited to one thread each; results in order.
+    NumPy releases the GIL in its array loops and BLAS calls, so chunks of an oracle check
+    run side by side.  With a label, a progress line is printed every `every` items."""
+    import threading
+
+    from threadpoolctl import threadpool_limits
+    items = list(items)
+    lock = threading.Lock()
+    done = [0]
+
+    def run(item):
+        out = fn(item)
+        if label:
+            with lock:
+                done[0] += 1
+                if done[0] % every == 0 or done[0] == len(items):
+                    print(f"  [{label}] {done[0]}/{len(items)}", flush=True)
+        return out
+
+    with threadpool_limits(limits=1), concurrent.futures.ThreadPoolExecutor(worker_count()) as ex:
+        return list(ex.map(run, items))
+
+
+def merge_reports(reps: list) -> dict:
+    """Totals and worst cases of several compare_codes reports (their idx / z dropped)."""
+    out = {"n": 0, "unexcused_idx": 0, "excused_idx": 0, "unexcused_z": 0, "excused_z": 0,
+           "nu_rel_err": 0.0, "gamma_abs_err": 0.0, "u_abs_err": None, "coords": 0}
+    for r in reps:
+        for k in ("n", "unexcused_idx", "excused_idx", "unexcused_z", "excused_z", "coords"):
+            out[k] += r[k]
+        out["nu_rel_err"] = max(out["nu_rel_err"], r["nu_rel_err"])
+        out["gamma_abs_err"] = max(out["gamma_abs_err"], r["gamma_abs_err"])
+        if r.get("u_abs_err") is not None:
+            out["u_abs_err"] = max(out["u_abs_err"] or 0.0, r["u_abs_err"])
+    out["excused_rate"] = (out["excused_idx"] + out["excused_z"]) / max(2 * out["coords"], 1)
+    return out
 
 DEV = torch.device("cuda:0")
 
@@ -87,11 +140,16 @@ def codes_np(codes: torch.Tensor, n: int, d: int, b: int) -> np.ndarray:
 
 
 def compare_codes(st: Setup, x64: np.ndarray, codes: np.ndarray, nu: np.ndarray,
-                  gamma: np.ndarray) -> dict:
-    """Compare GPU codes with the oracle on the same inputs; returns a report dict."""
+                  gamma: np.ndarray, u_gpu: np.ndarray | None = None, keep: bool = True) -> dict:
+    """Compare GPU codes with the oracle on the same inputs; returns a report dict.
+    u_gpu: the rotated coordinates the encoder reported (checked against the oracle's u);
+    keep: also return the unpacked GPU idx and z."""
     d, b = st.d, st.b
     idx_g, z_g = oracle.unpack_codes(codes, b)
     nu_o, xn, u = oracle.normalize_rotate(x64, st.Pi)
+    u_err = None
+    if u_gpu is not None:
+        u_err = float(np.max(np.abs(np.asarray(u_gpu, np.float64) - u))) if u.size else 0.0
     idx_o = oracle.bucketize(u, st.t_or)
     mism = idx_g != idx_o
     unexcused_idx = 0
@@ -119,12 +177,15 @@ def compare_codes(st: Setup, x64: np.ndarray, codes: np.ndarray, nu: np.ndarray,
     nu_err = float(np.max(np.abs(nu - nu_o) / np.maximum(nu_o, 1e-30))) if nu.size else 0.0
     gamma_err = float(np.max(np.abs(gamma - gam))) if gamma.size else 0.0
     total = idx_g.size
-    return {
+    rep = {
         "n": x64.shape[0], "unexcused_idx": unexcused_idx, "excused_idx": excused_idx,
-        "unexcused_z": unexcused_z, "excused_z": excused_z,
+        "unexcused_z": unexcused_z, "excused_z": excused_z, "coords": total,
         "excused_rate": (excused_idx + excused_z) / max(2 * total, 1),
-        "nu_rel_err": nu_err, "gamma_abs_err": gamma_err, "idx": idx_g, "z": z_g,
+        "nu_rel_err": nu_err, "gamma_abs_err": gamma_err, "u_abs_err": u_err,
     }
+    if keep:
+        rep["idx"], rep["z"] = idx_g, z_g
+    return rep
 
 
 def assert_codes_ok(rep: dict):
@@ -133,6 +194,8 @@ def assert_codes_ok(rep: dict):
     assert rep["excused_rate"] <= MAX_EXCUSED_RATE, rep["excused_rate"]
     assert rep["nu_rel_err"] <= 1e-5, rep["nu_rel_err"]
     assert rep["gamma_abs_err"] <= 1e-5, rep["gamma_abs_err"]
+    if rep.get("u_abs_err") is not None:
+        assert rep["u_abs_err"] <= ROTATION_TOL, rep["u_abs_err"]
 
 
 def logit_errors(st: Setup, q64: np.ndarray, idx, z, nu, gamma, logits: np.ndarray,
@@ -165,10 +228,23 @@ def gpu_score(st: Setup, qd: torch.Tensor, codes, nu, gamma, groups: int, G: int
 
 
 def describe(rep: dict) -> str:
+    u = rep.get("u_abs_err")
     return (f"n={rep['n']} idx unexcused={rep['unexcused_idx']} excused={rep['excused_idx']} "
             f"z unexcused={rep['unexcused_z']} excused={rep['excused_z']} "
             f"rate={rep['excused_rate']:.2e} nu_err={rep['nu_rel_err']:.1e} "
-            f"gamma_err={rep['gamma_abs_err']:.1e}")
+            f"gamma_err={rep['gamma_abs_err']:.1e}" + ("" if u is None else f" u_err={u:.1e}"))
+
+
+def gpu_quantize_rotation(st: Setup, xd: torch.Tensor):
+    """tq_quantize_with_rotation: codes, nu, gamma and the encoder's u [n][d] (on the GPU)."""
+    n = xd.shape[0]
+    codes = torch.full((n * (st.d // 32) * st.b,), -1, dtype=torch.int32, device=DEV)
+    nu = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
+    gamma = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
+    u = torch.full((n * st.d,), float("nan"), dtype=torch.float32, device=DEV)
+    tq.tq_quantize_with_rotation(st.params, st.d, st.b, xd, codes, nu, gamma, u)
+    torch.cuda.synchronize()
+    return codes, nu, gamma, u.view(n, st.d)
 
 
 def gpu_topk(st: Setup, qd: torch.Tensor, codes, nu, gamma, n: int, k: int, mode: int):
