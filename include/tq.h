@@ -235,6 +235,21 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
                 void* stream);
 
 /*
+ * tq_score_ip_noalloc — tq_score_ip for callers that cannot allocate or hand in a
+ * workspace (code under HIP graph capture, tight serving loops): the workspace is a fixed
+ * device array of tq_score_noalloc_max_ws_bytes() bytes (8 MiB) inside the library, one per
+ * GPU, held until the process ends; its address on a device is looked up on the first call
+ * there.  Arguments, results and errors as tq_score_ip without ws / ws_bytes; sizes whose
+ * tq_score_ws_bytes exceeds the fixed array return TQ_EUNSUPPORTED before any device call.
+ * This call allocates nothing.  All calls on one GPU share its array: calls that overlap on
+ * one GPU (e.g. on two streams) race and must be ordered by the caller.
+ */
+size_t tq_score_noalloc_max_ws_bytes(void);
+int tq_score_ip_noalloc(const void* params, int d, int b, const void* q, int q_dtype,
+                        const uint32_t* codes, const float* nu, const float* gamma, int64_t groups,
+                        int64_t G, int64_t T, int mode, float* logits, void* stream);
+
+/*
  * Fractional bit rates ([review, experiments paragraph] and [news, results paragraph]: KV
  * caches at 2.5 and 3.5 bits per channel; the pages give no mechanism).  Each row of d
  * channels is two channel groups, [0, d0) and [d0, d), each a TurboQuant instance of its

@@ -48,6 +48,8 @@ def load_library():
         "tq_dequantize": (I, [P, I, I, P, P, P, I64, I, P, P]),
         "tq_score_ws_bytes": (SZ, [I, I, I64, I64, I64]),
         "tq_score_ip": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P, SZ, P]),
+        "tq_score_ip_noalloc": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P]),
+        "tq_score_noalloc_max_ws_bytes": (SZ, []),
         "tq_quantize_mse": (I, [P, I, I, P, I, I64, P, P, P]),
         "tq_quantize_split": (I, [P, P, I, I, I, I, P, I, I64, P, P, P, P, P, P, P]),
         "tq_score_split_ws_bytes": (SZ, [I, I, I, I, I64, I64, I64]),
@@ -291,6 +293,28 @@ def tq_score_ip(params, d: int, b: int, q, codes, nu, gamma, groups: int, G: int
                                       _ptr(nu), _ptr(gamma), groups, G, T, int(mode), _ptr(logits),
                                       _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(stream, q.device)))
+
+
+def tq_score_noalloc_max_ws_bytes() -> int:
+    return int(load_library().tq_score_noalloc_max_ws_bytes())
+
+
+def tq_score_ip_noalloc(params, d: int, b: int, q, codes, nu, gamma, groups: int, G: int, T: int,
+                        mode: int, logits, stream=None):
+    """tq_score_ip with the library's fixed per-GPU scratch in place of a workspace."""
+    torch = _torch()
+    for tname, t in (("q", q), ("codes", codes), ("nu", nu), ("gamma", gamma), ("logits", logits),
+                     ("params", params)):
+        _dev(t, tname)
+    if q.numel() < groups * G * d:
+        raise ValueError("q holds fewer than groups*G*d elements")
+    _need(codes, "codes", groups * T * (d // 32) * b, torch.int32)
+    _need(nu, "nu", groups * T, torch.float32)
+    _need(gamma, "gamma", groups * T, torch.float32)
+    _need(logits, "logits", groups * G * T, torch.float32)
+    _check(load_library().tq_score_ip_noalloc(_ptr(params), d, b, _ptr(q), _dtype_code(q, "q"), _ptr(codes),
+                                              _ptr(nu), _ptr(gamma), groups, G, T, int(mode), _ptr(logits),
+                                              _stream(stream, q.device)))
 
 
 def tq_quantize_split(params0, params1, d: int, d0: int, b0: int, b1: int, x, codes0, nu0, gamma0,

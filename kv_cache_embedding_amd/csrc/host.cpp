@@ -842,3 +842,10 @@ int tq_topk(const void* params, int d, int b, const void* q, int q_dtype, int64_
 }
 
 }  // extern "C"
+
+namespace tq {
+
+// Sets the calling thread's tq_last_error() text (for entry points in other source files).
+int report_error(int status, const char* message) { return fail(status, "%s", message); }
+
+}  // namespace tq

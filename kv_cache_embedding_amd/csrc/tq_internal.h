@@ -70,6 +70,9 @@ constexpr size_t score_ws_per_group(int b) {
   return size_t(2 * score_words(b)) * 64 * 16 + 4 * 4 * 4;
 }
 
+// Sets the calling thread's tq_last_error() text and returns status (host.cpp).
+int report_error(int status, const char* message);
+
 // ---- kernel launchers (defined in the .hip files), return hipError_t
 hipError_t launch_quantize_d128(const void* params, int b, const void* x, int x_dtype, int64_t n,
                                 uint32_t* codes, float* nu, float* gamma, hipStream_t s);

@@ -131,6 +131,19 @@ def test_invalid_arguments_return_status_without_launch(lib):
     assert "misaligned" in tq.tq_last_error()
     assert lib.tq_quantize_mse_split(fake, fake, 128, 64, 3, 3, fake, 0, 10, P(0x1008), fake, fake, fake,
                                      None) == tq.TQ_EINVAL
+    # allocation-free scoring: a workspace beyond the fixed scratch is refused before any
+    # device call; empty sizes are a no-op
+    cap = lib.tq_score_noalloc_max_ws_bytes()
+    assert cap == 8 << 20
+    big = 1
+    while tq.tq_score_ws_bytes(128, 4, big, 4, 1024) <= cap:
+        big *= 2
+    assert lib.tq_score_ip_noalloc(fake, 128, 4, fake, 1, fake, fake, fake, big, 4, 1024, 0, fake,
+                                   None) == tq.TQ_EUNSUPPORTED
+    assert "scratch" in tq.tq_last_error()
+    assert lib.tq_score_ip_noalloc(fake, 128, 4, fake, 1, fake, fake, fake, 0, 4, 1024, 0, fake, None) == tq.TQ_OK
+    assert lib.tq_score_ip_noalloc(fake, 128, 4, fake, 1, fake, fake, fake, -1, 4, 1024, 0, fake,
+                                   None) == tq.TQ_EINVAL
     # scoring: bad mode, workspace too small, unsupported G
     args = (fake, 128, 4, fake, 1, fake, fake, fake, 8, 4, 1024)
     assert lib.tq_score_ip(*args, 9, fake, fake, 1 << 30, None) == tq.TQ_EINVAL
