@@ -53,6 +53,30 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // Row of the 32-row tile held by MFMA output lane rho % 32 (the fragment row permutation).
 __device__ __forceinline__ int row_coord(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
 
+// Lane masks of one comparison, and the two VALU ops that consume one: the comparison's
+// 64-bit lane mask stays in an SGPR pair, from which v_addc shifts the bit into a plane word
+// (w = 2 w + bit) and v_cndmask selects between two values.  Written as separate asm
+// statements so that the compiler schedules the comparisons of several coordinates ahead
+// of their uses.
+typedef unsigned long long lanemask;
+
+__device__ __forceinline__ lanemask ge_abs(float u, float t) {   // |u| >= t
+  lanemask m;
+  asm("v_cmp_ge_f32_e64 %0, |%1|, %2" : "=s"(m) : "v"(u), "v"(t));
+  return m;
+}
+__device__ __forceinline__ uint32_t shift_in(uint32_t w, lanemask m) {   // 2 w + bit
+  uint32_t r;
+  lanemask carry;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry) : "v"(w), "s"(m));
+  return r;
+}
+__device__ __forceinline__ float select(float if0, float if1, lanemask m) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if0), "v"(if1), "s"(m));
+  return r;
+}
+
 // Bucketize one 32-row tile of u (this lane's 16 coordinates of it) against nu-scaled
 // positive thresholds T and centroids M: the index planes' half words into hb[0 .. BITS-2]
 // (the top index bit is the sign of u; hb[BITS-1] is left for the QJL signs), the residual as
@@ -61,31 +85,30 @@ template <int BITS>
 __device__ __forceinline__ void bucketize_tile(const f32x16& Um, const float* T, const float* M,
                                                uint32_t* hb, bf16x8* rh, bf16x8* rl, float& g2) {
   // Index bits from |u| against the positive thresholds (a binary search over the
-  // magnitude index k of the level), the level's sign from u: for u >= 0 the index is
-  // L/2 + k, for u < 0 it is L/2 - 1 - k, i.e. the bits of k complemented.  So the index
-  // planes are the k planes xor the sign plane, applied once per 16-coordinate word.
+  // magnitude index k of the level; a tie goes to the outer cell), the level's side from
+  // the sign of u: for u >= 0 the index is L/2 + k, for u < 0 it is L/2 - 1 - k, i.e. the
+  // bits of k complemented.  So the index planes are the k planes xor the sign plane,
+  // applied once per 16-coordinate word.
   uint32_t w0 = 0, w1 = 0, ws = 0;
   float rr[16];
 #pragma unroll
   for (int r = 15; r >= 0; --r) {
     const float u = Um[r];
-    const float a = fabsf(u);
     ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(u), 31);   // 1 = u < 0
     float cm;
     if constexpr (BITS == 2) {
       cm = M[0];
     } else if constexpr (BITS == 3) {
-      const bool k0 = a >= T[0];
-      cm = k0 ? M[1] : M[0];
-      w0 = (w0 << 1) | uint32_t(k0);
+      const lanemask k0 = ge_abs(u, T[0]);
+      w0 = shift_in(w0, k0);
+      cm = select(M[0], M[1], k0);
     } else {
-      const bool k1 = a >= T[1];
-      const bool k0 = a >= (k1 ? T[2] : T[0]);
-      const float mlo = k0 ? M[1] : M[0];
-      const float mhi = k0 ? M[3] : M[2];
-      cm = k1 ? mhi : mlo;
-      w0 = (w0 << 1) | uint32_t(k0);
-      w1 = (w1 << 1) | uint32_t(k1);
+      // k = c0 + c1 + c2 with c_i = [|u| >= T_i] (monotone in i): bit 1 of k is c1, bit 0
+      // is c0 ^ c1 ^ c2, formed on the scalar unit from the lane masks
+      const lanemask c0 = ge_abs(u, T[0]), c1 = ge_abs(u, T[1]), c2 = ge_abs(u, T[2]);
+      w1 = shift_in(w1, c1);
+      w0 = shift_in(w0, c0 ^ c1 ^ c2);
+      cm = select(select(select(M[0], M[1], c0), M[2], c1), M[3], c2);
     }
     const float c = __uint_as_float((__float_as_uint(cm) & 0x7fffffffu) | (__float_as_uint(u) & 0x80000000u));
     const float rv = u - c;
@@ -104,21 +127,28 @@ __device__ __forceinline__ void bucketize_tile(const f32x16& Um, const float* T,
     hb[1] = w1 ^ sgn;
     hb[2] = wsign;
   }
+  // hi = RNE(v); lo = RNE(v - hi), two coordinates at a time.  v - hi is exact in float32
+  // and comes from one dot2 each: hi pair . (-1, 0) + v.  The two selector pairs are held in
+  // SGPRs (opaque to the compiler), so that no inline constant stands for a bf16 pair.
+  uint32_t sel_lo = 0x0000bf80u, sel_hi = 0xbf800000u;   // bf16 pairs (-1, 0) and (0, -1)
+  asm("" : "+s"(sel_lo), "+s"(sel_hi));
+  const bf16x2 neg_lo = __builtin_bit_cast(bf16x2, sel_lo);
+  const bf16x2 neg_hi = __builtin_bit_cast(bf16x2, sel_hi);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
+    uint32_t hw[4], lw[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      // hi = RNE(v); lo = RNE(v - hi): converted two at a time
-      const f32x2 v2 = {rr[8 * hf + e], rr[8 * hf + e + 1]};
+      const float v0 = rr[8 * hf + e], v1 = rr[8 * hf + e + 1];
+      const f32x2 v2 = {v0, v1};
       const bf16x2 h2 = __builtin_convertvector(v2, bf16x2);
-      const uint32_t hb2 = __builtin_bit_cast(uint32_t, h2);
-      const f32x2 hf2 = {__uint_as_float(hb2 << 16), __uint_as_float(hb2 & 0xffff0000u)};
-      const bf16x2 l2 = __builtin_convertvector(v2 - hf2, bf16x2);
-      rh[hf][e] = h2[0];
-      rh[hf][e + 1] = h2[1];
-      rl[hf][e] = l2[0];
-      rl[hf][e + 1] = l2[1];
+      const f32x2 l2f = {__builtin_amdgcn_fdot2_f32_bf16(h2, neg_lo, v0, false),
+                         __builtin_amdgcn_fdot2_f32_bf16(h2, neg_hi, v1, false)};
+      hw[e / 2] = __builtin_bit_cast(uint32_t, h2);
+      lw[e / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(l2f, bf16x2));
     }
+    rh[hf] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    rl[hf] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
   }
 }
 
