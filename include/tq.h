@@ -363,9 +363,11 @@ size_t tq_topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k);
  *   q       [nq][d] float32 or bfloat16; codes [n][d/32][b]; nu, gamma [n]
  *   idx     out [nq][k] int32 key indices;  score out [nq][k] float32
  *   1 <= k <= 1024, k <= n; n < 2^31.
- * k <= 32 runs the fused scan (fp16 MFMA scores, per-query running lists); larger k score
- * batches of queries against every key on the general scoring path (float32) and select
- * each query's k best by radix select, so their workspace holds up to 256 MiB of scores.
+ * k <= 26 runs the fused scan: fp16 MFMA scores keep the best 16 (k <= 10) or 32 candidates
+ * per query, whose float32 estimates (the general scoring path's formula) then give the k
+ * returned, so scores and order are float32's; larger k score batches of queries against
+ * every key on the general scoring path (float32) and select each query's k best by radix
+ * select, so their workspace holds up to 256 MiB of scores.
  * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EWORKSPACE, TQ_EHIP.
  */
 int tq_topk(const void* params, int d, int b, const void* q, int q_dtype, int64_t nq,

@@ -59,13 +59,21 @@ constexpr int TARGET_WGS = 512;               // two workgroups per CU over the 
 #endif
 constexpr int PF = TQ_TOPK_PF;                // A fragments in flight ahead of the MFMAs
 
+// The fp16 scan keeps kk >= k + KMARGIN candidates per query; their float32 estimates decide
+// the final k.  Larger k take the float32 score-and-select path.
+constexpr int KMARGIN = 6;
+constexpr int KFUSED = KMAX - KMARGIN;        // largest k of the fused path
+constexpr int list_len(int k) { return k + KMARGIN <= 16 ? 16 : KMAX; }
+
 struct Plan {
   long nq, n, qt, nb, rb, nsplit;
-  size_t off_q, off_qn, off_cand, off_ovf, total;
+  int kk;
+  size_t off_q, off_qn, off_qx, off_cand, off_top, off_ovf, total;
 };
 
 Plan plan(int d, int64_t nq, int64_t n, int k) {
   Plan p;
+  p.kk = list_len(k);
   p.nq = nq;
   p.n = n;
   p.qt = (nq + QROWS - 1) / QROWS;
@@ -77,8 +85,10 @@ Plan plan(int d, int64_t nq, int64_t n, int k) {
   p.nsplit = (p.nb + p.rb - 1) / p.rb;
   p.off_q = 0;
   p.off_qn = align256(size_t(p.qt) * (d / 32) * STEP_HALVES * 2);
-  p.off_cand = p.off_qn + align256(size_t(p.qt) * QROWS * 4);
-  p.off_ovf = p.off_cand + align256(size_t(nq) * p.nsplit * k * 8);
+  p.off_qx = p.off_qn + align256(size_t(p.qt) * QROWS * 4);
+  p.off_cand = p.off_qx + align256(size_t(nq) * 2 * d * 4);
+  p.off_top = p.off_cand + align256(size_t(nq) * p.nsplit * p.kk * 8);
+  p.off_ovf = p.off_top + align256(size_t(nq) * p.kk * 8);
   p.total = p.off_ovf + align256(size_t(p.qt) * p.nsplit * QROWS * KEYS * 8);
   return p;
 }
@@ -108,7 +118,8 @@ __global__ __launch_bounds__(256) void topk_qprep_kernel(const unsigned char* __
                                                           const void* __restrict__ q, int q_f32,
                                                           long nq, long rows_pad,
                                                           _Float16* __restrict__ qf,
-                                                          float* __restrict__ qn) {
+                                                          float* __restrict__ qn,
+                                                          float* __restrict__ qx) {
   const int lane = threadIdx.x & 63, h = lane >> 5, nl = lane & 31;
   const long wid = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const long rho_tiles = 2 * d / 32;
@@ -155,6 +166,7 @@ __global__ __launch_bounds__(256) void topk_qprep_kernel(const unsigned char* __
     float v = 0.f;
     if (ar < nq && nr > 0.f) v = acc[r] / nr * (rho < d ? 1.0f : rsd);
     qf[qfrag_offset(ar, rho % d, rho >= d ? 1 : 0, d / 32)] = (_Float16)v;
+    if (ar < nq) qx[size_t(ar) * 2 * d + rho] = acc[r];   // [Pi q | S q], float32
   }
 }
 
@@ -639,6 +651,91 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(int* __restrict__ cand_
   }
 }
 
+// ------------------------------------------------------------------ float32 rescore
+// One workgroup per query: the float32 estimate of each of the kk candidates that the fp16
+// scan kept, l = nu_j (<Pi q, chat_j> + alpha gamma_j <S q, 2 z_j - 1>) from the float32
+// products Pi q, S q of the query prep (the formula of the general scoring path), then the k
+// best by decreasing estimate, equal estimates by increasing key index.
+template <int B, bool PROD>
+__global__ __launch_bounds__(256) void topk_rescore_kernel(const unsigned char* __restrict__ params, int d,
+                                                            const uint32_t* __restrict__ codes,
+                                                            const float* __restrict__ nu,
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ qx,
+                                                            const int* __restrict__ top_idx, int kk, int k,
+                                                            int32_t* __restrict__ out_idx,
+                                                            float* __restrict__ out_score) {
+  __shared__ float qs[2 * 4096];     // Pi q, S q of this query
+  __shared__ float cs[KMAX];
+  __shared__ int ci[KMAX];
+  const long a = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = d / 32;
+  for (int t = tid; t < 2 * d; t += 256) qs[t] = qx[size_t(a) * 2 * d + t];
+  const Header* hdr = reinterpret_cast<const Header*>(params);
+  constexpr int L = 1 << (B - 1);
+  float cen[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) cen[i] = hdr->cen[i];
+  const float alpha = hdr->alpha;
+  __syncthreads();
+  for (int c = wave; c < kk; c += 4) {
+    const int j = top_idx[size_t(a) * kk + c];   // uniform over the wave
+    float mse = 0.f, qjl = 0.f;
+    if (j >= 0) {
+      for (int g = lane; g < G; g += 64) {
+        const uint32_t* w = codes + (size_t(j) * G + g) * B;
+        uint32_t pl[B];
+#pragma unroll
+        for (int p = 0; p < B; ++p) pl[p] = w[p];
+#pragma unroll 8
+        for (int t = 0; t < 32; ++t) {
+          int idx = 0;
+#pragma unroll
+          for (int p = 0; p < B - 1; ++p) idx |= int((pl[p] >> t) & 1u) << p;
+          float cv = cen[0];
+#pragma unroll
+          for (int i = 1; i < L; ++i) cv = idx == i ? cen[i] : cv;
+          mse = fmaf(qs[32 * g + t], cv, mse);
+          if constexpr (PROD) {
+            const float sv = qs[d + 32 * g + t];
+            qjl += ((pl[B - 1] >> t) & 1u) ? sv : -sv;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mse += __shfl_xor(mse, o);
+      qjl += __shfl_xor(qjl, o);
+    }
+    if (lane == 0) {
+      ci[c] = j;
+      cs[c] = j >= 0 ? nu[j] * (PROD ? mse + alpha * gamma[j] * qjl : mse) : -FLT_MAX;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // insertion sort of the kk (<= 32) candidates, best first; empty slots (key -1) last
+    for (int e = 1; e < kk; ++e) {
+      const float sv = cs[e];
+      const int iv = ci[e];
+      int pos = e;
+      while (pos > 0 && better_c(sv, iv, cs[pos - 1], ci[pos - 1])) {
+        cs[pos] = cs[pos - 1];
+        ci[pos] = ci[pos - 1];
+        --pos;
+      }
+      cs[pos] = sv;
+      ci[pos] = iv;
+    }
+    for (int e = 0; e < k; ++e) {
+      out_idx[size_t(a) * k + e] = ci[e];
+      out_score[size_t(a) * k + e] = cs[e];
+    }
+  }
+}
+
 template <int B, int KM>
 hipError_t launch_scan_km(bool prod, dim3 grid, const unsigned char* params, const _Float16* qf,
                           const uint32_t* codes, const float* nu, const float* gamma, int G,
@@ -674,7 +771,7 @@ hipError_t launch_scan(bool prod, dim3 grid, const unsigned char* params, const 
 
 size_t topk_ws_bytes(int d, int b, int64_t nq, int64_t n, int k) {
   (void)b;
-  if (k > KMAX) return topk_large_ws_bytes(d, nq, n);
+  if (k > KFUSED) return topk_large_ws_bytes(d, nq, n);
   return plan(d, nq, n, k).total;
 }
 
@@ -682,7 +779,7 @@ hipError_t launch_topk(const void* params_v, int d, int b, const void* q, int q_
                        const uint32_t* codes, const float* nu, const float* gamma, int64_t n,
                        int k, int mode, int32_t* idx, float* score, void* ws, hipStream_t s) {
   if (d % 32 != 0) return hipErrorNotSupported;
-  if (k > KMAX)
+  if (k > KFUSED)
     return launch_topk_large(params_v, d, b, q, q_dtype, nq, codes, nu, gamma, n, k, mode, idx, score,
                              ws, s);
   const unsigned char* params = static_cast<const unsigned char*>(params_v);
@@ -691,8 +788,12 @@ hipError_t launch_topk(const void* params_v, int d, int b, const void* q, int q_
   unsigned char* w = static_cast<unsigned char*>(ws);
   _Float16* qf = reinterpret_cast<_Float16*>(w + p.off_q);
   float* qn = reinterpret_cast<float*>(w + p.off_qn);
+  float* qx = reinterpret_cast<float*>(w + p.off_qx);
+  const int kk = p.kk;
   int* cand_idx = reinterpret_cast<int*>(w + p.off_cand);
-  float* cand_score = reinterpret_cast<float*>(w + p.off_cand + size_t(nq) * p.nsplit * k * 4);
+  float* cand_score = reinterpret_cast<float*>(w + p.off_cand + size_t(nq) * p.nsplit * kk * 4);
+  int* top_idx = reinterpret_cast<int*>(w + p.off_top);
+  float* top_score = reinterpret_cast<float*>(w + p.off_top + size_t(nq) * kk * 4);
   float2* ovf = reinterpret_cast<float2*>(w + p.off_ovf);
   const int G = d / 32;
 
@@ -700,7 +801,7 @@ hipError_t launch_topk(const void* params_v, int d, int b, const void* q, int q_
   const long rows_pad = p.qt * QROWS;
   const long waves = (rows_pad / 32) * (2 * d / 32);
   hipLaunchKernelGGL(topk_qprep_kernel, dim3(unsigned((waves + 3) / 4)), dim3(256), 0, s, params,
-                     lay.off_pi, lay.off_s, d, q, q_dtype == 0 ? 1 : 0, long(nq), rows_pad, qf, qn);
+                     lay.off_pi, lay.off_s, d, q, q_dtype == 0 ? 1 : 0, long(nq), rows_pad, qf, qn, qx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -713,15 +814,31 @@ hipError_t launch_topk(const void* params_v, int d, int b, const void* q, int q_
   const bool prod = mode == 0;
   switch (b) {
     case 2: e = launch_scan<2>(prod, grid, params, qf, codes, nu, gamma, G, s_unscale, n, int(p.qt), p.rb,
-                               p.nsplit, k, nq, qn, cand_idx, cand_score, ovf, s); break;
+                               p.nsplit, kk, nq, qn, cand_idx, cand_score, ovf, s); break;
     case 3: e = launch_scan<3>(prod, grid, params, qf, codes, nu, gamma, G, s_unscale, n, int(p.qt), p.rb,
-                               p.nsplit, k, nq, qn, cand_idx, cand_score, ovf, s); break;
+                               p.nsplit, kk, nq, qn, cand_idx, cand_score, ovf, s); break;
     default: e = launch_scan<4>(prod, grid, params, qf, codes, nu, gamma, G, s_unscale, n, int(p.qt), p.rb,
-                                p.nsplit, k, nq, qn, cand_idx, cand_score, ovf, s); break;
+                                p.nsplit, kk, nq, qn, cand_idx, cand_score, ovf, s); break;
   }
   if (e != hipSuccess) return e;
+  // the kk best fp16 candidates over all key ranges, then their float32 estimates decide
   hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(nq)), dim3(256), 0, s, cand_idx, cand_score,
-                     long(p.nsplit) * k, k, idx, score);
+                     long(p.nsplit) * kk, kk, top_idx, top_score);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+#define TQ_RESCORE(BB)                                                                              \
+  if (prod)                                                                                         \
+    hipLaunchKernelGGL((topk_rescore_kernel<BB, true>), dim3(unsigned(nq)), dim3(256), 0, s, params, d, \
+                       codes, nu, gamma, qx, top_idx, kk, k, idx, score);                             \
+  else                                                                                              \
+    hipLaunchKernelGGL((topk_rescore_kernel<BB, false>), dim3(unsigned(nq)), dim3(256), 0, s, params, d, \
+                       codes, nu, gamma, qx, top_idx, kk, k, idx, score);
+  switch (b) {
+    case 2: TQ_RESCORE(2) break;
+    case 3: TQ_RESCORE(3) break;
+    default: TQ_RESCORE(4) break;
+  }
+#undef TQ_RESCORE
   return hipGetLastError();
 }
 

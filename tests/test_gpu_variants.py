@@ -83,7 +83,7 @@ def test_topk_variants(d, b, n, nq, k):
         scale = np.linalg.norm(q64, axis=1)[:, None] * np.maximum(nu_h[None, :], 1e-30)
         worst, swapped = U.check_topk(idx_g, sc_g, ref, scale)
         print(f"[topk variant d={d} b={b} k={k} {name}] max err {worst:.2e} swaps {swapped}", flush=True)
-        assert worst <= U.LOGIT_TOL
+        assert worst <= U.TOPK_SCORE_TOL
 
 
 def test_orthogonal_and_gaussian_scales_differ():
