@@ -168,17 +168,19 @@ def bench_ubench(args):
     print(json.dumps(result), flush=True)
 
 
-def time_per_launch(torch, fn, R: int, K: int) -> float:
-    """Average duration (ms) of one call fn(r): the R calls r = 0 .. R-1 are captured into one
-    HIP graph (so the graph launch overhead is paid once per R calls, not per call) and the
-    graph is replayed until about K calls ran, between two events on the current stream."""
+def time_per_launch(torch, fn, R: int, K: int, min_calls: int = 8) -> float:
+    """Average duration (ms) of one call fn(r): M = max(R, min_calls) calls fn(i % R) are
+    captured into one HIP graph (so the graph launch overhead is paid once per M calls, not
+    per call) and the graph is replayed until about K calls ran, between two events on the
+    current stream."""
+    M = max(R, min_calls)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for r in range(R):
-            fn(r)
+        for i in range(M):
+            fn(i % R)
     g.replay()
     torch.cuda.synchronize()
-    reps = max(1, K // R)
+    reps = max(1, K // M)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -186,7 +188,7 @@ def time_per_launch(torch, fn, R: int, K: int) -> float:
         g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * R)
+    return e0.elapsed_time(e1) / (reps * M)
 
 
 def source_hash(*names) -> str:
@@ -879,9 +881,16 @@ def bench_kv(args):
     def quantize(r):
         tq.tq_quantize(params, d, b, xs[r % Rx], codes[r], nus[r], gms[r])
 
-    def score(r):
+    def score(r):       # the whole scoring call: query prep + scan
         tq.tq_score_ip(params, d, b, q, codes[r], nus[r], gms[r], groups, G, T, tq.TQ_EST_PROD,
                        logits[r], ws)
+
+    def prepare():      # the query prep alone (depends on q only)
+        tq.tq_score_prepare(params, d, b, q, groups, G, ws)
+
+    def scan(r):        # the scan against the prepared query operands
+        tq.tq_score_ip_prepared(params, d, b, codes[r], nus[r], gms[r], groups, G, T, tq.TQ_EST_PROD,
+                                logits[r], ws)
 
     if args.calibrate_copy_mb:
         a = torch.empty(args.calibrate_copy_mb * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
@@ -908,21 +917,33 @@ def bench_kv(args):
             fn(r)
         return g
 
-    g_step = [capture(lambda r: (quantize(r), score(r)), r) for r in range(R)]
+    # Serial steps: the query prep (which depends on the queries only) on a second stream
+    # (default priority, forked and joined inside the graph) beside the quantize of batch r,
+    # then the scan of batch r.
+    side = torch.cuda.Stream()
+
+    def serial(r):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            prepare()
+        quantize(r)
+        torch.cuda.current_stream().wait_stream(side)
+        scan(r)
+
+    g_step = [capture(serial, r) for r in range(R)]
     for r in range(R):
         g_step[r].replay()
     torch.cuda.synchronize()
 
-    # Pipelined steps: replay r quantizes batch r while a second stream (default priority,
-    # forked and joined inside the graph) scores batch r - 1, which the previous replay
-    # quantized; each replay is one step's work (one quantize + one scoring call)
-    side = torch.cuda.Stream()
-
+    # Pipelined steps: replay r quantizes batch r while the second stream prepares the
+    # queries and scans batch r - 1, which the previous replay quantized; each replay is one
+    # step's work (one quantize + one query prep + one scan)
     def pipe(r):
         side.wait_stream(torch.cuda.current_stream())
         quantize(r)
         with torch.cuda.stream(side):
-            score((r - 1) % R)
+            prepare()
+            scan((r - 1) % R)
         torch.cuda.current_stream().wait_stream(side)
 
     g_pipe = [capture(pipe, r) for r in range(R)]
@@ -945,6 +966,7 @@ def bench_kv(args):
 
     q_ms = time_per_launch(torch, quantize, R, K)
     s_ms = time_per_launch(torch, score, R, K)
+    scan_ms = time_per_launch(torch, scan, R, K)
     ms_step = min(serial_ms, pipe_ms)
 
     # The pages' comparison (attention logits with 4-bit keys against 32-bit keys): the same
@@ -1028,12 +1050,16 @@ def bench_kv(args):
                     f"{score_in_bytes / 2**20:.0f} MiB cycled per launch",
         },
         "steps_timing": {"serial_ms": serial_ms, "pipelined_ms": pipe_ms,
-                         "note": "ms_per_step is the faster of: serial (quantize then score of each batch) and "
-                                 "pipelined (batch i's quantize overlaps batch i-1's scoring on a second stream)"},
+                         "note": "ms_per_step is the faster of: serial (the query prep on a second stream beside "
+                                 "the quantize of batch i, then the scan of batch i) and pipelined (batch i's "
+                                 "quantize beside the query prep and scan of batch i-1 on a second stream)"},
         "quantize": {"ms": q_ms, "vectors_per_s": n / (q_ms * 1e-3), "hbm_gbs": q_gbs,
                      "hbm_frac": q_gbs / HBM_PEAK_GBS},
         "score": {"ms": s_ms, "logits_per_s": n_logits / (s_ms * 1e-3), "keys_per_s": n / (s_ms * 1e-3),
                   "hbm_gbs": s_gbs},
+        "scan": {"ms": scan_ms, "hbm_gbs": s_bytes / (scan_ms * 1e-3) / 1e9,
+                 "hbm_frac": s_bytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "note": "tq_score_ip_prepared alone (the query operands prepared once)"},
         "context": "pages: up to 8x faster attention logits with 4-bit keys vs 32-bit keys on H100 "
                    "(no absolute numbers); not a target",
     }

@@ -235,6 +235,25 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
                 void* stream);
 
 /*
+ * tq_score_prepare, tq_score_ip_prepared — tq_score_ip in its two phases, so that the query
+ * preparation (which depends only on q) can be issued ahead of, or beside, other work:
+ *   tq_score_prepare      writes the query operands of q [groups][G][d] (Pi q and S q in the
+ *                         form the scoring kernels read) into ws;
+ *   tq_score_ip_prepared  scores the keys (codes, nu, gamma as for tq_score_ip) against the
+ *                         operands in ws and writes logits [groups][G][T].
+ * tq_score_ip(..., ws) is tq_score_prepare followed by tq_score_ip_prepared on the same
+ * stream, and gives the same logits.  The prepared ws must come from tq_score_prepare with
+ * the same params, d, b, groups and G, must not be written in between, and can serve any
+ * number of scoring calls (any T, mode, key caches).  ws_bytes >= tq_score_ws_bytes(d, b,
+ * groups, G, T) (which does not depend on T).  Arguments and errors as for tq_score_ip.
+ */
+int tq_score_prepare(const void* params, int d, int b, const void* q, int q_dtype, int64_t groups,
+                     int64_t G, void* ws, size_t ws_bytes, void* stream);
+int tq_score_ip_prepared(const void* params, int d, int b, const uint32_t* codes, const float* nu,
+                         const float* gamma, int64_t groups, int64_t G, int64_t T, int mode, float* logits,
+                         const void* ws, size_t ws_bytes, void* stream);
+
+/*
  * tq_score_ip_noalloc — tq_score_ip for callers that cannot allocate or hand in a
  * workspace (code under HIP graph capture, tight serving loops): the workspace is a fixed
  * device array of tq_score_noalloc_max_ws_bytes() bytes (8 MiB) inside the library, one per

@@ -13,7 +13,7 @@ from ._binding import (  # noqa: F401
     tq_params_bytes, tq_prepare, tq_prepare_orthogonal_qjl, tq_quantize_split, tq_score_split_ws_bytes,
     tq_score_ip_split, tq_quantize_mse_split, tq_attention_split_ws_bytes, tq_attention_split,
     tq_quantize, tq_quantize_with_rotation, tq_quantize_mse, tq_append_ws_bytes, tq_append, tq_dequantize, tq_score_ws_bytes, tq_score_ip,
-    tq_score_ip_noalloc, tq_score_noalloc_max_ws_bytes,
+    tq_score_ip_noalloc, tq_score_noalloc_max_ws_bytes, tq_score_prepare, tq_score_ip_prepared,
     tq_attention_ws_bytes, tq_attention, tq_topk_ws_bytes, tq_topk, tq_last_error,
 )
 
@@ -24,6 +24,6 @@ __all__ = [
     "tq_quantize_split", "tq_score_split_ws_bytes", "tq_score_ip_split", "tq_quantize_mse_split",
     "tq_attention_split_ws_bytes", "tq_attention_split", "tq_quantize", "tq_quantize_with_rotation", "tq_quantize_mse", "tq_append_ws_bytes", "tq_append",
     "tq_dequantize",
-    "tq_score_ws_bytes", "tq_score_ip", "tq_score_ip_noalloc", "tq_score_noalloc_max_ws_bytes", "tq_attention_ws_bytes", "tq_attention",
+    "tq_score_ws_bytes", "tq_score_ip", "tq_score_ip_noalloc", "tq_score_noalloc_max_ws_bytes", "tq_score_prepare", "tq_score_ip_prepared", "tq_attention_ws_bytes", "tq_attention",
     "tq_topk_ws_bytes", "tq_topk", "tq_last_error",
 ]

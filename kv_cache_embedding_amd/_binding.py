@@ -49,6 +49,8 @@ def load_library():
         "tq_score_ws_bytes": (SZ, [I, I, I64, I64, I64]),
         "tq_score_ip": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P, SZ, P]),
         "tq_score_ip_noalloc": (I, [P, I, I, P, I, P, P, P, I64, I64, I64, I, P, P]),
+        "tq_score_prepare": (I, [P, I, I, P, I, I64, I64, P, SZ, P]),
+        "tq_score_ip_prepared": (I, [P, I, I, P, P, P, I64, I64, I64, I, P, P, SZ, P]),
         "tq_score_noalloc_max_ws_bytes": (SZ, []),
         "tq_quantize_mse": (I, [P, I, I, P, I, I64, P, P, P]),
         "tq_quantize_split": (I, [P, P, I, I, I, I, P, I, I64, P, P, P, P, P, P, P]),
@@ -293,6 +295,32 @@ def tq_score_ip(params, d: int, b: int, q, codes, nu, gamma, groups: int, G: int
                                       _ptr(nu), _ptr(gamma), groups, G, T, int(mode), _ptr(logits),
                                       _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(stream, q.device)))
+
+
+def tq_score_prepare(params, d: int, b: int, q, groups: int, G: int, ws, stream=None):
+    """Query operands of q [groups][G][d] into ws, for tq_score_ip_prepared."""
+    for tname, t in (("q", q), ("ws", ws), ("params", params)):
+        _dev(t, tname)
+    if q.numel() < groups * G * d:
+        raise ValueError("q holds fewer than groups*G*d elements")
+    _check(load_library().tq_score_prepare(_ptr(params), d, b, _ptr(q), _dtype_code(q, "q"), groups, G,
+                                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream, q.device)))
+
+
+def tq_score_ip_prepared(params, d: int, b: int, codes, nu, gamma, groups: int, G: int, T: int,
+                         mode: int, logits, ws, stream=None):
+    """logits[groups][G][T] from the query operands tq_score_prepare left in ws."""
+    torch = _torch()
+    for tname, t in (("codes", codes), ("nu", nu), ("gamma", gamma), ("logits", logits), ("ws", ws),
+                     ("params", params)):
+        _dev(t, tname)
+    _need(codes, "codes", groups * T * (d // 32) * b, torch.int32)
+    _need(nu, "nu", groups * T, torch.float32)
+    _need(gamma, "gamma", groups * T, torch.float32)
+    _need(logits, "logits", groups * G * T, torch.float32)
+    _check(load_library().tq_score_ip_prepared(_ptr(params), d, b, _ptr(codes), _ptr(nu), _ptr(gamma), groups,
+                                               G, T, int(mode), _ptr(logits), _ptr(ws),
+                                               ws.numel() * ws.element_size(), _stream(stream, codes.device)))
 
 
 def tq_score_noalloc_max_ws_bytes() -> int:

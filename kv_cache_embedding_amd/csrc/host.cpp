@@ -565,12 +565,12 @@ static bool score_grid_fits(int d, int64_t groups, int64_t G, int64_t T) {
 static hipError_t launch_score_any(const void* params, int d, int b, const void* q, int q_dtype,
                                    const uint32_t* codes, const float* nu, const float* gamma,
                                    int64_t groups, int64_t G, int64_t T, int mode, float* logits,
-                                   void* ws, hipStream_t s) {
+                                   void* ws, hipStream_t s, int phases = tq::kScoreBoth) {
   return score_uses_d128(d, G)
              ? tq::launch_score_d128(params, b, q, q_dtype, codes, nu, gamma, groups, G, T, mode,
-                                     logits, ws, s)
+                                     logits, ws, s, phases)
              : tq::launch_score_generic(params, d, b, q, q_dtype, codes, nu, gamma, groups, G, T,
-                                        mode, logits, ws, s);
+                                        mode, logits, ws, s, 0, phases);
 }
 
 size_t tq_score_ws_bytes(int d, int b, int64_t groups, int64_t G, int64_t T) {
@@ -604,6 +604,47 @@ int tq_score_ip(const void* params, int d, int b, const void* q, int q_dtype,
   hipError_t e = launch_score_any(params, d, b, q, q_dtype, codes, nu, gamma, groups, G, T, mode,
                                   logits, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tq_score_ip launch");
+  return ok();
+}
+
+int tq_score_prepare(const void* params, int d, int b, const void* q, int q_dtype, int64_t groups,
+                     int64_t G, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad q_dtype %d", q_dtype);
+  if (groups < 0 || G < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0 || G == 0) return ok();
+  if (!params || !q || !ws) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(q, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B)");
+  if (!score_grid_fits(d, groups, G, 1))
+    return fail(TQ_EUNSUPPORTED, "tq_score_prepare: groups * G too large for one launch");
+  const size_t need = tq_score_ws_bytes(d, b, groups, G, 1);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipError_t e = launch_score_any(params, d, b, q, q_dtype, nullptr, nullptr, nullptr, groups, G, 1,
+                                  TQ_EST_PROD, nullptr, ws, static_cast<hipStream_t>(stream), tq::kScorePrep);
+  if (e != hipSuccess) return hip_fail(e, "tq_score_prepare launch");
+  return ok();
+}
+
+int tq_score_ip_prepared(const void* params, int d, int b, const uint32_t* codes, const float* nu,
+                         const float* gamma, int64_t groups, int64_t G, int64_t T, int mode, float* logits,
+                         const void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_shape(d, b)) return fail(TQ_EINVAL, "unsupported shape d=%d b=%d", d, b);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (groups < 0 || G < 0 || T < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0 || G == 0 || T == 0) return ok();
+  if (T >= (int64_t(1) << 31)) return fail(TQ_EINVAL, "T must be < 2^31");
+  if (!params || !codes || !nu || !gamma || !logits || !ws) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(codes, 16) || !aligned(logits, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; codes 16 B)");
+  if (!score_grid_fits(d, groups, G, T))
+    return fail(TQ_EUNSUPPORTED, "tq_score_ip_prepared: groups * G * T too large for one launch");
+  const size_t need = tq_score_ws_bytes(d, b, groups, G, T);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipError_t e = launch_score_any(params, d, b, nullptr, TQ_F32, codes, nu, gamma, groups, G, T, mode,
+                                  logits, const_cast<void*>(ws), static_cast<hipStream_t>(stream),
+                                  tq::kScoreScan);
+  if (e != hipSuccess) return hip_fail(e, "tq_score_ip_prepared launch");
   return ok();
 }
 

@@ -282,15 +282,18 @@ __global__ __launch_bounds__(256) void score_kernel(const uint32_t* __restrict__
 template <int BITS>
 hipError_t launch_b(const void* params, const void* q, int q_dtype, const uint32_t* codes,
                     const float* nu, const float* gamma, int64_t kv_groups, int64_t Gq, int64_t T,
-                    int mode, float* logits, void* ws, hipStream_t s) {
+                    int mode, float* logits, void* ws, hipStream_t s, int phases) {
   const Layout lay(D, BITS);
   const long qpg = long(Gq / G);
   const int64_t groups = kv_groups * qpg;       // virtual groups of 4 query heads
-  hipLaunchKernelGGL((score_qprep_kernel<BITS>), dim3(unsigned(2 * groups)), dim3(QP_THREADS), 0, s,
-                     static_cast<const unsigned char*>(params), lay.off_tr, q,
-                     q_dtype == 0 ? 1 : 0, static_cast<unsigned char*>(ws));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (phases & kScorePrep) {
+    hipLaunchKernelGGL((score_qprep_kernel<BITS>), dim3(unsigned(2 * groups)), dim3(QP_THREADS), 0, s,
+                       static_cast<const unsigned char*>(params), lay.off_tr, q,
+                       q_dtype == 0 ? 1 : 0, static_cast<unsigned char*>(ws));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(phases & kScoreScan)) return hipSuccess;
   const long tiles_per_group = (T + 15) / 16;
   const long total_tiles = long(groups) * tiles_per_group;
   long tpr = (total_tiles + long(cu_count_s()) * WAVES_PER_CU - 1) / (long(cu_count_s()) * WAVES_PER_CU);
@@ -315,11 +318,11 @@ hipError_t launch_b(const void* params, const void* q, int q_dtype, const uint32
 hipError_t launch_score_d128(const void* params, int b, const void* q, int q_dtype,
                              const uint32_t* codes, const float* nu, const float* gamma,
                              int64_t groups, int64_t Gq, int64_t T, int mode, float* logits,
-                             void* ws, hipStream_t s) {
+                             void* ws, hipStream_t s, int phases) {
   switch (b) {
-    case 2: return launch_b<2>(params, q, q_dtype, codes, nu, gamma, groups, Gq, T, mode, logits, ws, s);
-    case 3: return launch_b<3>(params, q, q_dtype, codes, nu, gamma, groups, Gq, T, mode, logits, ws, s);
-    case 4: return launch_b<4>(params, q, q_dtype, codes, nu, gamma, groups, Gq, T, mode, logits, ws, s);
+    case 2: return launch_b<2>(params, q, q_dtype, codes, nu, gamma, groups, Gq, T, mode, logits, ws, s, phases);
+    case 3: return launch_b<3>(params, q, q_dtype, codes, nu, gamma, groups, Gq, T, mode, logits, ws, s, phases);
+    case 4: return launch_b<4>(params, q, q_dtype, codes, nu, gamma, groups, Gq, T, mode, logits, ws, s, phases);
     default: return hipErrorInvalidValue;
   }
 }

@@ -283,7 +283,7 @@ hipError_t launch_b(const void* params0, int d0, const void* params1, int d1, co
                     int q_dtype, long qpitch, const uint32_t* codes0, const float* nu0,
                     const float* gamma0, const uint32_t* codes1, const float* nu1,
                     const float* gamma1, int64_t groups, int64_t G, int64_t T, int mode,
-                    float* logits, void* ws, hipStream_t s) {
+                    float* logits, void* ws, hipStream_t s, int phases) {
   const long rows = long(groups) * G;
   const size_t esz = q_dtype == 0 ? 4 : 2;
   const Layout lay0(d0, B0);
@@ -297,14 +297,17 @@ hipError_t launch_b(const void* params0, int d0, const void* params1, int d1, co
     float* qs1 = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
                                           align256(score_generic_ws_bytes(d0, groups, G)));
     g1 = QprepGroup{static_cast<const unsigned char*>(params1), lay1.off_pi, lay1.off_s, d1,
-                    static_cast<const unsigned char*>(q) + size_t(d0) * esz, qs1,
+                    q ? static_cast<const unsigned char*>(q) + size_t(d0) * esz : nullptr, qs1,
                     (rows + QR - 1) / QR * (2 * d1 / QO)};
     s1 = ScoreGroup{g1.params, qs1, codes1, nu1, gamma1, d1};
   }
-  hipLaunchKernelGGL(generic_qprep_kernel, dim3(unsigned(g0.blocks + g1.blocks)), dim3(256), 0, s, g0,
-                     g1, qpitch, q_dtype == 0 ? 1 : 0, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (phases & kScorePrep) {
+    hipLaunchKernelGGL(generic_qprep_kernel, dim3(unsigned(g0.blocks + g1.blocks)), dim3(256), 0, s, g0,
+                       g1, qpitch, q_dtype == 0 ? 1 : 0, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(phases & kScoreScan)) return hipSuccess;
   const ScoreGroup s0{g0.params, qs0, codes0, nu0, gamma0, d0};
   const long kblocks = (T + KEYS - 1) / KEYS;
   const long passes = (G + HB - 1) / HB;
@@ -323,12 +326,12 @@ hipError_t launch_b1(int b1, const void* params0, int d0, const void* params1, i
                      int q_dtype, long qpitch, const uint32_t* codes0, const float* nu0,
                      const float* gamma0, const uint32_t* codes1, const float* nu1,
                      const float* gamma1, int64_t groups, int64_t G, int64_t T, int mode,
-                     float* logits, void* ws, hipStream_t s) {
+                     float* logits, void* ws, hipStream_t s, int phases) {
   switch (b1) {
 #define TQ_GEN_CASE(B1)                                                                           \
   case B1:                                                                                        \
     return launch_b<B0, B1>(params0, d0, params1, d1, q, q_dtype, qpitch, codes0, nu0, gamma0,    \
-                            codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+                            codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s, phases);
     TQ_GEN_CASE(0)
     TQ_GEN_CASE(2)
     TQ_GEN_CASE(3)
@@ -342,14 +345,14 @@ hipError_t launch_groups(const void* params0, int d0, int b0, const void* params
                          const void* q, int q_dtype, long qpitch, const uint32_t* codes0,
                          const float* nu0, const float* gamma0, const uint32_t* codes1,
                          const float* nu1, const float* gamma1, int64_t groups, int64_t G,
-                         int64_t T, int mode, float* logits, void* ws, hipStream_t s) {
+                         int64_t T, int mode, float* logits, void* ws, hipStream_t s, int phases) {
   switch (b0) {
     case 2: return launch_b1<2>(b1, params0, d0, params1, d1, q, q_dtype, qpitch, codes0, nu0, gamma0,
-                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s, phases);
     case 3: return launch_b1<3>(b1, params0, d0, params1, d1, q, q_dtype, qpitch, codes0, nu0, gamma0,
-                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s, phases);
     case 4: return launch_b1<4>(b1, params0, d0, params1, d1, q, q_dtype, qpitch, codes0, nu0, gamma0,
-                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+                                codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s, phases);
     default: return hipErrorInvalidValue;
   }
 }
@@ -374,10 +377,10 @@ bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T) {
 hipError_t launch_score_generic(const void* params, int d, int b, const void* q, int q_dtype,
                                 const uint32_t* codes, const float* nu, const float* gamma,
                                 int64_t groups, int64_t G, int64_t T, int mode, float* logits,
-                                void* ws, hipStream_t s, int64_t qpitch) {
+                                void* ws, hipStream_t s, int64_t qpitch, int phases) {
   const long qp = qpitch > 0 ? long(qpitch) : long(d);
   return launch_groups(params, d, b, nullptr, 0, 0, q, q_dtype, qp, codes, nu, gamma, nullptr, nullptr,
-                       nullptr, groups, G, T, mode, logits, ws, s);
+                       nullptr, groups, G, T, mode, logits, ws, s, phases);
 }
 
 hipError_t launch_score_generic_split(const void* params0, const void* params1, int d0, int d1, int b0,
@@ -387,7 +390,7 @@ hipError_t launch_score_generic_split(const void* params0, const void* params1, 
                                       int64_t T, int mode, float* logits, void* ws, hipStream_t s) {
   if (b1 < 2) return hipErrorInvalidValue;
   return launch_groups(params0, d0, b0, params1, d1, b1, q, q_dtype, long(d0) + d1, codes0, nu0,
-                       gamma0, codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
+                       gamma0, codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s, kScoreBoth);
 }
 
 }  // namespace tq

@@ -91,17 +91,21 @@ hipError_t launch_quantize_d128_split(const void* params0, const void* params1, 
 hipError_t launch_quantize_gemm(const void* params, int d, int b, const void* x, int x_dtype,
                                 int64_t n, uint32_t* codes, float* nu, float* gamma,
                                 hipStream_t s, int64_t xpitch = 0, float* u = nullptr);
+// Scoring in two phases: kScorePrep writes the query operands into ws (needs q), kScoreScan
+// scores the keys from them (needs codes, nu, gamma, logits); tq_score_ip runs both.
+constexpr int kScorePrep = 1, kScoreScan = 2, kScoreBoth = 3;
 hipError_t launch_score_d128(const void* params, int b, const void* q, int q_dtype,
                              const uint32_t* codes, const float* nu, const float* gamma,
                              int64_t groups, int64_t G, int64_t T, int mode, float* logits,
-                             void* ws, hipStream_t s);
+                             void* ws, hipStream_t s, int phases = kScoreBoth);
 // Scoring for shapes the d = 128 kernel does not take (any d, any G): fp32 query prep into
 // ws ([groups * G][2][d] floats: Pi q, S q), then one lane per key.  qpitch:
 // elements between query rows (0: d).
 hipError_t launch_score_generic(const void* params, int d, int b, const void* q, int q_dtype,
                                 const uint32_t* codes, const float* nu, const float* gamma,
                                 int64_t groups, int64_t G, int64_t T, int mode, float* logits,
-                                void* ws, hipStream_t s, int64_t qpitch = 0);
+                                void* ws, hipStream_t s, int64_t qpitch = 0,
+                                int phases = kScoreBoth);
 size_t score_generic_ws_bytes(int d, int64_t groups, int64_t G);
 // Two channel groups (coordinates 0..d0-1 and d0..d0+d1-1 of the query rows, each group its
 // own parameter block and codes): one query prep launch for both (group 1's operands at

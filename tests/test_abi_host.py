@@ -144,6 +144,19 @@ def test_invalid_arguments_return_status_without_launch(lib):
     assert lib.tq_score_ip_noalloc(fake, 128, 4, fake, 1, fake, fake, fake, 0, 4, 1024, 0, fake, None) == tq.TQ_OK
     assert lib.tq_score_ip_noalloc(fake, 128, 4, fake, 1, fake, fake, fake, -1, 4, 1024, 0, fake,
                                    None) == tq.TQ_EINVAL
+    # scoring in two phases: query prep and the prepared scan validate like tq_score_ip
+    assert lib.tq_score_prepare(fake, 100, 4, fake, 1, 8, 4, fake, 1 << 20, None) == tq.TQ_EINVAL
+    assert lib.tq_score_prepare(fake, 128, 4, fake, 5, 8, 4, fake, 1 << 20, None) == tq.TQ_EINVAL
+    assert lib.tq_score_prepare(fake, 128, 4, None, 1, 8, 4, fake, 1 << 20, None) == tq.TQ_EINVAL
+    assert lib.tq_score_prepare(fake, 128, 4, fake, 1, 8, 4, fake, 16, None) == tq.TQ_EWORKSPACE
+    assert lib.tq_score_prepare(None, 128, 4, None, 1, 0, 4, None, 0, None) == tq.TQ_OK
+    assert lib.tq_score_ip_prepared(fake, 128, 4, fake, fake, fake, 8, 4, 1024, 7, fake, fake, 1 << 20,
+                                    None) == tq.TQ_EINVAL
+    assert lib.tq_score_ip_prepared(fake, 128, 4, fake, fake, fake, 8, 4, 1024, 0, fake, fake, 16,
+                                    None) == tq.TQ_EWORKSPACE
+    assert lib.tq_score_ip_prepared(fake, 128, 4, P(0x1004), fake, fake, 8, 4, 1024, 0, fake, fake, 1 << 20,
+                                    None) == tq.TQ_EINVAL
+    assert lib.tq_score_ip_prepared(None, 128, 4, None, None, None, 8, 4, 0, 0, None, None, 0, None) == tq.TQ_OK
     # scoring: bad mode, workspace too small, unsupported G
     args = (fake, 128, 4, fake, 1, fake, fake, fake, 8, 4, 1024)
     assert lib.tq_score_ip(*args, 9, fake, fake, 1 << 30, None) == tq.TQ_EINVAL

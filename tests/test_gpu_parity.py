@@ -258,3 +258,26 @@ def test_quantize_d256_bf16_and_zero_vectors():
     _report("d256 bf16 b=3", rep)
     U.assert_codes_ok(rep)
     assert nu.cpu().numpy()[[0, 999]].tolist() == [0.0, 0.0]
+
+
+@pytest.mark.parametrize("d,b,G", [(128, 3, 4), (128, 4, 8), (64, 3, 3), (128, 2, 5)])
+def test_score_prepared_matches_score_ip(d, b, G):
+    # the query operands prepared once serve two key caches of different lengths; each scan
+    # gives exactly tq_score_ip's logits (same kernels, same operands)
+    groups = 5
+    st = U.make_setup(d, b, cfg=81)
+    q = U.to_device(gen.f32_to_bf16_bits(gen.unit_sphere(groups * G, d, cfg=81, role=gen.ROLE_QUERY) * 2.0),
+                    True)
+    ws = torch.empty(max(tq.tq_score_ws_bytes(d, b, groups, G, 1), 256), dtype=torch.uint8, device=U.DEV)
+    tq.tq_score_prepare(st.params, d, b, q, groups, G, ws)
+    for i, T in enumerate((3000, 517)):
+        x = gen.f32_to_bf16_bits(gen.unit_sphere(groups * T, d, cfg=82 + i, role=gen.ROLE_DATA) * 3.0)
+        codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, True))
+        ref = U.gpu_score(st, q, codes, nu, gamma, groups, G, T, tq.TQ_EST_PROD)
+        for mode in (tq.TQ_EST_PROD, tq.TQ_EST_MSE):
+            if mode == tq.TQ_EST_MSE:
+                ref = U.gpu_score(st, q, codes, nu, gamma, groups, G, T, mode)
+            out = torch.full((groups * G * T,), float("nan"), dtype=torch.float32, device=U.DEV)
+            tq.tq_score_ip_prepared(st.params, d, b, codes, nu, gamma, groups, G, T, mode, out, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy().reshape(groups, G, T), ref), (T, mode)
