@@ -57,7 +57,9 @@ __device__ __forceinline__ int row_coord(int rho) { return 16 * ((rho >> 2) & 1)
 // 64-bit lane mask stays in an SGPR pair, from which v_addc shifts the bit into a plane word
 // (w = 2 w + bit) and v_cndmask selects between two values.  Written as separate asm
 // statements so that the compiler schedules the comparisons of several coordinates ahead
-// of their uses.
+// of their uses.  The compiler keeps the wait states between such asm statements, but not
+// those between an MFMA and an asm statement that reads its result: code that compares
+// MFMA results reads them first with ordinary instructions behind a scheduling barrier.
 typedef unsigned long long lanemask;
 
 __device__ __forceinline__ lanemask ge_abs(float u, float t) {   // |u| >= t
@@ -92,9 +94,13 @@ __device__ __forceinline__ void bucketize_tile(const f32x16& Um, const float* T,
   uint32_t w0 = 0, w1 = 0, ws = 0;
   float rr[16];
 #pragma unroll
+  for (int r = 15; r >= 0; --r) ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(Um[r]), 31);   // 1 = u < 0
+  // Um holds MFMA results: the reads above carry the compiler's wait states after the MFMA,
+  // and the barrier keeps the asm comparisons below after them
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
   for (int r = 15; r >= 0; --r) {
     const float u = Um[r];
-    ws = __builtin_amdgcn_alignbit(ws, __float_as_uint(u), 31);   // 1 = u < 0
     float cm;
     if constexpr (BITS == 2) {
       cm = M[0];
