@@ -226,6 +226,17 @@ size_t tq_score_ws_bytes(int d, int b, int64_t groups, int64_t G, int64_t T);
  *            its contents are scratch (overwritten by this call)
  * d = 128 with G a multiple of 4 runs the tuned kernel (int8 MFMA over the key bit planes);
  * every other shape runs a general path (float32 query prep, one lane per key).
+ * Precision: the general path sums in float32.  The tuned kernel rounds each query value it
+ * uses (the codebook's Walsh coefficients e_w times Pi q, and S q) to an integer of at most
+ * 16000 in magnitude at the row's own scale (16000 / max|row|), held as two int8 digits
+ * 128 hi + lo; the sums over key bits are exact integers and the constant terms are float32
+ * sums of the unrounded values.  A logit therefore differs from the float64 estimate of the
+ * same codes by at most
+ *   nu_k (2 * 96 ne e_max max_t|(Pi q)_t| + gamma_k * 2 * 96 alpha max_t|(S q)_t|) / 16000
+ * (ne Walsh terms: 1, 2, 4 for b = 2, 3, 4; half the coordinates round to a half digit, the
+ * other half, stored halved, to a whole one) plus float32 rounding, about 1e-3 |q| nu_k at
+ * b = 4 for a typical query if every rounding fell the same way, 2e-5 |q| nu_k as a root mean
+ * square: far below the estimator's own error.
  * Errors: TQ_EINVAL, TQ_EUNSUPPORTED (groups * G * T beyond one launch of the general path),
  *         TQ_EWORKSPACE, TQ_EHIP.
  */

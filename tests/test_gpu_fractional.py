@@ -121,7 +121,7 @@ def test_score_split_parity(d, d0, b0, b1, G, T, q_bf16):
             worst = max(worst, float(np.max(np.abs(lg[g] - ref) / np.maximum(scale[g], 1e-30))))
         print(f"[split score d={d} ({d0}@{b0} + {d - d0}@{b1}) G={G} T={T} {name}] "
               f"max |dl|/sum|q_g|nu_g = {worst:.2e}", flush=True)
-        assert worst <= U.LOGIT_TOL
+        assert worst <= U.FP32_LOGIT_TOL   # the split score runs the general float32 path
         # the sum of the single-group calls on contiguous query copies
         ref_sum = np.zeros((groups, G, T))
         for st, (c, nu, ga), off, w in zip(sts, parts, (0, d0), (d0, d - d0)):
