@@ -124,6 +124,16 @@ int main() {
   EXPECT(tq_score_ip(f, 128, 4, f, TQ_BF16, fc, ff, ff, -1, 4, 1024, 0, ff, f, 16, nullptr) == TQ_EINVAL);
   EXPECT(tq_score_ip_noalloc(f, 128, 4, f, TQ_BF16, fc, ff, ff, 1 << 20, 4, 1024, 0, ff, nullptr) ==
          TQ_EUNSUPPORTED);
+  EXPECT(tq_score_noalloc_max_ws_bytes() == (size_t(8) << 20));
+  EXPECT(tq_score_prepare(f, 128, 4, f, 7, 8, 4, f, 1 << 30, nullptr) == TQ_EINVAL);
+  EXPECT(tq_score_prepare(f, 128, 4, f, TQ_BF16, 8, 4, f, 16, nullptr) == TQ_EWORKSPACE);
+  EXPECT(tq_score_prepare(f, 128, 4, f, TQ_BF16, 0, 4, nullptr, 0, nullptr) == TQ_OK);
+  EXPECT(tq_score_ip_prepared(f, 128, 4, fc, ff, ff, 8, 4, 1024, 9, ff, f, 1 << 30, nullptr) == TQ_EINVAL);
+  EXPECT(tq_score_ip_prepared(f, 128, 4, fc, ff, ff, 8, 4, 1024, 0, ff, f, 16, nullptr) == TQ_EWORKSPACE);
+  EXPECT(tq_score_ip_prepared(f, 128, 4, static_cast<uint32_t*>(odd), ff, ff, 8, 4, 1024, 0, ff, f, 1 << 30,
+                              nullptr) == TQ_EINVAL);
+  EXPECT(tq_score_split_ws_bytes(128, 64, 3, 3, 8, 4, 100) > 0);
+  EXPECT(tq_attention_split_ws_bytes(128, 64, 3, 3, 8, 4, 100) > 0);
   EXPECT(tq_topk(f, 128, 4, f, TQ_F32, 10, fc, ff, ff, 100, 0, 0, static_cast<int32_t*>(f), ff, f, 1 << 30,
                  nullptr) == TQ_EINVAL);
   EXPECT(tq_topk(f, 128, 4, f, TQ_F32, 10, fc, ff, ff, 5, 10, 0, static_cast<int32_t*>(f), ff, f, 1 << 30,
