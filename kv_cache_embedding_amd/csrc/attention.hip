@@ -6,16 +6,12 @@
 // linear, so the weighted sum runs in the values' rotated coordinates and one inverse
 // rotation per head finishes it:  o = Pi_v^T a,  a = sum_t p_t nu_t chat_t / sum_t p_t.
 //
-// attn_block_kernel: one workgroup per (group, pass of AH heads, block of KB keys).  Lanes
-//   first hold one key each: scaled logits, the block maximum per head, the weights
-//   p = exp(l - max) and p nu, which go to LDS as one float4 per key.  Then each wave walks
-//   its 64 keys with the lanes over the coordinates (64 per step): the wave's keys are first
-//   staged in LDS, lane j turning key j's plane words of each 32-coordinate group into one
-//   16-byte slot of 4-bit indices (coordinate 8 q + i in bits 4 i .. of dword q), so that
-//   per key a lane reads the weights (a broadcast) and its coordinate's dword, extracts the
-//   index with one bit-field op, looks the centroid up in LDS and accumulates it times the
-//   key's weight for every head.  Out: per block and head the maximum, the sum of p and the
-//   weighted sum of centroids.
+// attn_block_kernel: one workgroup per (group, pass of AH heads, block of KB keys), 64 keys per
+//   wave.  Lanes first hold one key each: scaled logits, the block maximum per head, the
+//   weights p = exp(l - max) and p nu.  The weighted sum of the keys' centroids then runs on
+//   the integer MFMA through the Walsh form of the codebook (value_block): the weights as
+//   exact integer digits, the value codes' bit planes as 0/1 bytes.  Out: per block and head
+//   the maximum, the sum of p and the weighted sum of centroids.
 // attn_combine_kernel: one workgroup per (group, head): merges the blocks (log-sum-exp) and
 //   applies Pi_v^T; threads split both sums into slices of independent float4 loads (rows
 //   of Pi_v are contiguous, so a slice reads coalesced columns), the first loads of both
@@ -44,14 +40,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Bits 0..7 of x to bits 0, 4, .., 28.
-__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
-  x &= 0xffu;
-  x = (x | (x << 12)) & 0x000f000fu;
-  x = (x | (x << 6)) & 0x03030303u;
-  return (x | (x << 3)) & 0x11111111u;
-}
-
 // The value operands of one channel group for the block kernel.
 struct BlockGroup {
   const unsigned char* params_v;
@@ -64,47 +52,118 @@ struct BlockGroup {
 };
 
 // One workgroup's block (256 keys) of one value channel group.  BV: index planes of a value
-// (1..3); NC: 64-coordinate steps per chunk (NC divides d / 64).  The LDS arrays come from
-// the kernel, sized for the largest codebook.
+// (1..3); NC: 64-coordinate steps per chunk (NC divides d / 64).
+// With the Walsh form of the odd-symmetric codebook, chat_tc = sum_P e_P (2 B_P,tc - 1) over
+// the index bit planes B_P (three index bits add the plane b0 ^ b1 ^ b2), so for head h and
+// coordinate c
+//   sum_t w_ht chat_tc = sum_P e_P (2 sum_t w_ht B_P,tc - sum_t w_ht).
+// Per wave and head the weights become integers v = round(w (2^21 - 1) / max_t w), three
+// 7-bit digits each, and v_mfma_i32_16x16x64_i8 sums them exactly over the keys whose plane bit
+// is set: A = 16 rows (head h: rows 4 h + {digit 0, 1, 2, zero}) over the wave's 64 keys, B =
+// those keys' bits of 16 coordinates as bytes 0/1.  In the 16x16 accumulator layout lane l
+// ends with head l / 16 and coordinate l % 16 of the tile, its three digit sums in registers
+// 0..2.  The value codes are staged in LDS byte-transposed, [plane][32-coordinate group]
+// [byte of the word][key], so the bit of one coordinate for 16 keys is one 16-byte read, a
+// shift and a mask.  Lanes hold their keys in the same order in A and B, so the MFMA's own
+// order within K does not matter.  The first chunk's code words are loaded before anything
+// waits, so their latency overlaps the logits and the softmax prologue.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Wave-wide reductions without LDS: within each 16-lane row by DPP rotations (every lane of the
+// row ends with the row's result), then across the four rows from lanes 0, 16, 32, 48 (wave
+// uniform results).
+template <int K>
+__device__ __forceinline__ int dpp_ror(int v) {   // row_ror:K
+  return __builtin_amdgcn_update_dpp(v, v, 0x120 + K, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, __int_as_float(dpp_ror<8>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_ror<4>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_ror<2>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_ror<1>(__float_as_int(v))));
+  const int i = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(i, 0)), __int_as_float(__builtin_amdgcn_readlane(i, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(i, 32)), __int_as_float(__builtin_amdgcn_readlane(i, 48))));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __int_as_float(dpp_ror<8>(__float_as_int(v)));
+  v += __int_as_float(dpp_ror<4>(__float_as_int(v)));
+  v += __int_as_float(dpp_ror<2>(__float_as_int(v)));
+  v += __int_as_float(dpp_ror<1>(__float_as_int(v)));
+  const int i = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(i, 0)) + __int_as_float(__builtin_amdgcn_readlane(i, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(i, 32)) + __int_as_float(__builtin_amdgcn_readlane(i, 48)));
+}
+__device__ __forceinline__ int wave_sum_int(int v) {
+  v += dpp_ror<8>(v);
+  v += dpp_ror<4>(v);
+  v += dpp_ror<2>(v);
+  v += dpp_ror<1>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
 template <int BV, int NC>
 __device__ __forceinline__ void value_block(const BlockGroup& bg, const float* __restrict__ logits,
                                             long G, long T, long nkb, long passes, float scale,
-                                            long blk, float* cen, float (*red)[AH],
-                                            float (*accs)[AH][64 * NC], uint4 (*kw)[64][2 * NC],
-                                            float4 (*wsh)[64]) {
-  static_assert(BV >= 1 && BV <= 3, "a value's index fits one 4-bit field");
-  constexpr int L = 1 << BV;
+                                            long blk, float (*red)[AH], float (*accs)[AH][64 * NC],
+                                            unsigned char* kb_all, unsigned char* ab_all) {
+  static_assert(BV >= 1 && BV <= 3, "one to three index planes");
+  constexpr int NE = BV == 3 ? 4 : BV;      // Walsh planes: b0 [, b1 [, b2, b0^b1^b2]]
+  constexpr int NG = 2 * NC;                // 32-coordinate groups per chunk
+  constexpr float kVMax = 2097151.f;        // 2^21 - 1: three 7-bit digits
   const unsigned char* __restrict__ params_v = bg.params_v;
   const uint32_t* __restrict__ vcodes = bg.vcodes;
   const float* __restrict__ vnu = bg.vnu;
   const int d = bg.d;
-  float* __restrict__ part_m = bg.part_m;
-  float* __restrict__ part_s = bg.part_s;
-  float* __restrict__ part_acc = bg.part_acc;
   const Header* hdr = reinterpret_cast<const Header*>(params_v);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar code loads
-  if (tid < L) cen[tid] = hdr->cen[tid];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  unsigned char* kb = kb_all + wave * (NE * NG * 4 * 64);   // [plane][group][byte][key]
+  unsigned char* ab = ab_all + wave * (16 * 64);            // [row][key] weight digits
 
-  const long kb = blk % nkb;
+  const long kblk = blk % nkb;
   const long gp = blk / nkb;
   const long g = gp / passes;
   const long h0 = (gp % passes) * AH;
-  const long nh = G - h0 < AH ? G - h0 : AH;   // heads of this pass
-  const long tw0 = kb * KB + wave * 64;        // first key of this wave
-  const long t = tw0 + lane;                   // the lane's key in the prologue
+  const long nh = G - h0 < AH ? G - h0 : AH;
+  const long tw0 = kblk * KB + wave * 64;
+  const long t = tw0 + lane;
   const bool valid = t < T;
+  const int W = d / 32;
 
-  // prologue: scaled logits of the lane's key, block maximum per head
+  // the lane's key's plane words of one chunk (zeros past the end)
+  uint32_t pw[NG][BV];
+  auto load_words = [&](int c0) {
+    if (valid) {
+      const uint32_t* kc = vcodes + (size_t(g * T + t) * W + c0 / 32) * BV;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+        for (int p = 0; p < BV; ++p) pw[gg][p] = kc[gg * BV + p];
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+        for (int p = 0; p < BV; ++p) pw[gg][p] = 0u;
+    }
+  };
+  load_words(0);
+
+  float e[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) e[i] = hdr->e[i];
+
+  // prologue: scaled logits of the lane's key, block maximum per head, weights p nu, sums of p
   float l[AH];
 #pragma unroll
   for (int hh = 0; hh < AH; ++hh) {
     const long h = h0 + (hh < nh ? hh : nh - 1);
     l[hh] = valid ? scale * logits[size_t(g * G + h) * T + t] : -INFINITY;
-    const float m = wave_max(l[hh]);
+    const float m = wave_max_dpp(l[hh]);
     if (lane == 0) red[wave][hh] = m;
   }
-  __syncthreads();   // also publishes cen
+  __syncthreads();
   float M[AH];
 #pragma unroll
   for (int hh = 0; hh < AH; ++hh)
@@ -116,78 +175,98 @@ __device__ __forceinline__ void value_block(const BlockGroup& bg, const float* _
   for (int hh = 0; hh < AH; ++hh) {
     const float p = valid ? __expf(l[hh] - M[hh]) : 0.f;
     w[hh] = p * nu_t;
-    const float sp = wave_sum(p);
+    const float sp = wave_sum_dpp(p);
     if (lane == 0) red[wave][hh] = sp;
   }
-  wsh[wave][lane] = make_float4(w[0], w[1], w[2], w[3]);
   __syncthreads();
   const long prow = g * G + h0;                 // partial rows of this pass: prow + hh
 #pragma unroll
   for (int hh = 0; hh < AH; ++hh) {
     if (tid == hh && hh < nh) {
-      part_m[(prow + hh) * nkb + kb] = M[hh];
-      part_s[(prow + hh) * nkb + kb] = (red[0][hh] + red[1][hh]) + (red[2][hh] + red[3][hh]);
+      bg.part_m[(prow + hh) * nkb + kblk] = M[hh];
+      bg.part_s[(prow + hh) * nkb + kblk] = (red[0][hh] + red[1][hh]) + (red[2][hh] + red[3][hh]);
     }
   }
 
-  // weighted sum of the centroids of the wave's keys, 64 NC coordinates per chunk
-  const int W = d / 32;
-  const long nk = T - tw0 < 64 ? (T - tw0 > 0 ? T - tw0 : 0) : 64;
+  // integer weights of the wave's keys and the A operand (rows 4 hh + j: digit j of head hh)
+  float inv_l = 0.f;      // this lane's head (lane / 16): 1 / scale
+  int tsum_l = 0;         // this lane's head: sum of its integer weights over the wave
+#pragma unroll
+  for (int hh = 0; hh < AH; ++hh) {
+    const float wm = wave_max_dpp(w[hh]);
+    const float sc = wm > 0.f ? kVMax / wm : 0.f;
+    int v = int(rintf(w[hh] * sc));
+    v = v < 2097151 ? v : 2097151;
+    const int ts = wave_sum_int(v);
+    if ((lane >> 4) == hh) {
+      inv_l = wm * (1.f / kVMax);
+      tsum_l = ts;
+    }
+    ab[(4 * hh + 0) * 64 + lane] = (unsigned char)(v & 127);
+    ab[(4 * hh + 1) * 64 + lane] = (unsigned char)((v >> 7) & 127);
+    ab[(4 * hh + 2) * 64 + lane] = (unsigned char)(v >> 14);
+    ab[(4 * hh + 3) * 64 + lane] = 0;
+  }
+  // the staging writes and the reads below use other types: order them explicitly
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const v4i A = *reinterpret_cast<const v4i*>(ab + (lane & 15) * 64 + 16 * (lane >> 4));
+
+  const int hl = lane >> 4;                     // this lane's head in the MFMA output
+  const int ksl = 16 * hl;                      // first of this lane's 16 keys in A and B
+  const uint32_t sh = lane & 7;                 // bit of the byte for coordinate lane % 16
   for (int c0 = 0; c0 < d; c0 += 64 * NC) {
-    // the chunk's plane words of the wave's keys: lane j loads those of key j (one pass of
-    // contiguous loads instead of a dependent scalar load per key)
-    if (lane < nk) {
-      const uint32_t* kc = vcodes + (size_t(g * T + tw0 + lane) * W + c0 / 32) * BV;
+    if (c0 > 0) load_words(c0);
+    // stage the chunk's words byte-transposed (the xor plane formed here)
 #pragma unroll
-      for (int e = 0; e < 2 * NC; ++e) {
-        const uint32_t p0 = kc[e * BV], p1 = BV > 1 ? kc[e * BV + 1] : 0u, p2 = BV > 2 ? kc[e * BV + 2] : 0u;
-        uint32_t nib[4];
+    for (int gg = 0; gg < NG; ++gg) {
+      uint32_t word[NE];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          nib[q] = spread_nibbles(p0 >> (8 * q)) | (spread_nibbles(p1 >> (8 * q)) << 1) |
-                   (spread_nibbles(p2 >> (8 * q)) << 2);
-        kw[wave][lane][e] = make_uint4(nib[0], nib[1], nib[2], nib[3]);
+      for (int p = 0; p < BV; ++p) word[p] = pw[gg][p];
+      if constexpr (BV == 3) word[3] = pw[gg][0] ^ pw[gg][1] ^ pw[gg][2];
+#pragma unroll
+      for (int pp = 0; pp < NE; ++pp)
+#pragma unroll
+        for (int by = 0; by < 4; ++by) kb[((pp * NG + gg) * 4 + by) * 64 + lane] = (unsigned char)(word[pp] >> (8 * by));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    float acc[2 * NG];
+#pragma unroll
+    for (int i = 0; i < 2 * NG; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NE; ++pp) {
+      // the plane's MFMAs first, then their results (the MFMA latency overlaps the gathers)
+      v4i r[2 * NG];
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          // coordinate 32 gg + 16 half + lane % 16: byte 2 half + (lane % 16) / 8 of the word
+          const int by = 2 * half + ((lane & 15) >> 3);
+          const uint4 q = *reinterpret_cast<const uint4*>(kb + ((pp * NG + gg) * 4 + by) * 64 + ksl);
+          const v4i B = {int((q.x >> sh) & 0x01010101u), int((q.y >> sh) & 0x01010101u),
+                         int((q.z >> sh) & 0x01010101u), int((q.w >> sh) & 0x01010101u)};
+          r[2 * gg + half] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NG; ++i) {
+        const int S = r[i][2] * 16384 + r[i][1] * 128 + r[i][0];
+        acc[i] = fmaf(e[pp], float(2 * S - tsum_l), acc[i]);
       }
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    float acc[AH][NC];
 #pragma unroll
-    for (int hh = 0; hh < AH; ++hh)
-#pragma unroll
-      for (int i = 0; i < NC; ++i) acc[hh][i] = 0.f;
-    // this lane's coordinate within a 32-coordinate group: dword q of the slot, field i
-    const int q = (lane & 31) >> 3, fsh = 4 * (lane & 7);
-    const uint32_t* kwd = reinterpret_cast<const uint32_t*>(&kw[wave][0][0]) + q;
-#pragma unroll 4
-    for (int j = 0; j < nk; ++j) {
-      const float4 wj = wsh[wave][j];
-#pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const uint32_t dw = kwd[(j * 2 * NC + 2 * i + (lane >> 5)) * 4];
-        const float c = cen[(dw >> fsh) & 0xfu];
-        acc[0][i] = fmaf(wj.x, c, acc[0][i]);
-        acc[1][i] = fmaf(wj.y, c, acc[1][i]);
-        acc[2][i] = fmaf(wj.z, c, acc[2][i]);
-        acc[3][i] = fmaf(wj.w, c, acc[3][i]);
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < AH; ++hh)
-#pragma unroll
-      for (int i = 0; i < NC; ++i) accs[wave][hh][64 * i + lane] = acc[hh][i];
+    for (int i = 0; i < 2 * NG; ++i) accs[wave][hl][16 * i + (lane & 15)] = acc[i] * inv_l;
     __syncthreads();
-    for (int e = tid; e < AH * 64 * NC; e += 256) {
-      const int hh = e / (64 * NC), c = e % (64 * NC);
+    for (int ei = tid; ei < AH * 64 * NC; ei += 256) {
+      const int hh = ei / (64 * NC), c = ei % (64 * NC);
       if (hh < nh)
-        part_acc[((prow + hh) * nkb + kb) * d + c0 + c] =
+        bg.part_acc[((prow + hh) * nkb + kblk) * d + c0 + c] =
             (accs[0][hh][c] + accs[1][hh][c]) + (accs[2][hh][c] + accs[3][hh][c]);
     }
     __syncthreads();
   }
 }
-
 
 // grid: the blocks of value channel group 0, then those of group 1 (BV1 > 0: a fractional
 // rate's second value group with the same chunk shape).
@@ -195,19 +274,20 @@ template <int BV0, int BV1, int NC>
 __global__ __launch_bounds__(256) void attn_block_kernel(BlockGroup b0, BlockGroup b1, long blocks0,
                                                          const float* __restrict__ logits, long G,
                                                          long T, long nkb, long passes, float scale) {
-  __shared__ float cen[8];
   __shared__ float red[4][AH];
   __shared__ float accs[4][AH][64 * NC];
-  __shared__ uint4 kw[4][64][2 * NC];   // a chunk's 4-bit indices: [wave][key][32-coordinate group]
-  __shared__ float4 wsh[4][64];         // p nu of the wave's keys for the 4 heads
+  __shared__ uint4 kbytes[4 * 4 * 2 * NC * 4 * 64 / 16];   // [wave][plane][group][byte][key]
+  __shared__ uint4 abytes[4 * 16 * 64 / 16];               // [wave][row][key] weight digits
+  unsigned char* kb = reinterpret_cast<unsigned char*>(kbytes);
+  unsigned char* ab = reinterpret_cast<unsigned char*>(abytes);
   const long blk = blockIdx.x;
   if constexpr (BV1 > 0) {
     if (blk >= blocks0) {
-      value_block<BV1, NC>(b1, logits, G, T, nkb, passes, scale, blk - blocks0, cen, red, accs, kw, wsh);
+      value_block<BV1, NC>(b1, logits, G, T, nkb, passes, scale, blk - blocks0, red, accs, kb, ab);
       return;
     }
   }
-  value_block<BV0, NC>(b0, logits, G, T, nkb, passes, scale, blk, cen, red, accs, kw, wsh);
+  value_block<BV0, NC>(b0, logits, G, T, nkb, passes, scale, blk, red, accs, kb, ab);
 }
 
 // The block partials and output columns of one value channel group.
