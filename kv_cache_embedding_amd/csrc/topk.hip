@@ -200,6 +200,12 @@ __device__ __forceinline__ uint32_t mse_pair(uint32_t ev, uint32_t od, uint32_t 
   return sign_pair(nsg, p, mag);
 }
 
+// v from lane ctrl(lane) of its row (a DPP move; every source lane is inside the row here)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ uint32_t f16_bits(float v) {
   return uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v));
 }
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void topk_scan_kernel(
   __shared__ __attribute__((aligned(16))) _Float16 Abuf0[STEP_HALVES];
   __shared__ __attribute__((aligned(16))) _Float16 Abuf1[STEP_HALVES];
   __shared__ __attribute__((aligned(16))) float theta[QROWS];   // score of each query's k-th entry
-  __shared__ __attribute__((aligned(16))) int thidx[QROWS];     // its key (-inf / INT_MAX until k held)
+  __shared__ __attribute__((aligned(16))) int thidx[QROWS];     // its key (INT_MAX until k held)
   __shared__ int cnt[QROWS];
   constexpr int CAND = cand_slots(KM);
   constexpr int CSTRIDE = CAND + 1;                             // padded: conflict-free both ways
@@ -334,12 +340,14 @@ __global__ __launch_bounds__(256, 1) void topk_scan_kernel(
     long jk[KT];
     bool ok[KT];
     uint32_t agp[KT];
+    float nuv[KT];   // loaded here, used by the selection after the block's MFMAs
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       jk[kt] = blk * KEYS + wave * 32 * KT + 32 * kt + nl;
       ok[kt] = jk[kt] < n;
       const uint32_t hv = (PROD && ok[kt]) ? f16_bits(ag_unit * gamma[jk[kt]]) : 0u;
       agp[kt] = hv | (hv << 16);
+      nuv[kt] = ok[kt] ? nu[jk[kt]] : 0.f;
     }
     f32x16 acc[RT][KT];
 #pragma unroll
@@ -457,22 +465,21 @@ __global__ __launch_bounds__(256, 1) void topk_scan_kernel(
     // ---- selection: accumulator register r of tile (i, kt) in lane l is query row
     //      32 i + 8 (r / 4) + 4 h + r % 4 and key jk[kt]; score = nu * acc (the |q| factor is
     //      applied on output).  Pending bit 16 (kt & 1) + r of word NW i + kt / 2.
-    float nuv[KT];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      nuv[kt] = ok[kt] ? nu[jk[kt]] : 0.f;
-      nus[wave * 32 * KT + 32 * kt + nl] = nuv[kt];
-    }
+    for (int kt = 0; kt < KT; ++kt) nus[wave * 32 * KT + 32 * kt + nl] = nuv[kt];
     // The lane's row offset 4 h, read back from LDS here (after the last step's barrier):
     // as a value of this block it keeps the compiler from precomputing the 128 row addresses
     // of the epilogue once for the whole loop, which would hold them in registers throughout.
     const int hb = hbase[lane];
     // First block of the range: seed every row's threshold with a lower bound of its k-th
-    // best score, the k-th largest of the maxima over 8 KT disjoint 16-key groups (k
+    // best score, the k-th largest of the maxima over 16 KT disjoint 8-key groups (k
     // distinct keys reach it).  Without it every key of the block would queue for a slot.
-    constexpr int NGRP = 8 * KT;
+    // A group's 8 keys sit in 8 consecutive lanes: quad swaps and a half-row mirror (DPP)
+    // leave the group maximum in each of them.
+    constexpr int NGRP = 16 * KT;
     if (blk == blk0 && k <= NGRP) {
       float* gm = reinterpret_cast<float*>(Abuf1);   // idle here; [QROWS][NGRP]
+      static_assert(QROWS * NGRP * 4 <= STEP_HALVES * 2, "group maxima fit the idle buffer");
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -480,28 +487,31 @@ __global__ __launch_bounds__(256, 1) void topk_scan_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             float v = ok[kt] ? acc[i][kt][r] * nuv[kt] : -INFINITY;
-            v = fmaxf(v, __shfl_xor(v, 1, 16));
-            v = fmaxf(v, __shfl_xor(v, 2, 16));
-            v = fmaxf(v, __shfl_xor(v, 4, 16));
-            v = fmaxf(v, __shfl_xor(v, 8, 16));
-            if ((lane & 15) == 0) {
+            v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+            v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+            v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+            if ((lane & 7) == 0) {
               const int row = 32 * i + 8 * (r >> 2) + hb + (r & 3);
-              gm[row * NGRP + (wave * KT + kt) * 2 + ((lane >> 4) & 1)] = v;
+              gm[row * NGRP + (wave * KT + kt) * 4 + ((lane >> 3) & 3)] = v;
             }
           }
       __syncthreads();
       if (tid < QROWS) {
-        float g[NGRP];
-#pragma unroll
-        for (int e = 0; e < NGRP; ++e) g[e] = gm[tid * NGRP + e];
-        // the value whose rank (larger first, ties by position) is k - 1
+        // the value whose rank (larger first, ties by position) is k - 1; read from LDS as
+        // compared (once per key range), so that no register array is live beside the
+        // accumulators
+        const float* gr = gm + tid * NGRP;
         float th = -INFINITY;
-#pragma unroll
+#pragma unroll 1
         for (int a2 = 0; a2 < NGRP; ++a2) {
+          const float ga = gr[a2];
           int rank = 0;
-#pragma unroll
-          for (int b2 = 0; b2 < NGRP; ++b2) rank += (g[b2] > g[a2] || (g[b2] == g[a2] && b2 < a2)) ? 1 : 0;
-          if (rank == k - 1) th = g[a2];
+#pragma unroll 8
+          for (int b2 = 0; b2 < NGRP; ++b2) {
+            const float gb = gr[b2];
+            rank += (gb > ga || (gb == ga && b2 < a2)) ? 1 : 0;
+          }
+          if (rank == k - 1) th = ga;
         }
         theta[tid] = th;
         thidx[tid] = 0x7fffffff;
