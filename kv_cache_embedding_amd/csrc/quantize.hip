@@ -456,23 +456,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
   }
 }
 
-int cu_count() {
-  static int cached = 0;
-  if (!cached) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    int c = 0;
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
-      c = 256;
-    cached = c;
-  }
-  return cached;
-}
-
 int grid_for(int64_t n) {
   const long ntiles = (n + VPW - 1) / VPW;
   const long need = (ntiles + WAVES - 1) / WAVES;
-  return int(need < cu_count() ? need : cu_count());
+  return int(need < device_cu_count() ? need : device_cu_count());
 }
 
 template <int BITS, bool F32IN, bool MSE = false>

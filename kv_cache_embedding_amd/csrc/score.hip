@@ -36,17 +36,6 @@ constexpr int UNR = 8;               // tiles loaded ahead per wave iteration
 constexpr int WAVES_PER_CU = 32;     // key ranges (waves) per compute unit
 constexpr float kDigitRange = 16000.f;
 
-int cu_count_s() {
-  static int cached = 0;
-  if (!cached) {
-    int dev = 0, c = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
-      c = 256;
-    cached = c;
-  }
-  return cached;
-}
 
 // ------------------------------------------------------------------------ query prep
 // Two workgroups per virtual group (G query heads): type 0 forms qh = Pi q and the MSE rows
@@ -296,7 +285,7 @@ hipError_t launch_b(const void* params, const void* q, int q_dtype, const uint32
   if (!(phases & kScoreScan)) return hipSuccess;
   const long tiles_per_group = (T + 15) / 16;
   const long total_tiles = long(groups) * tiles_per_group;
-  long tpr = (total_tiles + long(cu_count_s()) * WAVES_PER_CU - 1) / (long(cu_count_s()) * WAVES_PER_CU);
+  long tpr = (total_tiles + long(device_cu_count()) * WAVES_PER_CU - 1) / (long(device_cu_count()) * WAVES_PER_CU);
   if (tpr < 8) tpr = 8;
   tpr = (tpr + UNR - 1) / UNR * UNR;
   const long rpg = (tiles_per_group + tpr - 1) / tpr;

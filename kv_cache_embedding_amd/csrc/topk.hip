@@ -53,7 +53,6 @@ constexpr int KMAX = 32;                      // largest k held in the per-query
 // candidate slots per query for lists of KM entries (LDS of a workgroup stays <= 160 KiB)
 constexpr int cand_slots(int km) { return RT >= 8 ? (km <= 16 ? 24 : 8) : 32; }
 constexpr int STEP_HALVES = RT * 4 * 64 * 8;  // query operand of one 32-coordinate group (16 KiB)
-constexpr int TARGET_WGS = 512;               // two workgroups per CU over the whole scan
 #ifndef TQ_TOPK_PF
 #define TQ_TOPK_PF 3
 #endif
@@ -78,7 +77,10 @@ Plan plan(int d, int64_t nq, int64_t n, int k) {
   p.n = n;
   p.qt = (nq + QROWS - 1) / QROWS;
   p.nb = (n + KEYS - 1) / KEYS;
-  long want = TARGET_WGS / (p.qt > 0 ? p.qt : 1);
+  // one workgroup per CU over the whole scan: each key range as long as the CUs allow (a
+  // range's candidate rate falls as its thresholds rise, so fewer, longer ranges queue fewer
+  // candidates; a second round of workgroups cost 6% at 10^6 keys)
+  long want = device_cu_count() / (p.qt > 0 ? p.qt : 1);
   if (want < 1) want = 1;
   p.rb = (p.nb + want - 1) / want;
   if (p.rb < 1) p.rb = 1;

@@ -162,6 +162,19 @@ hipError_t launch_topk_large(const void* params, int d, int b, const void* q, in
                              hipStream_t s);
 size_t topk_large_ws_bytes(int d, int64_t nq, int64_t n);
 
+// Compute units of the current device (looked up once per process; 256 if the query fails).
+inline int device_cu_count() {
+  static int cached = 0;
+  if (!cached) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    cached = c;
+  }
+  return cached;
+}
+
 // vmcnt-only s_waitcnt immediate for gfx9 (expcnt and lgkmcnt left unconstrained).  Direct
 // global -> LDS loads count in vmcnt, and the compiler does not order later LDS reads after
 // them: kernels that use them wait explicitly.
