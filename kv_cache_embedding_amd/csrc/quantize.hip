@@ -229,9 +229,17 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     for (int i = 0; i < NRAW; ++i) raw[i] = p[i];
   };
   if (tile < t_end) load_tile(tile);      // in flight while the fragments fill LDS
+  // the fragments: every load first, then the LDS stores, so that the fill costs one round
+  // trip to memory rather than one per pass of a load-wait-store loop
+  constexpr int FILL = 2 * FRAG_U4 / (WAVES * 64);
+  static_assert(FILL * WAVES * 64 == 2 * FRAG_U4, "the threads fill the fragments evenly");
   if constexpr (!SPLIT) {
     const uint4* src = reinterpret_cast<const uint4*>(params + frag_off);
-    for (int i = threadIdx.x; i < 2 * FRAG_U4; i += WAVES * 64) frag[i] = src[i];
+    uint4 fv[FILL];
+#pragma unroll
+    for (int j = 0; j < FILL; ++j) fv[j] = src[threadIdx.x + j * WAVES * 64];
+#pragma unroll
+    for (int j = 0; j < FILL; ++j) frag[threadIdx.x + j * WAVES * 64] = fv[j];
   } else {
     // fragment element e of lane ln: Pi~ [s][mt][pass] holds Pi[32 mt + row_coord(ln % 32)]
     // [64 (ln / 32) + 8 s + e]; S'~ [mt][s][pass] holds S'[32 mt + row_coord(ln % 32)]
@@ -240,7 +248,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
     // 8192 and 12288), every other block zero
     const uint16_t* gm[2] = {reinterpret_cast<const uint16_t*>(params + gmat_off),
                              reinterpret_cast<const uint16_t*>(params1 + gmat_off)};
-    for (int i = threadIdx.x; i < 2 * FRAG_U4; i += WAVES * 64) {
+    uint4 fv[FILL];
+#pragma unroll
+    for (int f = 0; f < FILL; ++f) {
+      const int i = threadIdx.x + f * WAVES * 64;
       const bool is_s = i >= FRAG_U4;
       const int k = is_s ? i - FRAG_U4 : i;
       const int ln = k & 63, j = k >> 6, pass = j & 1, m = j >> 1;
@@ -254,8 +265,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void quantize_d128_kernel(
         const int row = 32 * mt + row_coord(ln & 31) - 64 * rg;
         v = *reinterpret_cast<const uint4*>(gm[rg] + (is_s ? 8192 : 0) + pass * 4096 + row * 64 + col);
       }
-      frag[i] = v;
+      fv[f] = v;
     }
+#pragma unroll
+    for (int f = 0; f < FILL; ++f) frag[threadIdx.x + f * WAVES * 64] = fv[f];
   }
   __syncthreads();
 
