@@ -909,12 +909,16 @@ def bench_kv(args):
         score(i % R)
     torch.cuda.synchronize()
 
-    # Each step is replayed from a HIP graph (one node per kernel launch) so that Python
-    # launch overhead does not pace the GPU; graph r works on input copy r % Rx, code set r.
-    def capture(fn, r):
+    # The steps are replayed from HIP graphs (one node per kernel launch) so that Python launch
+    # overhead does not pace the GPU: one graph holds the R steps of a cycle through the input
+    # copies and code sets (step r works on input copy r % Rx and code set r), so a graph
+    # launch is paid once per R steps; the K timed steps are K // R replays of it and one
+    # replay of a graph of the first K % R steps.
+    def capture(fn, rs):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            fn(r)
+            for r in rs:
+                fn(r)
         return g
 
     # Serial steps: the query prep (which depends on the queries only) on a second stream
@@ -930,14 +934,9 @@ def bench_kv(args):
         torch.cuda.current_stream().wait_stream(side)
         scan(r)
 
-    g_step = [capture(serial, r) for r in range(R)]
-    for r in range(R):
-        g_step[r].replay()
-    torch.cuda.synchronize()
-
-    # Pipelined steps: replay r quantizes batch r while the second stream prepares the
-    # queries and scans batch r - 1, which the previous replay quantized; each replay is one
-    # step's work (one quantize + one query prep + one scan)
+    # Pipelined steps: step r quantizes batch r while the second stream prepares the queries
+    # and scans batch r - 1, which the previous step quantized; each step is one quantize +
+    # one query prep + one scan
     def pipe(r):
         side.wait_stream(torch.cuda.current_stream())
         quantize(r)
@@ -946,23 +945,28 @@ def bench_kv(args):
             scan((r - 1) % R)
         torch.cuda.current_stream().wait_stream(side)
 
-    g_pipe = [capture(pipe, r) for r in range(R)]
-    for r in range(R):
-        g_pipe[r].replay()
-    torch.cuda.synchronize()
-
     K = args.steps
+    graphs = {}
+    for name, fn in (("serial", serial), ("pipe", pipe)):
+        full = capture(fn, range(R))
+        part = capture(fn, range(K % R)) if K % R else None
+        full.replay()
+        torch.cuda.synchronize()
+        graphs[name] = (full, part)
 
-    def wall(gs):
+    def wall(name):
+        full, part = graphs[name]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(K):
-            gs[i % R].replay()
+        for _ in range(K // R):
+            full.replay()
+        if part is not None:
+            part.replay()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / K
 
-    serial_ms = wall(g_step)
-    pipe_ms = wall(g_pipe)
+    serial_ms = wall("serial")
+    pipe_ms = wall("pipe")
 
     q_ms = time_per_launch(torch, quantize, R, K)
     s_ms = time_per_launch(torch, score, R, K)
