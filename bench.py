@@ -191,6 +191,32 @@ def time_per_launch(torch, fn, R: int, K: int, min_calls: int = 8) -> float:
     return e0.elapsed_time(e1) / (reps * M)
 
 
+def time_steps(torch, fn, R: int, K: int) -> float:
+    """Wall-clock ms per step over exactly K steps fn(0), fn(1), ... (step i works on replica
+    i % R).  The steps are replayed from HIP graphs (one node per kernel launch) so that
+    Python launch overhead does not pace the GPU: one graph holds the R steps of a cycle
+    through the replicas, so a graph launch is paid once per R steps; the K steps are K // R
+    replays of it and one replay of a graph of the first K % R steps."""
+    def capture(rs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in rs:
+                fn(r)
+        return g
+
+    full = capture(range(R))
+    part = capture(range(K % R)) if K % R else None
+    full.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K // R):
+        full.replay()
+    if part is not None:
+        part.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / K
+
+
 def source_hash(*names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -528,39 +554,11 @@ def bench_attention(args):
         attend(i % R)
     torch.cuda.synchronize()
 
-    def capture(fn, r):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn(r)
-        return g
-
-    g_att = [capture(attend, r) for r in range(R)]
-    g_app = [capture(append, r) for r in range(R)]
-    for r in range(R):
-        g_att[r].replay()
-    torch.cuda.synchronize()
     K = args.steps
-
-    def timed(gs):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(K):
-            gs[i % R].replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        g_att[i % R].replay()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    ms_step = time_steps(torch, attend, R, K)
     a_ms = time_per_launch(torch, attend, R, K)
     vq_ms = time_per_launch(torch, vquant, R, K)
-    app_ms = timed(g_app)
+    app_ms = time_steps(torch, append, R, K)
     pairs = groups * G * T
     a_bytes = n * per_key + groups * G * d * 4
     a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
@@ -692,28 +690,11 @@ def bench_fractional(args):
         score(i % R)
     torch.cuda.synchronize()
 
-    def capture(fn, r):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn(r)
-        return g
-
-    g_step = [capture(lambda r: (quantize(r), score(r)), r) for r in range(R)]
-    for r in range(R):
-        g_step[r].replay()
-    torch.cuda.synchronize()
-
     K = args.steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        g_step[i % R].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    ms_step = time_steps(torch, lambda r: (quantize(r), score(r)), R, K)
 
     q_ms = time_per_launch(torch, quantize, R, K)
     s_ms = time_per_launch(torch, score, R, K)
-    ms_step = (t1 - t0) * 1e3 / K
     n_logits = groups * G * T
     code_bytes = (d0 * b0 + (d - d0) * b1) // 8 + 16          # both groups' codes, nu, gamma
     q_bytes = n * (d * 2 + code_bytes)
@@ -909,18 +890,6 @@ def bench_kv(args):
         score(i % R)
     torch.cuda.synchronize()
 
-    # The steps are replayed from HIP graphs (one node per kernel launch) so that Python launch
-    # overhead does not pace the GPU: one graph holds the R steps of a cycle through the input
-    # copies and code sets (step r works on input copy r % Rx and code set r), so a graph
-    # launch is paid once per R steps; the K timed steps are K // R replays of it and one
-    # replay of a graph of the first K % R steps.
-    def capture(fn, rs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for r in rs:
-                fn(r)
-        return g
-
     # Serial steps: the query prep (which depends on the queries only) on a second stream
     # (default priority, forked and joined inside the graph) beside the quantize of batch r,
     # then the scan of batch r.
@@ -946,27 +915,8 @@ def bench_kv(args):
         torch.cuda.current_stream().wait_stream(side)
 
     K = args.steps
-    graphs = {}
-    for name, fn in (("serial", serial), ("pipe", pipe)):
-        full = capture(fn, range(R))
-        part = capture(fn, range(K % R)) if K % R else None
-        full.replay()
-        torch.cuda.synchronize()
-        graphs[name] = (full, part)
-
-    def wall(name):
-        full, part = graphs[name]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(K // R):
-            full.replay()
-        if part is not None:
-            part.replay()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / K
-
-    serial_ms = wall("serial")
-    pipe_ms = wall("pipe")
+    serial_ms = time_steps(torch, serial, R, K)
+    pipe_ms = time_steps(torch, pipe, R, K)
 
     q_ms = time_per_launch(torch, quantize, R, K)
     s_ms = time_per_launch(torch, score, R, K)
