@@ -993,8 +993,10 @@ def bench_kv(args):
             "kernel": "quantize_d128 (tq_quantize)",
             "bound": "mfma", "achieved": q_tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": q_tflops / BF16_MFMA_PEAK_TFLOPS,
+            "executed": q_tflops * 2.5,
             "note": "algorithmic 4 d^2 flop/vector; the kernel executes 10 d^2 on bf16 MFMA "
-                    "(hi/lo operand splits for float32-accurate rotation and projection)",
+                    "(hi/lo operand splits for float32-accurate rotation and projection): 'executed' "
+                    "is that rate, 'executed_frac_of_measured_peak' its fraction of a library bf16 GEMM's",
         },
         "roofline_score": {
             "kernel": "score_qprep + score (tq_score_ip)",
@@ -1022,6 +1024,9 @@ def bench_kv(args):
     copy_gbs = measured_copy_gbs(torch)
     with_measured_peak(result["roofline"], copy_gbs, "1 GiB device copy in this run (read + write bytes)")
     with_measured_peak(result["roofline_score"], copy_gbs, "1 GiB device copy in this run (read + write bytes)")
+    rm = with_measured_peak(result["roofline_mfma"], measured_gemm_tflops(torch, torch.bfloat16),
+                            "8192^3 library bf16 GEMM in this run")
+    rm["executed_frac_of_measured_peak"] = rm["executed"] / rm["measured_peak"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, b, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -12,11 +12,17 @@
 //   the integer MFMA through the Walsh form of the codebook (value_block): the weights as
 //   exact integer digits, the value codes' bit planes as 0/1 bytes.  Out: per block and head
 //   the maximum, the sum of p and the weighted sum of centroids.
+// attn_fused_kernel: the same block work for d = 128 keys scored by the int8 scorer, with the
+//   logits of the block's keys computed in the workgroup (score_tile.h) from the query operands
+//   of the scorer's query prep instead of read from memory: per wave 4 tiles of 16 keys, lane l
+//   holding head l / 16 of the quad for key l % 16 of each tile, so the block maxima, the sums
+//   of p and the weights' scales are reductions over 16-lane rows, and the weights land in the
+//   layout of the value MFMA's output (lane l: head l / 16).
 // attn_combine_kernel: one workgroup per (group, head): merges the blocks (log-sum-exp) and
 //   applies Pi_v^T; threads split both sums into slices of independent float4 loads (rows
 //   of Pi_v are contiguous, so a slice reads coalesced columns), the first loads of both
 //   issued before the maximum and the sum are reduced.
-#include "tq_internal.h"
+#include "score_tile.h"
 
 #include <algorithm>
 #include <cmath>
@@ -51,6 +57,16 @@ struct BlockGroup {
   float* part_acc;
 };
 
+// The key operands of the fused block kernel: the d = 128 key cache (4 coordinate groups of
+// BITS plane words per key, nu, gamma) and the query operands of the scorer's query prep, one
+// block per quad of query heads.
+struct KeyOps {
+  const uint32_t* codes;
+  const float* nu;
+  const float* gamma;
+  const unsigned char* qws;
+};
+
 // One workgroup's block (256 keys) of one value channel group.  BV: index planes of a value
 // (1..3); NC: 64-coordinate steps per chunk (NC divides d / 64).
 // With the Walsh form of the odd-symmetric codebook, chat_tc = sum_P e_P (2 B_P,tc - 1) over
@@ -67,44 +83,54 @@ struct BlockGroup {
 // shift and a mask.  Lanes hold their keys in the same order in A and B, so the MFMA's own
 // order within K does not matter.  The first chunk's code words are loaded before anything
 // waits, so their latency overlaps the logits and the softmax prologue.
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-// Wave-wide reductions without LDS: within each 16-lane row by DPP rotations (every lane of the
-// row ends with the row's result), then across the four rows from lanes 0, 16, 32, 48 (wave
-// uniform results).
+// Row and wave-wide reductions without LDS: within each 16-lane row by DPP rotations (every
+// lane of the row ends with the row's result), then, for a wave, across the four rows from
+// lanes 0, 16, 32, 48 (wave uniform results).
 template <int K>
 __device__ __forceinline__ int dpp_ror(int v) {   // row_ror:K
   return __builtin_amdgcn_update_dpp(v, v, 0x120 + K, 0xf, 0xf, false);
 }
-__device__ __forceinline__ float wave_max_dpp(float v) {
+__device__ __forceinline__ float row_max_dpp(float v) {
   v = fmaxf(v, __int_as_float(dpp_ror<8>(__float_as_int(v))));
   v = fmaxf(v, __int_as_float(dpp_ror<4>(__float_as_int(v))));
   v = fmaxf(v, __int_as_float(dpp_ror<2>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_ror<1>(__float_as_int(v))));
+  return fmaxf(v, __int_as_float(dpp_ror<1>(__float_as_int(v))));
+}
+__device__ __forceinline__ float row_sum_dpp(float v) {
+  v += __int_as_float(dpp_ror<8>(__float_as_int(v)));
+  v += __int_as_float(dpp_ror<4>(__float_as_int(v)));
+  v += __int_as_float(dpp_ror<2>(__float_as_int(v)));
+  return v + __int_as_float(dpp_ror<1>(__float_as_int(v)));
+}
+__device__ __forceinline__ int row_sum_int(int v) {
+  v += dpp_ror<8>(v);
+  v += dpp_ror<4>(v);
+  v += dpp_ror<2>(v);
+  return v + dpp_ror<1>(v);
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = row_max_dpp(v);
   const int i = __float_as_int(v);
   return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(i, 0)), __int_as_float(__builtin_amdgcn_readlane(i, 16))),
                fmaxf(__int_as_float(__builtin_amdgcn_readlane(i, 32)), __int_as_float(__builtin_amdgcn_readlane(i, 48))));
 }
 __device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += __int_as_float(dpp_ror<8>(__float_as_int(v)));
-  v += __int_as_float(dpp_ror<4>(__float_as_int(v)));
-  v += __int_as_float(dpp_ror<2>(__float_as_int(v)));
-  v += __int_as_float(dpp_ror<1>(__float_as_int(v)));
+  v = row_sum_dpp(v);
   const int i = __float_as_int(v);
   return (__int_as_float(__builtin_amdgcn_readlane(i, 0)) + __int_as_float(__builtin_amdgcn_readlane(i, 16))) +
          (__int_as_float(__builtin_amdgcn_readlane(i, 32)) + __int_as_float(__builtin_amdgcn_readlane(i, 48)));
 }
 __device__ __forceinline__ int wave_sum_int(int v) {
-  v += dpp_ror<8>(v);
-  v += dpp_ror<4>(v);
-  v += dpp_ror<2>(v);
-  v += dpp_ror<1>(v);
+  v = row_sum_int(v);
   return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
          (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
-template <int BV, int NC>
-__device__ __forceinline__ void value_block(const BlockGroup& bg, const float* __restrict__ logits,
+// KBITS = 0: the logits come from memory (one per (head, key)); KBITS = b of d = 128 keys: the
+// workgroup scores its keys itself (PROD: the inner-product estimate, else the MSE one).
+// red: 8 rows of AH floats (the block maxima of the waves, then their sums of p).
+template <int BV, int NC, int KBITS = 0, bool PROD = true>
+__device__ __forceinline__ void value_block(const BlockGroup& bg, const KeyOps& ko, const float* __restrict__ logits,
                                             long G, long T, long nkb, long passes, float scale,
                                             long blk, float (*red)[AH], float (*accs)[AH][64 * NC],
                                             unsigned char* kb_all, unsigned char* ab_all) {
@@ -154,59 +180,148 @@ __device__ __forceinline__ void value_block(const BlockGroup& bg, const float* _
 #pragma unroll
   for (int i = 0; i < NE; ++i) e[i] = hdr->e[i];
 
-  // prologue: scaled logits of the lane's key, block maximum per head, weights p nu, sums of p
-  float l[AH];
-#pragma unroll
-  for (int hh = 0; hh < AH; ++hh) {
-    const long h = h0 + (hh < nh ? hh : nh - 1);
-    l[hh] = valid ? scale * logits[size_t(g * G + h) * T + t] : -INFINITY;
-    const float m = wave_max_dpp(l[hh]);
-    if (lane == 0) red[wave][hh] = m;
-  }
-  __syncthreads();
-  float M[AH];
-#pragma unroll
-  for (int hh = 0; hh < AH; ++hh)
-    M[hh] = fmaxf(fmaxf(red[0][hh], red[1][hh]), fmaxf(red[2][hh], red[3][hh]));
-  __syncthreads();
-  const float nu_t = valid ? vnu[g * T + t] : 0.f;
-  float w[AH];
-#pragma unroll
-  for (int hh = 0; hh < AH; ++hh) {
-    const float p = valid ? __expf(l[hh] - M[hh]) : 0.f;
-    w[hh] = p * nu_t;
-    const float sp = wave_sum_dpp(p);
-    if (lane == 0) red[wave][hh] = sp;
-  }
-  __syncthreads();
+  float inv_l = 0.f;      // this lane's head (lane / 16): 1 / scale
+  int tsum_l = 0;         // this lane's head: sum of its integer weights over the wave
   const long prow = g * G + h0;                 // partial rows of this pass: prow + hh
+  if constexpr (KBITS == 0) {
+    // scaled logits of the lane's key, block maximum per head, weights p nu, sums of p
+    float l[AH];
 #pragma unroll
-  for (int hh = 0; hh < AH; ++hh) {
-    if (tid == hh && hh < nh) {
-      bg.part_m[(prow + hh) * nkb + kblk] = M[hh];
-      bg.part_s[(prow + hh) * nkb + kblk] = (red[0][hh] + red[1][hh]) + (red[2][hh] + red[3][hh]);
+    for (int hh = 0; hh < AH; ++hh) {
+      const long h = h0 + (hh < nh ? hh : nh - 1);
+      l[hh] = valid ? scale * logits[size_t(g * G + h) * T + t] : -INFINITY;
+      const float m = wave_max_dpp(l[hh]);
+      if (lane == 0) red[wave][hh] = m;
+    }
+    __syncthreads();
+    float M[AH];
+#pragma unroll
+    for (int hh = 0; hh < AH; ++hh)
+      M[hh] = fmaxf(fmaxf(red[0][hh], red[1][hh]), fmaxf(red[2][hh], red[3][hh]));
+    __syncthreads();
+    const float nu_t = valid ? vnu[g * T + t] : 0.f;
+    float w[AH];
+#pragma unroll
+    for (int hh = 0; hh < AH; ++hh) {
+      const float p = valid ? __expf(l[hh] - M[hh]) : 0.f;
+      w[hh] = p * nu_t;
+      const float sp = wave_sum_dpp(p);
+      if (lane == 0) red[wave][hh] = sp;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < AH; ++hh) {
+      if (tid == hh && hh < nh) {
+        bg.part_m[(prow + hh) * nkb + kblk] = M[hh];
+        bg.part_s[(prow + hh) * nkb + kblk] = (red[0][hh] + red[1][hh]) + (red[2][hh] + red[3][hh]);
+      }
+    }
+
+    // integer weights of the wave's keys and the A operand (rows 4 hh + j: digit j of head hh)
+#pragma unroll
+    for (int hh = 0; hh < AH; ++hh) {
+      const float wm = wave_max_dpp(w[hh]);
+      const float sc = wm > 0.f ? kVMax / wm : 0.f;
+      int v = int(rintf(w[hh] * sc));
+      v = v < 2097151 ? v : 2097151;
+      const int ts = wave_sum_int(v);
+      if ((lane >> 4) == hh) {
+        inv_l = wm * (1.f / kVMax);
+        tsum_l = ts;
+      }
+      ab[(4 * hh + 0) * 64 + lane] = (unsigned char)(v & 127);
+      ab[(4 * hh + 1) * 64 + lane] = (unsigned char)((v >> 7) & 127);
+      ab[(4 * hh + 2) * 64 + lane] = (unsigned char)(v >> 14);
+      ab[(4 * hh + 3) * 64 + lane] = 0;
+    }
+  } else {
+    // the block's logits: 4 tiles of 16 keys per wave, lane l holding head l / 16 of the quad
+    // for key 16 u + l % 16 of the wave (tile u)
+    constexpr int NW = score_words(KBITS);
+    constexpr int NWU = PROD ? NW : NW - 1;
+    const int hs = lane >> 4;
+    const unsigned char* qb = ko.qws + size_t(gp) * score_ws_per_group(KBITS);
+    v4i QA[2 * NW];
+#pragma unroll
+    for (int m = 0; m < 2 * NWU; ++m) QA[m] = reinterpret_cast<const v4i*>(qb)[m * 64 + lane];
+    const float4 cst = reinterpret_cast<const float4*>(qb + size_t(2 * NW) * 64 * 16)[hs];
+    const uint32_t* kc = ko.codes + size_t(g) * T * 4 * KBITS;
+    uint32_t kw[4][KBITS];
+    float nk[4], gk[4], nv[4];
+    bool ok[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long key = tw0 + 16 * u + (lane & 15);
+      ok[u] = key < T;
+      if (ok[u]) {
+        const uint32_t* src = kc + (size_t(key) * 4 + hs) * KBITS;
+        if constexpr (KBITS == 4) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src);
+          kw[u][0] = v.x; kw[u][1] = v.y; kw[u][2] = v.z; kw[u][3] = v.w;
+        } else if constexpr (KBITS == 2) {
+          const uint2 v = *reinterpret_cast<const uint2*>(src);
+          kw[u][0] = v.x; kw[u][1] = v.y;
+        } else {
+#pragma unroll
+          for (int p = 0; p < KBITS; ++p) kw[u][p] = src[p];
+        }
+        nk[u] = ko.nu[g * T + key];
+        gk[u] = PROD ? ko.gamma[g * T + key] : 0.f;
+        nv[u] = vnu[g * T + key];
+      } else {
+#pragma unroll
+        for (int p = 0; p < KBITS; ++p) kw[u][p] = 0u;
+        nk[u] = 0.f;
+        gk[u] = 0.f;
+        nv[u] = 0.f;
+      }
+    }
+    float l[4], mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      l[u] = ok[u] ? scale * score_tile_logit<KBITS, PROD>(QA, cst, kw[u], nk[u], gk[u]) : -INFINITY;
+      mx = fmaxf(mx, l[u]);
+    }
+    mx = row_max_dpp(mx);
+    if ((lane & 15) == 0) red[wave][hs] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0][hs], red[1][hs]), fmaxf(red[2][hs], red[3][hs]));
+    float w[4], sp = 0.f, wmx = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float p = ok[u] ? __expf(l[u] - M) : 0.f;
+      sp += p;
+      w[u] = p * nv[u];
+      wmx = fmaxf(wmx, w[u]);
+    }
+    sp = row_sum_dpp(sp);
+    if ((lane & 15) == 0) red[4 + wave][hs] = sp;
+    // integer weights (the lane's head is also its head in the value MFMA's output) and the
+    // A operand rows 4 hs + j: digit j of head hs
+    const float wm = row_max_dpp(wmx);
+    const float sc = wm > 0.f ? kVMax / wm : 0.f;
+    int vs = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int v = int(rintf(w[u] * sc));
+      v = v < 2097151 ? v : 2097151;
+      vs += v;
+      const int key = 16 * u + (lane & 15);
+      ab[(4 * hs + 0) * 64 + key] = (unsigned char)(v & 127);
+      ab[(4 * hs + 1) * 64 + key] = (unsigned char)((v >> 7) & 127);
+      ab[(4 * hs + 2) * 64 + key] = (unsigned char)(v >> 14);
+      ab[(4 * hs + 3) * 64 + key] = 0;
+    }
+    tsum_l = row_sum_int(vs);
+    inv_l = wm * (1.f / kVMax);
+    __syncthreads();
+    if (tid < nh) {
+      bg.part_m[(prow + tid) * nkb + kblk] =
+          fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+      bg.part_s[(prow + tid) * nkb + kblk] = (red[4][tid] + red[5][tid]) + (red[6][tid] + red[7][tid]);
     }
   }
 
-  // integer weights of the wave's keys and the A operand (rows 4 hh + j: digit j of head hh)
-  float inv_l = 0.f;      // this lane's head (lane / 16): 1 / scale
-  int tsum_l = 0;         // this lane's head: sum of its integer weights over the wave
-#pragma unroll
-  for (int hh = 0; hh < AH; ++hh) {
-    const float wm = wave_max_dpp(w[hh]);
-    const float sc = wm > 0.f ? kVMax / wm : 0.f;
-    int v = int(rintf(w[hh] * sc));
-    v = v < 2097151 ? v : 2097151;
-    const int ts = wave_sum_int(v);
-    if ((lane >> 4) == hh) {
-      inv_l = wm * (1.f / kVMax);
-      tsum_l = ts;
-    }
-    ab[(4 * hh + 0) * 64 + lane] = (unsigned char)(v & 127);
-    ab[(4 * hh + 1) * 64 + lane] = (unsigned char)((v >> 7) & 127);
-    ab[(4 * hh + 2) * 64 + lane] = (unsigned char)(v >> 14);
-    ab[(4 * hh + 3) * 64 + lane] = 0;
-  }
   // the staging writes and the reads below use other types: order them explicitly
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   const v4i A = *reinterpret_cast<const v4i*>(ab + (lane & 15) * 64 + 16 * (lane >> 4));
@@ -274,7 +389,7 @@ template <int BV0, int BV1, int NC>
 __global__ __launch_bounds__(256) void attn_block_kernel(BlockGroup b0, BlockGroup b1, long blocks0,
                                                          const float* __restrict__ logits, long G,
                                                          long T, long nkb, long passes, float scale) {
-  __shared__ float red[4][AH];
+  __shared__ float red[8][AH];
   __shared__ float accs[4][AH][64 * NC];
   __shared__ uint4 kbytes[4 * 4 * 2 * NC * 4 * 64 / 16];   // [wave][plane][group][byte][key]
   __shared__ uint4 abytes[4 * 16 * 64 / 16];               // [wave][row][key] weight digits
@@ -283,11 +398,27 @@ __global__ __launch_bounds__(256) void attn_block_kernel(BlockGroup b0, BlockGro
   const long blk = blockIdx.x;
   if constexpr (BV1 > 0) {
     if (blk >= blocks0) {
-      value_block<BV1, NC>(b1, logits, G, T, nkb, passes, scale, blk - blocks0, red, accs, kb, ab);
+      value_block<BV1, NC>(b1, KeyOps{}, logits, G, T, nkb, passes, scale, blk - blocks0, red, accs, kb, ab);
       return;
     }
   }
-  value_block<BV0, NC>(b0, logits, G, T, nkb, passes, scale, blk, red, accs, kb, ab);
+  value_block<BV0, NC>(b0, KeyOps{}, logits, G, T, nkb, passes, scale, blk, red, accs, kb, ab);
+}
+
+// d = 128 keys and values: the block's logits computed in the workgroup (grid: groups x quads
+// of heads x key blocks, as attn_block_kernel's).  At most 128 VGPRs, so that four workgroups
+// (one wave per SIMD each) stay resident per CU: a decode layer's whole grid in one round.
+template <int KBITS, bool PROD, int BV>
+__global__ __launch_bounds__(256, 4) void attn_fused_kernel(KeyOps ko, BlockGroup bg, long G, long T, long nkb,
+                                                         long passes, float scale) {
+  constexpr int NC = 2;
+  __shared__ float red[8][AH];
+  __shared__ float accs[4][AH][64 * NC];
+  __shared__ uint4 kbytes[4 * 4 * 2 * NC * 4 * 64 / 16];   // [wave][plane][group][byte][key]
+  __shared__ uint4 abytes[4 * 16 * 64 / 16];               // [wave][row][key] weight digits
+  value_block<BV, NC, KBITS, PROD>(bg, ko, nullptr, G, T, nkb, passes, scale, blockIdx.x, red, accs,
+                                   reinterpret_cast<unsigned char*>(kbytes),
+                                   reinterpret_cast<unsigned char*>(abytes));
 }
 
 // The block partials and output columns of one value channel group.
@@ -541,6 +672,59 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
   const long rows = long(groups) * G;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT), combine_lds_bytes(d), s, v.comb,
                      v.comb, rows, nkb, long(opitch > 0 ? opitch : d));
+  return hipGetLastError();
+}
+
+namespace {
+
+template <int KBITS, bool PROD>
+hipError_t launch_fused_kb(const KeyOps& ko, const ValueGroup& v, long blocks, int64_t G, int64_t T,
+                           float scale, hipStream_t s) {
+  const long nkb = (T + KB - 1) / KB;
+  const long passes = G / AH;
+  switch (v.bv) {
+    case 1: hipLaunchKernelGGL((attn_fused_kernel<KBITS, PROD, 1>), dim3(unsigned(blocks)), dim3(256), 0, s,
+                               ko, v.blk, long(G), long(T), nkb, passes, scale); break;
+    case 2: hipLaunchKernelGGL((attn_fused_kernel<KBITS, PROD, 2>), dim3(unsigned(blocks)), dim3(256), 0, s,
+                               ko, v.blk, long(G), long(T), nkb, passes, scale); break;
+    case 3: hipLaunchKernelGGL((attn_fused_kernel<KBITS, PROD, 3>), dim3(unsigned(blocks)), dim3(256), 0, s,
+                               ko, v.blk, long(G), long(T), nkb, passes, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int KBITS>
+hipError_t launch_fused_k(bool prod, const KeyOps& ko, const ValueGroup& v, long blocks, int64_t G,
+                          int64_t T, float scale, hipStream_t s) {
+  return prod ? launch_fused_kb<KBITS, true>(ko, v, blocks, G, T, scale, s)
+              : launch_fused_kb<KBITS, false>(ko, v, blocks, G, T, scale, s);
+}
+
+}  // namespace
+
+hipError_t launch_attention_fused(const void* params_v, int b_k, bool prod, const uint32_t* codes_k,
+                                  const float* nu_k, const float* gamma_k, const void* qws, int b_v,
+                                  const uint32_t* vcodes, const float* vnu, int64_t groups, int64_t G,
+                                  int64_t T, float scale, float* out, void* part, hipStream_t s) {
+  constexpr int d = 128;
+  if (b_v < 2 || b_v > 4 || G % AH != 0) return hipErrorInvalidValue;
+  const ValueGroup v = value_group(params_v, d, b_v, vcodes, vnu, groups, G, T, out, part);
+  if (v.nc != 2) return hipErrorInvalidValue;
+  const KeyOps ko{codes_k, nu_k, gamma_k, static_cast<const unsigned char*>(qws)};
+  const long nkb = (T + KB - 1) / KB;
+  const long blocks = long(groups) * (G / AH) * nkb;
+  hipError_t e;
+  switch (b_k) {
+    case 2: e = launch_fused_k<2>(prod, ko, v, blocks, G, T, scale, s); break;
+    case 3: e = launch_fused_k<3>(prod, ko, v, blocks, G, T, scale, s); break;
+    case 4: e = launch_fused_k<4>(prod, ko, v, blocks, G, T, scale, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const long rows = long(groups) * G;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT), combine_lds_bytes(d), s, v.comb,
+                     v.comb, rows, nkb, long(d));
   return hipGetLastError();
 }
 

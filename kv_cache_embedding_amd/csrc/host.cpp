@@ -843,11 +843,21 @@ int tq_attention(const void* params_k, const void* params_v, int d, int b_k, int
   void* sws = w + tq::align256(size_t(groups) * G * T * 4);
   void* part = static_cast<unsigned char*>(sws) + tq_score_ws_bytes(d, b_k, groups, G, T);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_score_any(params_k, d, b_k, q, q_dtype, codes_k, nu_k, gamma_k, groups, G, T,
-                                  mode, logits, sws, s);
-  if (e == hipSuccess)
-    e = tq::launch_attention_values(params_v, d, b_v, logits, codes_v, nu_v, groups, G, T, scale, out,
-                                    part, s);
+  hipError_t e;
+  if (score_uses_d128(d, G)) {
+    // the query operands, then the block kernel scores its own keys (no logits in memory)
+    e = launch_score_any(params_k, d, b_k, q, q_dtype, nullptr, nullptr, nullptr, groups, G, T, mode,
+                         nullptr, sws, s, tq::kScorePrep);
+    if (e == hipSuccess)
+      e = tq::launch_attention_fused(params_v, b_k, mode == TQ_EST_PROD, codes_k, nu_k, gamma_k, sws, b_v,
+                                     codes_v, nu_v, groups, G, T, scale, out, part, s);
+  } else {
+    e = launch_score_any(params_k, d, b_k, q, q_dtype, codes_k, nu_k, gamma_k, groups, G, T, mode, logits,
+                         sws, s);
+    if (e == hipSuccess)
+      e = tq::launch_attention_values(params_v, d, b_v, logits, codes_v, nu_v, groups, G, T, scale, out,
+                                      part, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "tq_attention launch");
   return ok();
 }

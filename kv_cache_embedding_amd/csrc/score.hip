@@ -20,12 +20,10 @@
 // the four partial sums of one logit, so the epilogue is lane-local.
 // The key planes stream from HBM once (coalesced 16 B per lane per 16-key tile); the
 // query operand stays in registers for the wave's whole key range.
-#include "tq_internal.h"
+#include "score_tile.h"
 
 namespace tq {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int G = 4;
@@ -235,34 +233,7 @@ __global__ __launch_bounds__(256) void score_kernel(const uint32_t* __restrict__
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      uint32_t word[NW];
-      if constexpr (BITS == 4) {
-        word[0] = w[u][0]; word[1] = w[u][1]; word[2] = w[u][2];
-        word[3] = w[u][0] ^ w[u][1] ^ w[u][2];
-        word[4] = w[u][3];
-      } else {
-#pragma unroll
-        for (int p = 0; p < BITS; ++p) word[p] = w[u][p];
-      }
-      v4i acc = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < NWU; ++i) {
-        const uint32_t W = word[i];
-        const uint32_t s2 = W >> 2, s4 = W >> 4, s6 = W >> 6;
-        const v4i b0 = {int(W & 0x01010101u), int(s2 & 0x01010101u), int(s4 & 0x01010101u),
-                        int(s6 & 0x01010101u)};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * i], b0, acc, 0, 0, 0);
-        const v4i b1 = {int(W & 0x02020202u), int(s2 & 0x02020202u), int(s4 & 0x02020202u),
-                        int(s6 & 0x02020202u)};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * i + 1], b1, acc, 0, 0, 0);
-      }
-      const int ai = acc[0] * 128 + acc[1];
-      float l = fmaf(float(ai), cst.x, -cst.y);
-      if constexpr (PROD) {
-        const int bi = acc[2] * 128 + acc[3];
-        l = fmaf(gk[u], fmaf(float(bi), cst.z, -cst.w), l);
-      }
-      l *= nk[u];
+      const float l = score_tile_logit<BITS, PROD>(A, cst, w[u], nk[u], gk[u]);
       if ((tb + u < t1) && key[u] < T) out[key[u]] = l;
     }
   }

@@ -132,6 +132,13 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
                                    const uint32_t* vcodes, const float* vnu, int64_t groups,
                                    int64_t G, int64_t T, float scale, float* out, void* part,
                                    hipStream_t s, int64_t opitch = 0);
+// d = 128 keys and values with G a multiple of 4: the block partials with each block's logits
+// computed in the block kernel from the query operands that the d = 128 scorer's query prep
+// wrote to qws (no logits in memory), then the merge.
+hipError_t launch_attention_fused(const void* params_v, int b_k, bool prod, const uint32_t* codes_k,
+                                  const float* nu_k, const float* gamma_k, const void* qws, int b_v,
+                                  const uint32_t* vcodes, const float* vnu, int64_t groups, int64_t G,
+                                  int64_t T, float scale, float* out, void* part, hipStream_t s);
 // Two value channel groups (output columns 0..d0-1 and d0..d0+d1-1): the block partials of
 // each group (group 1's at align256(attention_part_bytes(d0, ...)) in part), then one merge
 // launch for both.

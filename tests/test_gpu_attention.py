@@ -115,6 +115,7 @@ def _oracle_parts(stk, stv, d, q, q_bf16, ck, nk, gk, cv, nv, groups, G, T, mode
     (64, 3, 4, 3, 300, True, tq.TQ_EST_PROD, ""),
     (256, 2, 3, 4, 513, False, tq.TQ_EST_PROD, ""),
     (128, 4, 3, 4, 700, True, tq.TQ_EST_PROD, "sphere+orth"),
+    (128, 2, 3, 8, 777, False, tq.TQ_EST_PROD, ""),
     (192, 3, 4, 2, 333, True, tq.TQ_EST_PROD, "sphere+orth")])
 def test_attention_parity(d, b_k, b_v, G, T, q_bf16, mode, variant):
     groups = 3
