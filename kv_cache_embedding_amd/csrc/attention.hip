@@ -77,10 +77,12 @@ struct KeyOps {
 // 7-bit digits each, and v_mfma_i32_16x16x64_i8 sums them exactly over the keys whose plane bit
 // is set: A = 16 rows (head h: rows 4 h + {digit 0, 1, 2, zero}) over the wave's 64 keys, B =
 // those keys' bits of 16 coordinates as bytes 0/1.  In the 16x16 accumulator layout lane l
-// ends with head l / 16 and coordinate l % 16 of the tile, its three digit sums in registers
-// 0..2.  The value codes are staged in LDS byte-transposed, [plane][32-coordinate group]
-// [byte of the word][key], so the bit of one coordinate for 16 keys is one 16-byte read, a
-// shift and a mask.  Lanes hold their keys in the same order in A and B, so the MFMA's own
+// ends with head l / 16 and the tile's column l % 16, its three digit sums in registers 0..2.
+// The value codes are staged in LDS byte-transposed, [plane][32-coordinate group][byte of the
+// word][key], so one 16-byte read gives a lane one byte (8 coordinates) of 16 keys.  For a
+// chunk of 128 coordinates per plane (NC even) column n is byte n and MFMA j takes bit j, so
+// one read feeds the plane's 8 MFMAs and lane l ends with coordinates 8 (l % 16) .. + 7; for
+// NC odd column n is coordinate n of a 16-coordinate tile (one read per MFMA).  Lanes hold their keys in the same order in A and B, so the MFMA's own
 // order within K does not matter.  The first chunk's code words are loaded before anything
 // waits, so their latency overlaps the logits and the softmax prologue.
 // Row and wave-wide reductions without LDS: within each 16-lane row by DPP rotations (every
@@ -89,6 +91,10 @@ struct KeyOps {
 template <int K>
 __device__ __forceinline__ int dpp_ror(int v) {   // row_ror:K
   return __builtin_amdgcn_update_dpp(v, v, 0x120 + K, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_quad(uint32_t v) {   // quad_perm CTRL
+  return uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), CTRL, 0xf, 0xf, false));
 }
 __device__ __forceinline__ float row_max_dpp(float v) {
   v = fmaxf(v, __int_as_float(dpp_ror<8>(__float_as_int(v))));
@@ -329,9 +335,15 @@ __device__ __forceinline__ void value_block(const BlockGroup& bg, const KeyOps& 
   const int hl = lane >> 4;                     // this lane's head in the MFMA output
   const int ksl = 16 * hl;                      // first of this lane's 16 keys in A and B
   const uint32_t sh = lane & 7;                 // bit of the byte for coordinate lane % 16
+  const int qi = lane & 3;                      // the lane's byte in the quad transpose
+  // byte selectors of the two transpose steps (v_perm: 0..3 own bytes, 4..7 the partner's)
+  const uint32_t sel_a = (qi & 2) ? 0x03020706u : 0x05040100u;
+  const uint32_t sel_b = (qi & 1) ? 0x03070105u : 0x06020400u;
   for (int c0 = 0; c0 < d; c0 += 64 * NC) {
     if (c0 > 0) load_words(c0);
-    // stage the chunk's words byte-transposed (the xor plane formed here)
+    // stage the chunk's words byte-transposed (the xor plane formed here): a 4 x 4 byte
+    // transpose within each lane quad (16-bit halves with the lane two apart, then bytes with
+    // the neighbour) leaves lane 4 j + i with byte i of keys 4 j .. 4 j + 3, one dword store
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
       uint32_t word[NE];
@@ -339,39 +351,75 @@ __device__ __forceinline__ void value_block(const BlockGroup& bg, const KeyOps& 
       for (int p = 0; p < BV; ++p) word[p] = pw[gg][p];
       if constexpr (BV == 3) word[3] = pw[gg][0] ^ pw[gg][1] ^ pw[gg][2];
 #pragma unroll
-      for (int pp = 0; pp < NE; ++pp)
-#pragma unroll
-        for (int by = 0; by < 4; ++by) kb[((pp * NG + gg) * 4 + by) * 64 + lane] = (unsigned char)(word[pp] >> (8 * by));
+      for (int pp = 0; pp < NE; ++pp) {
+        const uint32_t x = __builtin_amdgcn_perm(dpp_quad<0x4E>(word[pp]), word[pp], sel_a);
+        const uint32_t y = __builtin_amdgcn_perm(dpp_quad<0xB1>(x), x, sel_b);
+        *reinterpret_cast<uint32_t*>(kb + ((pp * NG + gg) * 4 + qi) * 64 + (lane & ~3)) = y;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
     float acc[2 * NG];
 #pragma unroll
     for (int i = 0; i < 2 * NG; ++i) acc[i] = 0.f;
+    if constexpr (NC % 2 == 0) {
+      // MFMA column n = byte n of 16 consecutive bytes of the keys' plane (byte n of the chunk
+      // holds coordinates 8 n .. 8 n + 7), MFMA j = bit j: one 16-byte read per lane feeds the
+      // plane's 8 MFMAs of a 128-coordinate slice, and the lane ends with coordinates
+      // 8 (16 rr + lane % 16) + j of its head
 #pragma unroll
-    for (int pp = 0; pp < NE; ++pp) {
-      // the plane's MFMAs first, then their results (the MFMA latency overlaps the gathers)
-      v4i r[2 * NG];
+      for (int pp = 0; pp < NE; ++pp) {
+        v4i r[2 * NG];
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
+        for (int rr = 0; rr < NC / 2; ++rr) {
+          const uint4 q = *reinterpret_cast<const uint4*>(kb + (pp * NG * 4 + 16 * rr + (lane & 15)) * 64 + ksl);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          // coordinate 32 gg + 16 half + lane % 16: byte 2 half + (lane % 16) / 8 of the word
-          const int by = 2 * half + ((lane & 15) >> 3);
-          const uint4 q = *reinterpret_cast<const uint4*>(kb + ((pp * NG + gg) * 4 + by) * 64 + ksl);
-          const v4i B = {int((q.x >> sh) & 0x01010101u), int((q.y >> sh) & 0x01010101u),
-                         int((q.z >> sh) & 0x01010101u), int((q.w >> sh) & 0x01010101u)};
-          r[2 * gg + half] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+          for (int j = 0; j < 8; ++j) {
+            const v4i B = {int((q.x >> j) & 0x01010101u), int((q.y >> j) & 0x01010101u),
+                           int((q.z >> j) & 0x01010101u), int((q.w >> j) & 0x01010101u)};
+            r[8 * rr + j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * NG; ++i) {
+          const int S = r[i][2] * 16384 + r[i][1] * 128 + r[i][0];
+          acc[i] = fmaf(e[pp], float(2 * S - tsum_l), acc[i]);
         }
       }
 #pragma unroll
-      for (int i = 0; i < 2 * NG; ++i) {
-        const int S = r[i][2] * 16384 + r[i][1] * 128 + r[i][0];
-        acc[i] = fmaf(e[pp], float(2 * S - tsum_l), acc[i]);
+      for (int rr = 0; rr < NC / 2; ++rr) {
+        float4* dst = reinterpret_cast<float4*>(&accs[wave][hl][8 * (16 * rr + (lane & 15))]);
+        dst[0] = make_float4(acc[8 * rr] * inv_l, acc[8 * rr + 1] * inv_l, acc[8 * rr + 2] * inv_l,
+                             acc[8 * rr + 3] * inv_l);
+        dst[1] = make_float4(acc[8 * rr + 4] * inv_l, acc[8 * rr + 5] * inv_l, acc[8 * rr + 6] * inv_l,
+                             acc[8 * rr + 7] * inv_l);
       }
-    }
+    } else {
 #pragma unroll
-    for (int i = 0; i < 2 * NG; ++i) accs[wave][hl][16 * i + (lane & 15)] = acc[i] * inv_l;
+      for (int pp = 0; pp < NE; ++pp) {
+        // the plane's MFMAs first, then their results (the MFMA latency overlaps the gathers)
+        v4i r[2 * NG];
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            // coordinate 32 gg + 16 half + lane % 16: byte 2 half + (lane % 16) / 8 of the word
+            const int by = 2 * half + ((lane & 15) >> 3);
+            const uint4 q = *reinterpret_cast<const uint4*>(kb + ((pp * NG + gg) * 4 + by) * 64 + ksl);
+            const v4i B = {int((q.x >> sh) & 0x01010101u), int((q.y >> sh) & 0x01010101u),
+                           int((q.z >> sh) & 0x01010101u), int((q.w >> sh) & 0x01010101u)};
+            r[2 * gg + half] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * NG; ++i) {
+          const int S = r[i][2] * 16384 + r[i][1] * 128 + r[i][0];
+          acc[i] = fmaf(e[pp], float(2 * S - tsum_l), acc[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NG; ++i) accs[wave][hl][16 * i + (lane & 15)] = acc[i] * inv_l;
+    }
     __syncthreads();
     for (int ei = tid; ei < AH * 64 * NC; ei += 256) {
       const int hh = ei / (64 * NC), c = ei % (64 * NC);
@@ -390,7 +438,7 @@ __global__ __launch_bounds__(256) void attn_block_kernel(BlockGroup b0, BlockGro
                                                          const float* __restrict__ logits, long G,
                                                          long T, long nkb, long passes, float scale) {
   __shared__ float red[8][AH];
-  __shared__ float accs[4][AH][64 * NC];
+  __shared__ __align__(16) float accs[4][AH][64 * NC];
   __shared__ uint4 kbytes[4 * 4 * 2 * NC * 4 * 64 / 16];   // [wave][plane][group][byte][key]
   __shared__ uint4 abytes[4 * 16 * 64 / 16];               // [wave][row][key] weight digits
   unsigned char* kb = reinterpret_cast<unsigned char*>(kbytes);
@@ -413,7 +461,7 @@ __global__ __launch_bounds__(256, 4) void attn_fused_kernel(KeyOps ko, BlockGrou
                                                          long passes, float scale) {
   constexpr int NC = 2;
   __shared__ float red[8][AH];
-  __shared__ float accs[4][AH][64 * NC];
+  __shared__ __align__(16) float accs[4][AH][64 * NC];
   __shared__ uint4 kbytes[4 * 4 * 2 * NC * 4 * 64 / 16];   // [wave][plane][group][byte][key]
   __shared__ uint4 abytes[4 * 16 * 64 / 16];               // [wave][row][key] weight digits
   value_block<BV, NC, KBITS, PROD>(bg, ko, nullptr, G, T, nkb, passes, scale, blockIdx.x, red, accs,
@@ -475,8 +523,11 @@ __global__ __launch_bounds__(CT) void attn_combine_kernel(CombineGroup c0, Combi
     ppi[i] = okr ? P4[size_t(r) * d4 + q4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  float mx = -INFINITY;
-  for (long k = tid; k < nkb; k += CT) mx = fmaxf(mx, pm[k]);
+  // this thread's first block maximum and sum, in the same round trip as the loads above
+  const float pm0 = tid < nkb ? pm[tid] : -INFINITY;
+  const float ps0 = tid < nkb ? ps[tid] : 0.f;
+  float mx = pm0;
+  for (long k = tid + CT; k < nkb; k += CT) mx = fmaxf(mx, pm[k]);
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
@@ -484,8 +535,8 @@ __global__ __launch_bounds__(CT) void attn_combine_kernel(CombineGroup c0, Combi
 #pragma unroll
   for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
   __syncthreads();
-  float sum = 0.f;
-  for (long k = tid; k < nkb; k += CT) sum += __expf(pm[k] - M) * ps[k];
+  float sum = tid < nkb ? __expf(pm0 - M) * ps0 : 0.f;
+  for (long k = tid + CT; k < nkb; k += CT) sum += __expf(pm[k] - M) * ps[k];
   sum = wave_sum(sum);
   if (lane == 0) red[wave] = sum;
   __syncthreads();
