@@ -579,12 +579,12 @@ def bench_attention(args):
             "keys": n, "d": d, "key_bits": b_k, "value_index_bits": b_v - 1, "replicas": R,
         },
         "roofline": {
-            "kernel": "tq_attention (score qprep + score + attention blocks + combine)",
+            "kernel": "tq_attention (query prep + fused score/softmax/value blocks + combine)",
             "bound": "hbm", "achieved": a_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": a_gbs / HBM_PEAK_GBS, "traffic": None,
             "note": f"algorithmic bytes per key: {d // 8 * b_k} B key codes + 8 B nu, gamma + "
-                    f"{d // 8 * (b_v - 1)} B value codes + 4 B nu; the logits and block partials "
-                    "in the workspace are implementation traffic; timed over the whole call",
+                    f"{d // 8 * (b_v - 1)} B value codes + 4 B nu; the block partials in the "
+                    "workspace are implementation traffic; timed over the whole call",
         },
         "value_quantize": {"ms": vq_ms, "vectors_per_s": n / (vq_ms * 1e-3),
                            "hbm_gbs": vq_bytes / (vq_ms * 1e-3) / 1e9},
