@@ -317,6 +317,23 @@ def cpu_baseline_search(w, b, seconds: float):
     }
 
 
+def search_recall(torch, x, q, idx, k: int, chunk: int = 65536) -> float:
+    """Mean |returned top-k & exact top-k| / k over the queries; exact = float32 inner
+    products of the unquantized vectors (library GEMM in key chunks, running top-k)."""
+    nq = q.shape[0]
+    best_s = torch.full((nq, k), -float("inf"), device=q.device)
+    best_i = torch.zeros((nq, k), dtype=torch.int64, device=q.device)
+    for c0 in range(0, x.shape[0], chunk):
+        cs, ci = torch.topk(q @ x[c0:c0 + chunk].T, k, dim=1)
+        alls = torch.cat([best_s, cs], 1)
+        alli = torch.cat([best_i, ci + c0], 1)
+        o = torch.topk(alls, k, dim=1)
+        best_s, best_i = o.values, torch.gather(alli, 1, o.indices)
+    ex = best_i.cpu().numpy()
+    got = idx.to(torch.int64).cpu().numpy()
+    return float(np.mean([len(set(ex[i]) & set(got[i])) / k for i in range(nq)]))
+
+
 def bench_search(args):
     import torch
 
@@ -394,6 +411,7 @@ def bench_search(args):
 
     q_ms = timed(quantize)
     t_ms = timed(topk)
+    recall = search_recall(torch, x, q, idx.view(nq, k), k)
     pairs = nq * n
     q_flops = n * 4.0 * d * d                      # Pi x and S' r': 2 d^2 each
     t_flops = pairs * 3.0 * d                      # 2d (MSE dot) + d (signed QJL sum) per pair
@@ -433,6 +451,9 @@ def bench_search(args):
         "quantize": {"ms": q_ms, "vectors_per_s": n / (q_ms * 1e-3),
                      "hbm_gbs": q_bytes / (q_ms * 1e-3) / 1e9},
         "topk": {"ms": t_ms, "scores_per_s": pairs / (t_ms * 1e-3), "hbm_gbs": t_bytes / (t_ms * 1e-3) / 1e9},
+        "recall_at_k": {"value": recall, "k": k, "queries": nq,
+                        "note": "mean overlap of the returned top-k with the exact top-k of the float32 "
+                                "inner products (chunked library GEMM), after the timed region"},
     }
     with_measured_peak(result["roofline"], measured_gemm_tflops(torch, torch.float16),
                        "8192^3 fp16 library GEMM in this run")
