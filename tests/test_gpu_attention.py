@@ -116,6 +116,9 @@ def _oracle_parts(stk, stv, d, q, q_bf16, ck, nk, gk, cv, nv, groups, G, T, mode
     (256, 2, 3, 4, 513, False, tq.TQ_EST_PROD, ""),
     (128, 4, 3, 4, 700, True, tq.TQ_EST_PROD, "sphere+orth"),
     (128, 2, 3, 8, 777, False, tq.TQ_EST_PROD, ""),
+    (128, 3, 2, 12, 1333, True, tq.TQ_EST_PROD, ""),
+    (128, 4, 4, 4, 256, False, tq.TQ_EST_MSE, ""),
+    (128, 2, 4, 4, 65, True, tq.TQ_EST_PROD, ""),
     (192, 3, 4, 2, 333, True, tq.TQ_EST_PROD, "sphere+orth")])
 def test_attention_parity(d, b_k, b_v, G, T, q_bf16, mode, variant):
     groups = 3
