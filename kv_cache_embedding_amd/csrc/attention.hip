@@ -2,7 +2,8 @@
 // quantizer, values the MSE quantizer alone ([review, problem statement]: the two
 // quantizers; [news, KV-cache paragraph]: KV caches compressed to about 3 bits):
 //   o[g][h] = sum_t softmax_t(scale * l[g][h][t]) * nu_t Pi_v^T chat_t,
-// with l the unbiased logit estimate of the keys (the scoring kernels write it).  Pi_v^T is
+// with l the unbiased logit estimate of the keys (the scoring kernels write it, or, for the
+// d = 128 scorer's shapes, the block kernel computes it).  Pi_v^T is
 // linear, so the weighted sum runs in the values' rotated coordinates and one inverse
 // rotation per head finishes it:  o = Pi_v^T a,  a = sum_t p_t nu_t chat_t / sum_t p_t.
 //
