@@ -371,11 +371,13 @@ size_t tq_attention_ws_bytes(int d, int b_k, int64_t groups, int64_t G, int64_t 
  *                  nu_v [groups][T] from tq_quantize_mse
  *   q     [groups][G][d] float32 or bfloat16; scale: multiplies the logits (e.g. 1/sqrt(d))
  *   out   [groups][G][d] float32, 16-byte aligned
- *   ws    tq_attention_ws_bytes(d, b_k, groups, G, T) bytes, 256-aligned, scratch (logits,
- *         the scoring workspace and per-256-key-block partial sums)
+ *   ws    tq_attention_ws_bytes(d, b_k, groups, G, T) bytes, 256-aligned, scratch (the
+ *         scoring workspace, per-256-key-block partial sums and, for the shapes below that
+ *         score into memory, the logits)
  * With d = 128 and G a multiple of 4 the block kernel computes each 256-key block's logits
  * itself from the query operands (the same integer arithmetic as tq_score_ip, so the same
- * logits) and no logits pass through memory; other shapes score into ws first.
+ * logits) and no logits pass through memory or the workspace; other shapes score into ws
+ * first.
  * Errors: TQ_EINVAL (T = 0 with groups * G > 0, non-finite scale, ...), TQ_EUNSUPPORTED,
  *         TQ_EWORKSPACE, TQ_EHIP.
  */

@@ -808,9 +808,14 @@ int tq_attention_split(const void* params_k0, const void* params_k1, const void*
   return ok();
 }
 
+// Logits region of tq_attention's workspace: none where the block kernel scores its own keys.
+static size_t attention_logit_bytes(int d, int64_t groups, int64_t G, int64_t T) {
+  return score_uses_d128(d, G) ? 0 : tq::align256(size_t(groups) * G * T * 4);
+}
+
 size_t tq_attention_ws_bytes(int d, int b_k, int64_t groups, int64_t G, int64_t T) {
   if (!valid_shape(d, b_k) || groups < 0 || G < 0 || T < 0) return 0;
-  return tq::align256(size_t(groups) * G * T * 4) + tq_score_ws_bytes(d, b_k, groups, G, T) +
+  return attention_logit_bytes(d, groups, G, T) + tq_score_ws_bytes(d, b_k, groups, G, T) +
          tq::align256(tq::attention_part_bytes(d, groups, G, T));
 }
 
@@ -839,8 +844,8 @@ int tq_attention(const void* params_k, const void* params_v, int d, int b_k, int
   const size_t need = tq_attention_ws_bytes(d, b_k, groups, G, T);
   if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   unsigned char* w = static_cast<unsigned char*>(ws);
-  float* logits = reinterpret_cast<float*>(w);
-  void* sws = w + tq::align256(size_t(groups) * G * T * 4);
+  float* logits = reinterpret_cast<float*>(w);   // unused (size 0) on the fused path
+  void* sws = w + attention_logit_bytes(d, groups, G, T);
   void* part = static_cast<unsigned char*>(sws) + tq_score_ws_bytes(d, b_k, groups, G, T);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;

@@ -188,7 +188,12 @@ def test_invalid_arguments_return_status_without_launch(lib):
     assert att(100, 0.1, 7, 1 << 30) == tq.TQ_EINVAL
     assert att(100, 0.1, 0, 256) == tq.TQ_EWORKSPACE
     assert att(100, 0.1, 0, 0, groups=0) == tq.TQ_OK
-    assert tq.tq_attention_ws_bytes(128, 4, 2, 4, 100) >= 2 * 4 * 100 * 4 + tq.tq_score_ws_bytes(128, 4, 2, 4, 100)
+    # d = 128 with G a multiple of 4: the block kernel scores its own keys, no logits region;
+    # other shapes hold the logits too
+    assert tq.tq_attention_ws_bytes(128, 4, 2, 4, 100) > tq.tq_score_ws_bytes(128, 4, 2, 4, 100)
+    assert (tq.tq_attention_ws_bytes(128, 4, 2, 5, 100) - tq.tq_score_ws_bytes(128, 4, 2, 5, 100)
+            >= 2 * 5 * 100 * 4 + (tq.tq_attention_ws_bytes(128, 4, 2, 4, 100) - tq.tq_score_ws_bytes(128, 4, 2, 4, 100)))
+    assert tq.tq_attention_ws_bytes(64, 4, 2, 4, 100) >= 2 * 4 * 100 * 4 + tq.tq_score_ws_bytes(64, 4, 2, 4, 100)
     # append: pos outside [0, cap), bad mode, small workspace, gamma needed for keys, no groups
     def app(pos, cap=16, mode=0, ws_bytes=1 << 20, gamma=fake, groups=8):
         return lib.tq_append(fake, 128, 4, mode, fake, 1, groups, cap, pos, fake, fake, gamma, fake,
