@@ -1056,7 +1056,7 @@ def bench_kv(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     run = {"embedding_search": bench_search, "decode_attention": bench_attention,
