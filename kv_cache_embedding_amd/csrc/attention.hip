@@ -165,23 +165,21 @@ __device__ __forceinline__ void value_block(const BlockGroup& bg, const KeyOps& 
   const bool valid = t < T;
   const int W = d / 32;
 
-  // the lane's key's plane words of one chunk (zeros past the end)
+  // the lane's key's plane words of one chunk; lanes past the end read the last key's words
+  // (their weights are zero, so their bits add nothing), which keeps the loads unconditional
   uint32_t pw[NG][BV];
+  const long tc = valid ? t : T - 1;
   auto load_words = [&](int c0) {
-    if (valid) {
-      const uint32_t* kc = vcodes + (size_t(g * T + t) * W + c0 / 32) * BV;
+    const uint32_t* kc = vcodes + (size_t(g * T + tc) * W + c0 / 32) * BV;
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg)
+    for (int gg = 0; gg < NG; ++gg)
 #pragma unroll
-        for (int p = 0; p < BV; ++p) pw[gg][p] = kc[gg * BV + p];
-    } else {
-#pragma unroll
-      for (int gg = 0; gg < NG; ++gg)
-#pragma unroll
-        for (int p = 0; p < BV; ++p) pw[gg][p] = 0u;
-    }
+      for (int p = 0; p < BV; ++p) pw[gg][p] = kc[gg * BV + p];
   };
-  load_words(0);
+  // loads complete in issue order, so the operands needed first are loaded first: with logits
+  // from memory, the value words (their latency overlaps the softmax prologue); when the block
+  // scores its keys, the key words (the value words follow them, below)
+  if constexpr (KBITS == 0) load_words(0);
 
   float e[NE];
 #pragma unroll
@@ -256,37 +254,37 @@ __device__ __forceinline__ void value_block(const BlockGroup& bg, const KeyOps& 
     uint32_t kw[4][KBITS];
     float nk[4], gk[4], nv[4];
     bool ok[4];
+    // keys past the end read the last key (their logits are replaced by -inf below), so that
+    // no load sits under a branch
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const long key = tw0 + 16 * u + (lane & 15);
       ok[u] = key < T;
-      if (ok[u]) {
-        const uint32_t* src = kc + (size_t(key) * 4 + hs) * KBITS;
-        if constexpr (KBITS == 4) {
-          const uint4 v = *reinterpret_cast<const uint4*>(src);
-          kw[u][0] = v.x; kw[u][1] = v.y; kw[u][2] = v.z; kw[u][3] = v.w;
-        } else if constexpr (KBITS == 2) {
-          const uint2 v = *reinterpret_cast<const uint2*>(src);
-          kw[u][0] = v.x; kw[u][1] = v.y;
-        } else {
-#pragma unroll
-          for (int p = 0; p < KBITS; ++p) kw[u][p] = src[p];
-        }
-        nk[u] = ko.nu[g * T + key];
-        gk[u] = PROD ? ko.gamma[g * T + key] : 0.f;
-        nv[u] = vnu[g * T + key];
+      const long kr = ok[u] ? key : T - 1;
+      const uint32_t* src = kc + (size_t(kr) * 4 + hs) * KBITS;
+      if constexpr (KBITS == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        kw[u][0] = v.x; kw[u][1] = v.y; kw[u][2] = v.z; kw[u][3] = v.w;
+      } else if constexpr (KBITS == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        kw[u][0] = v.x; kw[u][1] = v.y;
       } else {
 #pragma unroll
-        for (int p = 0; p < KBITS; ++p) kw[u][p] = 0u;
-        nk[u] = 0.f;
-        gk[u] = 0.f;
-        nv[u] = 0.f;
+        for (int p = 0; p < KBITS; ++p) kw[u][p] = src[p];
       }
+      nk[u] = ko.nu[g * T + kr];
+      gk[u] = PROD ? ko.gamma[g * T + kr] : 0.f;
+      nv[u] = vnu[g * T + kr];
     }
+    load_words(0);   // in flight while the logits and the softmax are formed
+    // every load is issued before the first use (the scheduler would otherwise move the later
+    // tiles' loads down to their uses, one round trip each)
+    __builtin_amdgcn_sched_barrier(0);
     float l[4], mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      l[u] = ok[u] ? scale * score_tile_logit<KBITS, PROD>(QA, cst, kw[u], nk[u], gk[u]) : -INFINITY;
+      const float lv = scale * score_tile_logit<KBITS, PROD>(QA, cst, kw[u], nk[u], gk[u]);
+      l[u] = ok[u] ? lv : -INFINITY;
       mx = fmaxf(mx, l[u]);
     }
     mx = row_max_dpp(mx);
