@@ -25,8 +25,13 @@
 namespace tq {
 namespace {
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int D = 128;
 constexpr int G = 4;
+constexpr int RSRC_WORD3 = 0x00020000;   // raw (untyped) buffer resource, gfx9 family
 // Bytes in flight: each wave keeps UNR key tiles of loads outstanding, and the key ranges
 // are sized for WAVES_PER_CU waves per compute unit (both chosen by measurement on the
 // long-context workload: 4 / 16 -> 8 / 32 took the scan from 280 to 258 us).
@@ -170,7 +175,12 @@ __global__ __launch_bounds__(QP_THREADS) void score_qprep_kernel(const unsigned 
 }
 
 // --------------------------------------------------------------------------- scoring
-template <int BITS, bool PROD>
+// BUF: the group's codes, nu, gamma and its quad's logits are addressed through buffer
+// resources bounded by their arrays (byte offsets within 2^31, checked by the host): loads
+// past the last key read zeros and stores past it are dropped, so no access sits under a
+// branch (a branch around the store makes the compiler wait for every load in flight before
+// it: 8.0 against 9.1 us per decode-layer scan).  Without BUF, 64-bit addresses and guards.
+template <int BITS, bool PROD, bool BUF>
 __global__ __launch_bounds__(256) void score_kernel(const uint32_t* __restrict__ codes,
                                                      const float* __restrict__ nu,
                                                      const float* __restrict__ gamma,
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(256) void score_kernel(const uint32_t* __restrict__
   constexpr int NW = score_words(BITS);
   constexpr int NWU = PROD ? NW : NW - 1;     // MSE-only skips the sign plane
   const int lane = threadIdx.x & 63;
-  const long range = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const long range = long(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   if (range >= total_ranges) return;
   const long g = range / ranges_per_group;    // virtual group: key group g / qpg, quad g % qpg
   const long kg = g / qpg;
@@ -200,6 +210,47 @@ __global__ __launch_bounds__(256) void score_kernel(const uint32_t* __restrict__
   const uint32_t* gcodes = codes + size_t(kg) * T * (D / 32) * BITS;
   const float* gnu = nu + size_t(kg) * T;
   const float* ggm = gamma + size_t(kg) * T;
+  if constexpr (BUF) {
+    // (ranges hold a multiple of UNR tiles, so a tile past t1 is past the group's last key)
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(gcodes), 0, int(T * (D / 32) * BITS * 4), RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(gnu), 0, int(T * 4),
+                                                                        RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ggm), 0, int(T * 4),
+                                                                        RSRC_WORD3);
+    // the quad's G rows of logits, [head][key]; a key past the end stores past the resource
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(logits + size_t(g) * G * T, 0,
+                                                                        int(G * T * 4), RSRC_WORD3);
+    for (long tb = t0; tb < t1; tb += UNR) {
+      uint32_t w[UNR][BITS];
+      float nk[UNR], gk[UNR];
+      int key[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        key[u] = int((tb + u) * 16) + (lane & 15);
+        const int off = (key[u] * (D / 32) + grp) * BITS * 4;
+        if constexpr (BITS == 4) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(crs, off, 0, 0);
+          w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2]; w[u][3] = v[3];
+        } else if constexpr (BITS == 3) {
+          const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(crs, off, 0, 0);
+          w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2];
+        } else {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(crs, off, 0, 0);
+          w[u][0] = v[0]; w[u][1] = v[1];
+        }
+        nk[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(nrs, key[u] * 4, 0, 0));
+        gk[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, key[u] * 4, 0, 0));
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const float l = score_tile_logit<BITS, PROD>(A, cst, w[u], nk[u], gk[u]);
+        const int oo = key[u] < T ? (h * int(T) + key[u]) * 4 : int(G * T * 4);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), ors, oo, 0, 0);
+      }
+    }
+    return;
+  }
   float* out = logits + (size_t(g) * G + h) * T;
 
   for (long tb = t0; tb < t1; tb += UNR) {
@@ -262,14 +313,20 @@ hipError_t launch_b(const void* params, const void* q, int q_dtype, const uint32
   const long rpg = (tiles_per_group + tpr - 1) / tpr;
   const long total_ranges = long(groups) * rpg;
   const unsigned blocks = unsigned((total_ranges + 3) / 4);
-  if (mode == 0)
-    hipLaunchKernelGGL((score_kernel<BITS, true>), dim3(blocks), dim3(256), 0, s, codes, nu, gamma,
-                       static_cast<const unsigned char*>(ws), logits, long(T), qpg, tiles_per_group,
-                       rpg, tpr, total_ranges);
-  else
-    hipLaunchKernelGGL((score_kernel<BITS, false>), dim3(blocks), dim3(256), 0, s, codes, nu, gamma,
-                       static_cast<const unsigned char*>(ws), logits, long(T), qpg, tiles_per_group,
-                       rpg, tpr, total_ranges);
+  // buffer addressing needs every byte offset of a group's codes and of a quad's logits (keys
+  // padded to whole tiles) within 2^31
+  const int64_t Tp = tiles_per_group * 16;
+  const bool buf = Tp * (D / 32) * BITS * 4 < (int64_t(1) << 31) && Tp * G * 4 < (int64_t(1) << 31);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, codes, nu, gamma,
+                       static_cast<const unsigned char*>(ws), logits, long(T), qpg, tiles_per_group, rpg,
+                       tpr, total_ranges);
+  };
+  if (mode == 0) {
+    if (buf) go(score_kernel<BITS, true, true>); else go(score_kernel<BITS, true, false>);
+  } else {
+    if (buf) go(score_kernel<BITS, false, true>); else go(score_kernel<BITS, false, false>);
+  }
   return hipGetLastError();
 }
 
