@@ -180,8 +180,13 @@ __global__ __launch_bounds__(QP_THREADS) void score_qprep_kernel(const unsigned 
 // past the last key read zeros and stores past it are dropped, so no access sits under a
 // branch (a branch around the store makes the compiler wait for every load in flight before
 // it: 8.0 against 9.1 us per decode-layer scan).  Without BUF, 64-bit addresses and guards.
+// Waves per SIMD that the scan keeps resident (the register budget): without branches
+// between the tiles of an iteration the scheduler would hold all their MFMA accumulators at
+// once and halve the occupancy of the narrower codes.
+constexpr int scan_waves_per_simd(int bits) { return bits == 2 ? 6 : bits == 3 ? 5 : 4; }
+
 template <int BITS, bool PROD, bool BUF>
-__global__ __launch_bounds__(256) void score_kernel(const uint32_t* __restrict__ codes,
+__global__ __launch_bounds__(256, scan_waves_per_simd(BITS)) void score_kernel(const uint32_t* __restrict__ codes,
                                                      const float* __restrict__ nu,
                                                      const float* __restrict__ gamma,
                                                      const unsigned char* __restrict__ ws,
