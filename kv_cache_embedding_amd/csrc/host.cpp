@@ -687,9 +687,15 @@ int tq_quantize_split(const void* params0, const void* params1, int d, int d0, i
 }
 
 size_t tq_score_split_ws_bytes(int d, int d0, int b0, int b1, int64_t groups, int64_t G, int64_t T) {
-  (void)T;
   if (!valid_split(d, d0, b0, b1) || groups < 0 || G < 0) return 0;
-  return tq::align256(tq::score_generic_split_ws_bytes(d0, d - d0, groups, G));
+  size_t need = tq::align256(tq::score_generic_split_ws_bytes(d0, d - d0, groups, G));
+  // the larger of the two paths' needs, so that a size taken for one T also serves another
+  if (d == 128 && d0 == 64 && G % 4 == 0) {
+    const size_t n128 = tq::score_split_d128_ws_bytes(b0, b1, groups, G);
+    if (n128 > need) need = n128;
+  }
+  (void)T;
+  return need;
 }
 
 int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
@@ -710,15 +716,18 @@ int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, i
   if (!aligned(params0, 256) || !aligned(params1, 256) || !aligned(ws, 256) || !aligned(codes0, 16) ||
       !aligned(codes1, 16) || !aligned(q, 4) || !aligned(logits, 4))
     return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; codes 16 B)");
-  if (!tq::score_generic_grid_fits(groups, G, T))
+  const bool d128 = tq::score_split_d128_applies(d, d0, b0, b1, G, T);
+  if (!d128 && !tq::score_generic_grid_fits(groups, G, T))
     return fail(TQ_EUNSUPPORTED, "tq_score_ip_split: groups * G * T too large for one launch");
   const size_t need = tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, T);
   if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // one query prep launch for both groups, one scoring pass summing their estimates
-  const hipError_t e = tq::launch_score_generic_split(params0, params1, d0, d - d0, b0, b1, q, q_dtype,
-                                                      codes0, nu0, gamma0, codes1, nu1, gamma1, groups,
-                                                      G, T, mode, logits, ws, s);
+  const hipError_t e =
+      d128 ? tq::launch_score_split_d128(params0, params1, b0, b1, q, q_dtype, codes0, nu0, gamma0, codes1,
+                                         nu1, gamma1, groups, G, T, mode, logits, ws, s)
+           : tq::launch_score_generic_split(params0, params1, d0, d - d0, b0, b1, q, q_dtype, codes0, nu0,
+                                            gamma0, codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s);
   if (e != hipSuccess) return hip_fail(e, "tq_score_ip_split launch");
   return ok();
 }
@@ -785,7 +794,8 @@ int tq_attention_split(const void* params_k0, const void* params_k1, const void*
       !aligned(params_v1, 256) || !aligned(ws, 256) || !aligned(codes_k0, 16) || !aligned(codes_k1, 16) ||
       !aligned(codes_v0, 4) || !aligned(codes_v1, 4) || !aligned(q, 4) || !aligned(out, 16))
     return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; key codes, out 16 B)");
-  if (!tq::score_generic_grid_fits(groups, G, T) || !tq::attention_grid_fits(groups, G, T))
+  if ((!tq::score_split_d128_applies(d, d0, bk0, bk1, G, T) && !tq::score_generic_grid_fits(groups, G, T)) ||
+      !tq::attention_grid_fits(groups, G, T))
     return fail(TQ_EUNSUPPORTED, "tq_attention_split: groups * G * T too large for one launch");
   const size_t need = tq_attention_split_ws_bytes(d, d0, bk0, bk1, groups, G, T);
   if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

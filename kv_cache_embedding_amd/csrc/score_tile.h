@@ -11,14 +11,13 @@ namespace tq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Logit of the pair this lane holds in a 16-key tile: query head lane / 16 of the quad and
-// key lane % 16.  A: the 2 NW query operand registers of the quad (2 NWU used); cst: the
-// epilogue constants of the lane's head; w: the key's BITS plane words of coordinate group
-// lane / 16; nk, gk: the key's nu and gamma.  PROD adds the QJL term; without it the MSE
-// estimate alone.  Keys past the end pass zero words and nu = 0 and get 0.
+// Masked digit sums of the pair this lane holds in a 16-key tile: query head lane / 16 of the
+// quad and key lane % 16.  A: the 2 NW query operand registers of the quad (2 NWU used); w: the
+// key's BITS plane words of coordinate group lane / 16.  Registers 0, 1 of the result hold the
+// MSE digit sums (hi, lo), 2, 3 the QJL ones; PROD adds the QJL words, without it the MSE
+// estimate alone.
 template <int BITS, bool PROD>
-__device__ __forceinline__ float score_tile_logit(const v4i* A, const float4& cst, const uint32_t* w,
-                                                  float nk, float gk) {
+__device__ __forceinline__ v4i score_tile_sums(const v4i* A, const uint32_t* w) {
   constexpr int NW = score_words(BITS);
   constexpr int NWU = PROD ? NW : NW - 1;     // MSE-only skips the sign plane
   uint32_t word[NW];
@@ -42,6 +41,13 @@ __device__ __forceinline__ float score_tile_logit(const v4i* A, const float4& cs
                     int(s6 & 0x02020202u)};
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * i + 1], b1, acc, 0, 0, 0);
   }
+  return acc;
+}
+
+// The estimate from the digit sums: cst holds the epilogue constants of the lane's head
+// (l = nu (s_mse cst.x - cst.y + gamma (s_qjl cst.z - cst.w))); nk, gk: the key's nu and gamma.
+template <bool PROD>
+__device__ __forceinline__ float score_tile_estimate(const v4i& acc, const float4& cst, float nk, float gk) {
   const int ai = acc[0] * 128 + acc[1];
   float l = fmaf(float(ai), cst.x, -cst.y);
   if constexpr (PROD) {
@@ -49,6 +55,14 @@ __device__ __forceinline__ float score_tile_logit(const v4i* A, const float4& cs
     l = fmaf(gk, fmaf(float(bi), cst.z, -cst.w), l);
   }
   return l * nk;
+}
+
+// Logit of the pair this lane holds in a 16-key tile (see score_tile_sums); keys past the end
+// pass zero words and nu = 0 and get 0.
+template <int BITS, bool PROD>
+__device__ __forceinline__ float score_tile_logit(const v4i* A, const float4& cst, const uint32_t* w,
+                                                  float nk, float gk) {
+  return score_tile_estimate<PROD>(score_tile_sums<BITS, PROD>(A, w), cst, nk, gk);
 }
 
 }  // namespace tq

@@ -249,7 +249,11 @@ def test_split_calls_validate_without_launch(lib):
     assert lib.tq_quantize_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, 0, None, None, None, None, None,
                                  None, None) == tq.TQ_OK                       # n = 0: nothing to do
     need = lib.tq_score_split_ws_bytes(128, 64, 3, 2, 2, 4, 100)
-    assert need == 2 * (2 * 4 * 2 * 64 * 4)      # both groups' Pi q, S q operands side by side
+    # the larger of the general path's need (both groups' Pi q, S q operands side by side) and the
+    # integer scorer's (per quad of heads: 3 + 2 operand registers of 64 lanes x 16 bytes and 8
+    # float4 constants)
+    assert need == max(2 * (2 * 4 * 2 * 64 * 4), 2 * ((3 + 2) * 64 * 16 + 8 * 16))
+    assert lib.tq_score_split_ws_bytes(128, 64, 3, 2, 2, 3, 100) == 2 * (2 * 3 * 2 * 64 * 4)   # G % 4 != 0
     assert lib.tq_score_ip_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, P, P, P, P, P, P, 2, 4, 100,
                                  tq.TQ_EST_PROD, P, P, need - 256, None) == tq.TQ_EWORKSPACE
     assert lib.tq_score_ip_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, P, P, P, P, P, P, 2, 4, 100,
