@@ -18,7 +18,9 @@ scan over the codes); b = 4 unless --bits says otherwise.
 --workload decode_attention: one tq_attention decode step at the decode-layer shapes.
 --workload fractional_kv: decode_layer's keys and queries at a fractional rate (--rate 2.5
 or 3.5 bits per channel): channels 0..63 at the higher b and 64..127 at the lower one, each
-group its own TurboQuant instance; a step is tq_quantize_split + tq_score_ip_split.
+group its own TurboQuant instance; a step is tq_quantize_split + the split scoring
+(tq_score_split_prepare on a second stream beside the quantize, then
+tq_score_ip_split_prepared), as the KV workloads split tq_score_ip.
 --workload ubench: achievable HBM and MFMA rates of the GPU.
 
 Prints one JSON line.  Kernel durations come from HIP events recorded on the stream the
@@ -702,17 +704,48 @@ def bench_fractional(args):
         tq.tq_quantize_split(params[0], params[1], d, d0, b0, b1, xs[r], g0[0][r], g0[1][r], g0[2][r],
                              g1[0][r], g1[1][r], g1[2][r])
 
-    def score(r):
+    def score(r):       # the whole scoring call: both groups' query prep + one scan
         tq.tq_score_ip_split(params[0], params[1], d, d0, b0, b1, q, g0[0][r], g0[1][r], g0[2][r],
                              g1[0][r], g1[1][r], g1[2][r], groups, G, T, tq.TQ_EST_PROD, logits[r], ws)
+
+    def prepare():      # the query prep alone (depends on q only)
+        tq.tq_score_split_prepare(params[0], params[1], d, d0, b0, b1, q, groups, G, ws)
+
+    def scan(r):        # the scan against the prepared query operands
+        tq.tq_score_ip_split_prepared(params[0], params[1], d, d0, b0, b1, g0[0][r], g0[1][r], g0[2][r],
+                                      g1[0][r], g1[1][r], g1[2][r], groups, G, T, tq.TQ_EST_PROD, logits[r], ws)
 
     for i in range(max(args.warmup, 1)):
         quantize(i % R)
         score(i % R)
     torch.cuda.synchronize()
 
+    # steps as in the KV workloads: serial (the query prep on a second stream beside the quantize
+    # of batch r, then the scan of batch r) and pipelined (batch r quantized while the second
+    # stream prepares the queries and scans batch r - 1)
+    side = torch.cuda.Stream()
+
+    def serial(r):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            prepare()
+        quantize(r)
+        torch.cuda.current_stream().wait_stream(side)
+        scan(r)
+
+    def pipe(r):
+        side.wait_stream(torch.cuda.current_stream())
+        quantize(r)
+        with torch.cuda.stream(side):
+            prepare()
+            scan((r - 1) % R)
+        torch.cuda.current_stream().wait_stream(side)
+
     K = args.steps
-    ms_step = time_steps(torch, lambda r: (quantize(r), score(r)), R, K)
+    plain_ms = time_steps(torch, lambda r: (quantize(r), score(r)), R, K)
+    serial_ms = time_steps(torch, serial, R, K)
+    pipe_ms = time_steps(torch, pipe, R, K)
+    ms_step = min(serial_ms, pipe_ms)
 
     q_ms = time_per_launch(torch, quantize, R, K)
     s_ms = time_per_launch(torch, score, R, K)
@@ -804,6 +837,11 @@ def bench_fractional(args):
         "roofline_other": other,
         "quantize": {"ms": q_ms, "vectors_per_s": n / (q_ms * 1e-3), "hbm_gbs": q_gbs},
         "score": {"ms": s_ms, "logits_per_s": n_logits / (s_ms * 1e-3), "hbm_gbs": s_gbs},
+        "steps_timing": {"serial_ms": serial_ms, "pipelined_ms": pipe_ms, "one_stream_ms": plain_ms,
+                         "note": "ms_per_step is the faster of: serial (both groups' query prep on a second "
+                                 "stream beside the quantize of batch i, then the scan of batch i) and "
+                                 "pipelined (batch i's quantize beside the query prep and scan of batch i-1 "
+                                 "on a second stream); one_stream: quantize then tq_score_ip_split"},
         "value_quantize": {"ms": vq_ms, "vectors_per_s": n / (vq_ms * 1e-3),
                            "index_bits": [[d0, bv[0] - 1], [d - d0, bv[1] - 1]]},
         "attention": {"ms": a_ms, "pairs_per_s": n_logits / (a_ms * 1e-3),

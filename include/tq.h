@@ -293,8 +293,10 @@ int tq_score_ip_noalloc(const void* params, int d, int b, const void* q, int q_d
  * (the two rotations and QJL matrices as block-diagonal operands); other splits run the
  * tiled encoder once per group.  Scoring runs one query-prep launch for both groups and one
  * pass over the keys that adds the two groups' estimates in registers and stores each logit
- * once; tq_score_split_ws_bytes covers both groups' query operands.  Channels are read in
- * place (rows d apart).
+ * once: for a 64 + 64 split of d = 128 with G a multiple of 4 the integer MFMA scan of the
+ * d = 128 scorer (query values rounded to per-row digits, as tq_score_ip rounds them there),
+ * otherwise the float32 general path; tq_score_split_ws_bytes covers both paths' query
+ * operands.  Channels are read in place (rows d apart).
  *
  * tq_quantize_split — encode x [n][d] (x_dtype as for tq_quantize) into
  *   codes0 [n][d0/32][b0], nu0, gamma0 [n]     (channels 0 .. d0-1, params0)
@@ -320,6 +322,30 @@ int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, i
                       const float* gamma0, const uint32_t* codes1, const float* nu1,
                       const float* gamma1, int64_t groups, int64_t G, int64_t T, int mode,
                       float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tq_score_split_prepare, tq_score_ip_split_prepared — tq_score_ip_split in its two phases,
+ * as tq_score_prepare and tq_score_ip_prepared split tq_score_ip: the query preparation of
+ * both channel groups (which depends only on q) can be issued ahead of, or beside, the key
+ * encoding.  tq_score_ip_split(..., ws) gives the same logits as tq_score_split_prepare
+ * followed by tq_score_ip_split_prepared on the same stream, wherever tq_score_ip_split
+ * takes the path that the shape selects (every T below 2^26 keys per group).  The prepared
+ * ws must come from tq_score_split_prepare with the same params0, params1, d, d0, b0, b1,
+ * groups and G, must not be written in between, and serves any number of scoring calls (any
+ * T, mode and key caches).  ws_bytes >= tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, T)
+ * (which does not depend on T).
+ * Errors: as tq_score_ip_split; TQ_EUNSUPPORTED also where T is too large for the scan that
+ * the prepared operands belong to (64 + 64 splits of d = 128 with G a multiple of 4: T below
+ * 2^26; tq_score_ip_split then takes the general path).
+ */
+int tq_score_split_prepare(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                           const void* q, int q_dtype, int64_t groups, int64_t G, void* ws, size_t ws_bytes,
+                           void* stream);
+int tq_score_ip_split_prepared(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                               const uint32_t* codes0, const float* nu0, const float* gamma0,
+                               const uint32_t* codes1, const float* nu1, const float* gamma1, int64_t groups,
+                               int64_t G, int64_t T, int mode, float* logits, const void* ws, size_t ws_bytes,
+                               void* stream);
 
 /*
  * tq_quantize_mse_split — the MSE quantizer alone (as tq_quantize_mse) on the two channel

@@ -61,6 +61,9 @@ def load_library():
                                    I64, ctypes.c_float, I, P, P, SZ, P]),
         "tq_score_ip_split": (I, [P, P, I, I, I, I, P, I, P, P, P, P, P, P, I64, I64, I64, I, P, P, SZ,
                                   P]),
+        "tq_score_split_prepare": (I, [P, P, I, I, I, I, P, I, I64, I64, P, SZ, P]),
+        "tq_score_ip_split_prepared": (I, [P, P, I, I, I, I, P, P, P, P, P, P, I64, I64, I64, I, P, P, SZ,
+                                           P]),
         "tq_append_ws_bytes": (SZ, [I, I, I64]),
         "tq_append": (I, [P, I, I, I, P, I, I64, I64, I64, P, P, P, P, SZ, P]),
         "tq_attention_ws_bytes": (SZ, [I, I, I64, I64, I64]),
@@ -391,6 +394,39 @@ def tq_score_ip_split(params0, params1, d: int, d0: int, b0: int, b1: int, q, co
                                             _ptr(codes1), _ptr(nu1), _ptr(gamma1), groups, G, T,
                                             int(mode), _ptr(logits), _ptr(ws),
                                             ws.numel() * ws.element_size(), _stream(stream, q.device)))
+
+
+def tq_score_split_prepare(params0, params1, d: int, d0: int, b0: int, b1: int, q, groups: int, G: int,
+                           ws, stream=None):
+    """Both channel groups' query operands of q [groups][G][d] into ws, for tq_score_ip_split_prepared."""
+    for tname, t in (("q", q), ("ws", ws), ("params0", params0), ("params1", params1)):
+        _dev(t, tname)
+    if q.numel() < groups * G * d:
+        raise ValueError("q holds fewer than groups*G*d elements")
+    _check(load_library().tq_score_split_prepare(_ptr(params0), _ptr(params1), d, d0, b0, b1, _ptr(q),
+                                                 _dtype_code(q, "q"), groups, G, _ptr(ws),
+                                                 ws.numel() * ws.element_size(), _stream(stream, q.device)))
+
+
+def tq_score_ip_split_prepared(params0, params1, d: int, d0: int, b0: int, b1: int, codes0, nu0, gamma0,
+                               codes1, nu1, gamma1, groups: int, G: int, T: int, mode: int, logits, ws,
+                               stream=None):
+    """tq_score_ip_split's logits from the query operands tq_score_split_prepare left in ws."""
+    torch = _torch()
+    for tname, t in (("codes0", codes0), ("nu0", nu0), ("gamma0", gamma0), ("codes1", codes1), ("nu1", nu1),
+                     ("gamma1", gamma1), ("logits", logits), ("ws", ws), ("params0", params0),
+                     ("params1", params1)):
+        _dev(t, tname)
+    _need(codes0, "codes0", groups * T * (d0 // 32) * b0, torch.int32)
+    _need(codes1, "codes1", groups * T * ((d - d0) // 32) * b1, torch.int32)
+    for tname, t in (("nu0", nu0), ("gamma0", gamma0), ("nu1", nu1), ("gamma1", gamma1)):
+        _need(t, tname, groups * T, torch.float32)
+    _need(logits, "logits", groups * G * T, torch.float32)
+    _check(load_library().tq_score_ip_split_prepared(_ptr(params0), _ptr(params1), d, d0, b0, b1, _ptr(codes0),
+                                                     _ptr(nu0), _ptr(gamma0), _ptr(codes1), _ptr(nu1),
+                                                     _ptr(gamma1), groups, G, T, int(mode), _ptr(logits),
+                                                     _ptr(ws), ws.numel() * ws.element_size(),
+                                                     _stream(stream, codes0.device)))
 
 
 def tq_quantize_mse_split(params0, params1, d: int, d0: int, b0: int, b1: int, x, codes0, nu0, codes1,

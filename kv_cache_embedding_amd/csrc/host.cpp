@@ -732,6 +732,68 @@ int tq_score_ip_split(const void* params0, const void* params1, int d, int d0, i
   return ok();
 }
 
+int tq_score_split_prepare(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                           const void* q, int q_dtype, int64_t groups, int64_t G, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!valid_split(d, d0, b0, b1))
+    return fail(TQ_EINVAL, "unsupported split d=%d d0=%d b0=%d b1=%d", d, d0, b0, b1);
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "bad q_dtype %d", q_dtype);
+  if (groups < 0 || G < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0 || G == 0) return ok();
+  if (!params0 || !params1 || !q || !ws) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params0, 256) || !aligned(params1, 256) || !aligned(ws, 256) || !aligned(q, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B)");
+  // the path is chosen from the shape alone, as tq_score_ip_split_prepared chooses it
+  const bool d128 = tq::score_split_d128_shape(d, d0, b0, b1, G);
+  if (!d128 && !tq::score_generic_grid_fits(groups, G, 1))
+    return fail(TQ_EUNSUPPORTED, "tq_score_split_prepare: groups * G too large for one launch");
+  const size_t need = tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, 1);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      d128 ? tq::launch_score_split_d128(params0, params1, b0, b1, q, q_dtype, nullptr, nullptr, nullptr, nullptr,
+                                         nullptr, nullptr, groups, G, 1, TQ_EST_PROD, nullptr, ws, s,
+                                         tq::kScorePrep)
+           : tq::launch_score_generic_split(params0, params1, d0, d - d0, b0, b1, q, q_dtype, nullptr, nullptr,
+                                            nullptr, nullptr, nullptr, nullptr, groups, G, 1, TQ_EST_PROD,
+                                            nullptr, ws, s, tq::kScorePrep);
+  if (e != hipSuccess) return hip_fail(e, "tq_score_split_prepare launch");
+  return ok();
+}
+
+int tq_score_ip_split_prepared(const void* params0, const void* params1, int d, int d0, int b0, int b1,
+                               const uint32_t* codes0, const float* nu0, const float* gamma0,
+                               const uint32_t* codes1, const float* nu1, const float* gamma1, int64_t groups,
+                               int64_t G, int64_t T, int mode, float* logits, const void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (!valid_split(d, d0, b0, b1))
+    return fail(TQ_EINVAL, "unsupported split d=%d d0=%d b0=%d b1=%d", d, d0, b0, b1);
+  if (mode != TQ_EST_PROD && mode != TQ_EST_MSE) return fail(TQ_EINVAL, "bad mode %d", mode);
+  if (groups < 0 || G < 0 || T < 0) return fail(TQ_EINVAL, "negative size");
+  if (groups == 0 || G == 0 || T == 0) return ok();
+  if (T >= (int64_t(1) << 31)) return fail(TQ_EINVAL, "T must be < 2^31");
+  if (!params0 || !params1 || !codes0 || !nu0 || !gamma0 || !codes1 || !nu1 || !gamma1 || !logits || !ws)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(params0, 256) || !aligned(params1, 256) || !aligned(ws, 256) || !aligned(codes0, 16) ||
+      !aligned(codes1, 16) || !aligned(logits, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (params, ws 256 B; codes 16 B)");
+  const bool d128 = tq::score_split_d128_shape(d, d0, b0, b1, G);
+  if (d128 ? !tq::score_split_d128_applies(d, d0, b0, b1, G, T) : !tq::score_generic_grid_fits(groups, G, T))
+    return fail(TQ_EUNSUPPORTED, "tq_score_ip_split_prepared: T too large for the prepared operands' scan");
+  const size_t need = tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, T);
+  if (ws_bytes < need) return fail(TQ_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* w = const_cast<void*>(ws);
+  const hipError_t e =
+      d128 ? tq::launch_score_split_d128(params0, params1, b0, b1, nullptr, TQ_F32, codes0, nu0, gamma0, codes1,
+                                         nu1, gamma1, groups, G, T, mode, logits, w, s, tq::kScoreScan)
+           : tq::launch_score_generic_split(params0, params1, d0, d - d0, b0, b1, nullptr, TQ_F32, codes0, nu0,
+                                            gamma0, codes1, nu1, gamma1, groups, G, T, mode, logits, w, s,
+                                            tq::kScoreScan);
+  if (e != hipSuccess) return hip_fail(e, "tq_score_ip_split_prepared launch");
+  return ok();
+}
+
 int tq_quantize_mse_split(const void* params0, const void* params1, int d, int d0, int b0, int b1,
                           const void* x, int x_dtype, int64_t n, uint32_t* codes0, float* nu0,
                           uint32_t* codes1, float* nu1, void* stream) {

@@ -387,10 +387,11 @@ hipError_t launch_score_generic_split(const void* params0, const void* params1, 
                                       int b1, const void* q, int q_dtype, const uint32_t* codes0,
                                       const float* nu0, const float* gamma0, const uint32_t* codes1,
                                       const float* nu1, const float* gamma1, int64_t groups, int64_t G,
-                                      int64_t T, int mode, float* logits, void* ws, hipStream_t s) {
+                                      int64_t T, int mode, float* logits, void* ws, hipStream_t s,
+                                      int phases) {
   if (b1 < 2) return hipErrorInvalidValue;
   return launch_groups(params0, d0, b0, params1, d1, b1, q, q_dtype, long(d0) + d1, codes0, nu0,
-                       gamma0, codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s, kScoreBoth);
+                       gamma0, codes1, nu1, gamma1, groups, G, T, mode, logits, ws, s, phases);
 }
 
 }  // namespace tq

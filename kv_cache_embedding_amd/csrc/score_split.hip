@@ -307,15 +307,18 @@ template <int B0, int B1>
 hipError_t launch_bs(const void* params0, const void* params1, const void* q, int q_dtype,
                      const uint32_t* codes0, const float* nu0, const float* gamma0, const uint32_t* codes1,
                      const float* nu1, const float* gamma1, int64_t kv_groups, int64_t Gq, int64_t T, int mode,
-                     float* logits, void* ws, hipStream_t s) {
+                     float* logits, void* ws, hipStream_t s, int phases) {
   const Layout lay(DG, B0);   // the matrices' offsets do not depend on b
   const long qpg = long(Gq / G);
   const int64_t groups = kv_groups * qpg;
-  hipLaunchKernelGGL((split_qprep_kernel<B0, B1>), dim3(unsigned(2 * groups)), dim3(QP_THREADS), 0, s,
-                     static_cast<const unsigned char*>(params0), static_cast<const unsigned char*>(params1),
-                     lay.off_pi, lay.off_s, q, q_dtype == 0 ? 1 : 0, static_cast<unsigned char*>(ws));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (phases & kScorePrep) {
+    hipLaunchKernelGGL((split_qprep_kernel<B0, B1>), dim3(unsigned(2 * groups)), dim3(QP_THREADS), 0, s,
+                       static_cast<const unsigned char*>(params0), static_cast<const unsigned char*>(params1),
+                       lay.off_pi, lay.off_s, q, q_dtype == 0 ? 1 : 0, static_cast<unsigned char*>(ws));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(phases & kScoreScan)) return hipSuccess;
   const long tiles_per_group = (T + 15) / 16;
   const long total_tiles = long(groups) * tiles_per_group;
   long tpr = (total_tiles + long(device_cu_count()) * WAVES_PER_CU - 1) / (long(device_cu_count()) * WAVES_PER_CU);
@@ -338,25 +341,30 @@ template <int B0>
 hipError_t launch_b0(int b1, const void* params0, const void* params1, const void* q, int q_dtype,
                      const uint32_t* codes0, const float* nu0, const float* gamma0, const uint32_t* codes1,
                      const float* nu1, const float* gamma1, int64_t kv_groups, int64_t Gq, int64_t T, int mode,
-                     float* logits, void* ws, hipStream_t s) {
+                     float* logits, void* ws, hipStream_t s, int phases) {
   switch (b1) {
     case 2: return launch_bs<B0, 2>(params0, params1, q, q_dtype, codes0, nu0, gamma0, codes1, nu1, gamma1,
-                                     kv_groups, Gq, T, mode, logits, ws, s);
+                                     kv_groups, Gq, T, mode, logits, ws, s, phases);
     case 3: return launch_bs<B0, 3>(params0, params1, q, q_dtype, codes0, nu0, gamma0, codes1, nu1, gamma1,
-                                     kv_groups, Gq, T, mode, logits, ws, s);
+                                     kv_groups, Gq, T, mode, logits, ws, s, phases);
     case 4: return launch_bs<B0, 4>(params0, params1, q, q_dtype, codes0, nu0, gamma0, codes1, nu1, gamma1,
-                                     kv_groups, Gq, T, mode, logits, ws, s);
+                                     kv_groups, Gq, T, mode, logits, ws, s, phases);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
+bool score_split_d128_shape(int d, int d0, int b0, int b1, int64_t G) {
+  return d == 2 * DG && d0 == DG && G % 4 == 0 && b0 >= 2 && b0 <= 4 && b1 >= 2 && b1 <= 4;
+}
+
 bool score_split_d128_applies(int d, int d0, int b0, int b1, int64_t G, int64_t T) {
-  if (d != 2 * DG || d0 != DG || G % 4 != 0 || b0 < 2 || b0 > 4 || b1 < 2 || b1 > 4) return false;
-  // buffer byte offsets (keys padded to whole tiles) within 2^31
+  if (!score_split_d128_shape(d, d0, b0, b1, G)) return false;
+  // buffer byte offsets (keys padded to whole tiles) within 2^31: a key group's codes of up to
+  // 4 words per coordinate group, a quad's 4 rows of logits
   const int64_t tp = (T + 15) / 16 * 16;
-  return tp * 2 * 4 * 4 < (int64_t(1) << 31) && tp * G * 4 < (int64_t(1) << 31);
+  return tp * 2 * 4 * 4 < (int64_t(1) << 31) && tp * 4 * 4 < (int64_t(1) << 31);
 }
 
 size_t score_split_d128_ws_bytes(int b0, int b1, int64_t groups, int64_t G) {
@@ -367,14 +375,14 @@ hipError_t launch_score_split_d128(const void* params0, const void* params1, int
                                    int q_dtype, const uint32_t* codes0, const float* nu0, const float* gamma0,
                                    const uint32_t* codes1, const float* nu1, const float* gamma1,
                                    int64_t kv_groups, int64_t Gq, int64_t T, int mode, float* logits, void* ws,
-                                   hipStream_t s) {
+                                   hipStream_t s, int phases) {
   switch (b0) {
     case 2: return launch_b0<2>(b1, params0, params1, q, q_dtype, codes0, nu0, gamma0, codes1, nu1, gamma1,
-                                kv_groups, Gq, T, mode, logits, ws, s);
+                                kv_groups, Gq, T, mode, logits, ws, s, phases);
     case 3: return launch_b0<3>(b1, params0, params1, q, q_dtype, codes0, nu0, gamma0, codes1, nu1, gamma1,
-                                kv_groups, Gq, T, mode, logits, ws, s);
+                                kv_groups, Gq, T, mode, logits, ws, s, phases);
     case 4: return launch_b0<4>(b1, params0, params1, q, q_dtype, codes0, nu0, gamma0, codes1, nu1, gamma1,
-                                kv_groups, Gq, T, mode, logits, ws, s);
+                                kv_groups, Gq, T, mode, logits, ws, s, phases);
     default: return hipErrorInvalidValue;
   }
 }

@@ -114,17 +114,21 @@ hipError_t launch_score_generic_split(const void* params0, const void* params1, 
                                       int b1, const void* q, int q_dtype, const uint32_t* codes0,
                                       const float* nu0, const float* gamma0, const uint32_t* codes1,
                                       const float* nu1, const float* gamma1, int64_t groups, int64_t G,
-                                      int64_t T, int mode, float* logits, void* ws, hipStream_t s);
+                                      int64_t T, int mode, float* logits, void* ws, hipStream_t s,
+                                      int phases = kScoreBoth);
 size_t score_generic_split_ws_bytes(int d0, int d1, int64_t groups, int64_t G);
 // The 64 + 64 split of d = 128 with G a multiple of 4 on the d = 128 integer scorer: one query
 // prep launch writing both groups' operands, one scan summing the groups' estimates per key.
+// applies: the shape (d = 128, d0 = 64, G a multiple of 4, both b in 2..4) and T (buffer
+// offsets within 2^31); shape alone: what the query prep alone can decide.
+bool score_split_d128_shape(int d, int d0, int b0, int b1, int64_t G);
 bool score_split_d128_applies(int d, int d0, int b0, int b1, int64_t G, int64_t T);
 size_t score_split_d128_ws_bytes(int b0, int b1, int64_t groups, int64_t G);
 hipError_t launch_score_split_d128(const void* params0, const void* params1, int b0, int b1, const void* q,
                                    int q_dtype, const uint32_t* codes0, const float* nu0, const float* gamma0,
                                    const uint32_t* codes1, const float* nu1, const float* gamma1,
                                    int64_t groups, int64_t G, int64_t T, int mode, float* logits, void* ws,
-                                   hipStream_t s);
+                                   hipStream_t s, int phases = kScoreBoth);
 bool score_generic_grid_fits(int64_t groups, int64_t G, int64_t T);
 // The MSE stage alone (b-1 index planes and nu): d = 128 on the fused encoder without its
 // GEMM2, every other d on the tiled encoder's phase 1.

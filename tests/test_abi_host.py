@@ -258,3 +258,22 @@ def test_split_calls_validate_without_launch(lib):
                                  tq.TQ_EST_PROD, P, P, need - 256, None) == tq.TQ_EWORKSPACE
     assert lib.tq_score_ip_split(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, P, P, P, P, P, P, 2, 4, 100,
                                  7, P, P, need, None) == tq.TQ_EINVAL          # bad mode
+    # the two phases: the same validation, workspace and size limits, nothing launched
+    assert lib.tq_score_split_prepare(P, P, 128, 32, 3, 2, P, tq.TQ_BF16, 2, 4, P, need, None) == tq.TQ_EINVAL
+    assert lib.tq_score_split_prepare(P, P, 128, 64, 3, 2, P, 7, 2, 4, P, need, None) == tq.TQ_EINVAL
+    assert lib.tq_score_split_prepare(P, P, 128, 64, 3, 2, None, tq.TQ_BF16, 2, 4, P, need, None) == tq.TQ_EINVAL
+    assert lib.tq_score_split_prepare(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, 2, 4, P, need - 256,
+                                      None) == tq.TQ_EWORKSPACE
+    assert lib.tq_score_split_prepare(P, P, 128, 64, 3, 2, P, tq.TQ_BF16, 0, 4, None, 0, None) == tq.TQ_OK
+    assert lib.tq_score_ip_split_prepared(P, P, 128, 64, 3, 2, P, P, P, P, P, P, 2, 4, 100, 7, P, P, need,
+                                          None) == tq.TQ_EINVAL                # bad mode
+    assert lib.tq_score_ip_split_prepared(P, P, 128, 64, 3, 2, P, P, None, P, P, P, 2, 4, 100,
+                                          tq.TQ_EST_PROD, P, P, need, None) == tq.TQ_EINVAL
+    assert lib.tq_score_ip_split_prepared(P, P, 128, 64, 3, 2, P, P, P, P, P, P, 2, 4, 100, tq.TQ_EST_PROD,
+                                          P, P, need - 256, None) == tq.TQ_EWORKSPACE
+    assert lib.tq_score_ip_split_prepared(P, P, 128, 64, 3, 2, P, P, P, P, P, P, 2, 4, 0, tq.TQ_EST_PROD,
+                                          None, None, 0, None) == tq.TQ_OK     # T = 0: nothing to do
+    # operands prepared for the integer scan serve keys up to 2^26 per group (buffer offsets)
+    big = 1 << 26
+    assert lib.tq_score_ip_split_prepared(P, P, 128, 64, 3, 2, P, P, P, P, P, P, 1, 4, big, tq.TQ_EST_PROD,
+                                          P, P, need, None) == tq.TQ_EUNSUPPORTED

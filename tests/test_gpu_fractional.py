@@ -146,6 +146,38 @@ def test_score_split_parity(d, d0, b0, b1, G, T, q_bf16):
             assert np.max(np.abs(lg - ref_sum) / np.maximum(scale, 1e-30)) <= 1e-6
 
 
+@pytest.mark.parametrize("d,d0,b0,b1,G", [(128, 64, 4, 3, 8),     # the integer scan
+                                           (128, 64, 3, 2, 3),     # G % 4 != 0: the general path
+                                           (192, 64, 2, 4, 4)])
+def test_score_split_prepared_matches_one_call(d, d0, b0, b1, G):
+    # tq_score_split_prepare + tq_score_ip_split_prepared give tq_score_ip_split's logits bit for
+    # bit, and one prepared workspace serves caches of different lengths and both modes
+    groups, cfg = 2, 76
+    sts = _groups(d, d0, b0, b1, cfg)
+    chans = gen.outlier_channels(cfg, groups, d)
+    q = gen.kv_queries(cfg, 1, groups * G, d)[0]
+    qd = U.to_device(q, True)
+    T_max = 777
+    ws1 = torch.empty(tq.tq_score_split_ws_bytes(d, d0, b0, b1, groups, G, T_max), dtype=torch.uint8,
+                      device=U.DEV)
+    ws2 = torch.full_like(ws1, 0x5A)
+    tq.tq_score_split_prepare(sts[0].params, sts[1].params, d, d0, b0, b1, qd, groups, G, ws2)
+    for T in (T_max, 65):
+        keys = np.concatenate([gen.kv_keys_chunk(cfg, T, h, T, d, chans[h]) for h in range(groups)])
+        parts = _split_quantize(sts, d, d0, U.to_device(keys, True))
+        for mode in (tq.TQ_EST_PROD, tq.TQ_EST_MSE):
+            one = torch.full((groups * G * T,), float("nan"), device=U.DEV)
+            two = torch.full_like(one, float("nan"))
+            tq.tq_score_ip_split(sts[0].params, sts[1].params, d, d0, b0, b1, qd, *parts[0], *parts[1],
+                                 groups, G, T, mode, one, ws1)
+            tq.tq_score_ip_split_prepared(sts[0].params, sts[1].params, d, d0, b0, b1, *parts[0], *parts[1],
+                                          groups, G, T, mode, two, ws2)
+            torch.cuda.synchronize()
+            print(f"[split prepared d={d} ({d0}@{b0} + {d - d0}@{b1}) G={G} T={T} mode={mode}]", flush=True)
+            assert torch.isfinite(one).all()
+            assert torch.equal(one, two)
+
+
 def _rel_logit_mse(lg, exact):
     return float(np.sum((lg - exact) ** 2) / np.sum(exact ** 2))
 
