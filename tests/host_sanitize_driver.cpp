@@ -147,6 +147,18 @@ int main() {
   EXPECT(tq_quantize_split(f, f, 128, 32, 3, 3, f, TQ_BF16, 10, fc, ff, ff, fc, ff, ff, nullptr) == TQ_EINVAL);
   EXPECT(tq_score_ip_split(f, f, 128, 64, 5, 3, f, TQ_BF16, fc, ff, ff, fc, ff, ff, 8, 4, 100, 0, ff, f, 1 << 30,
                            nullptr) == TQ_EINVAL);
+  EXPECT(tq_score_ip_split(f, f, 128, 64, 3, 3, f, TQ_BF16, fc, ff, ff, fc, ff, ff, 8, 4, 100, 0, ff, f, 16,
+                           nullptr) == TQ_EWORKSPACE);
+  EXPECT(tq_score_split_prepare(f, f, 128, 64, 3, 3, f, 7, 8, 4, f, 1 << 30, nullptr) == TQ_EINVAL);
+  EXPECT(tq_score_split_prepare(f, f, 128, 64, 3, 3, f, TQ_BF16, 8, 4, f, 16, nullptr) == TQ_EWORKSPACE);
+  EXPECT(tq_score_split_prepare(f, f, 192, 64, 3, 3, f, TQ_BF16, 8, 5, f, 16, nullptr) == TQ_EWORKSPACE);
+  EXPECT(tq_score_split_prepare(f, f, 128, 64, 3, 3, f, TQ_BF16, 0, 4, nullptr, 0, nullptr) == TQ_OK);
+  EXPECT(tq_score_ip_split_prepared(f, f, 128, 64, 3, 3, fc, ff, ff, fc, ff, ff, 8, 4, 100, 9, ff, f, 1 << 30,
+                                    nullptr) == TQ_EINVAL);
+  EXPECT(tq_score_ip_split_prepared(f, f, 128, 64, 3, 3, fc, ff, ff, fc, ff, ff, 8, 4, 100, 0, ff, f, 16,
+                                    nullptr) == TQ_EWORKSPACE);
+  EXPECT(tq_score_ip_split_prepared(f, f, 128, 64, 3, 3, fc, ff, ff, fc, ff, ff, 1, 4, int64_t(1) << 26, 0, ff, f,
+                                    1 << 30, nullptr) == TQ_EUNSUPPORTED);
   EXPECT(tq_quantize_mse_split(f, f, 128, 64, 3, 3, f, TQ_BF16, 10, static_cast<uint32_t*>(odd), ff, fc, ff,
                                nullptr) == TQ_EINVAL);
   EXPECT(tq_attention_split(f, f, f, f, 128, 64, 4, 3, 4, 4, f, TQ_BF16, fc, ff, ff, fc, ff, ff, fc, ff, fc, ff,
