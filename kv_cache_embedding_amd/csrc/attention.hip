@@ -26,6 +26,7 @@
 #include "score_tile.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 
 namespace tq {
@@ -131,6 +132,118 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   v = row_sum_int(v);
   return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
          (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// The weighted sums of one chunk of value coordinates (c0 .. c0 + 64 NC - 1) over the wave's
+// 64 keys, and the block's partial sums of the chunk: the keys' plane words pw (the lane's key,
+// the chunk's 2 NC coordinate groups) are staged byte-transposed in the wave's LDS rows kb, the
+// value MFMAs run against the weight digits A, and the workgroup's four waves are summed into
+// part_acc.  e: the codebook's Walsh coefficients; tsum_l, inv_l: the sum of the integer weights
+// of the lane's head and their scale.
+template <int BV, int NC>
+__device__ __forceinline__ void value_chunk(const BlockGroup& bg, const uint32_t (&pw)[2 * NC][BV], const v4i& A,
+                                            const float (&e)[BV == 3 ? 4 : BV], int tsum_l, float inv_l,
+                                            long prow, long nh, long nkb, long kblk, int c0,
+                                            float (*accs)[AH][64 * NC], unsigned char* kb) {
+  constexpr int NE = BV == 3 ? 4 : BV;      // Walsh planes: b0 [, b1 [, b2, b0^b1^b2]]
+  constexpr int NG = 2 * NC;                // 32-coordinate groups per chunk
+  const int d = bg.d;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 4;                     // this lane's head in the MFMA output
+  const int ksl = 16 * hl;                      // first of this lane's 16 keys in A and B
+  const uint32_t sh = lane & 7;                 // bit of the byte for coordinate lane % 16
+  const int qi = lane & 3;                      // the lane's byte in the quad transpose
+  // byte selectors of the two transpose steps (v_perm: 0..3 own bytes, 4..7 the partner's)
+  const uint32_t sel_a = (qi & 2) ? 0x03020706u : 0x05040100u;
+  const uint32_t sel_b = (qi & 1) ? 0x03070105u : 0x06020400u;
+  // stage the chunk's words byte-transposed (the xor plane formed here): a 4 x 4 byte
+  // transpose within each lane quad (16-bit halves with the lane two apart, then bytes with
+  // the neighbour) leaves lane 4 j + i with byte i of keys 4 j .. 4 j + 3, one dword store
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    uint32_t word[NE];
+#pragma unroll
+    for (int p = 0; p < BV; ++p) word[p] = pw[gg][p];
+    if constexpr (BV == 3) word[3] = pw[gg][0] ^ pw[gg][1] ^ pw[gg][2];
+#pragma unroll
+    for (int pp = 0; pp < NE; ++pp) {
+      const uint32_t x = __builtin_amdgcn_perm(dpp_quad<0x4E>(word[pp]), word[pp], sel_a);
+      const uint32_t y = __builtin_amdgcn_perm(dpp_quad<0xB1>(x), x, sel_b);
+      *reinterpret_cast<uint32_t*>(kb + ((pp * NG + gg) * 4 + qi) * 64 + (lane & ~3)) = y;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+  float acc[2 * NG];
+#pragma unroll
+  for (int i = 0; i < 2 * NG; ++i) acc[i] = 0.f;
+  if constexpr (NC % 2 == 0) {
+    // MFMA column n = byte n of 16 consecutive bytes of the keys' plane (byte n of the chunk
+    // holds coordinates 8 n .. 8 n + 7), MFMA j = bit j: one 16-byte read per lane feeds the
+    // plane's 8 MFMAs of a 128-coordinate slice, and the lane ends with coordinates
+    // 8 (16 rr + lane % 16) + j of its head
+#pragma unroll
+    for (int pp = 0; pp < NE; ++pp) {
+      v4i r[2 * NG];
+#pragma unroll
+      for (int rr = 0; rr < NC / 2; ++rr) {
+        const uint4 q = *reinterpret_cast<const uint4*>(kb + (pp * NG * 4 + 16 * rr + (lane & 15)) * 64 + ksl);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const v4i B = {int((q.x >> j) & 0x01010101u), int((q.y >> j) & 0x01010101u),
+                         int((q.z >> j) & 0x01010101u), int((q.w >> j) & 0x01010101u)};
+          r[8 * rr + j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NG; ++i) {
+        const int S = r[i][2] * 16384 + r[i][1] * 128 + r[i][0];
+        acc[i] = fmaf(e[pp], float(2 * S - tsum_l), acc[i]);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < NC / 2; ++rr) {
+      float4* dst = reinterpret_cast<float4*>(&accs[wave][hl][8 * (16 * rr + (lane & 15))]);
+      dst[0] = make_float4(acc[8 * rr] * inv_l, acc[8 * rr + 1] * inv_l, acc[8 * rr + 2] * inv_l,
+                           acc[8 * rr + 3] * inv_l);
+      dst[1] = make_float4(acc[8 * rr + 4] * inv_l, acc[8 * rr + 5] * inv_l, acc[8 * rr + 6] * inv_l,
+                           acc[8 * rr + 7] * inv_l);
+    }
+  } else {
+#pragma unroll
+    for (int pp = 0; pp < NE; ++pp) {
+      // the plane's MFMAs first, then their results (the MFMA latency overlaps the gathers)
+      v4i r[2 * NG];
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          // coordinate 32 gg + 16 half + lane % 16: byte 2 half + (lane % 16) / 8 of the word
+          const int by = 2 * half + ((lane & 15) >> 3);
+          const uint4 q = *reinterpret_cast<const uint4*>(kb + ((pp * NG + gg) * 4 + by) * 64 + ksl);
+          const v4i B = {int((q.x >> sh) & 0x01010101u), int((q.y >> sh) & 0x01010101u),
+                         int((q.z >> sh) & 0x01010101u), int((q.w >> sh) & 0x01010101u)};
+          r[2 * gg + half] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NG; ++i) {
+        const int S = r[i][2] * 16384 + r[i][1] * 128 + r[i][0];
+        acc[i] = fmaf(e[pp], float(2 * S - tsum_l), acc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NG; ++i) accs[wave][hl][16 * i + (lane & 15)] = acc[i] * inv_l;
+  }
+  __syncthreads();
+  for (int ei = tid; ei < AH * 64 * NC; ei += 256) {
+    const int hh = ei / (64 * NC), c = ei % (64 * NC);
+    if (hh < nh)
+      bg.part_acc[((prow + hh) * nkb + kblk) * d + c0 + c] =
+          (accs[0][hh][c] + accs[1][hh][c]) + (accs[2][hh][c] + accs[3][hh][c]);
+  }
+  __syncthreads();
 }
 
 // KBITS = 0: the logits come from memory (one per (head, key)); KBITS = b of d = 128 keys: the
@@ -331,102 +444,9 @@ __device__ __forceinline__ void value_block(const BlockGroup& bg, const KeyOps& 
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   const v4i A = *reinterpret_cast<const v4i*>(ab + (lane & 15) * 64 + 16 * (lane >> 4));
 
-  const int hl = lane >> 4;                     // this lane's head in the MFMA output
-  const int ksl = 16 * hl;                      // first of this lane's 16 keys in A and B
-  const uint32_t sh = lane & 7;                 // bit of the byte for coordinate lane % 16
-  const int qi = lane & 3;                      // the lane's byte in the quad transpose
-  // byte selectors of the two transpose steps (v_perm: 0..3 own bytes, 4..7 the partner's)
-  const uint32_t sel_a = (qi & 2) ? 0x03020706u : 0x05040100u;
-  const uint32_t sel_b = (qi & 1) ? 0x03070105u : 0x06020400u;
   for (int c0 = 0; c0 < d; c0 += 64 * NC) {
     if (c0 > 0) load_words(c0);
-    // stage the chunk's words byte-transposed (the xor plane formed here): a 4 x 4 byte
-    // transpose within each lane quad (16-bit halves with the lane two apart, then bytes with
-    // the neighbour) leaves lane 4 j + i with byte i of keys 4 j .. 4 j + 3, one dword store
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      uint32_t word[NE];
-#pragma unroll
-      for (int p = 0; p < BV; ++p) word[p] = pw[gg][p];
-      if constexpr (BV == 3) word[3] = pw[gg][0] ^ pw[gg][1] ^ pw[gg][2];
-#pragma unroll
-      for (int pp = 0; pp < NE; ++pp) {
-        const uint32_t x = __builtin_amdgcn_perm(dpp_quad<0x4E>(word[pp]), word[pp], sel_a);
-        const uint32_t y = __builtin_amdgcn_perm(dpp_quad<0xB1>(x), x, sel_b);
-        *reinterpret_cast<uint32_t*>(kb + ((pp * NG + gg) * 4 + qi) * 64 + (lane & ~3)) = y;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-
-    float acc[2 * NG];
-#pragma unroll
-    for (int i = 0; i < 2 * NG; ++i) acc[i] = 0.f;
-    if constexpr (NC % 2 == 0) {
-      // MFMA column n = byte n of 16 consecutive bytes of the keys' plane (byte n of the chunk
-      // holds coordinates 8 n .. 8 n + 7), MFMA j = bit j: one 16-byte read per lane feeds the
-      // plane's 8 MFMAs of a 128-coordinate slice, and the lane ends with coordinates
-      // 8 (16 rr + lane % 16) + j of its head
-#pragma unroll
-      for (int pp = 0; pp < NE; ++pp) {
-        v4i r[2 * NG];
-#pragma unroll
-        for (int rr = 0; rr < NC / 2; ++rr) {
-          const uint4 q = *reinterpret_cast<const uint4*>(kb + (pp * NG * 4 + 16 * rr + (lane & 15)) * 64 + ksl);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const v4i B = {int((q.x >> j) & 0x01010101u), int((q.y >> j) & 0x01010101u),
-                           int((q.z >> j) & 0x01010101u), int((q.w >> j) & 0x01010101u)};
-            r[8 * rr + j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 2 * NG; ++i) {
-          const int S = r[i][2] * 16384 + r[i][1] * 128 + r[i][0];
-          acc[i] = fmaf(e[pp], float(2 * S - tsum_l), acc[i]);
-        }
-      }
-#pragma unroll
-      for (int rr = 0; rr < NC / 2; ++rr) {
-        float4* dst = reinterpret_cast<float4*>(&accs[wave][hl][8 * (16 * rr + (lane & 15))]);
-        dst[0] = make_float4(acc[8 * rr] * inv_l, acc[8 * rr + 1] * inv_l, acc[8 * rr + 2] * inv_l,
-                             acc[8 * rr + 3] * inv_l);
-        dst[1] = make_float4(acc[8 * rr + 4] * inv_l, acc[8 * rr + 5] * inv_l, acc[8 * rr + 6] * inv_l,
-                             acc[8 * rr + 7] * inv_l);
-      }
-    } else {
-#pragma unroll
-      for (int pp = 0; pp < NE; ++pp) {
-        // the plane's MFMAs first, then their results (the MFMA latency overlaps the gathers)
-        v4i r[2 * NG];
-#pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            // coordinate 32 gg + 16 half + lane % 16: byte 2 half + (lane % 16) / 8 of the word
-            const int by = 2 * half + ((lane & 15) >> 3);
-            const uint4 q = *reinterpret_cast<const uint4*>(kb + ((pp * NG + gg) * 4 + by) * 64 + ksl);
-            const v4i B = {int((q.x >> sh) & 0x01010101u), int((q.y >> sh) & 0x01010101u),
-                           int((q.z >> sh) & 0x01010101u), int((q.w >> sh) & 0x01010101u)};
-            r[2 * gg + half] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 2 * NG; ++i) {
-          const int S = r[i][2] * 16384 + r[i][1] * 128 + r[i][0];
-          acc[i] = fmaf(e[pp], float(2 * S - tsum_l), acc[i]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * NG; ++i) accs[wave][hl][16 * i + (lane & 15)] = acc[i] * inv_l;
-    }
-    __syncthreads();
-    for (int ei = tid; ei < AH * 64 * NC; ei += 256) {
-      const int hh = ei / (64 * NC), c = ei % (64 * NC);
-      if (hh < nh)
-        bg.part_acc[((prow + hh) * nkb + kblk) * d + c0 + c] =
-            (accs[0][hh][c] + accs[1][hh][c]) + (accs[2][hh][c] + accs[3][hh][c]);
-    }
-    __syncthreads();
+    value_chunk<BV, NC>(bg, pw, A, e, tsum_l, inv_l, prow, nh, nkb, kblk, c0, accs, kb);
   }
 }
 
@@ -466,6 +486,192 @@ __global__ __launch_bounds__(256, 4) void attn_fused_kernel(KeyOps ko, BlockGrou
   value_block<BV, NC, KBITS, PROD>(bg, ko, nullptr, G, T, nkb, passes, scale, blockIdx.x, red, accs,
                                    reinterpret_cast<unsigned char*>(kbytes),
                                    reinterpret_cast<unsigned char*>(abytes));
+}
+
+// ------------------------------------------------- fused blocks of a 64 + 64 split cache
+// The key operands of the fused split block kernel: the two channel groups' key caches (each
+// [groups][T] keys of 2 coordinate groups x b plane words, nu, gamma) and the query operands
+// that the split scorer's query prep wrote (score_split_ws_per_group bytes per quad of heads).
+struct SplitKeyOps {
+  const uint32_t* codes0;
+  const float* nu0;
+  const float* gamma0;
+  const uint32_t* codes1;
+  const float* nu1;
+  const float* gamma1;
+  const unsigned char* qws;
+};
+
+// A key's BITS plane words of one coordinate group (one vector load where the size allows).
+template <int BITS>
+__device__ __forceinline__ void load_plane_words(const uint32_t* src, uint32_t* w) {
+  if constexpr (BITS == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (BITS == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(src);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) w[p] = src[p];
+  }
+}
+
+// The block work of attn_fused_kernel for keys and values held as two 64-channel groups (keys
+// at KB0, KB1 bits, values at BV0, BV1 index planes), inner-product keys.  The logits are the
+// split scorer's (score_split_tile_sums per key group, the two estimates added); the softmax is
+// shared, and each value group then forms its own weights p nu_v,g, digits and 64-coordinate
+// value sums into its own partials (both groups' partials carry the same maxima and sums of p).
+// At most 168 VGPRs (three waves per SIMD).
+template <int KB0, int KB1, int BV0, int BV1>
+__global__ __launch_bounds__(256, 3) void attn_fused_split_kernel(SplitKeyOps ko, BlockGroup bg0, BlockGroup bg1,
+                                                                long G, long T, long nkb, long passes,
+                                                                float scale) {
+  constexpr int NW0 = score_words(KB0), NW1 = score_words(KB1);
+  constexpr int NE0 = BV0 == 3 ? 4 : BV0, NE1 = BV1 == 3 ? 4 : BV1;
+  constexpr int NEM = NE0 > NE1 ? NE0 : NE1;
+  constexpr float kVMax = 2097151.f;        // 2^21 - 1: three 7-bit digits
+  __shared__ float red[8][AH];
+  __shared__ __align__(16) float accs[4][AH][64];
+  __shared__ uint4 kbytes[4 * NEM * 2 * 4 * 64 / 16];      // [wave][plane][group][byte][key]
+  __shared__ uint4 abytes[4 * 16 * 64 / 16];               // [wave][row][key] weight digits
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  unsigned char* kb = reinterpret_cast<unsigned char*>(kbytes) + wave * (NEM * 2 * 4 * 64);
+  unsigned char* ab = reinterpret_cast<unsigned char*>(abytes) + wave * (16 * 64);
+  const long blk = blockIdx.x;
+  const long kblk = blk % nkb;
+  const long gp = blk / nkb;
+  const long g = gp / passes;
+  const long h0 = (gp % passes) * AH;
+  const long tw0 = kblk * KB + wave * 64;
+  const long prow = g * G + h0;
+  const int hs = lane >> 4;                 // the lane's head (rows of the MFMA outputs)
+  const int cg = lane >> 5;                 // B operand: coordinate group of the channel group
+  const uint32_t mj = 0x01010101u << ((lane >> 4) & 1);   // and bit parity
+
+  // the quad's query operands, then every key and value load of the block
+  const unsigned char* qb = ko.qws + size_t(gp) * score_split_ws_per_group(KB0, KB1);
+  v4i A0[NW0], A1[NW1];
+#pragma unroll
+  for (int m = 0; m < NW0; ++m) A0[m] = reinterpret_cast<const v4i*>(qb)[m * 64 + lane];
+#pragma unroll
+  for (int m = 0; m < NW1; ++m) A1[m] = reinterpret_cast<const v4i*>(qb + size_t(NW0) * 64 * 16)[m * 64 + lane];
+  const float4* cst = reinterpret_cast<const float4*>(qb + size_t(NW0 + NW1) * 64 * 16);
+  const float4 c0 = cst[hs], c1 = cst[AH + hs];
+  const uint32_t* kc0 = ko.codes0 + size_t(g) * T * 2 * KB0;
+  const uint32_t* kc1 = ko.codes1 + size_t(g) * T * 2 * KB1;
+  uint32_t kw0[4][KB0], kw1[4][KB1];
+  float nk0[4], nk1[4], gk0[4], gk1[4], nv0[4], nv1[4];
+  // keys past the end read the last key (their logits are replaced by -inf below), so that no
+  // load sits under a branch
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const long key = tw0 + 16 * u + (lane & 15);
+    const long kr = key < T ? key : T - 1;
+    load_plane_words<KB0>(kc0 + (size_t(kr) * 2 + cg) * KB0, kw0[u]);
+    load_plane_words<KB1>(kc1 + (size_t(kr) * 2 + cg) * KB1, kw1[u]);
+    nk0[u] = ko.nu0[g * T + kr];
+    nk1[u] = ko.nu1[g * T + kr];
+    gk0[u] = ko.gamma0[g * T + kr];
+    gk1[u] = ko.gamma1[g * T + kr];
+    nv0[u] = bg0.vnu[g * T + kr];
+    nv1[u] = bg1.vnu[g * T + kr];
+    // loads return in issue order: a tile's loads stay together, ahead of the next tile's
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the value words of key tw0 + lane (both groups' 2 coordinate groups), in flight while the
+  // logits and the softmax are formed
+  const long t = tw0 + lane;
+  const long tc = t < T ? t : T - 1;
+  uint32_t pw0[2][BV0], pw1[2][BV1];
+  {
+    const uint32_t* v0 = bg0.vcodes + size_t(g * T + tc) * 2 * BV0;
+    const uint32_t* v1 = bg1.vcodes + size_t(g * T + tc) * 2 * BV1;
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+#pragma unroll
+      for (int p = 0; p < BV0; ++p) pw0[gg][p] = v0[gg * BV0 + p];
+#pragma unroll
+      for (int p = 0; p < BV1; ++p) pw1[gg][p] = v1[gg * BV1 + p];
+    }
+  }
+  // every load is issued before the first use
+  __builtin_amdgcn_sched_barrier(0);
+
+  float l[4], mx = -INFINITY;
+  bool ok[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ok[u] = tw0 + 16 * u + (lane & 15) < T;
+    const v4i s0 = score_split_tile_sums<KB0, true>(A0, kw0[u], mj);
+    const v4i s1 = score_split_tile_sums<KB1, true>(A1, kw1[u], mj);
+    const float lv = scale * (score_tile_estimate<true>(s0, c0, nk0[u], gk0[u]) +
+                              score_tile_estimate<true>(s1, c1, nk1[u], gk1[u]));
+    l[u] = ok[u] ? lv : -INFINITY;
+    mx = fmaxf(mx, l[u]);
+  }
+  mx = row_max_dpp(mx);
+  if ((lane & 15) == 0) red[wave][hs] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0][hs], red[1][hs]), fmaxf(red[2][hs], red[3][hs]));
+  float p[4], sp = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    p[u] = ok[u] ? __expf(l[u] - M) : 0.f;
+    sp += p[u];
+  }
+  sp = row_sum_dpp(sp);
+  if ((lane & 15) == 0) red[4 + wave][hs] = sp;
+  __syncthreads();
+  if (tid < AH) {
+    const float bm = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+    const float bs = (red[4][tid] + red[5][tid]) + (red[6][tid] + red[7][tid]);
+    bg0.part_m[(prow + tid) * nkb + kblk] = bm;
+    bg0.part_s[(prow + tid) * nkb + kblk] = bs;
+    bg1.part_m[(prow + tid) * nkb + kblk] = bm;
+    bg1.part_s[(prow + tid) * nkb + kblk] = bs;
+  }
+
+  // one value group: weights p nu_v, their digits as the A operand (rows 4 hs + j: digit j of
+  // head hs; the lane's head is also its head in the value MFMA's output), the value sums
+  auto value_group_sums = [&](const BlockGroup& bg, const float (&nv)[4], auto& pw, auto bv_tag) {
+    constexpr int BV = decltype(bv_tag)::value;
+    constexpr int NE = BV == 3 ? 4 : BV;
+    const Header* hdr = reinterpret_cast<const Header*>(bg.params_v);
+    float e[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) e[i] = hdr->e[i];
+    float w[4], wmx = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u] = p[u] * nv[u];
+      wmx = fmaxf(wmx, w[u]);
+    }
+    const float wm = row_max_dpp(wmx);
+    const float sc = wm > 0.f ? kVMax / wm : 0.f;
+    int vs = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int v = int(rintf(w[u] * sc));
+      v = v < 2097151 ? v : 2097151;
+      vs += v;
+      const int key = 16 * u + (lane & 15);
+      ab[(4 * hs + 0) * 64 + key] = (unsigned char)(v & 127);
+      ab[(4 * hs + 1) * 64 + key] = (unsigned char)((v >> 7) & 127);
+      ab[(4 * hs + 2) * 64 + key] = (unsigned char)(v >> 14);
+      ab[(4 * hs + 3) * 64 + key] = 0;
+    }
+    const int tsum_l = row_sum_int(vs);
+    const float inv_l = wm * (1.f / kVMax);
+    // the staging writes and the reads below use other types: order them explicitly
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const v4i A = *reinterpret_cast<const v4i*>(ab + (lane & 15) * 64 + 16 * (lane >> 4));
+    value_chunk<BV, 1>(bg, pw, A, e, tsum_l, inv_l, prow, AH, nkb, kblk, 0, accs, kb);
+  };
+  value_group_sums(bg0, nv0, pw0, std::integral_constant<int, BV0>{});
+  // (value_chunk ends with a barrier: the wave's digit and staging rows are free again)
+  value_group_sums(bg1, nv1, pw1, std::integral_constant<int, BV1>{});
 }
 
 // The block partials and output columns of one value channel group.
@@ -804,6 +1010,72 @@ hipError_t launch_attention_values_split(const void* params_v0, const void* para
   hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(2 * rows)), dim3(CT),
                      std::max(combine_lds_bytes(d0), combine_lds_bytes(d1)), s, v0.comb, v1.comb, rows,
                      nkb, long(d0) + d1);
+  return hipGetLastError();
+}
+
+namespace {
+
+template <int KB0, int KB1, int BV0, int BV1>
+void launch_fused_split_t(const SplitKeyOps& ko, const ValueGroup& v0, const ValueGroup& v1, long blocks,
+                          int64_t G, int64_t T, float scale, hipStream_t s) {
+  const long nkb = (T + KB - 1) / KB;
+  hipLaunchKernelGGL((attn_fused_split_kernel<KB0, KB1, BV0, BV1>), dim3(unsigned(blocks)), dim3(256), 0, s, ko,
+                     v0.blk, v1.blk, long(G), long(T), nkb, long(G / AH), scale);
+}
+
+// value index planes (BV0, BV1) of the instantiated kernels: equal, or group 0 one above
+template <int KB0, int KB1>
+hipError_t launch_fused_split_k(const SplitKeyOps& ko, const ValueGroup& v0, const ValueGroup& v1, long blocks,
+                                int64_t G, int64_t T, float scale, hipStream_t s) {
+  const int p = v0.bv * 4 + v1.bv;
+  switch (p) {
+    case 1 * 4 + 1: launch_fused_split_t<KB0, KB1, 1, 1>(ko, v0, v1, blocks, G, T, scale, s); break;
+    case 2 * 4 + 1: launch_fused_split_t<KB0, KB1, 2, 1>(ko, v0, v1, blocks, G, T, scale, s); break;
+    case 2 * 4 + 2: launch_fused_split_t<KB0, KB1, 2, 2>(ko, v0, v1, blocks, G, T, scale, s); break;
+    case 3 * 4 + 2: launch_fused_split_t<KB0, KB1, 3, 2>(ko, v0, v1, blocks, G, T, scale, s); break;
+    case 3 * 4 + 3: launch_fused_split_t<KB0, KB1, 3, 3>(ko, v0, v1, blocks, G, T, scale, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attention_fused_split_applies(int bk0, int bk1, int bv0, int bv1) {
+  // the instantiated kernels: group 0's bits equal to group 1's or one above, for keys and for
+  // values (a fractional rate puts the extra bit in the first group)
+  auto pair = [](int a, int b, int lo, int hi) { return b >= lo && a <= hi && (a == b || a == b + 1); };
+  return pair(bk0, bk1, 2, 4) && pair(bv0, bv1, 2, 4);
+}
+
+hipError_t launch_attention_fused_split(const void* params_v0, const void* params_v1, int bk0, int bk1,
+                                        const uint32_t* codes_k0, const float* nu_k0, const float* gamma_k0,
+                                        const uint32_t* codes_k1, const float* nu_k1, const float* gamma_k1,
+                                        const void* qws, int bv0, int bv1, const uint32_t* vcodes0,
+                                        const float* vnu0, const uint32_t* vcodes1, const float* vnu1,
+                                        int64_t groups, int64_t G, int64_t T, float scale, float* out, void* part,
+                                        hipStream_t s) {
+  constexpr int d0 = 64, d1 = 64;
+  if (!attention_fused_split_applies(bk0, bk1, bv0, bv1) || G % AH != 0) return hipErrorInvalidValue;
+  void* part1 = static_cast<unsigned char*>(part) + align256(attention_part_bytes(d0, groups, G, T));
+  const ValueGroup v0 = value_group(params_v0, d0, bv0, vcodes0, vnu0, groups, G, T, out, part);
+  const ValueGroup v1 = value_group(params_v1, d1, bv1, vcodes1, vnu1, groups, G, T, out + d0, part1);
+  const SplitKeyOps ko{codes_k0, nu_k0, gamma_k0, codes_k1, nu_k1, gamma_k1, static_cast<const unsigned char*>(qws)};
+  const long nkb = (T + KB - 1) / KB;
+  const long blocks = long(groups) * (G / AH) * nkb;
+  hipError_t e;
+  switch (bk0 * 8 + bk1) {
+    case 2 * 8 + 2: e = launch_fused_split_k<2, 2>(ko, v0, v1, blocks, G, T, scale, s); break;
+    case 3 * 8 + 2: e = launch_fused_split_k<3, 2>(ko, v0, v1, blocks, G, T, scale, s); break;
+    case 3 * 8 + 3: e = launch_fused_split_k<3, 3>(ko, v0, v1, blocks, G, T, scale, s); break;
+    case 4 * 8 + 3: e = launch_fused_split_k<4, 3>(ko, v0, v1, blocks, G, T, scale, s); break;
+    case 4 * 8 + 4: e = launch_fused_split_k<4, 4>(ko, v0, v1, blocks, G, T, scale, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const long rows = long(groups) * G;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(2 * rows)), dim3(CT), combine_lds_bytes(d0), s, v0.comb,
+                     v1.comb, rows, nkb, long(d0) + d1);
   return hipGetLastError();
 }
 

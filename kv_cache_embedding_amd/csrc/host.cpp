@@ -866,13 +866,27 @@ int tq_attention_split(const void* params_k0, const void* params_k1, const void*
   const size_t sws_bytes = tq_score_split_ws_bytes(d, d0, bk0, bk1, groups, G, T);
   void* sws = w + tq::align256(size_t(groups) * G * T * 4);
   void* part = static_cast<unsigned char*>(sws) + sws_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (tq::score_split_d128_shape(d, d0, bk0, bk1, G) && mode == TQ_EST_PROD &&
+      tq::attention_fused_split_applies(bk0, bk1, bv0, bv1)) {
+    // the split scorer's query prep, then block kernels that score their own keys (the logits
+    // region of the workspace stays unused) and one merge of both value groups
+    hipError_t e = tq::launch_score_split_d128(params_k0, params_k1, bk0, bk1, q, q_dtype, nullptr, nullptr,
+                                               nullptr, nullptr, nullptr, nullptr, groups, G, 1, TQ_EST_PROD,
+                                               nullptr, sws, s, tq::kScorePrep);
+    if (e == hipSuccess)
+      e = tq::launch_attention_fused_split(params_v0, params_v1, bk0, bk1, codes_k0, nu_k0, gamma_k0, codes_k1,
+                                           nu_k1, gamma_k1, sws, bv0, bv1, codes_v0, nu_v0, codes_v1, nu_v1,
+                                           groups, G, T, scale, out, part, s);
+    if (e != hipSuccess) return hip_fail(e, "tq_attention_split launch");
+    return ok();
+  }
   // logits of the split keys, then each value group's block partials and one merge of both
   // groups into their columns of out
   const int rc = tq_score_ip_split(params_k0, params_k1, d, d0, bk0, bk1, q, q_dtype, codes_k0, nu_k0,
                                    gamma_k0, codes_k1, nu_k1, gamma_k1, groups, G, T, mode, logits, sws,
                                    sws_bytes, stream);
   if (rc != TQ_OK) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = tq::launch_attention_values_split(params_v0, params_v1, d0, d - d0, bv0, bv1, logits,
                                                          codes_v0, nu_v0, codes_v1, nu_v1, groups, G, T,
                                                          scale, out, part, s);

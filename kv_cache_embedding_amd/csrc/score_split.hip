@@ -29,12 +29,6 @@ constexpr int RSRC_WORD3 = 0x00020000;   // raw (untyped) buffer resource, gfx9 
 constexpr int QP_THREADS = 512;
 constexpr int QP_SLICES = QP_THREADS / (2 * DG);
 
-// Workspace per quad of heads: group 0's NW0 operand registers (64 lanes x 16 bytes each),
-// group 1's NW1, then float4 constants [group][head].
-constexpr size_t split_ws_per_group(int b0, int b1) {
-  return size_t(score_words(b0) + score_words(b1)) * 64 * 16 + size_t(2) * G * 16;
-}
-
 // -------------------------------------------------------------------------- query prep
 // Two workgroups per quad (type 0: Pi q and the MSE rows; type 1: S q and the QJL rows).
 // Thread i forms row i % 128 (row r of group r / 64) over a quarter of that group's 64
@@ -117,7 +111,7 @@ __global__ __launch_bounds__(QP_THREADS) void split_qprep_kernel(const unsigned 
   }
   __syncthreads();
 
-  unsigned char* base = ws + size_t(g) * split_ws_per_group(B0, B1);
+  unsigned char* base = ws + size_t(g) * score_split_ws_per_group(B0, B1);
   // A operand chunks of this half: group 0's items, then group 1's; per head NW MFMAs x 4
   // K chunks x 2 rows (digit hi, lo)
   constexpr int ITEMS0 = G * NW0 * 4 * 2, ITEMS = ITEMS0 + G * NW1 * 4 * 2;
@@ -178,34 +172,6 @@ __global__ __launch_bounds__(QP_THREADS) void split_qprep_kernel(const unsigned 
 }
 
 // ---------------------------------------------------------------------------- scoring
-// Digit sums of one channel group for the pair this lane holds in a 16-key tile (head
-// lane % 16 / 4 of the quad, key lane % 16): A, the group's NW operand registers; w, the
-// key's BITS plane words of coordinate group lane / 32; mj, this lane's bit parity mask
-// (0x01 or 0x02 in every byte).  Registers 0, 1 of the result hold the MSE digit sums (hi,
-// lo), 2, 3 the QJL ones.
-template <int BITS, bool PROD>
-__device__ __forceinline__ v4i split_tile_sums(const v4i* A, const uint32_t* w, uint32_t mj) {
-  constexpr int NW = score_words(BITS);
-  constexpr int NWU = PROD ? NW : NW - 1;     // MSE-only skips the sign plane
-  uint32_t word[NW];
-  if constexpr (BITS == 4) {
-    word[0] = w[0]; word[1] = w[1]; word[2] = w[2];
-    word[3] = w[0] ^ w[1] ^ w[2];
-    word[4] = w[3];
-  } else {
-#pragma unroll
-    for (int p = 0; p < BITS; ++p) word[p] = w[p];
-  }
-  v4i acc = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < NWU; ++i) {
-    const uint32_t W = word[i];
-    const v4i b = {int(W & mj), int((W >> 2) & mj), int((W >> 4) & mj), int((W >> 6) & mj)};
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], b, acc, 0, 0, 0);
-  }
-  return acc;
-}
-
 template <int B> __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t rs, int off, uint32_t* w) {
   if constexpr (B == 4) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
@@ -246,7 +212,7 @@ __global__ __launch_bounds__(256, split_waves_per_simd(B0, B1)) void split_score
   long t1 = t0 + tiles_per_range;
   if (t1 > tiles_per_group) t1 = tiles_per_group;
 
-  const unsigned char* base = ws + size_t(g) * split_ws_per_group(B0, B1);
+  const unsigned char* base = ws + size_t(g) * score_split_ws_per_group(B0, B1);
   v4i A0[NW0], A1[NW1];
 #pragma unroll
   for (int m = 0; m < NWU0; ++m) A0[m] = reinterpret_cast<const v4i*>(base)[m * 64 + lane];
@@ -293,8 +259,8 @@ __global__ __launch_bounds__(256, split_waves_per_simd(B0, B1)) void split_score
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       __builtin_amdgcn_sched_barrier(0);
-      const v4i s0 = split_tile_sums<B0, PROD>(A0, w0[u], mj);
-      const v4i s1 = split_tile_sums<B1, PROD>(A1, w1[u], mj);
+      const v4i s0 = score_split_tile_sums<B0, PROD>(A0, w0[u], mj);
+      const v4i s1 = score_split_tile_sums<B1, PROD>(A1, w1[u], mj);
       const float l = score_tile_estimate<PROD>(s0, c0, nk0[u], gk0[u]) +
                       score_tile_estimate<PROD>(s1, c1, nk1[u], gk1[u]);
       const int oo = key[u] < T ? (hq * int(T) + key[u]) * 4 : int(G * T * 4);
@@ -368,7 +334,7 @@ bool score_split_d128_applies(int d, int d0, int b0, int b1, int64_t G, int64_t 
 }
 
 size_t score_split_d128_ws_bytes(int b0, int b1, int64_t groups, int64_t G) {
-  return align256(size_t(groups) * size_t(G / 4) * split_ws_per_group(b0, b1));
+  return align256(size_t(groups) * size_t(G / 4) * score_split_ws_per_group(b0, b1));
 }
 
 hipError_t launch_score_split_d128(const void* params0, const void* params1, int b0, int b1, const void* q,

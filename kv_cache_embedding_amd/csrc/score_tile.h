@@ -44,6 +44,35 @@ __device__ __forceinline__ v4i score_tile_sums(const v4i* A, const uint32_t* w) 
   return acc;
 }
 
+// The same sums for one 64-channel group of a key split 64 + 64 (a fractional rate), where one
+// MFMA's K = 64 covers the whole channel group: K chunk lane / 16 is coordinate group lane / 32
+// of the channel group and bit parity (lane / 16) % 2.  A: the group's NW operand registers
+// (one per plane word); w: the key's BITS plane words of coordinate group lane / 32 (the B
+// operand's column lane % 16); mj: the lane's parity mask (0x01 or 0x02 in every byte).  The
+// result is laid out as score_tile_sums's (head lane / 16, key lane % 16).
+template <int BITS, bool PROD>
+__device__ __forceinline__ v4i score_split_tile_sums(const v4i* A, const uint32_t* w, uint32_t mj) {
+  constexpr int NW = score_words(BITS);
+  constexpr int NWU = PROD ? NW : NW - 1;     // MSE-only skips the sign plane
+  uint32_t word[NW];
+  if constexpr (BITS == 4) {
+    word[0] = w[0]; word[1] = w[1]; word[2] = w[2];
+    word[3] = w[0] ^ w[1] ^ w[2];
+    word[4] = w[3];
+  } else {
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) word[p] = w[p];
+  }
+  v4i acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < NWU; ++i) {
+    const uint32_t W = word[i];
+    const v4i b = {int(W & mj), int((W >> 2) & mj), int((W >> 4) & mj), int((W >> 6) & mj)};
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], b, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // The estimate from the digit sums: cst holds the epilogue constants of the lane's head
 // (l = nu (s_mse cst.x - cst.y + gamma (s_qjl cst.z - cst.w))); nk, gk: the key's nu and gamma.
 template <bool PROD>

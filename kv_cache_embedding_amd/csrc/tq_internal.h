@@ -70,6 +70,13 @@ constexpr size_t score_ws_per_group(int b) {
   return size_t(2 * score_words(b)) * 64 * 16 + 4 * 4 * 4;
 }
 
+// Split scoring workspace (a key split 64 + 64 of d = 128) per quad of query heads: group 0's
+// NW0 MFMA operand registers (64 lanes x 16 bytes each), group 1's NW1, then float4 constants
+// [group][head] (l_g = nu_g (x s_mse - y + gamma_g (z s_qjl - w))).
+constexpr size_t score_split_ws_per_group(int b0, int b1) {
+  return size_t(score_words(b0) + score_words(b1)) * 64 * 16 + size_t(2) * 4 * 16;
+}
+
 // Sets the calling thread's tq_last_error() text and returns status (host.cpp).
 int report_error(int status, const char* message);
 
@@ -161,6 +168,19 @@ hipError_t launch_attention_values_split(const void* params_v0, const void* para
                                          const uint32_t* vcodes1, const float* vnu1, int64_t groups,
                                          int64_t G, int64_t T, float scale, float* out, void* part,
                                          hipStream_t s);
+// A 64 + 64 split of d = 128 keys (inner-product estimate) and values with G a multiple of 4:
+// the block partials with each block's logits computed in the block kernel from the query
+// operands that the split scorer's query prep wrote to qws (no logits in memory), then one
+// merge of both value groups (partials of group 1 at align256(attention_part_bytes(64, ...))).
+// applies: the bit pairs with a kernel (each group 0 count equal to group 1's or one above).
+bool attention_fused_split_applies(int bk0, int bk1, int bv0, int bv1);
+hipError_t launch_attention_fused_split(const void* params_v0, const void* params_v1, int bk0, int bk1,
+                                        const uint32_t* codes_k0, const float* nu_k0, const float* gamma_k0,
+                                        const uint32_t* codes_k1, const float* nu_k1, const float* gamma_k1,
+                                        const void* qws, int bv0, int bv1, const uint32_t* vcodes0,
+                                        const float* vnu0, const uint32_t* vcodes1, const float* vnu1,
+                                        int64_t groups, int64_t G, int64_t T, float scale, float* out, void* part,
+                                        hipStream_t s);
 // Cache append: copies vector g's words, nu and gamma (gamma may be NULL) of a contiguous
 // batch to slot (g, pos) of [groups][cap] caches.
 hipError_t launch_scatter_slot(const uint32_t* src_codes, const float* src_nu,

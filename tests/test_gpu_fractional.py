@@ -259,7 +259,11 @@ def _mse_split(svs, d, d0, xd):
 
 
 @pytest.mark.parametrize("d,d0,bk0,bk1,bv0,bv1,G,T,q_bf16", [
-    (128, 64, 3, 2, 4, 3, 4, 700, True),      # 2.5-bit keys, 2.5-bit values (b - 1 index bits)
+    (128, 64, 3, 2, 4, 3, 4, 700, True),      # 2.5-bit keys, 2.5-bit values (b - 1 index bits);
+    (128, 64, 4, 3, 4, 4, 8, 777, False),     # 64 + 64 with whole quads: blocks score their keys
+    (128, 64, 3, 3, 3, 2, 4, 65, True),
+    (128, 64, 2, 2, 2, 2, 12, 300, False),
+    (128, 64, 3, 4, 4, 4, 4, 129, True),      # group 1 at more bits: scoring pass + block grid
     (128, 64, 4, 3, 4, 3, 3, 257, False),
     (192, 128, 4, 2, 3, 4, 2, 300, True),     # chunk shapes differ: a block launch per group
     (256, 128, 3, 4, 2, 4, 5, 513, False)])   # two 128-channel groups in one block grid
