@@ -22,7 +22,8 @@
 // attn_combine_kernel: one workgroup per (group, head): merges the blocks (log-sum-exp) and
 //   applies Pi_v^T; threads split both sums into slices of independent float4 loads (rows
 //   of Pi_v are contiguous, so a slice reads coalesced columns), the first loads of both
-//   issued before the maximum and the sum are reduced.
+//   issued before the maximum and the sum are reduced (DPP wave reductions, four waves up to
+//   d = 1024).
 #include "score_tile.h"
 
 #include <algorithm>
@@ -34,19 +35,7 @@ namespace {
 
 constexpr int AH = 4;      // query heads per pass
 constexpr int KB = 256;    // keys per workgroup (64 per wave)
-constexpr int CT = 1024;   // threads of a combine workgroup (one per (group, head))
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
+constexpr int CT = 1024;   // threads of a combine workgroup for d > 1024 (256 below)
 
 // The value operands of one channel group for the block kernel.
 struct BlockGroup {
@@ -687,13 +676,15 @@ struct CombineGroup {
 
 // grid: the rows (group * G + head) of channel group 0, then those of group 1 (a fractional
 // rate's second value group; none otherwise).  out rows are opitch floats apart (a channel
-// group of wider output rows: its columns only).
-__global__ __launch_bounds__(CT) void attn_combine_kernel(CombineGroup c0, CombineGroup c1, long rows0,
-                                                          long nkb, long opitch) {
-  constexpr int NW = CT / 64;
-  constexpr int PF = 8;              // loads of each sum issued before the reductions
+// group of wider output rows: its columns only).  CTT threads, CTT / 4 >= d / 4 of the
+// larger group (256 up to d = 1024, else 1024): a thread owns one float4 column of a slice.
+template <int CTT>
+__global__ __launch_bounds__(CTT) void attn_combine_kernel(CombineGroup c0, CombineGroup c1, long rows0,
+                                                           long nkb, long opitch) {
+  constexpr int NW = CTT / 64;
+  constexpr int PF = CTT <= 256 ? 16 : 8;   // loads of each sum issued before the reductions
   extern __shared__ float4 lds4[];   // [slices][d / 4] partial sums, then a[d / 4]
-  __shared__ float red[NW];
+  __shared__ float red[2][NW];
   const bool second = long(blockIdx.x) >= rows0;
   const CombineGroup& cg = second ? c1 : c0;
   const long row = second ? long(blockIdx.x) - rows0 : long(blockIdx.x);
@@ -708,10 +699,10 @@ __global__ __launch_bounds__(CT) void attn_combine_kernel(CombineGroup c0, Combi
   const float* pm = part_m + row * nkb;
   const float* ps = part_s + row * nkb;
   // threads = (float4 column q4, slice sl): a slice sums every nsl-th block (and, for the
-  // inverse rotation, every nsl-th row of Pi_v); d / 4 <= CT, so a thread owns one column
+  // inverse rotation, every nsl-th row of Pi_v)
   const int d4 = d / 4;
-  const int cols = d4 < CT ? d4 : CT;
-  const int nsl = CT / cols;
+  const int cols = d4 < CTT ? d4 : CTT;
+  const int nsl = CTT / cols;
   const int q4 = tid % cols, sl = tid / cols;
   const bool act = sl < nsl;
   const float4* pa = reinterpret_cast<const float4*>(part_acc) + row * nkb * d4;
@@ -728,26 +719,26 @@ __global__ __launch_bounds__(CT) void attn_combine_kernel(CombineGroup c0, Combi
     ppi[i] = okr ? P4[size_t(r) * d4 + q4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  // this thread's first block maximum and sum, in the same round trip as the loads above
+  // this thread's first block maximum and sum, in the same round trip as the loads above;
+  // wave reductions by DPP, then one value per wave through LDS
   const float pm0 = tid < nkb ? pm[tid] : -INFINITY;
   const float ps0 = tid < nkb ? ps[tid] : 0.f;
   float mx = pm0;
-  for (long k = tid + CT; k < nkb; k += CT) mx = fmaxf(mx, pm[k]);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
+  for (long k = tid + CTT; k < nkb; k += CTT) mx = fmaxf(mx, pm[k]);
+  mx = wave_max_dpp(mx);
+  if (lane == 0) red[0][wave] = mx;
   __syncthreads();
-  float M = red[0];
+  float M = red[0][0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
-  __syncthreads();
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[0][i]);
   float sum = tid < nkb ? __expf(pm0 - M) * ps0 : 0.f;
-  for (long k = tid + CT; k < nkb; k += CT) sum += __expf(pm[k] - M) * ps[k];
-  sum = wave_sum(sum);
-  if (lane == 0) red[wave] = sum;
+  for (long k = tid + CTT; k < nkb; k += CTT) sum += __expf(pm[k] - M) * ps[k];
+  sum = wave_sum_dpp(sum);
+  if (lane == 0) red[1][wave] = sum;
   __syncthreads();
   float tot = 0.f;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) tot += red[i];
+  for (int i = 0; i < NW; ++i) tot += red[1][i];
   const float inv = 1.f / tot;
 
   float4* part = lds4;                    // [nsl][d4]
@@ -774,8 +765,10 @@ __global__ __launch_bounds__(CT) void attn_combine_kernel(CombineGroup c0, Combi
     part[sl * d4 + q4] = v;
   }
   __syncthreads();
-  for (int c4 = tid; c4 < d4; c4 += CT) {
+  // slice sums: the reads of a column's slices are independent, so they go out together
+  for (int c4 = tid; c4 < d4; c4 += CTT) {
     float4 v = part[c4];
+#pragma unroll 8
     for (int t = 1; t < nsl; ++t) {
       const float4 x = part[t * d4 + c4];
       v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
@@ -810,8 +803,9 @@ __global__ __launch_bounds__(CT) void attn_combine_kernel(CombineGroup c0, Combi
   }
   __syncthreads();
   float4* o4 = reinterpret_cast<float4*>(out + row * opitch);
-  for (int j4 = tid; j4 < d4; j4 += CT) {
+  for (int j4 = tid; j4 < d4; j4 += CTT) {
     float4 v = part[j4];
+#pragma unroll 8
     for (int t = 1; t < nsl; ++t) {
       const float4 x = part[t * d4 + j4];
       v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
@@ -908,9 +902,22 @@ hipError_t launch_blocks_one(const ValueGroup& v, long blocks, const float* logi
   return e != hipSuccess ? e : hipGetLastError();
 }
 
-size_t combine_lds_bytes(int d) {
-  const int d4 = d / 4, cols = d4 < CT ? d4 : CT, nsl = CT / cols;
-  return (size_t(nsl) * d4 + d4) * 16;
+// One combine launch over rows (rows0 of group c0, then rows - rows0 of c1); the thread count
+// follows the larger group's d.
+hipError_t launch_combine(const CombineGroup& c0, const CombineGroup& c1, long rows, long rows0, long nkb,
+                          long opitch, hipStream_t s) {
+  const int dmax = std::max(c0.d, rows > rows0 ? c1.d : c0.d);
+  const int ct = dmax / 4 <= 256 ? 256 : CT;
+  size_t lds = 0;
+  for (const int d : {c0.d, rows > rows0 ? c1.d : c0.d}) {
+    const int d4 = d / 4, cols = d4 < ct ? d4 : ct, nsl = ct / cols;
+    lds = std::max(lds, (size_t(nsl) * d4 + d4) * 16);
+  }
+  if (ct == 256)
+    hipLaunchKernelGGL(attn_combine_kernel<256>, dim3(unsigned(rows)), dim3(256), lds, s, c0, c1, rows0, nkb, opitch);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<CT>, dim3(unsigned(rows)), dim3(CT), lds, s, c0, c1, rows0, nkb, opitch);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -926,9 +933,7 @@ hipError_t launch_attention_values(const void* params_v, int d, int b_v, const f
   hipError_t e = launch_blocks_one(v, blocks, logits, G, T, scale, s);
   if (e != hipSuccess) return e;
   const long rows = long(groups) * G;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT), combine_lds_bytes(d), s, v.comb,
-                     v.comb, rows, nkb, long(opitch > 0 ? opitch : d));
-  return hipGetLastError();
+  return launch_combine(v.comb, v.comb, rows, rows, nkb, long(opitch > 0 ? opitch : d), s);
 }
 
 namespace {
@@ -979,9 +984,7 @@ hipError_t launch_attention_fused(const void* params_v, int b_k, bool prod, cons
   }
   if (e != hipSuccess) return e;
   const long rows = long(groups) * G;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(rows)), dim3(CT), combine_lds_bytes(d), s, v.comb,
-                     v.comb, rows, nkb, long(d));
-  return hipGetLastError();
+  return launch_combine(v.comb, v.comb, rows, rows, nkb, long(d), s);
 }
 
 hipError_t launch_attention_values_split(const void* params_v0, const void* params_v1, int d0, int d1,
@@ -1007,10 +1010,7 @@ hipError_t launch_attention_values_split(const void* params_v0, const void* para
   }
   if (e != hipSuccess) return e;
   const long rows = long(groups) * G;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(2 * rows)), dim3(CT),
-                     std::max(combine_lds_bytes(d0), combine_lds_bytes(d1)), s, v0.comb, v1.comb, rows,
-                     nkb, long(d0) + d1);
-  return hipGetLastError();
+  return launch_combine(v0.comb, v1.comb, 2 * rows, rows, nkb, long(d0) + d1, s);
 }
 
 namespace {
@@ -1074,9 +1074,7 @@ hipError_t launch_attention_fused_split(const void* params_v0, const void* param
   }
   if (e != hipSuccess) return e;
   const long rows = long(groups) * G;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(2 * rows)), dim3(CT), combine_lds_bytes(d0), s, v0.comb,
-                     v1.comb, rows, nkb, long(d0) + d1);
-  return hipGetLastError();
+  return launch_combine(v0.comb, v1.comb, 2 * rows, rows, nkb, long(d0) + d1, s);
 }
 
 bool attention_grid_fits(int64_t groups, int64_t G, int64_t T) {
