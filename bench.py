@@ -219,6 +219,17 @@ def time_steps(torch, fn, R: int, K: int) -> float:
     return (time.perf_counter() - t0) * 1e3 / K
 
 
+def calibration_copy(torch, dev, mib: int) -> None:
+    """A device copy of known size (mib MiB each way) in the run, for scaling HBM byte counters."""
+    a = torch.empty(mib * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    bb = torch.empty_like(a)
+    a.fill_(1.0)
+    torch.cuda.synchronize()
+    bb.copy_(a)
+    torch.cuda.synchronize()
+    del a, bb
+
+
 def source_hash(*names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -227,17 +238,19 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_file: str, workload: str):
+def traffic_from_profiles(kernel_files, workload: str):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json, keyed
-    "<source file>:<workload>"), if they were taken on the current source; else None."""
+    "<source file[+source file...]>:<workload>"), if they were taken on the current sources;
+    else None."""
+    files = (kernel_files,) if isinstance(kernel_files, str) else tuple(kernel_files)
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(f"{kernel_file}:{workload}")
+        rec = json.load(open(path)).get(f"{'+'.join(files)}:{workload}")
     except Exception:
         return None
-    if not rec or rec.get("source_hash") != source_hash(kernel_file):
+    if not rec or rec.get("source_hash") != source_hash(*files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -378,13 +391,7 @@ def bench_search(args):
         tq.tq_topk(params, d, b, q, codes, nu, gamma, n, k, tq.TQ_EST_PROD, idx, score, ws)
 
     if args.calibrate_copy_mb:   # a device copy of known size, for scaling HBM byte counters
-        a = torch.empty(args.calibrate_copy_mb * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-        bb = torch.empty_like(a)
-        a.fill_(1.0)
-        torch.cuda.synchronize()
-        bb.copy_(a)
-        torch.cuda.synchronize()
-        del a, bb
+        calibration_copy(torch, dev, args.calibrate_copy_mb)
 
     for _ in range(max(args.warmup, 1)):
         quantize()
@@ -576,6 +583,8 @@ def bench_attention(args):
     for i in range(max(args.warmup, 1)):
         attend(i % R)
     torch.cuda.synchronize()
+    if args.calibrate_copy_mb:
+        calibration_copy(torch, dev, args.calibrate_copy_mb)
 
     K = args.steps
     ms_step = time_steps(torch, attend, R, K)
@@ -604,10 +613,12 @@ def bench_attention(args):
         "roofline": {
             "kernel": "tq_attention (query prep + fused score/softmax/value blocks + combine)",
             "bound": "hbm", "achieved": a_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": a_gbs / HBM_PEAK_GBS, "traffic": None,
+            "frac": a_gbs / HBM_PEAK_GBS,
+            "traffic": traffic_from_profiles(("score.hip", "score_tile.h", "attention.hip"), "decode_attention"),
             "note": f"algorithmic bytes per key: {d // 8 * b_k} B key codes + 8 B nu, gamma + "
                     f"{d // 8 * (b_v - 1)} B value codes + 4 B nu; the block partials in the "
-                    "workspace are implementation traffic; timed over the whole call",
+                    "workspace are implementation traffic; timed over the whole call; traffic = "
+                    "counter-measured bytes per call (query prep + block kernel + combine)",
         },
         "value_quantize": {"ms": vq_ms, "vectors_per_s": n / (vq_ms * 1e-3),
                            "hbm_gbs": vq_bytes / (vq_ms * 1e-3) / 1e9},
@@ -741,6 +752,8 @@ def bench_fractional(args):
             scan((r - 1) % R)
         torch.cuda.current_stream().wait_stream(side)
 
+    if args.calibrate_copy_mb:
+        calibration_copy(torch, dev, args.calibrate_copy_mb)
     K = args.steps
     plain_ms = time_steps(torch, lambda r: (quantize(r), score(r)), R, K)
     serial_ms = time_steps(torch, serial, R, K)
@@ -762,14 +775,15 @@ def bench_fractional(args):
     rq = {"kernel": "tq_quantize_split (fused d = 128 encoder, split mode: both groups in one pass)",
           "bound": "hbm",
           "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_gbs / HBM_PEAK_GBS,
-          "traffic": None,
+          "traffic": traffic_from_profiles("quantize.hip", f"fractional_kv_{args.rate}"),
           "note": f"algorithmic bytes per vector: {d * 2} B bf16 key in, {code_bytes} B codes, nu and gamma "
                   f"of both groups out; {q_flops / n:.0f} flop per vector"}
     rs = {"kernel": "tq_score_ip_split (" + ("integer MFMA scan, both channel groups per key tile" if int_path
                                              else "general scoring path, two channel groups") + ")",
           "bound": "hbm",
           "achieved": s_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": s_gbs / HBM_PEAK_GBS,
-          "traffic": None,
+          "traffic": traffic_from_profiles(("score_split.hip", "score_tile.h"), f"fractional_kv_{args.rate}")
+          if int_path else None,
           "note": f"algorithmic bytes per key: {code_bytes} B codes, nu and gamma of both groups in; "
                   + ("fp32 logits written once" if int_path
                      else "fp32 logits written and, by the second group, read back")}
@@ -939,13 +953,7 @@ def bench_kv(args):
                                 logits[r], ws)
 
     if args.calibrate_copy_mb:
-        a = torch.empty(args.calibrate_copy_mb * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-        bb = torch.empty_like(a)
-        a.fill_(1.0)
-        torch.cuda.synchronize()
-        bb.copy_(a)
-        torch.cuda.synchronize()
-        del a, bb
+        calibration_copy(torch, dev, args.calibrate_copy_mb)
 
     for r in range(R):
         quantize(r)
