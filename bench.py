@@ -313,7 +313,8 @@ def cpu_baseline_search(w, b, seconds: float):
     basis = gen.lowrank_basis(d, rank, w.cfg)
     q = gen.lowrank_queries(w.nq, d, rank, snr, cfg=w.cfg).astype(np.float64)
     blocks, vectors, pairs, elapsed = 0, 0, 0, 0.0
-    while elapsed < seconds and vectors < w.n:
+    # one sample per seeded block (its first 2048 vectors), while blocks remain
+    while elapsed < seconds and blocks * gen.LOWRANK_BLOCK < w.n:
         x = gen.lowrank_block(blocks, d, rank, snr, w.cfg, 0, basis, n_total=w.n).astype(np.float64)
         x = x[:2048]
         t0 = time.perf_counter()
