@@ -119,7 +119,9 @@ def _oracle_parts(stk, stv, d, q, q_bf16, ck, nk, gk, cv, nv, groups, G, T, mode
     (128, 3, 2, 12, 1333, True, tq.TQ_EST_PROD, ""),
     (128, 4, 4, 4, 256, False, tq.TQ_EST_MSE, ""),
     (128, 2, 4, 4, 65, True, tq.TQ_EST_PROD, ""),
-    (192, 3, 4, 2, 333, True, tq.TQ_EST_PROD, "sphere+orth")])
+    (192, 3, 4, 2, 333, True, tq.TQ_EST_PROD, "sphere+orth"),
+    (1024, 3, 3, 4, 300, False, tq.TQ_EST_PROD, ""),     # the largest d of the four-wave combine
+    (1536, 4, 3, 4, 300, False, tq.TQ_EST_PROD, "")])    # d > 1024: the 1024-thread combine
 def test_attention_parity(d, b_k, b_v, G, T, q_bf16, mode, variant):
     groups = 3
     scale = 1.0 / math.sqrt(d)
