@@ -55,33 +55,38 @@ def test_quantize_f32_nonunit(b):
     U.assert_codes_ok(rep)
 
 
-def test_quantize_zero_vectors_and_empty():
-    st = U.make_setup(128, 4, cfg=6)
-    x = gen.unit_sphere(40, 128, cfg=6, role=gen.ROLE_DATA)
+@pytest.mark.parametrize("d", [128, 192])     # the fused encoder and the tiled one
+def test_quantize_zero_vectors_and_empty(d):
+    st = U.make_setup(d, 4, cfg=6)
+    x = gen.unit_sphere(40, d, cfg=6, role=gen.ROLE_DATA)
     x[[0, 7, 39]] = 0.0
     codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
-    rep = U.compare_codes(st, U.host64(x, False), U.codes_np(codes, 40, 128, 4),
+    rep = U.compare_codes(st, U.host64(x, False), U.codes_np(codes, 40, d, 4),
                           nu.cpu().numpy(), gamma.cpu().numpy())
     U.assert_codes_ok(rep)
     assert nu.cpu().numpy()[[0, 7, 39]].tolist() == [0.0, 0.0, 0.0]
     # zero vector: all indices L/2 (u = 0 sits on the middle threshold, upper cell)
     assert np.all(rep["idx"][[0, 7, 39]] == 4)
     # n = 0: no-op
-    e = torch.empty((0, 128), dtype=torch.float32, device=U.DEV)
+    e = torch.empty((0, d), dtype=torch.float32, device=U.DEV)
     z = torch.empty(0, dtype=torch.int32, device=U.DEV)
     f = torch.empty(0, dtype=torch.float32, device=U.DEV)
-    tq.tq_quantize(st.params, 128, 4, e, z, f, f)
+    tq.tq_quantize(st.params, d, 4, e, z, f, f)
 
 
-def test_quantize_nonfinite_inputs_do_not_fault():
-    st = U.make_setup(128, 3, cfg=7)
-    x = gen.unit_sphere(64, 128, cfg=7, role=gen.ROLE_DATA)
+@pytest.mark.parametrize("d", [128, 192])
+def test_quantize_nonfinite_inputs_do_not_fault(d):
+    # a vector with a NaN or an infinite coordinate gets unspecified codes; every other vector
+    # of the launch is encoded as usual
+    st = U.make_setup(d, 3, cfg=7)
+    x = gen.unit_sphere(300, d, cfg=7, role=gen.ROLE_DATA)
     x[3, 5] = np.nan
     x[9, 0] = np.inf
+    x[290, d - 1] = -np.inf
     codes, nu, gamma = U.gpu_quantize(st, U.to_device(x, False))
-    good = np.array([i not in (3, 9) for i in range(64)])
+    good = np.array([i not in (3, 9, 290) for i in range(300)])
     rep = U.compare_codes(st, U.host64(x[good], False),
-                          U.codes_np(codes, 64, 128, 3)[good], nu.cpu().numpy()[good],
+                          U.codes_np(codes, 300, d, 3)[good], nu.cpu().numpy()[good],
                           gamma.cpu().numpy()[good])
     U.assert_codes_ok(rep)
 
