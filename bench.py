@@ -907,6 +907,8 @@ def bench_kv(args):
     b = args.bits or w.bits[0]
     if b not in w.bits:
         raise SystemExit(f"{w.name} is defined for b in {w.bits}")
+    # counter records of a workload defined at several b are kept per b
+    traffic_key = w.name if len(w.bits) == 1 else f"{w.name}_b{b}"
     groups, G, T = w.groups, w.G, w.T
     n = w.n_keys
 
@@ -1056,7 +1058,7 @@ def bench_kv(args):
             "kernel": "quantize_d128 (tq_quantize)",
             "bound": "hbm", "achieved": q_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": q_gbs / HBM_PEAK_GBS,
-            "traffic": traffic_from_profiles("quantize.hip", w.name),
+            "traffic": traffic_from_profiles("quantize.hip", traffic_key),
             "note": f"algorithmic bytes per vector: {d * 2} B bf16 key in, {d // 8 * b} B codes and 8 B "
                     f"nu, gamma out; at 4 d^2 flop per vector the arithmetic intensity "
                     f"({4 * d * d / (d * 2 + d // 8 * b + 8):.0f} flop/B) is below the MFMA ridge "
@@ -1075,7 +1077,7 @@ def bench_kv(args):
         "roofline_score": {
             "kernel": "score_qprep + score (tq_score_ip)",
             "bound": "hbm", "achieved": s_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": s_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profiles("score.hip", w.name),
+            "frac": s_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profiles("score.hip", traffic_key),
             "note": f"the whole call (query prep + scan) over {R} code sets of "
                     f"{score_in_bytes / 2**20:.0f} MiB cycled per launch",
         },
