@@ -21,11 +21,13 @@ or 3.5 bits per channel): channels 0..63 at the higher b and 64..127 at the lowe
 group its own TurboQuant instance; a step is tq_quantize_split + the split scoring
 (tq_score_split_prepare on a second stream beside the quantize, then
 tq_score_ip_split_prepared), as the KV workloads split tq_score_ip.
+--workload toy: 4096 float32 unit vectors in R^128 at b = 4 and all 64 x 4096 logits of 64
+unit queries (latency-bound; its replicas fit the MALL, so it is reported, not held to a roofline).
 --workload ubench: achievable HBM and MFMA rates of the GPU.
 
 Prints one JSON line.  Kernel durations come from HIP events recorded on the stream the
-kernels run on; every per-launch timing cycles through more than 512 MB of distinct
-inputs, so that the 256 MB MALL does not serve them from cache.
+kernels run on; every per-launch timing of the other workloads cycles through more than
+512 MB of distinct inputs, so that the 256 MB MALL does not serve them from cache.
 """
 from __future__ import annotations
 
@@ -54,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_context",
                     choices=["long_context", "decode_layer", "decode_batch16", "embedding_search",
-                             "decode_attention", "fractional_kv", "ubench"])
+                             "decode_attention", "fractional_kv", "toy", "ubench"])
     ap.add_argument("--rate", type=float, default=3.5, help="fractional_kv: bits per channel (2.5 or 3.5)")
     ap.add_argument("--bits", type=int, default=0,
                     help="b of workloads defined at several (embedding_search: 4, decode_batch16: 2)")
@@ -1108,6 +1110,94 @@ def bench_kv(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_toy(args):
+    """The toy configuration: 4096 float32 unit vectors in R^128 at b = 4 and 64 unit queries; a
+    step quantizes the vectors and computes all 64 x 4096 logits (one group of 64 query heads).
+    At 3.7 MB per step it is launch- and latency-bound: reported, not held to a roofline."""
+    import torch
+
+    import kv_cache_embedding_amd as tq
+    import oracle
+    from workloads import gen
+
+    w = gen.TOY
+    dev = torch.device("cuda:0")
+    d, b, n, nq = w.d, w.bits[0], w.n, w.nq
+    Pi = gen.haar_orthogonal(d, w.cfg)
+    S = gen.gaussian_matrix(d, d, w.cfg)
+    c, t = tq.tq_codebook_build(b - 1, d)
+    params = torch.empty(tq.tq_params_bytes(d, b), dtype=torch.uint8, device=dev)
+    tq.tq_prepare(d, b, Pi, S, c, t, params)
+    xh = gen.unit_sphere(n, d, cfg=w.cfg, role=gen.ROLE_DATA)
+    qh = gen.unit_sphere(nq, d, cfg=w.cfg, role=gen.ROLE_QUERY)
+    R = 64
+    xs = [torch.from_numpy(xh).to(dev) for _ in range(R)]
+    q = torch.from_numpy(qh).to(dev)
+    codes = [torch.empty(n * d // 32 * b, dtype=torch.int32, device=dev) for _ in range(R)]
+    nus = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
+    gms = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
+    logits = [torch.empty(nq * n, dtype=torch.float32, device=dev) for _ in range(R)]
+    ws = torch.empty(tq.tq_score_ws_bytes(d, b, 1, nq, n), dtype=torch.uint8, device=dev)
+
+    def quantize(r):
+        tq.tq_quantize(params, d, b, xs[r], codes[r], nus[r], gms[r])
+
+    def score(r):
+        tq.tq_score_ip(params, d, b, q, codes[r], nus[r], gms[r], 1, nq, n, tq.TQ_EST_PROD, logits[r], ws)
+
+    def step(r):
+        quantize(r)
+        score(r)
+
+    for i in range(max(args.warmup, 1)):
+        step(i % R)
+    torch.cuda.synchronize()
+    K = args.steps
+    ms_step = time_steps(torch, step, R, K)
+    q_ms = time_per_launch(torch, quantize, R, K)
+    s_ms = time_per_launch(torch, score, R, K)
+    step_bytes = n * (d * 4 + d // 8 * b + 8) + n * (d // 8 * b + 8) + nq * n * 4
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": "quantized-key logits/s (GB/s vs HBM peak) + vectors quantized/s, 1 MI355X",
+        "value": nq * n / (ms_step * 1e-3),
+        "unit": "logits/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0, I) vectors and queries scaled to unit length, float32; random "
+                "rotation and QJL matrix)",
+        "config": {"workload": f"toy: {n} x d={d} float32 unit vectors, b={b}, {nq} unit queries, all "
+                               f"{nq} x {n} logits", "n": n, "d": d, "bits": b, "queries": nq, "replicas": R},
+        "roofline": {
+            "kernel": "tq_quantize + tq_score_ip (whole step)",
+            "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "note": f"algorithmic bytes of a step: float32 vectors in, codes + nu + gamma out and back in, "
+                    f"fp32 logits out ({step_bytes / 1e6:.2f} MB); at this size two kernel launches and one "
+                    "memory round trip each set the time, so the fraction is not a bandwidth figure "
+                    f"(the {R} replicas fit the MALL)",
+        },
+        "quantize": {"ms": q_ms, "vectors_per_s": n / (q_ms * 1e-3)},
+        "score": {"ms": s_ms, "logits_per_s": nq * n / (s_ms * 1e-3)},
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        c64, t64 = oracle.codebook(b - 1, d)
+        r = oracle.quantize(xh.astype(np.float64), Pi, S, c64, t64)
+        oracle.estimate_ip(qh.astype(np.float64), Pi, S, r["idx"], r["z"], r["nu"], r["gamma"], c64)
+        el = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        result["cpu_baseline"] = {"value": nq * n / el, "unit": "logits/s", "cores": int(cores),
+                                  "cpu_model": cpu_model(), "kind": "oracle",
+                                  "sample": f"the whole workload ({n} vectors quantized, {nq * n} logits), "
+                                            f"float64 NumPy oracle, {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -1115,7 +1205,8 @@ def main():
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     run = {"embedding_search": bench_search, "decode_attention": bench_attention,
-           "fractional_kv": bench_fractional, "ubench": bench_ubench}.get(args.workload, bench_kv)
+           "fractional_kv": bench_fractional, "ubench": bench_ubench,
+           "toy": bench_toy}.get(args.workload, bench_kv)
     run(args)
 
 
